@@ -1,0 +1,204 @@
+/*
+ * kda_oracle.c -- fp64 CPU oracle for Kimi Delta Attention (KDA).
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this library.  It shares no code, header or constant
+ * with the HIP kernels of the package; it is plain C99 with OpenMP over the
+ * independent (sequence, head) units.
+ *
+ * What it computes (the plain definition, token by token, in double):
+ *   per (sequence n, head h) the state S is a dk x dv matrix, and for every
+ *   token t of the sequence, in order:
+ *     a   = exp(g_t)                      per-key-channel decay
+ *     S   = diag(a) S                     decay the rows (key channels)
+ *     p   = S^T k_t                       the state's prediction for k_t
+ *     u   = beta_t (v_t - p)              delta-rule correction
+ *     S   = S + k_t u^T                   write
+ *     y_t = sigmoid(z_t) * (scale S^T q_t)  read after the write, then gate
+ *
+ * Sources (pages, cited by title and section):
+ *   - "Kimi K3 second-pass study ledger" (llm-atlas research/K3_RESEARCH.md),
+ *     section 1, question ledger: row Q04 (fixed-shape recurrent state,
+ *     channel-wise decay, delta-rule write), row Q05 (before writing a new
+ *     value, subtract what the state already predicts for the current key),
+ *     row Q07 (decode is an O(1) state update), row Q08 (input-dependent,
+ *     full-rank output gate on the readout).
+ *   - "Kimi K3 plain-language guide", section 5.1 (a fixed-size recurrent
+ *     state replaces a growing KV cache; the update is serial).
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   decay before the prediction; decay on the key channels (rows of S);
+ *   read after the write; the gate is sigmoid of a logit z with no
+ *   normalisation in between; beta and g arrive as values (beta in [0,1],
+ *   g a natural-log decay, g = -inf allowed and gives a = 0).
+ *
+ * Parity unpinned: the report's own equation for KDA is cited by the ledger
+ * but not printed on the pages, so the readings above cannot be checked
+ * against it.  Everything else is pinned by the tests (exact brute force,
+ * closed forms, invariants).
+ *
+ * Layouts (row-major, all contiguous):
+ *   q, k, g    [T_total, H, dk]      v, z, out  [T_total, H, dv]
+ *   beta       [T_total, H]          state      [N, H, dk, dv]
+ *   cu_seqlens [N + 1], int64, cu[0] = 0, non-decreasing, cu[N] = T_total.
+ * Inputs are either double or float (in_f32 = 1); float inputs are widened
+ * exactly to double on read.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double rd(const void *p, int in_f32, int64_t i)
+{
+    return in_f32 ? (double)((const float *)p)[i] : ((const double *)p)[i];
+}
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* One token of the recurrence on the state S (dk x dv, row-major).
+ * qo, ko, vo, bo: element offsets of this token-head in the inputs.
+ * a, p, u: scratch of length dk, dv, dv.  Writes dv outputs to y. */
+static void kda_token(const void *q, const void *k, const void *v, const void *g,
+                      const void *beta, const void *z, int in_f32,
+                      int64_t qo, int64_t vo, int64_t bo, int64_t dk, int64_t dv,
+                      double scale, double *S, double *a, double *p, double *u,
+                      double *y)
+{
+    int64_t i, j;
+    for (i = 0; i < dk; ++i)
+        a[i] = exp(rd(g, in_f32, qo + i));
+    /* decay: every row i (key channel) scales by a[i] */
+    for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j)
+            S[i * dv + j] *= a[i];
+    /* prediction of the decayed state for the current key */
+    for (j = 0; j < dv; ++j)
+        p[j] = 0.0;
+    for (i = 0; i < dk; ++i) {
+        double ki = rd(k, in_f32, qo + i);
+        for (j = 0; j < dv; ++j)
+            p[j] += S[i * dv + j] * ki;
+    }
+    /* delta-rule correction */
+    double b = rd(beta, in_f32, bo);
+    for (j = 0; j < dv; ++j)
+        u[j] = b * (rd(v, in_f32, vo + j) - p[j]);
+    /* write */
+    for (i = 0; i < dk; ++i) {
+        double ki = rd(k, in_f32, qo + i);
+        for (j = 0; j < dv; ++j)
+            S[i * dv + j] += ki * u[j];
+    }
+    /* read by the query after the write, then the output gate */
+    for (j = 0; j < dv; ++j)
+        p[j] = 0.0;
+    for (i = 0; i < dk; ++i) {
+        double qi = rd(q, in_f32, qo + i);
+        for (j = 0; j < dv; ++j)
+            p[j] += S[i * dv + j] * qi;
+    }
+    for (j = 0; j < dv; ++j)
+        y[j] = sigmoid(rd(z, in_f32, vo + j)) * (scale * p[j]);
+}
+
+/* Whole-sequence forward.  init_state may be NULL (zeros); final_state may
+ * be NULL (not written); out may be NULL (not written).
+ * Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
+int kda_oracle_forward(const void *q, const void *k, const void *v, const void *g,
+                       const void *beta, const void *z, int in_f32,
+                       const double *init_state, double *out, double *final_state,
+                       const int64_t *cu_seqlens, int64_t n_seq, int64_t H,
+                       int64_t dk, int64_t dv, double scale, int n_threads)
+{
+    if (!q || !k || !v || !g || !beta || !z || !cu_seqlens)
+        return -1;
+    if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    for (int64_t n = 0; n < n_seq; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n] || cu_seqlens[0] != 0)
+            return -1;
+    int64_t units = n_seq * H;
+    int failed = 0;
+    if (n_threads <= 0)
+        n_threads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+    for (int64_t unit = 0; unit < units; ++unit) {
+        int64_t n = unit / H, h = unit % H;
+        double *S = (double *)malloc(sizeof(double) * dk * dv);
+        double *a = (double *)malloc(sizeof(double) * dk);
+        double *p = (double *)malloc(sizeof(double) * dv);
+        double *u = (double *)malloc(sizeof(double) * dv);
+        double *y = (double *)malloc(sizeof(double) * dv);
+        if (!S || !a || !p || !u || !y) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            const double *S0 = init_state ? init_state + unit * dk * dv : NULL;
+            for (int64_t e = 0; e < dk * dv; ++e)
+                S[e] = S0 ? S0[e] : 0.0;
+            for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
+                int64_t qo = (t * H + h) * dk, vo = (t * H + h) * dv, bo = t * H + h;
+                kda_token(q, k, v, g, beta, z, in_f32, qo, vo, bo, dk, dv, scale,
+                          S, a, p, u, y);
+                if (out)
+                    memcpy(out + vo, y, sizeof(double) * dv);
+            }
+            if (final_state)
+                memcpy(final_state + unit * dk * dv, S, sizeof(double) * dk * dv);
+        }
+        free(S);
+        free(a);
+        free(p);
+        free(u);
+        free(y);
+    }
+    return failed ? -2 : 0;
+}
+
+/* One decode step for N independent sequences: the body of the recurrence
+ * applied once to state [N, H, dk, dv] in place.  q, k, g [N, H, dk];
+ * v, z, out [N, H, dv]; beta [N, H]. */
+int kda_oracle_decode_step(const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const void *z, int in_f32, double *state,
+                           double *out, int64_t N, int64_t H, int64_t dk, int64_t dv,
+                           double scale, int n_threads)
+{
+    if (!q || !k || !v || !g || !beta || !z || !state || !out)
+        return -1;
+    if (N < 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    int failed = 0;
+    if (n_threads <= 0)
+        n_threads = 1;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(n_threads)
+    for (int64_t unit = 0; unit < N * H; ++unit) {
+        double *a = (double *)malloc(sizeof(double) * dk);
+        double *p = (double *)malloc(sizeof(double) * dv);
+        double *u = (double *)malloc(sizeof(double) * dv);
+        if (!a || !p || !u) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            kda_token(q, k, v, g, beta, z, in_f32, unit * dk, unit * dv, unit, dk, dv,
+                      scale, state + unit * dk * dv, a, p, u, out + unit * dv);
+        }
+        free(a);
+        free(p);
+        free(u);
+    }
+    return failed ? -2 : 0;
+}
+
+/* Threads OpenMP would use by default (for reporting the CPU baseline). */
+int kda_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
