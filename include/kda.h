@@ -1,0 +1,143 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library,
+ * libkda.so.
+ *
+ * KDA keeps, per sequence and head, a fixed-shape recurrent state
+ * S (dk x dv, fp32).  Each token decays the rows of S by exp(g) (one log-decay
+ * per key channel), subtracts the state's prediction for the current key
+ * before writing the new value (delta rule), is read by the query after the
+ * write, and the readout goes through an input-dependent sigmoid gate:
+ *
+ *     S   <- diag(exp(g_t)) S
+ *     u   =  beta_t (v_t - S^T k_t)
+ *     S   <- S + k_t u^T
+ *     y_t =  sigmoid(z_t) * (scale * S^T q_t)
+ *
+ * Sources: "Kimi K3 second-pass study ledger" (llm-atlas K3_RESEARCH.md),
+ * section 1 rows Q04 (fixed-shape state, channel-wise decay, delta-rule
+ * write), Q05 (subtract the existing prediction for the key), Q06 (log-decay
+ * floor -5), Q07 (chunkwise-parallel prefill with the state passed between
+ * chunks; O(1) decode), Q08 (input-dependent output gate); "Kimi K3 report
+ * reveals training and systems stack", confirmed list (FlashKDA, 16-token
+ * tiles).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates no device or host memory and keeps no global state;
+ *     calls are re-entrant.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns without synchronising.  Arguments are validated on the host
+ *     before anything is launched: on any error a status code is returned and
+ *     nothing is written.  A failed launch returns KDA_ERR_HIP.
+ *   - Layouts are row-major and contiguous.  Element types: `dt` gives the
+ *     type of q, k, v, g, beta, gate and out; the state is always fp32.
+ *   - Values are not range-checked on the device.  Documented preconditions:
+ *     beta in [0, 1]; for the chunked forward g must be finite with
+ *     g >= -5 (KDA_G_MIN), which bounds the reciprocal of the cumulative decay
+ *     inside a 16-token subtile by exp(80) so the subtile products stay in the
+ *     bf16/fp32 range ("Kimi K3 second-pass study ledger", section 1 row Q06).
+ *     The decode step has no lower bound (g = -inf gives a decay of 0).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_G_MIN (-5.0f)
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL                 */
+    KDA_ERR_BAD_SHAPE = 2,          /* negative/zero size, B > 1 with cu_seqlens  */
+    KDA_ERR_BAD_DTYPE = 3,          /* dt is not a kda_dtype value                */
+    KDA_ERR_UNSUPPORTED = 4,        /* (dt, dk, dv, chunk) outside the supported set */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 5,/* workspace_bytes below the required size    */
+    KDA_ERR_HIP = 6                 /* a HIP launch or runtime call failed        */
+} kda_status;
+
+typedef enum {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kda_status_str(kda_status s);
+
+/* Supported (dt, dk, dv, chunk) combinations of kda_chunk_fwd:
+ *   KDA_BF16, dk = dv = 128, chunk = 64 (four 16-token subtiles; bf16 matrix
+ *            cores, fp32 accumulation and fp32 state)
+ *   KDA_F32,  dk = dv = 16,  chunk = 16 (fp32 arithmetic throughout)
+ * kda_decode_step supports both dtypes with dk = dv in {16, 128}.
+ * Returns 1 if supported, 0 otherwise. */
+int kda_chunk_fwd_supported(kda_dtype dt, int dk, int dv, int chunk);
+int kda_decode_step_supported(kda_dtype dt, int dk, int dv);
+
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 when none
+ * is needed, (size_t)-1 for an unsupported or invalid combination).
+ * `N` is the number of sequences; `varlen` is 1 when cu_seqlens will be
+ * passed.  The size depends only on the arguments, not on cu_seqlens'
+ * contents: with cu_seqlens the bound floor(T / chunk) + N chunk slots is
+ * used for every head. */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv, int chunk,
+                                     kda_dtype dt, int varlen);
+
+/* Chunkwise-parallel KDA forward (prefill / training forward).
+ *
+ * The sequence is cut into chunks of `chunk` tokens; inside a chunk the
+ * tokens are processed with dense matrix products, and the state is passed
+ * recurrently from one chunk to the next ("Kimi K3 second-pass study
+ * ledger", section 1 row Q07).  Chunking restarts at every sequence start;
+ * the last chunk of a sequence may be partial.  The result equals the
+ * token-by-token recurrence above up to rounding.
+ *
+ *   q, k, g  [B, T, H, dk]   dt          (g: natural-log decay, see above)
+ *   v, gate  [B, T, H, dv]   dt          (gate: logits z; sigmoid applied here)
+ *   beta     [B, T, H]       dt
+ *   init_state  [N, H, dk, dv] fp32, or NULL for a zero initial state
+ *   out         [B, T, H, dv]  dt, written (rounded to nearest even for bf16)
+ *   final_state [N, H, dk, dv] fp32, or NULL (not written); it may alias
+ *               init_state (in-place update of a state cache)
+ *   cu_seqlens  NULL: B sequences of length T each, N must equal B.
+ *               non-NULL: device int32 [N + 1], B must be 1; sequence n is
+ *               tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the packed T.
+ *               Preconditions (not checked): cu[0] = 0, non-decreasing,
+ *               cu[N] = T.  Zero-length sequences are allowed; their final
+ *               state equals their initial state.
+ *   scale       multiplies the readout S^T q (1.0 for the plain form)
+ *   workspace   device memory of at least kda_chunk_fwd_workspace_bytes(...)
+ *               bytes, 256-byte aligned; contents on entry are ignored and
+ *               left undefined.  May be NULL when the size is 0.
+ * Overlapping calls that share a workspace race; out must not alias any input.
+ */
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const void *gate, const float *init_state,
+                         void *out, float *final_state, const int32_t *cu_seqlens, int B, int T,
+                         int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One O(1) recurrent decode step for N independent sequences, updating the
+ * state in place ("Kimi K3 second-pass study ledger", section 1 row Q07;
+ * section 8 device row, fused decode): decay, prediction, correction, write,
+ * read and gate in one pass over each state slice.
+ *
+ *   q, k, g  [N, H, dk]  dt        v, gate, out [N, H, dv]  dt
+ *   beta     [N, H]      dt
+ *   state    [N, H, dk, dv] fp32, read and overwritten in place
+ * out must not alias the state or any input.
+ */
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const void *gate, float *state, void *out, int N,
+                           int H, int dk, int dv, float scale, kda_dtype dt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,225 @@
+"""Kimi Delta Attention (KDA) for MI355X (gfx950): Python binding of libkda.so.
+
+The binding only marshals arguments: it checks tensor shapes, dtypes and
+devices, allocates outputs and the workspace with PyTorch, and calls the C ABI
+declared in ``include/kda.h`` on the current HIP stream.  Every step of the
+computation runs in the HIP kernels of ``libkda.so``; there is no fallback.
+If the library is missing the calls raise ``KdaLibraryError``.
+
+Entry points (names follow the C ABI):
+  chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
+            cu_seqlens=None, chunk=None, scale=1.0) -> (out, final_state)
+  decode_step(q, k, v, g, beta, gate, state, scale=1.0) -> out   (state in place)
+  chunk_fwd_workspace_bytes(...), chunk_fwd_supported(...), decode_step_supported(...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "KdaError", "KdaLibraryError", "chunk_fwd", "decode_step", "chunk_fwd_workspace_bytes",
+    "chunk_fwd_supported", "decode_step_supported", "library_path", "load_library",
+    "KDA_F32", "KDA_BF16", "G_MIN",
+]
+
+KDA_F32 = 0
+KDA_BF16 = 1
+G_MIN = -5.0
+_DEFAULT_CHUNK = {KDA_F32: 16, KDA_BF16: 64}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libkda.so"
+_lib = None
+
+
+class KdaError(RuntimeError):
+    """A libkda call returned an error status."""
+
+
+class KdaLibraryError(ImportError):
+    """libkda.so is missing or cannot be loaded."""
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+_SIGNATURES = {
+    "kda_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "kda_chunk_fwd_supported": ([ctypes.c_int] * 4, ctypes.c_int),
+    "kda_decode_step_supported": ([ctypes.c_int] * 3, ctypes.c_int),
+    "kda_chunk_fwd_workspace_bytes": ([ctypes.c_int] * 9, ctypes.c_size_t),
+    "kda_chunk_fwd": ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
+                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "kda_decode_step": ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
+                        ctypes.c_void_p], ctypes.c_int),
+}
+
+
+def load_library(path: str | None = None):
+    """Load libkda.so (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise KdaLibraryError(
+            f"{p} not found: build it with `python -m kimi_delta_attention_chunkwise_amd._build`")
+    try:
+        lib = ctypes.CDLL(p)
+    except OSError as exc:  # pragma: no cover - depends on the loader
+        raise KdaLibraryError(f"cannot load {p}: {exc}") from exc
+    for name, (argtypes, restype) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().kda_status_str(status).decode()
+        raise KdaError(f"libkda returned {msg} ({status})")
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return KDA_F32
+    if t == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd_supported(dtype: torch.dtype, dk: int, dv: int, chunk: int) -> bool:
+    return bool(load_library().kda_chunk_fwd_supported(_dtype_code(dtype), dk, dv, chunk))
+
+
+def decode_step_supported(dtype: torch.dtype, dk: int, dv: int) -> bool:
+    return bool(load_library().kda_decode_step_supported(_dtype_code(dtype), dk, dv))
+
+
+def chunk_fwd_workspace_bytes(B: int, T: int, N: int, H: int, dk: int, dv: int, chunk: int,
+                              dtype: torch.dtype, varlen: bool) -> int:
+    n = load_library().kda_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk,
+                                                     _dtype_code(dtype), int(varlen))
+    if n == ctypes.c_size_t(-1).value:
+        raise KdaError("unsupported or invalid sizes for kda_chunk_fwd")
+    return int(n)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
+              cu_seqlens=None, chunk=None, scale=1.0, workspace=None, out=None,
+              final_state=None):
+    """Chunkwise-parallel KDA forward on the GPU.
+
+    q, k, g ``[B, T, H, dk]``; v, gate ``[B, T, H, dv]``; beta ``[B, T, H]``, all
+    of one dtype (bf16 or fp32) on one HIP device.  ``gate`` holds logits.
+    ``init_state``: fp32 ``[N, H, dk, dv]`` or None.  ``cu_seqlens``: int32
+    ``[N + 1]`` on the device (then B must be 1) or None (N = B).
+    Optional preallocated ``workspace`` (uint8, at least
+    ``chunk_fwd_workspace_bytes`` bytes), ``out`` and ``final_state``.
+    Returns ``(out, final_state)``; final_state is None unless requested.
+    """
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda.chunk_fwd runs on a HIP device; tensors are on " + str(dev))
+    dt = q.dtype
+    code = _dtype_code(dt)
+    chunk = _DEFAULT_CHUNK[code] if chunk is None else int(chunk)
+    for name, t, shp in (("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("gate", gate, (B, T, H, dv)),
+                         ("beta", beta, (B, T, H))):
+        _need(t, name, shp, dt, dev)
+    _need(q, "q", (B, T, H, dk), dt, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+        _need(cu_seqlens, "cu_seqlens", cu_seqlens.shape, torch.int32, dev)
+        if B != 1:
+            raise ValueError("cu_seqlens requires B == 1")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if init_state is not None:
+        _need(init_state, "init_state", (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", (B, T, H, dv), dt, dev)
+    if output_final_state:
+        if final_state is None:
+            final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        else:
+            _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
+    else:
+        final_state = None
+    nbytes = chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < nbytes:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {nbytes} bytes on {dev}")
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
+                           _ptr(init_state), _ptr(out), _ptr(final_state), _ptr(cu_seqlens),
+                           B, T, N, H, dk, dv, chunk, float(scale), code, _ptr(workspace),
+                           workspace.numel(), _stream_ptr(dev))
+    _check(st)
+    return out, final_state
+
+
+def decode_step(q, k, v, g, beta, gate, state, scale=1.0, out=None):
+    """One recurrent KDA step on the GPU; ``state`` (fp32 ``[N, H, dk, dv]``)
+    is updated in place.  q, k, g ``[N, H, dk]``; v, gate ``[N, H, dv]``;
+    beta ``[N, H]``.  Returns the gated output ``[N, H, dv]``."""
+    lib = load_library()
+    if state.dim() != 4:
+        raise ValueError("state must be [N, H, dk, dv]")
+    N, H, dk, dv = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("kda.decode_step runs on a HIP device; state is on " + str(dev))
+    _need(state, "state", (N, H, dk, dv), torch.float32, dev)
+    dt = q.dtype
+    code = _dtype_code(dt)
+    for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("g", g, (N, H, dk)),
+                         ("v", v, (N, H, dv)), ("gate", gate, (N, H, dv)), ("beta", beta, (N, H))):
+        _need(t, name, shp, dt, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", (N, H, dv), dt, dev)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
+                             _ptr(state), _ptr(out), N, H, dk, dv, float(scale), code,
+                             _stream_ptr(dev))
+    _check(st)
+    return out

@@ -1,0 +1,130 @@
+// kda_api.hip -- the extern "C" entry points of libkda.so: host-side argument
+// validation, workspace sizing and dispatch to the gfx950 kernels.  Nothing
+// here allocates memory or keeps state between calls.
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool valid_dtype(kda_dtype dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+
+bool chunk_supported(kda_dtype dt, int dk, int dv, int chunk)
+{
+    if (dt == KDA_BF16)
+        return dk == kda::kDK && dv == kda::kDV && chunk == kda::kChunk;
+    if (dt == KDA_F32)
+        return dk == 16 && dv == 16 && chunk == 16;
+    return false;
+}
+
+bool decode_supported(kda_dtype dt, int dk, int dv)
+{
+    return valid_dtype(dt) && dk == dv && (dk == 16 || dk == 128);
+}
+
+// Number of chunk slots per head the bf16 path uses (see seq_info).
+int64_t chunk_slots(int B, int T, int N, int chunk, int varlen)
+{
+    if (varlen)
+        return (int64_t)T / chunk + N;
+    return (int64_t)B * ((T + chunk - 1) / chunk);
+}
+
+kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_str(kda_status s)
+{
+    switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL_POINTER: return "KDA_ERR_NULL_POINTER";
+    case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE";
+    case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+int kda_chunk_fwd_supported(kda_dtype dt, int dk, int dv, int chunk)
+{
+    return chunk_supported(dt, dk, dv, chunk) ? 1 : 0;
+}
+
+int kda_decode_step_supported(kda_dtype dt, int dk, int dv)
+{
+    return decode_supported(dt, dk, dv) ? 1 : 0;
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv, int chunk,
+                                     kda_dtype dt, int varlen)
+{
+    if (!valid_dtype(dt) || !chunk_supported(dt, dk, dv, chunk))
+        return (size_t)-1;
+    if (B < 1 || T < 0 || N < 0 || H < 1 || (varlen && B != 1) || (!varlen && N != B))
+        return (size_t)-1;
+    if (dt == KDA_F32)
+        return 0;
+    return (size_t)chunk_slots(B, T, N, chunk, varlen) * (size_t)H * kda::kRecBytes;
+}
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const void *gate, const float *init_state,
+                         void *out, float *final_state, const int32_t *cu_seqlens, int B, int T,
+                         int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!valid_dtype(dt))
+        return KDA_ERR_BAD_DTYPE;
+    if (!chunk_supported(dt, dk, dv, chunk))
+        return KDA_ERR_UNSUPPORTED;
+    const int varlen = cu_seqlens != nullptr;
+    if (B < 1 || T < 0 || N < 0 || H < 1)
+        return KDA_ERR_BAD_SHAPE;
+    if (varlen ? B != 1 : N != B)
+        return KDA_ERR_BAD_SHAPE;
+    const bool has_tokens = (int64_t)B * T > 0;
+    if (has_tokens && (!q || !k || !v || !g || !beta || !gate || !out))
+        return KDA_ERR_NULL_POINTER;
+    const size_t need = kda_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
+    if (need > 0 && !workspace)
+        return KDA_ERR_NULL_POINTER;
+    if (workspace_bytes < need)
+        return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (N == 0)
+        return KDA_OK;
+    if (dt == KDA_F32)
+        return from_hip(kda::launch_chunk_f32(
+            (const float *)q, (const float *)k, (const float *)v, (const float *)g,
+            (const float *)beta, (const float *)gate, init_state, (float *)out, final_state,
+            cu_seqlens, N, T, H, scale, stream));
+    return from_hip(kda::launch_chunk_bf16(
+        (const kda::bf16 *)q, (const kda::bf16 *)k, (const kda::bf16 *)v, (const kda::bf16 *)g,
+        (const kda::bf16 *)beta, (const kda::bf16 *)gate, init_state, (kda::bf16 *)out,
+        final_state, cu_seqlens, N, T, H, chunk_slots(B, T, N, chunk, varlen), scale, workspace,
+        stream));
+}
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const void *gate, float *state, void *out, int N,
+                           int H, int dk, int dv, float scale, kda_dtype dt, hipStream_t stream)
+{
+    if (!valid_dtype(dt))
+        return KDA_ERR_BAD_DTYPE;
+    if (!decode_supported(dt, dk, dv))
+        return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || H < 1)
+        return KDA_ERR_BAD_SHAPE;
+    if (N == 0)
+        return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !gate || !state || !out)
+        return KDA_ERR_NULL_POINTER;
+    return from_hip(kda::launch_decode(q, k, v, g, beta, gate, state, out, N, H, dk, dv, scale,
+                                       dt == KDA_BF16, stream));
+}
+
+}  // extern "C"

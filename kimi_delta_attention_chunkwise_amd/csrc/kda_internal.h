@@ -1,0 +1,114 @@
+// kda_internal.h -- shared definitions of the gfx950 KDA kernels (not part of
+// the public ABI; see include/kda.h for that).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 chunk
+// Geometry of the bf16 chunk path: 64-token chunks made of four 16-token
+// subtiles, dk = dv = 128, value channels split into 16-wide blocks that run
+// as independent recurrences (columns of the state never mix).
+constexpr int kChunk = 64;
+constexpr int kSub = 16;
+constexpr int kDK = 128;
+constexpr int kDV = 128;
+constexpr int kVBlock = 16;
+constexpr int kNumVBlocks = kDV / kVBlock;
+
+// Per-(chunk slot, head) record written by the prep kernel and read by the
+// chain kernel.  Matrices are stored as ready-to-load MFMA operand fragments
+// of v_mfma_f32_16x16x32_bf16: 64 lanes x 8 bf16 = 1 KiB per fragment, lane
+// l at byte 16 l.  "perm" is the k order the chain kernel uses for operands
+// built from its accumulators: within a 32-wide k-step ks, lane group b and
+// element e (0..7) stand for row 32 ks + 16 (e / 4) + 4 b + (e % 4).
+//   WN  : -W (chunk rows x dk), 4 row tiles x 4 dk k-steps, k in perm order
+//   QB  : scale * Q * exp(G), same shape and order as WN
+//   KP  : K'^T (dk x chunk rows), 8 dk tiles x 2 chunk k-steps, perm order
+//   PP  : scale * P (chunk x chunk, lower incl.), 4 x 2 fragments, perm order
+//   UT  : U~ (chunk rows x dv) per 16-wide value block, in accumulator order:
+//         [block][lane][row tile t][i] -> row 16 t + 4 (lane / 16) + i,
+//         column 16 block + lane % 16
+//   DEC : exp(G_end) per key channel, fp32
+constexpr size_t kFragBytes = 1024;
+constexpr size_t kOffWN = 0;
+constexpr size_t kOffQB = kOffWN + 16 * kFragBytes;
+constexpr size_t kOffKP = kOffQB + 16 * kFragBytes;
+constexpr size_t kOffPP = kOffKP + 16 * kFragBytes;
+constexpr size_t kOffUT = kOffPP + 8 * kFragBytes;
+constexpr size_t kOffDEC = kOffUT + kNumVBlocks * 2048;
+constexpr size_t kRecBytes = kOffDEC + kDK * sizeof(float);
+static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
+
+// Row of the k-step-local permutation described above.
+__host__ __device__ constexpr int perm_row(int ks, int b, int e)
+{
+    return 32 * ks + 16 * (e >> 2) + 4 * b + (e & 3);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Sequence bounds and first chunk slot of sequence n.  Without cu_seqlens the
+// B sequences have length T and slot = n * ceil(T / chunk) + j.  With
+// cu_seqlens, slot(n, j) = floor(cu[n] / chunk) + n + j, an injective map
+// into [0, floor(T / chunk) + N) that needs no prefix scan.
+struct SeqInfo {
+    int64_t bos;
+    int64_t len;
+    int64_t slot0;
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const int32_t *cu, int n, int T, int chunk)
+{
+    SeqInfo s;
+    if (cu) {
+        int64_t a = cu[n], b = cu[n + 1];
+        s.bos = a;
+        s.len = b - a;
+        s.slot0 = a / chunk + n;
+    } else {
+        s.bos = (int64_t)n * T;
+        s.len = T;
+        s.slot0 = (int64_t)n * ((T + chunk - 1) / chunk);
+    }
+    return s;
+}
+
+// ------------------------------------------------------------- launchers
+// All return hipSuccess or the launch error.
+hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const void *gate, float *state, void *out, int N,
+                         int H, int dk, int dv, float scale, int is_bf16, hipStream_t stream);
+
+hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, const float *g,
+                            const float *beta, const float *gate, const float *init,
+                            float *out, float *final_state, const int32_t *cu, int N, int T,
+                            int H, float scale, hipStream_t stream);
+
+hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
+                             const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
+                             float *final_state, const int32_t *cu, int N, int T, int H,
+                             int64_t n_slots, float scale, void *workspace,
+                             hipStream_t stream);
+
+}  // namespace kda

@@ -38,7 +38,7 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(_LIB_PATH):
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+    cmd = ["gcc", "-std=c99", "-O3", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH

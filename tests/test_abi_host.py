@@ -1,0 +1,146 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+``include/kda.h`` declares, sizes its workspace as documented and rejects bad
+arguments with the documented status codes before launching anything (no
+GPU is touched by these calls)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import kimi_delta_attention_chunkwise_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULLP, SHAPE, DTYPE, UNSUP, WS, HIP = range(7)
+REC = 74240   # bytes per (chunk slot, head) record of the bf16 path
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.library_path()):
+        pytest.skip("libkda.so not built")
+    return kda.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes",
+              "kda_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["KDA_OK", "KDA_ERR_NULL_POINTER", "KDA_ERR_BAD_SHAPE",
+                                 "KDA_ERR_BAD_DTYPE", "KDA_ERR_UNSUPPORTED",
+                                 "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_HIP"]):
+        assert lib.kda_status_str(code).decode() == name
+    assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
+
+
+def test_supported_sets(lib):
+    assert lib.kda_chunk_fwd_supported(1, 128, 128, 64) == 1
+    assert lib.kda_chunk_fwd_supported(0, 16, 16, 16) == 1
+    for args in [(1, 128, 128, 16), (1, 64, 64, 64), (0, 128, 128, 64), (0, 16, 16, 64),
+                 (2, 128, 128, 64)]:
+        assert lib.kda_chunk_fwd_supported(*args) == 0
+    for dt in (0, 1):
+        for d in (16, 128):
+            assert lib.kda_decode_step_supported(dt, d, d) == 1
+    assert lib.kda_decode_step_supported(1, 64, 64) == 0
+    assert lib.kda_decode_step_supported(1, 128, 16) == 0
+
+
+def test_workspace_bytes(lib):
+    ws = lib.kda_chunk_fwd_workspace_bytes
+    # fixed length: B * ceil(T / 64) slots per head
+    assert ws(1, 4096, 1, 8, 128, 128, 64, 1, 0) == 64 * 8 * REC
+    assert ws(3, 100, 3, 2, 128, 128, 64, 1, 0) == 3 * 2 * 2 * REC
+    assert ws(1, 0, 1, 4, 128, 128, 64, 1, 0) == 0
+    # varlen: floor(T / 64) + N slots per head
+    assert ws(1, 67000, 4, 32, 128, 128, 64, 1, 1) == (67000 // 64 + 4) * 32 * REC
+    assert ws(1, 1 << 20, 1, 16, 128, 128, 64, 1, 0) == 16384 * 16 * REC
+    # fp32 path needs none
+    assert ws(1, 64, 1, 2, 16, 16, 16, 0, 0) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert ws(1, 64, 1, 2, 64, 64, 64, 1, 0) == bad           # unsupported dims
+    assert ws(2, 64, 1, 2, 128, 128, 64, 1, 1) == bad         # varlen needs B = 1
+    assert ws(2, 64, 3, 2, 128, 128, 64, 1, 0) == bad         # N must equal B
+
+
+def _chunk(lib, **kw):
+    a = dict(q=1, k=1, v=1, g=1, beta=1, gate=1, init=None, out=1, final=None, cu=None,
+             B=1, T=64, N=1, H=2, dk=128, dv=128, chunk=64, scale=1.0, dt=1, ws=None,
+             ws_bytes=0)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_chunk_fwd(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]),
+                             p(a["gate"]), p(a["init"]), p(a["out"]), p(a["final"]), p(a["cu"]),
+                             a["B"], a["T"], a["N"], a["H"], a["dk"], a["dv"], a["chunk"],
+                             a["scale"], a["dt"], p(a["ws"]), a["ws_bytes"], None)
+
+
+def test_chunk_fwd_rejects_bad_arguments_before_launch(lib):
+    assert _chunk(lib, dt=7) == DTYPE
+    assert _chunk(lib, dk=64, dv=64) == UNSUP
+    assert _chunk(lib, chunk=16) == UNSUP
+    assert _chunk(lib, H=0) == SHAPE
+    assert _chunk(lib, T=-1) == SHAPE
+    assert _chunk(lib, B=2, N=1) == SHAPE
+    assert _chunk(lib, B=2, N=2, cu=1) == SHAPE               # varlen needs B = 1
+    assert _chunk(lib, q=None, ws=1, ws_bytes=10 ** 9) == NULLP
+    assert _chunk(lib, gate=None, ws=1, ws_bytes=10 ** 9) == NULLP
+    assert _chunk(lib, ws=None, ws_bytes=0) == NULLP          # bf16 needs a workspace
+    assert _chunk(lib, ws=1, ws_bytes=REC) == WS              # 2 heads need 2 records
+    # nothing to do: zero sequences
+    assert _chunk(lib, cu=1, N=0, T=0, q=None, k=None, v=None, g=None, beta=None, gate=None,
+                  out=None) == OK
+
+
+def test_decode_step_rejects_bad_arguments_before_launch(lib):
+    p = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(q=1, k=1, v=1, g=1, beta=1, gate=1, state=1, out=1, N=4, H=2, dk=128, dv=128,
+                 scale=1.0, dt=1)
+        a.update(kw)
+        ptr = lambda x: None if x is None else p(x)
+        return lib.kda_decode_step(ptr(a["q"]), ptr(a["k"]), ptr(a["v"]), ptr(a["g"]),
+                                   ptr(a["beta"]), ptr(a["gate"]), ptr(a["state"]), ptr(a["out"]),
+                                   a["N"], a["H"], a["dk"], a["dv"], a["scale"], a["dt"], None)
+    assert call(dt=5) == DTYPE
+    assert call(dk=64, dv=64) == UNSUP
+    assert call(N=-1) == SHAPE
+    assert call(H=0) == SHAPE
+    assert call(state=None) == NULLP
+    assert call(out=None) == NULLP
+    assert call(N=0, q=None) == OK
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(q, q, q, q, torch.zeros(1, 4, 1), q)
+    st = torch.zeros(1, 1, 16, 16)
+    with pytest.raises(ValueError):
+        kda.decode_step(q[0], q[0], q[0], q[0], torch.zeros(1, 1), q[0], st)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(kda.KdaLibraryError):
+        kda.load_library(str(tmp_path / "nope.so"))
