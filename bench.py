@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one ``kda_chunk_fwd`` call (prep + chain kernels) over one batch of
+the prefill workload (B=1, H=8, T=4096, dk=dv=128, bf16 inputs, fp32 state,
+64-token chunks).  Inputs are resident in HBM before timing starts; the steps
+rotate over several independent input sets whose total size exceeds the
+256 MB Infinity Cache, so every step reads cold inputs.  The decode workload
+(256 sequences x 32 heads, 512 MiB fp32 state updated in place, 128 steps) is
+timed the same way and reported under "decode".
+
+Prints one JSON line:
+  value      prefill tokens/s (B * T per call / seconds per call)
+  roofline   the prefill call against the HBM roof: algorithmic bytes per call
+             (1,538 B per token-head + the fp32 final state) / call time,
+             over 8 TB/s; traffic is the HBM bytes from rocprofv3 counters when
+             a summary taken on the current kernel sources exists in profiles/
+  mfma       algorithmic flops per call / call time over the bf16 dense peak
+  cpu_baseline  the fp64 oracle on the same workload on the host cores
+  decode     steps/s, tokens/s and HBM GB/s of the decode step
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-calibration   (a 1 GiB device copy, for counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+PREFILL_BYTES_PER_TOKEN_HEAD = 1538      # q, k, g, v, z, out at 256 B each + beta at 2 B
+STATE_BYTES = 128 * 128 * 4              # one fp32 state slice
+DK = DV = 128
+CHUNK = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_prefill_t4096_h8_traffic.json")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "kimi_delta_attention_chunkwise_amd", "csrc", f)
+    for f in ("kda_chunk_bf16.hip", "kda_internal.h", "kda_api.hip")
+]
+
+
+def flops_per_token_head(C=CHUNK, dk=DK, dv=DV):
+    """The method's own flops per token-head at chunk C (no masked or padded work):
+    6 dk dv (W S, Q~ S, K'^T U) + (3C - 1) dk (A, P, T K) + 2 C dv (T V, P U) + C^2 / 3."""
+    return 6 * dk * dv + (3 * C - 1) * dk + 2 * C * dv + C * C / 3.0
+
+
+def source_digest(paths=KERNEL_SOURCES) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(bytes_per_call):
+    """HBM traffic per call from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest():
+        return None
+    return float(t["hbm_bytes_per_call"])
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def copy_calibration(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": 5}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the KDA path here is single-GPU; see the sharding notes in DESIGN.md)",
+              file=sys.stderr, flush=True)
+        return 2
+    import torch
+
+    import kimi_delta_attention_chunkwise_amd as kda
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return 0
+    dev = torch.device("cuda:0")
+    kda.load_library()
+    w = W.WORKLOADS["prefill_t4096_h8"]
+    B, T, H = w.B, w.T, w.H
+    in_bytes_per_set = B * T * H * (5 * 256 + 2)
+    n_sets = max(2, -(-600 * 2 ** 20 // in_bytes_per_set))      # > 2x the 256 MB MALL
+    sets = [W.prefill_inputs(w, device=dev, seed=s) for s in range(n_sets)]
+    ws = torch.empty(kda.chunk_fwd_workspace_bytes(B, T, B, H, DK, DV, CHUNK, torch.bfloat16,
+                                                   False), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, T, H, DV, dtype=torch.bfloat16, device=dev)
+    fin = torch.empty(B, H, DK, DV, dtype=torch.float32, device=dev)
+
+    def step(i):
+        x = sets[i % n_sets]
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], workspace=ws, out=out,
+                      final_state=fin)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] prefill warmup done ({args.warmup} steps, {n_sets} input sets)",
+          file=sys.stderr, flush=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] prefill timed: {args.steps} steps, {ms:.4f} ms/step (wall {wall:.3f} s)",
+          file=sys.stderr, flush=True)
+
+    tokens = B * T
+    token_heads = tokens * H
+    bytes_call = PREFILL_BYTES_PER_TOKEN_HEAD * token_heads + B * H * STATE_BYTES
+    flops_call = flops_per_token_head() * token_heads
+    t_s = ms / 1e3
+    achieved = bytes_call / t_s / 1e9
+    traffic = load_traffic(bytes_call)
+    result = {
+        "metric": "KDA prefill tokens/s + decode steps/s; % bf16 MFMA peak / % HBM GB/s peak",
+        "value": tokens / t_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_t4096_h8", "B": B, "T": T, "H": H, "dk": DK, "dv": DV,
+                   "chunk": CHUNK, "global_batch": B, "seq_len": T, "parallelism": "none",
+                   "state": "fp32, zero init, final state written", "input_sets": n_sets},
+        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd (prep + chain kernels)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_call": bytes_call},
+        "mfma": {"achieved": flops_call / t_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": flops_call / t_s / 1e12 / BF16_PEAK_TFLOPS,
+                 "algorithmic_flops_per_call": flops_call},
+    }
+    del sets
+
+    if not args.no_decode:
+        result["decode"] = bench_decode(torch, kda, W, dev, args)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_decode(torch, kda, W, dev, args):
+    w = W.WORKLOADS["decode_n256_h32"]
+    N, H = w.N, w.H
+    state = W.decode_init_state(w, device=dev)
+    n_sets = 8
+    sets = [W.decode_inputs(w, step=s, device=dev) for s in range(n_sets)]
+    out = torch.empty(N, H, DV, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        x = sets[i % n_sets]
+        kda.decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], state, out=out)
+
+    for i in range(max(4, args.warmup // 4)):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.decode_steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.decode_steps
+    print(f"[bench] decode timed: {args.decode_steps} steps, {ms:.4f} ms/step",
+          file=sys.stderr, flush=True)
+    bytes_step = N * H * (2 * STATE_BYTES + PREFILL_BYTES_PER_TOKEN_HEAD)
+    gbs = bytes_step / (ms / 1e3) / 1e9
+    return {"workload": "decode_n256_h32", "N": N, "H": H, "steps": args.decode_steps,
+            "ms_per_step": ms, "steps_per_s": 1e3 / ms, "tokens_per_s": N * 1e3 / ms,
+            "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "algorithmic_bytes_per_step": bytes_step}}
+
+
+def cpu_baseline(w):
+    """The fp64 oracle (as it stands) on the same prefill workload, host cores."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    x = W.prefill_inputs(w, device="cpu", seed=0)
+    arrs = [x[k].float().numpy() for k in ("q", "k", "v", "g", "beta", "z")]
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    units = w.B * w.H
+    reps, elapsed = 0, 0.0
+    while elapsed < 10.0 and reps < 20:
+        t0 = time.perf_counter()
+        oracle.forward(*arrs, n_threads=threads)
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    per_call = elapsed / reps
+    del np
+    return {"value": w.B * w.T / per_call, "unit": "tokens/s", "cores": min(threads, units),
+            "kind": "oracle",
+            "sample": f"full prefill_t4096_h8 call (B=1, H=8, T=4096) repeated {reps}x, "
+                      f"{elapsed:.1f} s total; OpenMP over the {units} (sequence, head) units"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

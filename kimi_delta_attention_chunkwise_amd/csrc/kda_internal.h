@@ -25,26 +25,31 @@ constexpr int kVBlock = 16;
 constexpr int kNumVBlocks = kDV / kVBlock;
 
 // Per-(chunk slot, head) record written by the prep kernel and read by the
-// chain kernel.  Matrices are stored as ready-to-load MFMA operand fragments
-// of v_mfma_f32_16x16x32_bf16: 64 lanes x 8 bf16 = 1 KiB per fragment, lane
-// l at byte 16 l.  "perm" is the k order the chain kernel uses for operands
-// built from its accumulators: within a 32-wide k-step ks, lane group b and
-// element e (0..7) stand for row 32 ks + 16 (e / 4) + 4 b + (e % 4).
-//   WN  : -W (chunk rows x dk), 4 row tiles x 4 dk k-steps, k in perm order
-//   QB  : scale * Q * exp(G), same shape and order as WN
-//   KP  : K'^T (dk x chunk rows), 8 dk tiles x 2 chunk k-steps, perm order
-//   PP  : scale * P (chunk x chunk, lower incl.), 4 x 2 fragments, perm order
-//   UT  : U~ (chunk rows x dv) per 16-wide value block, in accumulator order:
-//         [block][lane][row tile t][i] -> row 16 t + 4 (lane / 16) + i,
-//         column 16 block + lane % 16
-//   DEC : exp(G_end) per key channel, fp32
+// chain kernel.  With L = K'^T W (dk x dk), Bm = K'^T U~ (dk x dv),
+// Q^ = Q~ - P W (chunk x dk) and O0 = P U~ (chunk x dv), one chunk maps the
+// entry state S to
+//     S_next = diag(dec) S + Bm - L S,        O = Q^ S + O0.
+// Matrices the chain multiplies are stored as ready-to-load MFMA operand
+// fragments of v_mfma_f32_16x16x32_bf16 (64 lanes x 8 bf16 = 1 KiB, lane l at
+// byte 16 l) whose k index follows "perm": within a 32-wide k-step ks, lane
+// group b = lane / 16 and element e (0..7) stand for row
+// 32 ks + 16 (e / 4) + 4 b + (e % 4), which is exactly how the chain holds the
+// state in its accumulators.  Additive terms are stored in accumulator order.
+//   LN  : -L, 8 dk row tiles x 4 dk k-steps                      (32 KiB)
+//   QH  : Q^, 4 chunk row tiles x 4 dk k-steps                   (16 KiB)
+//   BM  : Bm per 16-wide value block, [block][wave w][lane][8]:
+//         elements 0..3 -> rows 32 w + 4 b + i, 4..7 -> rows 32 w + 16 + 4 b + i,
+//         column 16 block + lane % 16                              (32 KiB)
+//   O0  : O0 per value block, [block][row tile t][lane][4] -> row 16 t + lane % 16,
+//         columns 16 block + 4 b .. + 3
+//                                                                  (16 KiB)
+//   DEC : exp(G_end) per key channel, fp32                        (512 B)
 constexpr size_t kFragBytes = 1024;
-constexpr size_t kOffWN = 0;
-constexpr size_t kOffQB = kOffWN + 16 * kFragBytes;
-constexpr size_t kOffKP = kOffQB + 16 * kFragBytes;
-constexpr size_t kOffPP = kOffKP + 16 * kFragBytes;
-constexpr size_t kOffUT = kOffPP + 8 * kFragBytes;
-constexpr size_t kOffDEC = kOffUT + kNumVBlocks * 2048;
+constexpr size_t kOffLN = 0;
+constexpr size_t kOffQH = kOffLN + 32 * kFragBytes;
+constexpr size_t kOffBM = kOffQH + 16 * kFragBytes;
+constexpr size_t kOffO0 = kOffBM + kNumVBlocks * 4096;
+constexpr size_t kOffDEC = kOffO0 + kNumVBlocks * 2048;
 constexpr size_t kRecBytes = kOffDEC + kDK * sizeof(float);
 static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
 
