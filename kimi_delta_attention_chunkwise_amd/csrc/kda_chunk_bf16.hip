@@ -54,7 +54,7 @@ constexpr int kColLd = 72;    // bf16 row stride of channel-major 128 x 64 tiles
 constexpr int kALd = 65;      // fp32 row stride of A and T
 
 struct PrepSmem {
-    // -- live in phases 1-2 only; T and its scratch reuse this space afterwards
+    // -- live in phases 1-2 only; T reuses this space afterwards
     bf16 KR[kChunk][kRowLd];      // k e^{G - B_i(r)}      (row operand of A)
     bf16 KCD[kChunk][kRowLd];     // k e^{B_i(r) - G}      (column operand, diagonal ref.)
     float F[6][kDK];              // e^{B_i - B_j}, i > j  (pairs 10 20 21 30 31 32)
@@ -64,18 +64,16 @@ struct PrepSmem {
     bf16 VB[kDV][kColLd];         // beta v, channel-major
     bf16 KPT[kDK][kColLd];        // K' = k e^{G_end - G}, channel-major
     bf16 PM[kChunk][kColLd];      // scale P, lower incl., zero above
-    float AM[kChunk][kALd];       // diag(beta) A, strict lower (scan scratch in phase 1)
-    float Bref[4][kDK];           // B_0 = 0, B_1..B_3
-    float Gend[kDK];
-    float beta[kChunk];
+    float AM[kChunk][kALd];       // diag(beta) A, strict lower
+    float eB[4][kDK];             // e^{B_i}
+    float eGB[4][kDK];            // e^{G_end - B_i}
+    float Gref[4][kDK];           // G at the end of subtiles 0, 1, 2, 3 (B_1, B_2, B_3, G_end)
 };
 
-struct TSmem {                    // overlays KR / KCD / F after phase 2
+struct TSmem {                    // overlays KR after phase 2
     float TM[kChunk][kALd];
-    float X[3][kSub][kSub + 1];
 };
-static_assert(sizeof(TSmem) <= 2 * sizeof(bf16) * kChunk * kRowLd + 6 * kDK * sizeof(float),
-              "T overlay fits");
+static_assert(sizeof(TSmem) <= sizeof(bf16) * kChunk * kRowLd, "T overlay fits");
 
 __device__ __forceinline__ int pair_index(int i, int j) { return (i * (i - 1)) / 2 + j; }
 
@@ -100,6 +98,35 @@ __device__ __forceinline__ bf16x8 acc_to_frag(const f32x4 &lo, const f32x4 &hi)
 __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4 &a, float s)
 {
     return bf16x4{(bf16)(s * a[0]), (bf16)(s * a[1]), (bf16)(s * a[2]), (bf16)(s * a[3])};
+}
+
+__device__ __forceinline__ f32x4 mfma4_f32(float a, float b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// DPP lane move (as int bits) with every lane active; lanes whose source is
+// out of range (bound_ctrl) or whose row is masked off read 0
+template <int kCtrl, int kRowMask, bool kBound>
+__device__ __forceinline__ float dpp_add_src(float x)
+{
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xf, kBound));
+}
+
+// inclusive prefix sum over the 64 lanes of a wave (lane = row of the chunk):
+// row_shr 1/2/4/8 inside each 16-lane row, then row_bcast 15 (rows 1 and 3
+// take the last lane of the row before) and row_bcast 31 (rows 2 and 3 take
+// lane 31)
+__device__ __forceinline__ float wave_inclusive_sum(float x)
+{
+    x += dpp_add_src<0x111, 0xf, true>(x);
+    x += dpp_add_src<0x112, 0xf, true>(x);
+    x += dpp_add_src<0x114, 0xf, true>(x);
+    x += dpp_add_src<0x118, 0xf, true>(x);
+    x += dpp_add_src<0x142, 0xa, false>(x);
+    x += dpp_add_src<0x143, 0xc, false>(x);
+    return x;
 }
 
 // Chunk slot -> (sequence, chunk index).  Returns false for an unused slot.
@@ -148,120 +175,85 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
     uint8_t *rec = ws + ((int64_t)slot * H + h) * (int64_t)kRecBytes;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, b = lane >> 4;
-    const int64_t tstride = (int64_t)H * kDK;   // elements between consecutive tokens
 
     // ---- phase 1: loads, cumulative log-decay, elementwise operands -----------
-    // thread -> channels 8 cg .. 8 cg + 7 of rows 2 rg, 2 rg + 1
-    const int cg = tid & 15, rg = tid >> 4;
-    float qv[2][8], kv[2][8], vv[2][8], Gl[2][8];
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-        const int r = 2 * rg + rr;
-        bf16x8 q8 = {}, k8 = {}, v8 = {}, g8 = {};
-        if (r < len) {
-            const int64_t o = (tok0 + r) * tstride + (int64_t)h * kDK + 8 * cg;
-            q8 = *reinterpret_cast<const bf16x8 *>(q + o);
-            k8 = *reinterpret_cast<const bf16x8 *>(k + o);
-            v8 = *reinterpret_cast<const bf16x8 *>(v + o);
-            g8 = *reinterpret_cast<const bf16x8 *>(g + o);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            qv[rr][e] = (float)q8[e];
-            kv[rr][e] = (float)k8[e];
-            vv[rr][e] = (float)v8[e];
-            Gl[rr][e] = (float)g8[e] + (rr ? Gl[0][e] : 0.f);
-        }
-    }
-    if (tid < kChunk)
-        sm.beta[tid] = tid < len ? (float)beta[(tok0 + tid) * H + h] : 0.f;
+    // lane = row r of the chunk, wave = channels 16 w .. 16 w + 15
     {
-        // zero P (the upper blocks stay zero) while the loads land
-        bf16 *pm = &sm.PM[0][0];
-        for (int i = tid; i < kChunk * kColLd; i += kPrepThreads)
-            pm[i] = (bf16)0.f;
-    }
-    float(*tot)[kDK] = reinterpret_cast<float(*)[kDK]>(&sm.AM[0][0]);   // [32][128]
-    *reinterpret_cast<f32x4 *>(&tot[rg][8 * cg]) = f32x4{Gl[1][0], Gl[1][1], Gl[1][2], Gl[1][3]};
-    *reinterpret_cast<f32x4 *>(&tot[rg][8 * cg + 4]) = f32x4{Gl[1][4], Gl[1][5], Gl[1][6], Gl[1][7]};
-    __syncthreads();
-    if (tid < kDK) {
-        // exclusive scan over the 32 row pairs of channel tid
-        float t[32];
+        const int r = lane;
+        const bool ok = r < len;
+        const int64_t orow = ((tok0 + r) * H + h) * (int64_t)kDK + 16 * wave;
+        bf16x8 q8[2] = {}, k8[2] = {}, v8[2] = {}, g8[2] = {};
+        float br = 0.f;
+        if (ok) {
 #pragma unroll
-        for (int x = 0; x < 32; ++x)
-            t[x] = tot[x][tid];
-        float run = 0.f;
-#pragma unroll
-        for (int x = 0; x < 32; ++x) {
-            const float nx = run + t[x];
-            tot[x][tid] = run;
-            if (x == 8)
-                sm.Bref[1][tid] = run;
-            if (x == 16)
-                sm.Bref[2][tid] = run;
-            if (x == 24)
-                sm.Bref[3][tid] = run;
-            run = nx;
-        }
-        sm.Bref[0][tid] = 0.f;
-        sm.Gend[tid] = run;
-    }
-    __syncthreads();
-    {
-        const int bi = rg >> 3;                      // subtile of both rows
-        float ex[8], Bi[8], eB[8], eGB[8];
-        const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&tot[rg][8 * cg]);
-        const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&tot[rg][8 * cg + 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            ex[e] = e0[e];
-            ex[4 + e] = e1[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            Bi[e] = sm.Bref[bi][8 * cg + e];
-            eB[e] = __expf(Bi[e]);                                   // e^{B_i} <= 1
-            eGB[e] = __expf(sm.Gend[8 * cg + e] - Bi[e]);             // e^{G_end - B_i} <= 1
-        }
-        bf16 xb[2][8], vb[2][8], kp[2][8];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int r = 2 * rg + rr;
-            const float br = sm.beta[r];
-            bf16x8 kr8, qr8, kc8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float G = ex[e] + Gl[rr][e];
-                const float fr = __expf(G - Bi[e]);          // e^{G - B_i} in [e^-80, 1]
-                const float fc = __frcp_rn(fr);              // e^{B_i - G} in [1, e^80]
-                kr8[e] = (bf16)(kv[rr][e] * fr);
-                qr8[e] = (bf16)(qv[rr][e] * fr);
-                kc8[e] = (bf16)(kv[rr][e] * fc);
-                xb[rr][e] = (bf16)(br * kv[rr][e] * (fr * eB[e]));         // beta k e^G
-                vb[rr][e] = (bf16)(br * vv[rr][e]);
-                kp[rr][e] = (bf16)(kv[rr][e] * (eGB[e] * fc));             // k e^{G_end - G}
+            for (int h2 = 0; h2 < 2; ++h2) {
+                q8[h2] = *reinterpret_cast<const bf16x8 *>(q + orow + 8 * h2);
+                k8[h2] = *reinterpret_cast<const bf16x8 *>(k + orow + 8 * h2);
+                v8[h2] = *reinterpret_cast<const bf16x8 *>(v + orow + 8 * h2);
+                g8[h2] = *reinterpret_cast<const bf16x8 *>(g + orow + 8 * h2);
             }
-            *reinterpret_cast<bf16x8 *>(&sm.KR[r][8 * cg]) = kr8;
-            *reinterpret_cast<bf16x8 *>(&sm.QR[r][8 * cg]) = qr8;
-            *reinterpret_cast<bf16x8 *>(&sm.KCD[r][8 * cg]) = kc8;
+            br = (float)beta[(tok0 + r) * H + h];
         }
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        for (int i = tid; i < kChunk * kColLd / 8; i += kPrepThreads)   // zero P (upper blocks stay 0)
+            reinterpret_cast<bf16x8 *>(&sm.PM[0][0])[i] = bf16x8{};
+        const int ib = r >> 4;                            // subtile of this row
+        float G[16];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = 8 * cg + e;
-            *reinterpret_cast<bf16x2 *>(&sm.XB[c][2 * rg]) = bf16x2{xb[0][e], xb[1][e]};
-            *reinterpret_cast<bf16x2 *>(&sm.VB[c][2 * rg]) = bf16x2{vb[0][e], vb[1][e]};
-            *reinterpret_cast<bf16x2 *>(&sm.KPT[c][2 * rg]) = bf16x2{kp[0][e], kp[1][e]};
+        for (int c = 0; c < 16; ++c)
+            G[c] = wave_inclusive_sum((float)g8[c >> 3][c & 7]);
+        // G at the ends of the subtiles: B_1, B_2, B_3 and G_end, per channel
+        if ((lane & 15) == 15) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                sm.Gref[ib][16 * wave + c] = G[c];
         }
-    }
-    if (tid < kDK) {
-        int p = 0;
+        __syncthreads();
+        if (lane < 16) {
+            // per-channel constants of channel 16 w + lane
+            const int ch = 16 * wave + lane;
+            const float b1 = sm.Gref[0][ch], b2 = sm.Gref[1][ch], b3 = sm.Gref[2][ch];
+            const float ge = sm.Gref[3][ch];
+            sm.eB[0][ch] = 1.f;
+            sm.eB[1][ch] = __expf(b1);
+            sm.eB[2][ch] = __expf(b2);
+            sm.eB[3][ch] = __expf(b3);
+            sm.eGB[0][ch] = __expf(ge);
+            sm.eGB[1][ch] = __expf(ge - b1);
+            sm.eGB[2][ch] = __expf(ge - b2);
+            sm.eGB[3][ch] = __expf(ge - b3);
+            sm.F[0][ch] = __expf(b1);                    // e^{B_1 - B_0}
+            sm.F[1][ch] = __expf(b2);                    // e^{B_2 - B_0}
+            sm.F[2][ch] = __expf(b2 - b1);
+            sm.F[3][ch] = __expf(b3);
+            sm.F[4][ch] = __expf(b3 - b1);
+            sm.F[5][ch] = __expf(b3 - b2);
+            reinterpret_cast<float *>(rec + kOffDEC)[ch] = __expf(ge);
+        }
+        __syncthreads();
+        bf16x8 kr8[2], qr8[2], kc8[2];
 #pragma unroll
-        for (int i = 1; i < 4; ++i)
+        for (int c = 0; c < 16; ++c) {
+            const int h2 = c >> 3, e = c & 7, ch = 16 * wave + c;
+            const float Bi = ib == 0 ? 0.f : sm.Gref[ib - 1][ch];
+            const float fr = __expf(G[c] - Bi);           // e^{G - B_i} in [e^-80, 1]
+            const float fc = __frcp_rn(fr);               // e^{B_i - G} in [1, e^80]
+            const float kv = (float)k8[h2][e];
+            kr8[h2][e] = (bf16)(kv * fr);
+            qr8[h2][e] = (bf16)((float)q8[h2][e] * fr);
+            kc8[h2][e] = (bf16)(kv * fc);
+            sm.XB[ch][r] = (bf16)(br * kv * (fr * sm.eB[ib][ch]));       // beta k e^G
+            sm.VB[ch][r] = (bf16)(br * (float)v8[h2][e]);               // beta v
+            sm.KPT[ch][r] = (bf16)(kv * (sm.eGB[ib][ch] * fc));         // k e^{G_end - G}
+        }
 #pragma unroll
-            for (int jj = 0; jj < i; ++jj)
-                sm.F[p++][tid] = __expf(sm.Bref[i][tid] - sm.Bref[jj][tid]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+            *reinterpret_cast<bf16x8 *>(&sm.KR[r][16 * wave + 8 * h2]) = kr8[h2];
+            *reinterpret_cast<bf16x8 *>(&sm.QR[r][16 * wave + 8 * h2]) = qr8[h2];
+            *reinterpret_cast<bf16x8 *>(&sm.KCD[r][16 * wave + 8 * h2]) = kc8[h2];
+        }
+        // beta per row, for A's row scaling: keep it next to the A tile
+        if (wave == 0)
+            sm.AM[r][kChunk] = br;
     }
     __syncthreads();
 
@@ -289,7 +281,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * i + 4 * b + e, col = 16 * jb + m;
-            sm.AM[row][col] = (jb < i || col < row) ? sm.beta[row] * accA[e] : 0.f;
+            sm.AM[row][col] = (jb < i || col < row) ? sm.AM[row][kChunk] * accA[e] : 0.f;
             sm.PM[row][col] = (bf16)((jb < i || col <= row) ? scale * accP[e] : 0.f);
         }
     }
@@ -299,51 +291,51 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
     if (wave == 0) {
         // diagonal 16 x 16 blocks by forward substitution, one column per lane;
         // x[s] = 0 for s < col, so the full-range sums only add zeros there
+        // (column form: once x[s] is final it updates every later row at once,
+        // so the dependency depth is 16 instead of 120)
         const int blk = lane >> 4, col = lane & 15, o = 16 * blk;
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == col) ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r)
+            x[r] = (r == col) ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 0; s < r; ++s)
-                acc -= sm.AM[o + r][o + s] * x[s];
-            x[r] = (r < col) ? 0.f : acc;
-        }
+        for (int s2 = 0; s2 < 15; ++s2)
+#pragma unroll
+            for (int r = s2 + 1; r < 16; ++r)
+                x[r] -= sm.AM[o + r][o + s2] * x[s2];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             ts.TM[o + r][o + col] = x[r];
     } else if (wave <= 2) {
         // T_01 and T_23 are read by the W / U~ products: zero them
-        const int t = tid - 64, o = (wave == 1) ? 0 : 32;
-        for (int e = t % 64; e < 256; e += 64)
+        const int o = (wave == 1) ? 0 : 32;
+#pragma unroll
+        for (int e = lane; e < 256; e += 64)
             ts.TM[o + e / 16][o + 16 + e % 16] = 0.f;
     }
     __syncthreads();
-    {
-        // off-diagonal blocks by distance: T_ab = -T_aa (sum_{mm=b}^{a-1} A_a,mm T_mm,b)
-        const int rr = (tid >> 4) & 15, cc = tid & 15, grp = tid >> 8;
-        for (int dist = 1; dist < 4; ++dist) {
-            const int nb = 4 - dist;
-            for (int p = grp; p < nb; p += 2) {
-                const int a = p + dist, bb = p;
-                float acc = 0.f;
-                for (int mm = bb; mm < a; ++mm)
+    // off-diagonal blocks by distance on fp32 MFMA (16x16x4), one block per wave:
+    // X = sum_{mm=bb}^{a-1} A_a,mm T_mm,bb ;  T_a,bb = -T_aa X
+    for (int dist = 1; dist < 4; ++dist) {
+        if (wave < 4 - dist) {
+            const int a = wave + dist, bb = wave;
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            for (int mm = bb; mm < a; ++mm) {
 #pragma unroll
-                    for (int s = 0; s < 16; ++s)
-                        acc += sm.AM[16 * a + rr][16 * mm + s] * ts.TM[16 * mm + s][16 * bb + cc];
-                ts.X[p][rr][cc] = acc;
+                for (int kk = 0; kk < 4; ++kk)
+                    X = mfma4_f32(sm.AM[16 * a + m][16 * mm + 4 * kk + b],
+                                  ts.TM[16 * mm + 4 * kk + b][16 * bb + m], X);
             }
-            __syncthreads();
-            for (int p = grp; p < nb; p += 2) {
-                const int a = p + dist, bb = p;
-                float acc = 0.f;
+            // k order: MFMA kk takes k = 4 b + kk, which is X's own accumulator row
+            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 16; ++s)
-                    acc -= ts.TM[16 * a + rr][16 * a + s] * ts.X[p][s][cc];
-                ts.TM[16 * a + rr][16 * bb + cc] = acc;
-            }
-            __syncthreads();
+            for (int kk = 0; kk < 4; ++kk)
+                Y = mfma4_f32(ts.TM[16 * a + m][16 * a + 4 * b + kk], X[kk], Y);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ts.TM[16 * a + 4 * b + i][16 * bb + m] = -Y[i];
         }
+        __syncthreads();
     }
 
     // ---- phase 4: W = T X and U~ = T V for the wave's 16 channels --------------
@@ -419,10 +411,11 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                 pf[ks] = perm8(&sm.PM[16 * mt + m][0], ks, b);
             // scale Q e^G at row 16 mt + m, channels 16 nt + 4 b .. + 3, from q e^{G - B_mt}
             const bf16x4 qr = *reinterpret_cast<const bf16x4 *>(&sm.QR[16 * mt + m][16 * nt + 4 * b]);
+            const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[mt][16 * nt + 4 * b]);
             f32x4 qh;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                qh[i] = -scale * (float)qr[i] * __expf(sm.Bref[mt][16 * nt + 4 * b + i]);
+                qh[i] = -scale * (float)qr[i] * eb[i];
             f32x4 o0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -435,69 +428,51 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                 to_bf16x4(o0, 1.f);
         }
     }
-    if (tid < kDK)
-        reinterpret_cast<float *>(rec + kOffDEC)[tid] = __expf(sm.Gend[tid]);
 }
 
 namespace {
 
 // Chain workgroup: 4 compute waves and 1 store wave.  Compute wave w keeps
-// state rows 32 w .. 32 w + 31 (two 16-row tiles) and produces output token
-// rows 16 w .. 16 w + 15 of each chunk; it only ever loads from global memory,
-// and writes its gated outputs to LDS.  The store wave copies each chunk's
-// outputs from LDS to global memory one chunk later.  Keeping loads and stores
-// in different waves lets the compiler wait for exactly the prefetched stage
-// it needs (with both kinds pending it can only wait for everything).
+// state rows 32 w .. 32 w + 31 (two 16-row tiles) and applies
+// S' = dec S + Bm - L S chunk after chunk; the waves exchange the new state as
+// bf16 MFMA fragments through LDS.  Compute waves only ever load from global
+// memory; the store wave copies each chunk's entry state from LDS to the
+// workspace for the output kernel.  Keeping loads and stores in different
+// waves lets the compiler wait for exactly the prefetched stage it needs
+// (with both kinds pending it can only wait for everything).
 constexpr int kComputeWaves = 4;
 constexpr int kChainThreads = 64 * (kComputeWaves + 1);
-constexpr int kPrefetch = 3;         // chunks of operands in flight per compute wave
+constexpr int kPrefetch = 4;         // chunks of operands in flight per compute wave
 
 struct ChainStage {
     bf16x8 ln[2][4];   // -L rows of the wave's two state tiles, 4 dk k-steps each
-    bf16x8 qh[4];      // Q^ rows of the wave's output tile
     bf16x8 bm;         // Bm of the wave's 32 state rows, this value block
     f32x4 dec[2];      // e^{G_end} of the wave's state rows
-    bf16x4 o0;         // O0 of the wave's output token row, 4 value channels
-    bf16x4 z;          // gate logits of the same token row and channels
 };
 
-// Every load is unconditional (rows past a partial chunk re-read the chunk's
-// last row), so each loop iteration issues the same memory operations.
-__device__ __forceinline__ void chain_load(ChainStage &st, const uint8_t *rec, const bf16 *gate,
-                                           int64_t tok0, int64_t lenc, int H, int h, int w,
-                                           int lane, int blk)
+__device__ __forceinline__ void chain_load(ChainStage &st, const uint8_t *rec, int w, int lane,
+                                           int blk)
 {
-    const int m = lane & 15, b = lane >> 4;
+    const int b = lane >> 4;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             st.ln[t][ks] = *reinterpret_cast<const bf16x8 *>(
                 rec + kOffLN + ((2 * w + t) * 4 + ks) * kFragBytes + lane * 16);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        st.qh[ks] = *reinterpret_cast<const bf16x8 *>(rec + kOffQH + (w * 4 + ks) * kFragBytes +
-                                                      lane * 16);
     st.bm = *reinterpret_cast<const bf16x8 *>(rec + kOffBM + blk * 4096 + w * 1024 + lane * 16);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
         st.dec[t] = *reinterpret_cast<const f32x4 *>(rec + kOffDEC + (32 * w + 16 * t + 4 * b) * 4);
-    st.o0 = *reinterpret_cast<const bf16x4 *>(rec + kOffO0 + blk * 2048 + w * 512 + lane * 8);
-    const int64_t row = 16 * w + m;
-    const int64_t r = row < lenc ? row : lenc - 1;
-    st.z = *reinterpret_cast<const bf16x4 *>(gate + ((tok0 + r) * H + h) * kDV + kVBlock * blk +
-                                             4 * b);
 }
 
 }  // namespace
 
 __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
-    const bf16 *__restrict__ gate, const float *__restrict__ init, bf16 *__restrict__ out,
-    float *__restrict__ final_state, const int32_t *__restrict__ cu, int T, int H, int units,
-    const uint8_t *__restrict__ ws)
+    const float *__restrict__ init, float *__restrict__ final_state,
+    const int32_t *__restrict__ cu, int T, int H, int units, uint8_t *__restrict__ ws)
 {
     __shared__ bf16x8 sbuf[2][4][64];                 // state as 4 k-step fragments
-    __shared__ bf16x4 ybuf[2][kChunk][kVBlock / 4];   // gated outputs of one chunk
 
     // all value blocks of one (sequence, head) land on the same XCD (blocks are
     // dealt to the 8 XCDs round-robin), so they share that XCD's L2
@@ -512,23 +487,22 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     const int m = lane & 15, b = lane >> 4;
     const SeqInfo si = seq_info(cu, n, T, kChunk);
     const int64_t nch = (si.len + kChunk - 1) / kChunk;
+    auto rec_of = [&](int64_t jc) { return ws + ((si.slot0 + jc) * H + h) * (int64_t)kRecBytes; };
 
     // the chunk loop runs in rounds of kPrefetch iterations; iterations past the
-    // last chunk (at most kPrefetch - 1) leave the state unchanged and store nothing
+    // last chunk (at most kPrefetch - 1) leave the state unchanged
     const int64_t niter = (nch + kPrefetch - 1) / kPrefetch * kPrefetch;
     if (w == kComputeWaves) {
-        // store wave: lane r copies token row r of a finished chunk (32 bytes)
+        // store wave: copy the entry state of chunk jc (4 fragments, 16 B per lane each)
         __syncthreads();
-        for (int64_t jc = 0; jc <= niter; ++jc) {
-            if (jc > 0 && lane < si.len - (jc - 1) * kChunk) {
-                const bf16x8 *src = reinterpret_cast<const bf16x8 *>(&ybuf[(jc - 1) & 1][lane][0]);
-                bf16x8 *dst = reinterpret_cast<bf16x8 *>(
-                    out + ((si.bos + (jc - 1) * kChunk + lane) * H + h) * kDV + kVBlock * blk);
-                dst[0] = src[0];
-                dst[1] = src[1];
+        for (int64_t jc = 0; jc < niter; ++jc) {
+            if (jc < nch) {
+                bf16x8 *dst = reinterpret_cast<bf16x8 *>(rec_of(jc) + kOffSB + blk * 4096) + lane;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    dst[ks * 64] = sbuf[jc & 1][ks][lane];
             }
-            if (jc < niter)
-                __syncthreads();
+            __syncthreads();
         }
         return;
     }
@@ -547,12 +521,13 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
 
     // the scheduling barriers keep each stage's loads together and in stage
     // order, in the prologue and in the loop alike, so the loop-entry wait
-    // state is the same on both paths and every wait stays partial
+    // state is the same on both paths and every wait stays partial; stage
+    // loads past the last chunk re-read the last chunk so that every iteration
+    // issues the same loads
     auto load_stage = [&](ChainStage &stage, int64_t jc) {
         const int64_t jl = jc < nch ? jc : nch - 1;
         __builtin_amdgcn_sched_barrier(0);
-        chain_load(stage, ws + ((si.slot0 + jl) * H + h) * (int64_t)kRecBytes, gate,
-                   si.bos + jl * kChunk, si.len - jl * kChunk, H, h, w, lane, blk);
+        chain_load(stage, rec_of(jl), w, lane, blk);
         __builtin_amdgcn_sched_barrier(0);
     };
     ChainStage st[kPrefetch];
@@ -566,7 +541,6 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
 #pragma unroll
         for (int s = 0; s < kPrefetch; ++s) {
             const int64_t jc = j0 + s;
-            const bool live = jc < nch;
             const ChainStage &c = st[s];
             const bf16x8 *sb = &sbuf[jc & 1][0][lane];
             // S' = dec S + Bm - L S for the wave's 32 rows
@@ -576,29 +550,17 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     acc[t][i] = c.dec[t][i] * S[t][i] + (float)c.bm[4 * t + i];
-            // O^T = S^T Q^^T + O0^T: this lane gets token row 16 w + m, value
-            // channels 16 blk + 4 b .. + 3 (the state fragments serve as A)
-            f32x4 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[i] = (float)c.o0[i];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 f = sb[ks * 64];
                 acc[0] = mfma16(c.ln[0][ks], f, acc[0]);
                 acc[1] = mfma16(c.ln[1][ks], f, acc[1]);
-                o = mfma16(f, c.qh[ks], o);
             }
-            if (live) {
+            if (jc < nch) {
                 S[0] = acc[0];
                 S[1] = acc[1];
             }
             sbuf[(jc + 1) & 1][w][lane] = acc_to_frag(S[0], S[1]);
-            bf16x4 y;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                y[i] = (bf16)(o[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-(float)c.z[i])));
-            ybuf[jc & 1][16 * w + m][b] = y;
             load_stage(st[s], jc + kPrefetch);
             __syncthreads();
         }
@@ -609,6 +571,58 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 final_state[sbase + (32 * w + 16 * t + 4 * b + i) * kDV + col] = S[t][i];
+    }
+}
+
+// Output of every chunk, in parallel: O = Q^ S + O0 with S the chunk's entry
+// state, then the gate.  Wave t produces token rows 16 t .. 16 t + 15 of the
+// chunk for all value blocks; as O^T = S^T Q^^T + O0^T each lane gets one token
+// row and 4 consecutive value channels (8-byte gate loads and output stores).
+__global__ __launch_bounds__(256) void kda_output_bf16_kernel(
+    const bf16 *__restrict__ gate, bf16 *__restrict__ out, const int32_t *__restrict__ cu,
+    int N, int T, int H, const uint8_t *__restrict__ ws)
+{
+    const int64_t slot = blockIdx.x;
+    const int h = blockIdx.y;
+    int n;
+    int64_t j;
+    if (!slot_to_chunk(cu, N, T, slot, n, j))
+        return;
+    const SeqInfo si = seq_info(cu, n, T, kChunk);
+    const int64_t tok0 = si.bos + j * kChunk;
+    const int64_t lenc = si.len - j * kChunk;
+    const uint8_t *rec = ws + ((int64_t)slot * H + h) * (int64_t)kRecBytes;
+    const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+    const int m = lane & 15, b = lane >> 4;
+    const int64_t row = 16 * t + m;
+    const int64_t rr = row < lenc ? row : lenc - 1;
+    const bf16 *zrow = gate + ((tok0 + rr) * H + h) * kDV + 4 * b;
+    bf16 *orow = out + ((tok0 + row) * H + h) * kDV + 4 * b;
+
+    bf16x8 qh[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        qh[ks] = *reinterpret_cast<const bf16x8 *>(rec + kOffQH + (t * 4 + ks) * kFragBytes +
+                                                   lane * 16);
+#pragma unroll 2
+    for (int blk = 0; blk < kNumVBlocks; ++blk) {
+        const bf16x4 o0 = *reinterpret_cast<const bf16x4 *>(rec + kOffO0 + blk * 2048 + t * 512 +
+                                                            lane * 8);
+        const bf16x4 z = *reinterpret_cast<const bf16x4 *>(zrow + kVBlock * blk);
+        f32x4 o = {(float)o0[0], (float)o0[1], (float)o0[2], (float)o0[3]};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 sb = *reinterpret_cast<const bf16x8 *>(
+                rec + kOffSB + blk * 4096 + ks * kFragBytes + lane * 16);
+            o = mfma16(sb, qh[ks], o);
+        }
+        if (row < lenc) {
+            bf16x4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                y[i] = (bf16)(o[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-(float)z[i])));
+            *reinterpret_cast<bf16x4 *>(orow + kVBlock * blk) = y;
+        }
     }
 }
 
@@ -638,8 +652,15 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     if (units > 0) {
         const int64_t blocks = (units + 7) / 8 * 8 * kNumVBlocks;
         hipLaunchKernelGGL(kda_chain_bf16_kernel, dim3((unsigned)blocks), dim3(kChainThreads), 0,
-                           stream,
-                           gate, init, out, final_state, cu, T, H, (int)units,
+                           stream, init, final_state, cu, T, H, (int)units,
+                           static_cast<uint8_t *>(workspace));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    if (n_slots > 0 && H > 0) {
+        hipLaunchKernelGGL(kda_output_bf16_kernel, dim3((unsigned)n_slots, (unsigned)H), dim3(256),
+                           0, stream, gate, out, cu, N, T, H,
                            static_cast<const uint8_t *>(workspace));
         return hipGetLastError();
     }

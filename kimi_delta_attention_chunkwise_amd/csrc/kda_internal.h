@@ -44,13 +44,17 @@ constexpr int kNumVBlocks = kDV / kVBlock;
 //         columns 16 block + 4 b .. + 3
 //                                                                  (16 KiB)
 //   DEC : exp(G_end) per key channel, fp32                        (512 B)
+//   SB  : the state on entry to the chunk, per value block, as the 4 k-step
+//         B fragments (bf16, perm order) the output product reads  (32 KiB)
+// LN, QH, BM, O0 and DEC are written by the prep kernel, SB by the chain.
 constexpr size_t kFragBytes = 1024;
 constexpr size_t kOffLN = 0;
 constexpr size_t kOffQH = kOffLN + 32 * kFragBytes;
 constexpr size_t kOffBM = kOffQH + 16 * kFragBytes;
 constexpr size_t kOffO0 = kOffBM + kNumVBlocks * 4096;
 constexpr size_t kOffDEC = kOffO0 + kNumVBlocks * 2048;
-constexpr size_t kRecBytes = kOffDEC + kDK * sizeof(float);
+constexpr size_t kOffSB = kOffDEC + kDK * sizeof(float);
+constexpr size_t kRecBytes = kOffSB + kNumVBlocks * 4 * kFragBytes;
 static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
 
 // Row of the k-step-local permutation described above.

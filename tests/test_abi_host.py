@@ -16,7 +16,6 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
 OK, NULLP, SHAPE, DTYPE, UNSUP, WS, HIP = range(7)
-REC = 74240   # bytes per (chunk slot, head) record of the bf16 path
 
 
 def declared_functions():
@@ -67,6 +66,8 @@ def test_supported_sets(lib):
 
 def test_workspace_bytes(lib):
     ws = lib.kda_chunk_fwd_workspace_bytes
+    REC = ws(1, 64, 1, 1, 128, 128, 64, 1, 0)       # one 64-token chunk of one head
+    assert REC > 0 and REC % 256 == 0
     # fixed length: B * ceil(T / 64) slots per head
     assert ws(1, 4096, 1, 8, 128, 128, 64, 1, 0) == 64 * 8 * REC
     assert ws(3, 100, 3, 2, 128, 128, 64, 1, 0) == 3 * 2 * 2 * REC
@@ -95,6 +96,7 @@ def _chunk(lib, **kw):
 
 
 def test_chunk_fwd_rejects_bad_arguments_before_launch(lib):
+    REC = lib.kda_chunk_fwd_workspace_bytes(1, 64, 1, 1, 128, 128, 64, 1, 0)
     assert _chunk(lib, dt=7) == DTYPE
     assert _chunk(lib, dk=64, dv=64) == UNSUP
     assert _chunk(lib, chunk=16) == UNSUP
