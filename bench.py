@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the KDA hot path on one MI355X.
 
-One step = one ``kda_chunk_fwd`` call (prep + chain kernels) over one batch of
+One step = one ``kda_chunk_fwd`` call (prep, chain and output kernels) over one batch of
 the prefill workload (B=1, H=8, T=4096, dk=dv=128, bf16 inputs, fp32 state,
 64-token chunks).  Inputs are resident in HBM before timing starts; the steps
 rotate over several independent input sets whose total size exceeds the
@@ -43,7 +43,7 @@ CHUNK = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_prefill_t4096_h8_traffic.json")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "kimi_delta_attention_chunkwise_amd", "csrc", f)
-    for f in ("kda_chunk_bf16.hip", "kda_internal.h", "kda_api.hip")
+    for f in ("kda_chunk_bf16.hip", "kda_decode.hip", "kda_internal.h", "kda_api.hip")
 ]
 
 
@@ -61,9 +61,10 @@ def source_digest(paths=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(bytes_per_call):
-    """HBM traffic per call from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel sources; else None."""
+def load_traffic(key):
+    """HBM bytes (``hbm_bytes_per_call`` for prefill, ``decode_hbm_bytes_per_step``
+    for decode) from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
@@ -71,7 +72,7 @@ def load_traffic(bytes_per_call):
         return None
     if t.get("source_digest") != source_digest():
         return None
-    return float(t["hbm_bytes_per_call"])
+    return float(t[key])
 
 
 def parse():
@@ -157,7 +158,7 @@ def main():
     flops_call = flops_per_token_head() * token_heads
     t_s = ms / 1e3
     achieved = bytes_call / t_s / 1e9
-    traffic = load_traffic(bytes_call)
+    traffic = load_traffic("hbm_bytes_per_call")
     result = {
         "metric": "KDA prefill tokens/s + decode steps/s; % bf16 MFMA peak / % HBM GB/s peak",
         "value": tokens / t_s,
@@ -174,7 +175,7 @@ def main():
         "config": {"workload": "prefill_t4096_h8", "B": B, "T": T, "H": H, "dk": DK, "dv": DV,
                    "chunk": CHUNK, "global_batch": B, "seq_len": T, "parallelism": "none",
                    "state": "fp32, zero init, final state written", "input_sets": n_sets},
-        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd (prep + chain kernels)",
+        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd call (prep + chain + output kernels)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_call": bytes_call},
@@ -225,6 +226,7 @@ def bench_decode(torch, kda, W, dev, args):
             "ms_per_step": ms, "steps_per_s": 1e3 / ms, "tokens_per_s": N * 1e3 / ms,
             "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": load_traffic("decode_hbm_bytes_per_step"),
                          "algorithmic_bytes_per_step": bytes_step}}
 
 

@@ -29,17 +29,22 @@
 // 16 tokens (5 * 16 = 80 < ln(FLT_MAX) = 88.7).  Below the diagonal the
 // column factor is formed as e^{B_j - G_s} e^{B_i - B_j}.
 //
-// Two kernels:
-//   prep  (512 threads per (chunk slot, head); all chunks in parallel):
-//         G, A and P (bf16 MFMA), T (fp32 substitution), W and U~ (MFMA), then
-//         L, Bm, Q^ and O0 (MFMA) written as the chain's operands.
-//   chain (256 threads per (sequence, head, 16-wide value block)): walks the
-//         chunks in order.  Wave w keeps rows 32 w .. 32 w + 31 of the fp32
-//         state slice in its accumulators and computes those rows of
-//         S' = dec S + Bm - L S and rows 16 w .. 16 w + 15 of O = Q^ S + O0;
-//         the four waves exchange the new state as bf16 MFMA fragments
-//         through 8 KiB of LDS, one barrier per chunk.  The operands of the
-//         next chunks are prefetched into registers.
+// Three kernels, in stream order:
+//   prep   (512 threads per (chunk slot, head); all chunks in parallel):
+//          G, A and P (bf16 MFMA), T (fp32 substitution and fp32 MFMA), W and
+//          U~ (MFMA), then L, Bm, Q^ and O0 (MFMA) written to the chunk's
+//          workspace record as the later kernels' operand fragments.
+//   chain  (320 threads per (sequence, head, 16-wide value block)): walks the
+//          chunks in order and carries only the state.  Compute wave w keeps
+//          rows 32 w .. 32 w + 31 of the fp32 state slice in its accumulators
+//          and computes those rows of S' = dec S + Bm - L S; the four compute
+//          waves exchange the new state as bf16 MFMA fragments through LDS,
+//          one barrier per chunk, with the operands of the next chunks
+//          prefetched into registers.  A fifth wave copies each chunk's entry
+//          state fragments from LDS to the record, so no wave has both loads
+//          and stores in flight.
+//   output (256 threads per (chunk slot, head)): O = Q^ S + O0 from the
+//          record, gated by sigmoid(z), rounded to bf16; all chunks in parallel.
 #include "kda_internal.h"
 
 #include <mutex>
