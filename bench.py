@@ -241,7 +241,7 @@ def cpu_baseline(w):
     threads = max(1, min(os.cpu_count() or 1, 16))
     units = w.B * w.H
     reps, elapsed = 0, 0.0
-    while elapsed < 10.0 and reps < 20:
+    while elapsed < 10.0 and reps < 5000:
         t0 = time.perf_counter()
         oracle.forward(*arrs, n_threads=threads)
         elapsed += time.perf_counter() - t0

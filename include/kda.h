@@ -122,6 +122,34 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void
                          int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* State snapshots for prefix caching and replay ("Kimi K3 second-pass study
+ * ledger", section 1 row Q31 and section 3 Fig. 12: the serving engine keeps
+ * sparse checkpoints of the fixed-size KDA state at hash-block boundaries, and
+ * a cache hit resumes from such a checkpoint).
+ *
+ * kda_chunk_fwd_snapshots is kda_chunk_fwd plus `snapshots`: when non-NULL,
+ * the fp32 state after the first m * snapshot_interval tokens of each sequence
+ * is written for m = 1 .. floor(len / snapshot_interval) (a sequence whose
+ * length is a multiple of the interval gets its final state as its last
+ * snapshot).  snapshot_interval must be a positive multiple of `chunk`
+ * (else KDA_ERR_BAD_SHAPE).  Snapshot m of sequence n goes to slot
+ *     n * floor(T / interval) + m - 1                 (cu_seqlens NULL)
+ *     floor(cu_seqlens[n] / interval) + n + m - 1     (cu_seqlens given)
+ * of snapshots [slots, H, dk, dv] fp32, slots = kda_snapshot_slots(...);
+ * slots that match no snapshot are not written.  Replaying a sequence from
+ * snapshot m = kda_chunk_fwd on tokens m * interval .. with the snapshot as
+ * init_state.  With snapshots NULL the call is exactly kda_chunk_fwd.
+ * kda_snapshot_slots returns (size_t)-1 for invalid sizes. */
+size_t kda_snapshot_slots(int B, int T, int N, int chunk, int interval, int varlen);
+
+kda_status kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, const void *gate, const float *init_state,
+                                   void *out, float *final_state, float *snapshots,
+                                   int snapshot_interval, const int32_t *cu_seqlens, int B,
+                                   int T, int N, int H, int dk, int dv, int chunk, float scale,
+                                   kda_dtype dt, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 /* One O(1) recurrent decode step for N independent sequences, updating the
  * state in place ("Kimi K3 second-pass study ledger", section 1 row Q07;
  * section 8 device row, fused decode): decay, prediction, correction, write,

@@ -9,8 +9,11 @@ If the library is missing the calls raise ``KdaLibraryError``.
 Entry points (names follow the C ABI):
   chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
             cu_seqlens=None, chunk=None, scale=1.0) -> (out, final_state)
+  chunk_fwd_snapshots(q, k, v, g, beta, gate, interval, ...)
+            -> (out, final_state, snapshots)
   decode_step(q, k, v, g, beta, gate, state, scale=1.0) -> out   (state in place)
-  chunk_fwd_workspace_bytes(...), chunk_fwd_supported(...), decode_step_supported(...)
+  chunk_fwd_workspace_bytes(...), snapshot_slots(...), chunk_fwd_supported(...),
+  decode_step_supported(...)
 """
 from __future__ import annotations
 
@@ -20,7 +23,8 @@ import os
 import torch
 
 __all__ = [
-    "KdaError", "KdaLibraryError", "chunk_fwd", "decode_step", "chunk_fwd_workspace_bytes",
+    "KdaError", "KdaLibraryError", "chunk_fwd", "chunk_fwd_snapshots", "decode_step",
+    "chunk_fwd_workspace_bytes", "snapshot_slots", "snapshot_index",
     "chunk_fwd_supported", "decode_step_supported", "library_path", "load_library",
     "KDA_F32", "KDA_BF16", "G_MIN",
 ]
@@ -54,6 +58,10 @@ _SIGNATURES = {
     "kda_chunk_fwd_workspace_bytes": ([ctypes.c_int] * 9, ctypes.c_size_t),
     "kda_chunk_fwd": ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "kda_snapshot_slots": ([ctypes.c_int] * 6, ctypes.c_size_t),
+    "kda_chunk_fwd_snapshots": ([ctypes.c_void_p] * 10 + [ctypes.c_int] + [ctypes.c_void_p]
+                                + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
+                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "kda_decode_step": ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
                         ctypes.c_void_p], ctypes.c_int),
 }
@@ -133,19 +141,31 @@ def _need(t: torch.Tensor, name: str, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
-              cu_seqlens=None, chunk=None, scale=1.0, workspace=None, out=None,
-              final_state=None):
-    """Chunkwise-parallel KDA forward on the GPU.
+def snapshot_slots(B: int, T: int, N: int, chunk: int, interval: int, varlen: bool) -> int:
+    """Number of snapshot slots ``kda_chunk_fwd_snapshots`` indexes for these sizes."""
+    n = load_library().kda_snapshot_slots(B, T, N, chunk, interval, int(varlen))
+    if n == ctypes.c_size_t(-1).value:
+        raise KdaError("invalid sizes or snapshot interval")
+    return int(n)
 
-    q, k, g ``[B, T, H, dk]``; v, gate ``[B, T, H, dv]``; beta ``[B, T, H]``, all
-    of one dtype (bf16 or fp32) on one HIP device.  ``gate`` holds logits.
-    ``init_state``: fp32 ``[N, H, dk, dv]`` or None.  ``cu_seqlens``: int32
-    ``[N + 1]`` on the device (then B must be 1) or None (N = B).
-    Optional preallocated ``workspace`` (uint8, at least
-    ``chunk_fwd_workspace_bytes`` bytes), ``out`` and ``final_state``.
-    Returns ``(out, final_state)``; final_state is None unless requested.
-    """
+
+def snapshot_index(lengths, interval: int, varlen: bool, T: int | None = None):
+    """Host-side map of the snapshot slots: a list of (sequence n, tokens m *
+    interval, slot) for every snapshot the library writes.  ``lengths`` are the
+    sequence lengths (for varlen, in packing order); ``T`` is the common
+    length when not varlen."""
+    res = []
+    start = 0
+    for n, ln in enumerate(lengths):
+        base = (start // interval + n) if varlen else n * (T // interval)
+        for m in range(1, ln // interval + 1):
+            res.append((n, m * interval, base + m - 1))
+        start += ln
+    return res
+
+
+def _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state, cu_seqlens, chunk,
+                scale, workspace, out, final_state, interval, snapshots):
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
@@ -189,12 +209,54 @@ def chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < nbytes:
         raise ValueError(f"workspace must be a uint8 tensor of at least {nbytes} bytes on {dev}")
-    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
-                           _ptr(init_state), _ptr(out), _ptr(final_state), _ptr(cu_seqlens),
-                           B, T, N, H, dk, dv, chunk, float(scale), code, _ptr(workspace),
-                           workspace.numel(), _stream_ptr(dev))
+    if interval is None:
+        st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
+                               _ptr(init_state), _ptr(out), _ptr(final_state), _ptr(cu_seqlens),
+                               B, T, N, H, dk, dv, chunk, float(scale), code, _ptr(workspace),
+                               workspace.numel(), _stream_ptr(dev))
+        _check(st)
+        return out, final_state, None
+    slots = snapshot_slots(B, T, N, chunk, int(interval), cu_seqlens is not None)
+    if snapshots is None:
+        snapshots = torch.empty((slots, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _need(snapshots, "snapshots", (slots, H, dk, dv), torch.float32, dev)
+    st = lib.kda_chunk_fwd_snapshots(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate), _ptr(init_state), _ptr(out),
+        _ptr(final_state), _ptr(snapshots), int(interval), _ptr(cu_seqlens), B, T, N, H, dk, dv,
+        chunk, float(scale), code, _ptr(workspace), workspace.numel(), _stream_ptr(dev))
     _check(st)
+    return out, final_state, snapshots
+
+
+def chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
+              cu_seqlens=None, chunk=None, scale=1.0, workspace=None, out=None,
+              final_state=None):
+    """Chunkwise-parallel KDA forward on the GPU.
+
+    q, k, g ``[B, T, H, dk]``; v, gate ``[B, T, H, dv]``; beta ``[B, T, H]``, all
+    of one dtype (bf16 or fp32) on one HIP device.  ``gate`` holds logits.
+    ``init_state``: fp32 ``[N, H, dk, dv]`` or None.  ``cu_seqlens``: int32
+    ``[N + 1]`` on the device (then B must be 1) or None (N = B).
+    Optional preallocated ``workspace`` (uint8, at least
+    ``chunk_fwd_workspace_bytes`` bytes), ``out`` and ``final_state``.
+    Returns ``(out, final_state)``; final_state is None unless requested.
+    """
+    out, final_state, _ = _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state,
+                                      cu_seqlens, chunk, scale, workspace, out, final_state,
+                                      None, None)
     return out, final_state
+
+
+def chunk_fwd_snapshots(q, k, v, g, beta, gate, interval, init_state=None,
+                        output_final_state=True, cu_seqlens=None, chunk=None, scale=1.0,
+                        workspace=None, out=None, final_state=None, snapshots=None):
+    """``chunk_fwd`` that also returns fp32 state snapshots every ``interval``
+    tokens of each sequence (a multiple of the chunk length), as
+    ``[snapshot_slots(...), H, dk, dv]``; ``snapshot_index`` maps slots to
+    (sequence, token count).  Returns ``(out, final_state, snapshots)``."""
+    return _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state, cu_seqlens,
+                       chunk, scale, workspace, out, final_state, interval, snapshots)
 
 
 def decode_step(q, k, v, g, beta, gate, state, scale=1.0, out=None):

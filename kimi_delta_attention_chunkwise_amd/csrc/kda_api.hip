@@ -72,11 +72,23 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
     return (size_t)chunk_slots(B, T, N, chunk, varlen) * (size_t)H * kda::kRecBytes;
 }
 
-kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
-                         const void *beta, const void *gate, const float *init_state,
-                         void *out, float *final_state, const int32_t *cu_seqlens, int B, int T,
-                         int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
-                         void *workspace, size_t workspace_bytes, hipStream_t stream)
+size_t kda_snapshot_slots(int B, int T, int N, int chunk, int interval, int varlen)
+{
+    if (B < 1 || T < 0 || N < 0 || chunk < 1 || interval < chunk || interval % chunk != 0 ||
+        (varlen && B != 1) || (!varlen && N != B))
+        return (size_t)-1;
+    if (varlen)
+        return (size_t)(T / interval) + (size_t)N;
+    return (size_t)B * (size_t)(T / interval);
+}
+
+kda_status kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, const void *gate, const float *init_state,
+                                   void *out, float *final_state, float *snapshots,
+                                   int snapshot_interval, const int32_t *cu_seqlens, int B,
+                                   int T, int N, int H, int dk, int dv, int chunk, float scale,
+                                   kda_dtype dt, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream)
 {
     if (!valid_dtype(dt))
         return KDA_ERR_BAD_DTYPE;
@@ -86,6 +98,8 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void
     if (B < 1 || T < 0 || N < 0 || H < 1)
         return KDA_ERR_BAD_SHAPE;
     if (varlen ? B != 1 : N != B)
+        return KDA_ERR_BAD_SHAPE;
+    if (snapshots && (snapshot_interval < chunk || snapshot_interval % chunk != 0))
         return KDA_ERR_BAD_SHAPE;
     const bool has_tokens = (int64_t)B * T > 0;
     if (has_tokens && (!q || !k || !v || !g || !beta || !gate || !out))
@@ -97,16 +111,28 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void
         return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (N == 0)
         return KDA_OK;
+    const int interval = snapshots ? snapshot_interval : 0;
     if (dt == KDA_F32)
         return from_hip(kda::launch_chunk_f32(
             (const float *)q, (const float *)k, (const float *)v, (const float *)g,
             (const float *)beta, (const float *)gate, init_state, (float *)out, final_state,
-            cu_seqlens, N, T, H, scale, stream));
+            snapshots, interval, cu_seqlens, N, T, H, scale, stream));
     return from_hip(kda::launch_chunk_bf16(
         (const kda::bf16 *)q, (const kda::bf16 *)k, (const kda::bf16 *)v, (const kda::bf16 *)g,
         (const kda::bf16 *)beta, (const kda::bf16 *)gate, init_state, (kda::bf16 *)out,
-        final_state, cu_seqlens, N, T, H, chunk_slots(B, T, N, chunk, varlen), scale, workspace,
-        stream));
+        final_state, snapshots, interval, cu_seqlens, N, T, H,
+        chunk_slots(B, T, N, chunk, varlen), scale, workspace, stream));
+}
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const void *gate, const float *init_state,
+                         void *out, float *final_state, const int32_t *cu_seqlens, int B, int T,
+                         int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return kda_chunk_fwd_snapshots(q, k, v, g, beta, gate, init_state, out, final_state,
+                                   nullptr, 0, cu_seqlens, B, T, N, H, dk, dv, chunk, scale, dt,
+                                   workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *g,

@@ -473,11 +473,18 @@ __device__ __forceinline__ void chain_load(ChainStage &st, const uint8_t *rec, i
 
 }  // namespace
 
+// With kSnap the chain also writes fp32 state snapshots every snap_chunks
+// chunks (see snap_slot0): the compute waves park the state in LDS at a
+// snapshot boundary and the store wave writes it out in the next iteration, so
+// the compute waves still issue no stores inside the loop.
+template <bool kSnap>
 __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
-    const float *__restrict__ init, float *__restrict__ final_state,
-    const int32_t *__restrict__ cu, int T, int H, int units, uint8_t *__restrict__ ws)
+    const float *__restrict__ init, float *__restrict__ final_state, float *__restrict__ snaps,
+    int snap_chunks, const int32_t *__restrict__ cu, int T, int H, int units,
+    uint8_t *__restrict__ ws)
 {
     __shared__ bf16x8 sbuf[2][4][64];                 // state as 4 k-step fragments
+    __shared__ float snap_s[kSnap ? 2 : 1][kSnap ? kDK : 1][kVBlock];
 
     // all value blocks of one (sequence, head) land on the same XCD (blocks are
     // dealt to the 8 XCDs round-robin), so they share that XCD's L2
@@ -493,12 +500,29 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     const SeqInfo si = seq_info(cu, n, T, kChunk);
     const int64_t nch = (si.len + kChunk - 1) / kChunk;
     auto rec_of = [&](int64_t jc) { return ws + ((si.slot0 + jc) * H + h) * (int64_t)kRecBytes; };
+    // a snapshot is due on entry to chunk jb (after jb full chunks)
+    auto snap_at = [&](int64_t jb) {
+        return kSnap && jb >= 1 && jb <= nch && jb % snap_chunks == 0 && jb * kChunk <= si.len;
+    };
 
     // the chunk loop runs in rounds of kPrefetch iterations; iterations past the
     // last chunk (at most kPrefetch - 1) leave the state unchanged
     const int64_t niter = (nch + kPrefetch - 1) / kPrefetch * kPrefetch;
     if (w == kComputeWaves) {
         // store wave: copy the entry state of chunk jc (4 fragments, 16 B per lane each)
+        // snapshot jb: rows 16 i + lane / 4, channels 16 blk + 4 (lane % 4) .. + 3
+        auto write_snap = [&](int64_t jb) {
+            const int64_t slot =
+                snap_slot0(cu, n, T, snap_chunks * kChunk) + jb / snap_chunks - 1;
+            float *dst = snaps + (slot * H + h) * (int64_t)(kDK * kDV) + kVBlock * blk +
+                         4 * (lane & 3);
+#pragma unroll
+            for (int i = 0; i < kDK / 16; ++i) {
+                const int row = 16 * i + (lane >> 2);
+                *reinterpret_cast<f32x4 *>(dst + row * kDV) =
+                    *reinterpret_cast<const f32x4 *>(&snap_s[jb & 1][row][4 * (lane & 3)]);
+            }
+        };
         __syncthreads();
         for (int64_t jc = 0; jc < niter; ++jc) {
             if (jc < nch) {
@@ -507,7 +531,15 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
                 for (int ks = 0; ks < 4; ++ks)
                     dst[ks * 64] = sbuf[jc & 1][ks][lane];
             }
+            if constexpr (kSnap) {
+                if (snap_at(jc))
+                    write_snap(jc);
+            }
             __syncthreads();
+        }
+        if constexpr (kSnap) {
+            if (snap_at(niter))
+                write_snap(niter);
         }
         return;
     }
@@ -566,6 +598,15 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
                 S[1] = acc[1];
             }
             sbuf[(jc + 1) & 1][w][lane] = acc_to_frag(S[0], S[1]);
+            if constexpr (kSnap) {
+                if (snap_at(jc + 1)) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            snap_s[(jc + 1) & 1][32 * w + 16 * t + 4 * b + i][m] = S[t][i];
+                }
+            }
             load_stage(st[s], jc + kPrefetch);
             __syncthreads();
         }
@@ -580,13 +621,21 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
 }
 
 // Output of every chunk, in parallel: O = Q^ S + O0 with S the chunk's entry
-// state, then the gate.  Wave t produces token rows 16 t .. 16 t + 15 of the
-// chunk for all value blocks; as O^T = S^T Q^^T + O0^T each lane gets one token
-// row and 4 consecutive value channels (8-byte gate loads and output stores).
+// state, then the gate.  The workgroup copies the chunk's 32 KiB of state
+// fragments into LDS once; wave t then forms token rows 16 t .. 16 t + 15 as
+// O^T = S^T Q^^T + O0^T (each lane: one token row, 4 consecutive value
+// channels) for four value blocks at a time, parks the fp32 tile in LDS, and
+// reads it back row-major so that gate loads and output stores are 16 bytes
+// per lane and whole 128-byte lines per 8 lanes.
+constexpr int kOutLd = 68;        // fp32 row stride of a wave's 16 x 64 staging tile
+
 __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
     const bf16 *__restrict__ gate, bf16 *__restrict__ out, const int32_t *__restrict__ cu,
     int N, int T, int H, const uint8_t *__restrict__ ws)
 {
+    __shared__ bf16x8 sb_s[kNumVBlocks * 4][64];
+    __shared__ float ot_s[4][kSub][kOutLd];
+
     const int64_t slot = blockIdx.x;
     const int h = blockIdx.y;
     int n;
@@ -597,44 +646,73 @@ __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
     const int64_t tok0 = si.bos + j * kChunk;
     const int64_t lenc = si.len - j * kChunk;
     const uint8_t *rec = ws + ((int64_t)slot * H + h) * (int64_t)kRecBytes;
-    const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, t = tid >> 6;
     const int m = lane & 15, b = lane >> 4;
-    const int64_t row = 16 * t + m;
-    const int64_t rr = row < lenc ? row : lenc - 1;
-    const bf16 *zrow = gate + ((tok0 + rr) * H + h) * kDV + 4 * b;
-    bf16 *orow = out + ((tok0 + row) * H + h) * kDV + 4 * b;
 
+    // state fragments: 2048 x 16 B, 8 per thread
+    const bf16x8 *sbg = reinterpret_cast<const bf16x8 *>(rec + kOffSB);
+    bf16x8 stage[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        stage[i] = sbg[i * 256 + tid];
     bf16x8 qh[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
         qh[ks] = *reinterpret_cast<const bf16x8 *>(rec + kOffQH + (t * 4 + ks) * kFragBytes +
                                                    lane * 16);
-#pragma unroll 2
-    for (int blk = 0; blk < kNumVBlocks; ++blk) {
-        const bf16x4 o0 = *reinterpret_cast<const bf16x4 *>(rec + kOffO0 + blk * 2048 + t * 512 +
-                                                            lane * 8);
-        const bf16x4 z = *reinterpret_cast<const bf16x4 *>(zrow + kVBlock * blk);
-        f32x4 o = {(float)o0[0], (float)o0[1], (float)o0[2], (float)o0[3]};
+    bf16x4 o0[kNumVBlocks];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 sb = *reinterpret_cast<const bf16x8 *>(
-                rec + kOffSB + blk * 4096 + ks * kFragBytes + lane * 16);
-            o = mfma16(sb, qh[ks], o);
-        }
-        if (row < lenc) {
-            bf16x4 y;
+    for (int blk = 0; blk < kNumVBlocks; ++blk)
+        o0[blk] = *reinterpret_cast<const bf16x4 *>(rec + kOffO0 + blk * 2048 + t * 512 +
+                                                    lane * 8);
+    bf16x8 *sbl = &sb_s[0][0];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                y[i] = (bf16)(o[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-(float)z[i])));
-            *reinterpret_cast<bf16x4 *>(orow + kVBlock * blk) = y;
+    for (int i = 0; i < 8; ++i)
+        sbl[i * 256 + tid] = stage[i];
+    __syncthreads();
+
+    // read-back mapping: lane -> row 8 p + lane / 8 of the wave's tile, channels 8 (lane % 8) ..
+    const int rq = lane >> 3, c8 = 8 * (lane & 7);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int blk = 4 * half + bb;
+            f32x4 o = {(float)o0[blk][0], (float)o0[blk][1], (float)o0[blk][2],
+                       (float)o0[blk][3]};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                o = mfma16(sb_s[blk * 4 + ks][lane], qh[ks], o);
+            *reinterpret_cast<f32x4 *>(&ot_s[t][m][16 * bb + 4 * b]) = o;
         }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int r = 8 * p + rq;
+            const int64_t row = 16 * t + r;
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(&ot_s[t][r][c8]);
+            const f32x4 hi = *reinterpret_cast<const f32x4 *>(&ot_s[t][r][c8 + 4]);
+            if (row < lenc) {
+                const int64_t off = ((tok0 + row) * H + h) * kDV + 64 * half + c8;
+                const bf16x8 z = *reinterpret_cast<const bf16x8 *>(gate + off);
+                bf16x8 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    y[i] = (bf16)(lo[i] * sigmoidf_((float)z[i]));
+                    y[4 + i] = (bf16)(hi[i] * sigmoidf_((float)z[4 + i]));
+                }
+                *reinterpret_cast<bf16x8 *>(out + off) = y;
+            }
+        }
+        __syncthreads();
     }
 }
 
 hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                              const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
-                             float *final_state, const int32_t *cu, int N, int T, int H,
-                             int64_t n_slots, float scale, void *workspace, hipStream_t stream)
+                             float *final_state, float *snaps, int snap_interval,
+                             const int32_t *cu, int N, int T, int H, int64_t n_slots,
+                             float scale, void *workspace, hipStream_t stream)
 {
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
@@ -656,9 +734,15 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     const int64_t units = (int64_t)N * H;
     if (units > 0) {
         const int64_t blocks = (units + 7) / 8 * 8 * kNumVBlocks;
-        hipLaunchKernelGGL(kda_chain_bf16_kernel, dim3((unsigned)blocks), dim3(kChainThreads), 0,
-                           stream, init, final_state, cu, T, H, (int)units,
-                           static_cast<uint8_t *>(workspace));
+        if (snaps)
+            hipLaunchKernelGGL(kda_chain_bf16_kernel<true>, dim3((unsigned)blocks),
+                               dim3(kChainThreads), 0, stream, init, final_state, snaps,
+                               snap_interval / kChunk, cu, T, H, (int)units,
+                               static_cast<uint8_t *>(workspace));
+        else
+            hipLaunchKernelGGL(kda_chain_bf16_kernel<false>, dim3((unsigned)blocks),
+                               dim3(kChainThreads), 0, stream, init, final_state, snaps, 1, cu, T,
+                               H, (int)units, static_cast<uint8_t *>(workspace));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

@@ -30,7 +30,8 @@ __global__ __launch_bounds__(256) void kda_chunk_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ gate,
     const float *__restrict__ init, float *__restrict__ out, float *__restrict__ final_state,
-    const int32_t *__restrict__ cu, int T, int H, float scale)
+    float *__restrict__ snaps, int snap_interval, const int32_t *__restrict__ cu, int T, int H,
+    float scale)
 {
     __shared__ float sS[D][LD], sG[D][LD], sQb[D][LD], sKb[D][LD], sKc[D][LD], sKp[D][LD];
     __shared__ float sX[D][LD], sVb[D][LD], sA[D][LD], sP[D][LD], sT[D][LD], sW[D][LD];
@@ -121,6 +122,12 @@ __global__ __launch_bounds__(256) void kda_chunk_f32_kernel(
             sn += sKp[s][r] * sU[s][c];
         __syncthreads();
         sS[r][c] = sn;
+        // snapshot of the state after the first c0 + L tokens
+        const int64_t pos = c0 + L;
+        if (snaps && pos % snap_interval == 0) {
+            const int64_t slot = snap_slot0(cu, n, T, snap_interval) + pos / snap_interval - 1;
+            snaps[(slot * H + h) * D * D + r * D + c] = sn;
+        }
         __syncthreads();
     }
     __syncthreads();
@@ -130,14 +137,16 @@ __global__ __launch_bounds__(256) void kda_chunk_f32_kernel(
 
 hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, const float *g,
                             const float *beta, const float *gate, const float *init, float *out,
-                            float *final_state, const int32_t *cu, int N, int T, int H,
-                            float scale, hipStream_t stream)
+                            float *final_state, float *snaps, int snap_interval,
+                            const int32_t *cu, int N, int T, int H, float scale,
+                            hipStream_t stream)
 {
     const int64_t units = (int64_t)N * H;
     if (units == 0)
         return hipSuccess;
     hipLaunchKernelGGL(kda_chunk_f32_kernel, dim3((unsigned)units), dim3(256), 0, stream, q, k,
-                       v, g, beta, gate, init, out, final_state, cu, T, H, scale);
+                       v, g, beta, gate, init, out, final_state, snaps, snap_interval, cu, T, H,
+                       scale);
     return hipGetLastError();
 }
 

@@ -103,21 +103,34 @@ __device__ __forceinline__ SeqInfo seq_info(const int32_t *cu, int n, int T, int
     return s;
 }
 
+// First snapshot slot of sequence n for snapshots every `interval` tokens
+// (a multiple of the chunk length).  Snapshot m = 1 .. floor(len / interval)
+// of sequence n, the state after its first m * interval tokens, goes to slot
+// snap_slot0(n) + m - 1.  Without cu_seqlens that is n * floor(T / interval)
+// + m - 1; with cu_seqlens floor(cu[n] / interval) + n + m - 1, injective into
+// [0, floor(T / interval) + N) for the same reason as the chunk slots.
+__device__ __forceinline__ int64_t snap_slot0(const int32_t *cu, int n, int T, int interval)
+{
+    return cu ? (int64_t)cu[n] / interval + n : (int64_t)n * (T / interval);
+}
+
 // ------------------------------------------------------------- launchers
 // All return hipSuccess or the launch error.
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
                          const void *beta, const void *gate, float *state, void *out, int N,
                          int H, int dk, int dv, float scale, int is_bf16, hipStream_t stream);
 
+// snaps / snap_interval: state snapshots (see snap_slot0); NULL / 0 for none.
 hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, const float *g,
                             const float *beta, const float *gate, const float *init,
-                            float *out, float *final_state, const int32_t *cu, int N, int T,
-                            int H, float scale, hipStream_t stream);
+                            float *out, float *final_state, float *snaps, int snap_interval,
+                            const int32_t *cu, int N, int T, int H, float scale,
+                            hipStream_t stream);
 
 hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                              const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
-                             float *final_state, const int32_t *cu, int N, int T, int H,
-                             int64_t n_slots, float scale, void *workspace,
-                             hipStream_t stream);
+                             float *final_state, float *snaps, int snap_interval,
+                             const int32_t *cu, int N, int T, int H, int64_t n_slots,
+                             float scale, void *workspace, hipStream_t stream);
 
 }  // namespace kda

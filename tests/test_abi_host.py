@@ -34,7 +34,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes",
-              "kda_status_str"):
+              "kda_status_str", "kda_chunk_fwd_snapshots", "kda_snapshot_slots"):
         assert n in names
 
 
@@ -111,6 +111,45 @@ def test_chunk_fwd_rejects_bad_arguments_before_launch(lib):
     # nothing to do: zero sequences
     assert _chunk(lib, cu=1, N=0, T=0, q=None, k=None, v=None, g=None, beta=None, gate=None,
                   out=None) == OK
+
+
+def test_snapshot_slots(lib):
+    slots = lib.kda_snapshot_slots
+    bad = ctypes.c_size_t(-1).value
+    assert slots(2, 700, 2, 64, 128, 0) == 2 * 5
+    assert slots(1, 1000, 3, 64, 128, 1) == 1000 // 128 + 3
+    assert slots(1, 0, 0, 64, 64, 1) == 0
+    assert slots(1, 64, 1, 64, 100, 0) == bad          # not a multiple of the chunk
+    assert slots(1, 64, 1, 64, 32, 0) == bad           # shorter than a chunk
+    assert slots(2, 64, 1, 64, 64, 1) == bad           # varlen needs B = 1
+    assert slots(2, 64, 3, 64, 64, 0) == bad           # N must equal B
+
+
+def test_snapshot_index_matches_the_documented_slots():
+    # varlen: floor(cu[n] / I) + n + m - 1; fixed: n * floor(T / I) + m - 1
+    idx = kda.snapshot_index([300, 0, 256, 700], 128, True)
+    assert idx == [(0, 128, 0), (0, 256, 1), (2, 128, 4), (2, 256, 5), (3, 128, 7),
+                   (3, 256, 8), (3, 384, 9), (3, 512, 10), (3, 640, 11)]
+    assert max(s for _, _, s in idx) < 1256 // 128 + 4
+    idx = kda.snapshot_index([700, 700], 192, False, 700)
+    assert idx == [(0, 192, 0), (0, 384, 1), (0, 576, 2), (1, 192, 3), (1, 384, 4), (1, 576, 5)]
+
+
+def test_chunk_fwd_snapshots_rejects_bad_arguments(lib):
+    REC = lib.kda_chunk_fwd_workspace_bytes(1, 64, 1, 1, 128, 128, 64, 1, 0)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(snaps, interval, **kw):
+        a = dict(B=1, T=64, N=1, H=1, ws=1, ws_bytes=REC)
+        a.update(kw)
+        return lib.kda_chunk_fwd_snapshots(p(1), p(1), p(1), p(1), p(1), p(1), None, p(1), None,
+                                           p(snaps), interval, None, a["B"], a["T"], a["N"],
+                                           a["H"], 128, 128, 64, 1.0, 1, p(a["ws"]),
+                                           a["ws_bytes"], None)
+    assert call(1, 100) == SHAPE
+    assert call(1, 0) == SHAPE
+    assert call(1, 64, ws_bytes=REC - 1) == WS
+    assert call(1, 64, B=2) == SHAPE
 
 
 def test_decode_step_rejects_bad_arguments_before_launch(lib):
