@@ -57,7 +57,8 @@ typedef enum {
     KDA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL                 */
     KDA_ERR_BAD_SHAPE = 2,          /* negative/zero size, B > 1 with cu_seqlens  */
     KDA_ERR_BAD_DTYPE = 3,          /* dt is not a kda_dtype value                */
-    KDA_ERR_UNSUPPORTED = 4,        /* (dt, dk, dv, chunk) outside the supported set */
+    KDA_ERR_UNSUPPORTED = 4,        /* (dt, dk, dv, chunk) outside the supported set, or
+                                       more than 2^31 - 1 (chunk slot, head) pairs */
     KDA_ERR_WORKSPACE_TOO_SMALL = 5,/* workspace_bytes below the required size    */
     KDA_ERR_HIP = 6                 /* a HIP launch or runtime call failed        */
 } kda_status;

@@ -111,6 +111,9 @@ kda_status kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, 
         return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (N == 0)
         return KDA_OK;
+    // one workgroup per (chunk slot, head) on a 1-D grid
+    if (dt == KDA_BF16 && chunk_slots(B, T, N, chunk, varlen) * (int64_t)H > INT32_MAX)
+        return KDA_ERR_UNSUPPORTED;
     const int interval = snapshots ? snapshot_interval : 0;
     if (dt == KDA_F32)
         return from_hip(kda::launch_chunk_f32(

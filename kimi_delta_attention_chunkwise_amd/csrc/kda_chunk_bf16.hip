@@ -119,18 +119,14 @@ __device__ __forceinline__ float dpp_add_src(float x)
         __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xf, kBound));
 }
 
-// inclusive prefix sum over the 64 lanes of a wave (lane = row of the chunk):
-// row_shr 1/2/4/8 inside each 16-lane row, then row_bcast 15 (rows 1 and 3
-// take the last lane of the row before) and row_bcast 31 (rows 2 and 3 take
-// lane 31)
-__device__ __forceinline__ float wave_inclusive_sum(float x)
+// inclusive prefix sum over each 16-lane row of a wave (row_shr 1, 2, 4, 8;
+// lanes whose source falls outside the row add 0)
+__device__ __forceinline__ float row_inclusive_sum(float x)
 {
     x += dpp_add_src<0x111, 0xf, true>(x);
     x += dpp_add_src<0x112, 0xf, true>(x);
     x += dpp_add_src<0x114, 0xf, true>(x);
     x += dpp_add_src<0x118, 0xf, true>(x);
-    x += dpp_add_src<0x142, 0xa, false>(x);
-    x += dpp_add_src<0x143, 0xc, false>(x);
     return x;
 }
 
@@ -159,316 +155,411 @@ __device__ __forceinline__ bool slot_to_chunk(const int32_t *cu, int N, int T, i
 
 }  // namespace
 
+// Inputs of one prep task held in registers: lane (tg, cq) of wave w has
+// tokens 4 tg .. 4 tg + 3 of the chunk and key / value channels
+// 16 w + 4 cq .. 16 w + 4 cq + 3 (tg = lane % 16, cq = lane / 16).
+struct PrepIn {
+    bf16x4 q[4], k[4], v[4], g[4];   // [token within the group]
+    bf16 beta[4];
+};
+
+// One (chunk slot, head) task of the prep kernel.
+struct PrepTask {
+    bool valid;                      // false: padding slot of the varlen bound
+    int h;
+    int len;                         // tokens in the chunk, 1 .. 64
+    int64_t tok0;                    // first token
+    int64_t rec;                     // record index: slot * H + h
+};
+
+__device__ __forceinline__ PrepTask prep_task(const int32_t *cu, int N, int T, int H, int64_t t)
+{
+    // slot-major task order: t = slot * H + h
+    PrepTask pt;
+    const int64_t slot = t / H;
+    pt.h = (int)(t % H);
+    pt.rec = t;
+    int n;
+    int64_t j;
+    pt.valid = slot_to_chunk(cu, N, T, slot, n, j);
+    pt.len = 0;
+    pt.tok0 = 0;
+    if (pt.valid) {
+        const SeqInfo si = seq_info(cu, n, T, kChunk);
+        pt.tok0 = si.bos + j * kChunk;
+        pt.len = (int)((si.len - j * kChunk) < kChunk ? (si.len - j * kChunk) : kChunk);
+    }
+    return pt;
+}
+
+// Rows past the end of the chunk re-read its last row (every load stays in
+// the sequence) and are zeroed when used.
+__device__ __forceinline__ void prep_load(PrepIn &in, const bf16 *q, const bf16 *k, const bf16 *v,
+                                          const bf16 *g, const bf16 *beta, const PrepTask &pt,
+                                          int H, int wave, int tg, int cq)
+{
+    const int ch = 16 * wave + 4 * cq;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int r = 4 * tg + t < pt.len ? 4 * tg + t : pt.len - 1;
+        const int64_t tok = pt.tok0 + r;
+        const int64_t off = (tok * H + pt.h) * (int64_t)kDK + ch;
+        in.q[t] = *reinterpret_cast<const bf16x4 *>(q + off);
+        in.k[t] = *reinterpret_cast<const bf16x4 *>(k + off);
+        in.v[t] = *reinterpret_cast<const bf16x4 *>(v + off);
+        in.g[t] = *reinterpret_cast<const bf16x4 *>(g + off);
+        in.beta[t] = beta[tok * H + pt.h];
+    }
+}
+
+// The prep kernel is persistent: workgroup b handles tasks b, b + G, b + 2 G,
+// ... (G = grid size, a multiple of 8 so that with H a multiple of 8 every
+// task of head h runs on XCD h % 8, where the chain walks head h).  The inputs
+// of the next task are loaded into registers while the current one is in its
+// matrix phases, so only the first task of a workgroup waits for memory.
 __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ g, const bf16 *__restrict__ beta, const int32_t *__restrict__ cu,
-    int N, int T, int H, float scale, uint8_t *__restrict__ ws)
+    int N, int T, int H, int64_t n_tasks, float scale, uint8_t *__restrict__ ws)
 {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
     TSmem &ts = *reinterpret_cast<TSmem *>(smem_raw);
 
-    const int64_t slot = blockIdx.x;
-    const int h = blockIdx.y;
-    int n;
-    int64_t j;
-    if (!slot_to_chunk(cu, N, T, slot, n, j))
-        return;
-    const SeqInfo si = seq_info(cu, n, T, kChunk);
-    const int64_t tok0 = si.bos + j * kChunk;
-    const int len = (int)((si.len - j * kChunk) < kChunk ? (si.len - j * kChunk) : kChunk);
-    uint8_t *rec = ws + ((int64_t)slot * H + h) * (int64_t)kRecBytes;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, b = lane >> 4;
+    const int tg = lane & 15, cq = lane >> 4;     // phase-1 roles: token group, channel quad
 
-    // ---- phase 1: loads, cumulative log-decay, elementwise operands -----------
-    // lane = row r of the chunk, wave = channels 16 w .. 16 w + 15
-    {
-        const int r = lane;
-        const bool ok = r < len;
-        const int64_t orow = ((tok0 + r) * H + h) * (int64_t)kDK + 16 * wave;
-        bf16x8 q8[2] = {}, k8[2] = {}, v8[2] = {}, g8[2] = {};
-        float br = 0.f;
-        if (ok) {
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                q8[h2] = *reinterpret_cast<const bf16x8 *>(q + orow + 8 * h2);
-                k8[h2] = *reinterpret_cast<const bf16x8 *>(k + orow + 8 * h2);
-                v8[h2] = *reinterpret_cast<const bf16x8 *>(v + orow + 8 * h2);
-                g8[h2] = *reinterpret_cast<const bf16x8 *>(g + orow + 8 * h2);
-            }
-            br = (float)beta[(tok0 + r) * H + h];
+    int64_t t = blockIdx.x;
+    PrepTask next = t < n_tasks ? prep_task(cu, N, T, H, t) : PrepTask{};
+    PrepIn in;
+    if (t < n_tasks && next.valid)
+        prep_load(in, q, k, v, g, beta, next, H, wave, tg, cq);
+    for (; t < n_tasks; t += gridDim.x) {
+        const PrepTask pt = next;
+        const int64_t tn = t + gridDim.x;
+        if (tn < n_tasks)
+            next = prep_task(cu, N, T, H, tn);
+        const bool load_next = tn < n_tasks && next.valid;
+        if (!pt.valid) {
+            if (load_next)
+                prep_load(in, q, k, v, g, beta, next, H, wave, tg, cq);
+            continue;
         }
-        for (int i = tid; i < kChunk * kColLd / 8; i += kPrepThreads)   // zero P (upper blocks stay 0)
-            reinterpret_cast<bf16x8 *>(&sm.PM[0][0])[i] = bf16x8{};
-        const int ib = r >> 4;                            // subtile of this row
-        float G[16];
+        uint8_t *rec = ws + pt.rec * (int64_t)kRecBytes;
+
+        // ---- phase 1: cumulative log-decay and elementwise operands -----------
+        // lane (tg, cq): tokens 4 tg .. + 3, channels 16 wave + 4 cq .. + 3
+        {
+            const int ch0 = 16 * wave + 4 * cq;
+            const int ib = tg >> 2;                       // subtile of the lane's tokens
+            for (int i = tid; i < kChunk * kColLd / 8; i += kPrepThreads)   // zero P
+                reinterpret_cast<bf16x8 *>(&sm.PM[0][0])[i] = bf16x8{};
+            // G: inclusive prefix over the lane's 4 tokens, then across the 16
+            // token groups of the row (rows past len carry g = 0)
+            float G[4][4];                                 // [token][channel]
+            float br[4];
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-            G[c] = wave_inclusive_sum((float)g8[c >> 3][c & 7]);
-        // G at the ends of the subtiles: B_1, B_2, B_3 and G_end, per channel
-        if ((lane & 15) == 15) {
+            for (int tt = 0; tt < 4; ++tt)
+                br[tt] = 4 * tg + tt < pt.len ? (float)in.beta[tt] : 0.f;
 #pragma unroll
-            for (int c = 0; c < 16; ++c)
-                sm.Gref[ib][16 * wave + c] = G[c];
+            for (int c = 0; c < 4; ++c) {
+                float run = 0.f;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    run += 4 * tg + tt < pt.len ? (float)in.g[tt][c] : 0.f;
+                    G[tt][c] = run;
+                }
+                const float excl = row_inclusive_sum(run) - run;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    G[tt][c] += excl;
+            }
+            // G at the ends of the subtiles: B_1, B_2, B_3 and G_end
+            if ((tg & 3) == 3)
+                *reinterpret_cast<f32x4 *>(&sm.Gref[ib][ch0]) =
+                    f32x4{G[3][0], G[3][1], G[3][2], G[3][3]};
+            if (wave == 0 && cq == 0) {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    sm.AM[4 * tg + tt][kChunk] = br[tt];  // beta per row, for A
+            }
+            __syncthreads();
+            if (lane < 16) {
+                // per-channel constants of channel 16 w + lane
+                const int ch = 16 * wave + lane;
+                const float b1 = sm.Gref[0][ch], b2 = sm.Gref[1][ch], b3 = sm.Gref[2][ch];
+                const float ge = sm.Gref[3][ch];
+                sm.eB[0][ch] = 1.f;
+                sm.eB[1][ch] = __expf(b1);
+                sm.eB[2][ch] = __expf(b2);
+                sm.eB[3][ch] = __expf(b3);
+                sm.eGB[0][ch] = __expf(ge);
+                sm.eGB[1][ch] = __expf(ge - b1);
+                sm.eGB[2][ch] = __expf(ge - b2);
+                sm.eGB[3][ch] = __expf(ge - b3);
+                sm.F[0][ch] = __expf(b1);                    // e^{B_1 - B_0}
+                sm.F[1][ch] = __expf(b2);                    // e^{B_2 - B_0}
+                sm.F[2][ch] = __expf(b2 - b1);
+                sm.F[3][ch] = __expf(b3);
+                sm.F[4][ch] = __expf(b3 - b1);
+                sm.F[5][ch] = __expf(b3 - b2);
+                reinterpret_cast<float *>(rec + kOffDEC)[ch] = __expf(ge);
+            }
+            __syncthreads();
+            const f32x4 Bi = ib == 0 ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                     : *reinterpret_cast<const f32x4 *>(&sm.Gref[ib - 1][ch0]);
+            const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[ib][ch0]);
+            const f32x4 egb = *reinterpret_cast<const f32x4 *>(&sm.eGB[ib][ch0]);
+            bf16x4 xb[4], vb[4], kp[4];                    // [channel][token]
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int r = 4 * tg + tt;
+                const bool ok = r < pt.len;
+                bf16x4 kr, qr, kc;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float fr = __expf(G[tt][c] - Bi[c]);   // e^{G - B_i} in [e^-80, 1]
+                    const float fc = __builtin_amdgcn_rcpf(fr);  // e^{B_i - G} in [1, e^80]
+                    const float kv = ok ? (float)in.k[tt][c] : 0.f;
+                    const float qv = ok ? (float)in.q[tt][c] : 0.f;
+                    const float vv = ok ? (float)in.v[tt][c] : 0.f;
+                    kr[c] = (bf16)(kv * fr);
+                    qr[c] = (bf16)(qv * fr);
+                    kc[c] = (bf16)(kv * fc);
+                    xb[c][tt] = (bf16)(br[tt] * kv * (fr * eb[c]));    // beta k e^G
+                    vb[c][tt] = (bf16)(br[tt] * vv);                   // beta v
+                    kp[c][tt] = (bf16)(kv * (egb[c] * fc));            // k e^{G_end - G}
+                }
+                *reinterpret_cast<bf16x4 *>(&sm.KR[r][ch0]) = kr;
+                *reinterpret_cast<bf16x4 *>(&sm.QR[r][ch0]) = qr;
+                *reinterpret_cast<bf16x4 *>(&sm.KCD[r][ch0]) = kc;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                *reinterpret_cast<bf16x4 *>(&sm.XB[ch0 + c][4 * tg]) = xb[c];
+                *reinterpret_cast<bf16x4 *>(&sm.VB[ch0 + c][4 * tg]) = vb[c];
+                *reinterpret_cast<bf16x4 *>(&sm.KPT[ch0 + c][4 * tg]) = kp[c];
+            }
         }
         __syncthreads();
-        if (lane < 16) {
-            // per-channel constants of channel 16 w + lane
-            const int ch = 16 * wave + lane;
-            const float b1 = sm.Gref[0][ch], b2 = sm.Gref[1][ch], b3 = sm.Gref[2][ch];
-            const float ge = sm.Gref[3][ch];
-            sm.eB[0][ch] = 1.f;
-            sm.eB[1][ch] = __expf(b1);
-            sm.eB[2][ch] = __expf(b2);
-            sm.eB[3][ch] = __expf(b3);
-            sm.eGB[0][ch] = __expf(ge);
-            sm.eGB[1][ch] = __expf(ge - b1);
-            sm.eGB[2][ch] = __expf(ge - b2);
-            sm.eGB[3][ch] = __expf(ge - b3);
-            sm.F[0][ch] = __expf(b1);                    // e^{B_1 - B_0}
-            sm.F[1][ch] = __expf(b2);                    // e^{B_2 - B_0}
-            sm.F[2][ch] = __expf(b2 - b1);
-            sm.F[3][ch] = __expf(b3);
-            sm.F[4][ch] = __expf(b3 - b1);
-            sm.F[5][ch] = __expf(b3 - b2);
-            reinterpret_cast<float *>(rec + kOffDEC)[ch] = __expf(ge);
-        }
-        __syncthreads();
-        bf16x8 kr8[2], qr8[2], kc8[2];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const int h2 = c >> 3, e = c & 7, ch = 16 * wave + c;
-            const float Bi = ib == 0 ? 0.f : sm.Gref[ib - 1][ch];
-            const float fr = __expf(G[c] - Bi);           // e^{G - B_i} in [e^-80, 1]
-            const float fc = __frcp_rn(fr);               // e^{B_i - G} in [1, e^80]
-            const float kv = (float)k8[h2][e];
-            kr8[h2][e] = (bf16)(kv * fr);
-            qr8[h2][e] = (bf16)((float)q8[h2][e] * fr);
-            kc8[h2][e] = (bf16)(kv * fc);
-            sm.XB[ch][r] = (bf16)(br * kv * (fr * sm.eB[ib][ch]));       // beta k e^G
-            sm.VB[ch][r] = (bf16)(br * (float)v8[h2][e]);               // beta v
-            sm.KPT[ch][r] = (bf16)(kv * (sm.eGB[ib][ch] * fc));         // k e^{G_end - G}
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            *reinterpret_cast<bf16x8 *>(&sm.KR[r][16 * wave + 8 * h2]) = kr8[h2];
-            *reinterpret_cast<bf16x8 *>(&sm.QR[r][16 * wave + 8 * h2]) = qr8[h2];
-            *reinterpret_cast<bf16x8 *>(&sm.KCD[r][16 * wave + 8 * h2]) = kc8[h2];
-        }
-        // beta per row, for A's row scaling: keep it next to the A tile
-        if (wave == 0)
-            sm.AM[r][kChunk] = br;
-    }
-    __syncthreads();
+        // the registers of this task's inputs are free: fetch the next task's
+        if (load_next)
+            prep_load(in, q, k, v, g, beta, next, H, wave, tg, cq);
 
-    // ---- phase 2: 16 x 16 blocks of A and P (bf16 MFMA, fp32 accumulate) -------
-    for (int blk = wave; blk < 10; blk += kPrepThreads / 64) {
-        // blk -> (i, jb): 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) ...
-        const int i = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
-        const int jb = blk - (i * (i + 1)) / 2;
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase 2: 16 x 16 blocks of A and P (bf16 MFMA, fp32 accumulate) -------
+        for (int blk = wave; blk < 10; blk += kPrepThreads / 64) {
+            // blk -> (i, jb): 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) ...
+            const int i = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
+            const int jb = blk - (i * (i + 1)) / 2;
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int ch = 32 * ks + 8 * b;
-            const bf16x8 ar = lds8(&sm.KR[16 * i + m][ch]);
-            const bf16x8 aq = lds8(&sm.QR[16 * i + m][ch]);
-            bf16x8 bc = lds8(&sm.KCD[16 * jb + m][ch]);
-            if (jb < i) {
-                const float *f = &sm.F[pair_index(i, jb)][ch];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    bc[e] = (bf16)((float)bc[e] * f[e]);
-            }
-            accA = mfma16(ar, bc, accA);
-            accP = mfma16(aq, bc, accP);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * i + 4 * b + e, col = 16 * jb + m;
-            sm.AM[row][col] = (jb < i || col < row) ? sm.AM[row][kChunk] * accA[e] : 0.f;
-            sm.PM[row][col] = (bf16)((jb < i || col <= row) ? scale * accP[e] : 0.f);
-        }
-    }
-    __syncthreads();
-
-    // ---- phase 3: T = (I + A)^-1 ------------------------------------------------
-    if (wave == 0) {
-        // diagonal 16 x 16 blocks by forward substitution, one column per lane;
-        // x[s] = 0 for s < col, so the full-range sums only add zeros there
-        // (column form: once x[s] is final it updates every later row at once,
-        // so the dependency depth is 16 instead of 120)
-        const int blk = lane >> 4, col = lane & 15, o = 16 * blk;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            x[r] = (r == col) ? 1.f : 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < 15; ++s2)
-#pragma unroll
-            for (int r = s2 + 1; r < 16; ++r)
-                x[r] -= sm.AM[o + r][o + s2] * x[s2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            ts.TM[o + r][o + col] = x[r];
-    } else if (wave <= 2) {
-        // T_01 and T_23 are read by the W / U~ products: zero them
-        const int o = (wave == 1) ? 0 : 32;
-#pragma unroll
-        for (int e = lane; e < 256; e += 64)
-            ts.TM[o + e / 16][o + 16 + e % 16] = 0.f;
-    }
-    __syncthreads();
-    // off-diagonal blocks by distance on fp32 MFMA (16x16x4), one block per wave:
-    // X = sum_{mm=bb}^{a-1} A_a,mm T_mm,bb ;  T_a,bb = -T_aa X
-    for (int dist = 1; dist < 4; ++dist) {
-        if (wave < 4 - dist) {
-            const int a = wave + dist, bb = wave;
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
-            for (int mm = bb; mm < a; ++mm) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    X = mfma4_f32(sm.AM[16 * a + m][16 * mm + 4 * kk + b],
-                                  ts.TM[16 * mm + 4 * kk + b][16 * bb + m], X);
-            }
-            // k order: MFMA kk takes k = 4 b + kk, which is X's own accumulator row
-            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                Y = mfma4_f32(ts.TM[16 * a + m][16 * a + 4 * b + kk], X[kk], Y);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ts.TM[16 * a + 4 * b + i][16 * bb + m] = -Y[i];
-        }
-        __syncthreads();
-    }
-
-    // ---- phase 4: W = T X and U~ = T V for the wave's 16 channels --------------
-    const int nt = wave;                       // channels 16 nt .. 16 nt + 15
-    f32x4 accW[4], accU[4];
-    {
-        bf16x8 tf[4][2];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 f = {};
-                if (ks <= (mt >> 1)) {
+            for (int ks = 0; ks < 4; ++ks) {
+                const int ch = 32 * ks + 8 * b;
+                const bf16x8 ar = lds8(&sm.KR[16 * i + m][ch]);
+                const bf16x8 aq = lds8(&sm.QR[16 * i + m][ch]);
+                bf16x8 bc = lds8(&sm.KCD[16 * jb + m][ch]);
+                if (jb < i) {
+                    const float *f = &sm.F[pair_index(i, jb)][ch];
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        f[e] = (bf16)ts.TM[16 * mt + m][32 * ks + 8 * b + e];
+                        bc[e] = (bf16)((float)bc[e] * f[e]);
                 }
-                tf[mt][ks] = f;
+                accA = mfma16(ar, bc, accA);
+                accP = mfma16(aq, bc, accP);
             }
-        bf16x8 xf[2], vf[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            xf[ks] = lds8(&sm.XB[16 * nt + m][32 * ks + 8 * b]);
-            vf[ks] = lds8(&sm.VB[16 * nt + m][32 * ks + 8 * b]);
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * i + 4 * b + e, col = 16 * jb + m;
+                sm.AM[row][col] = (jb < i || col < row) ? sm.AM[row][kChunk] * accA[e] : 0.f;
+                sm.PM[row][col] = (bf16)((jb < i || col <= row) ? scale * accP[e] : 0.f);
+            }
         }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            accW[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accU[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                if (ks <= (mt >> 1)) {
-                    accW[mt] = mfma16(tf[mt][ks], xf[ks], accW[mt]);
-                    accU[mt] = mfma16(tf[mt][ks], vf[ks], accU[mt]);
-                }
-        }
-    }
+        __syncthreads();
 
-    // ---- phase 5: L, Bm, Q^, O0 for the wave's 16 channels ----------------------
-    {
-        bf16x8 wf[2], uf[2];                   // W^T as A operand, U~ as B operand (perm k)
+        // ---- phase 3: T = (I + A)^-1 ------------------------------------------------
+        if (wave == 0) {
+            // diagonal 16 x 16 blocks by forward substitution, one column per lane;
+            // x[s] = 0 for s < col, so the full-range sums only add zeros there
+            // (column form: once x[s] is final it updates every later row at once,
+            // so the dependency depth is 16 instead of 120)
+            const int blk = lane >> 4, col = lane & 15, o = 16 * blk;
+            float x[16];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            wf[ks] = acc_to_frag(accW[2 * ks], accW[2 * ks + 1]);
-            uf[ks] = acc_to_frag(accU[2 * ks], accU[2 * ks + 1]);
+            for (int r = 0; r < 16; ++r)
+                x[r] = (r == col) ? 1.f : 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < 15; ++s2)
+#pragma unroll
+                for (int r = s2 + 1; r < 16; ++r)
+                    x[r] -= sm.AM[o + r][o + s2] * x[s2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                ts.TM[o + r][o + col] = x[r];
+        } else if (wave <= 2) {
+            // T_01 and T_23 are read by the W / U~ products: zero them
+            const int o = (wave == 1) ? 0 : 32;
+#pragma unroll
+            for (int e = lane; e < 256; e += 64)
+                ts.TM[o + e / 16][o + 16 + e % 16] = 0.f;
         }
-        const int half = nt & 1, kq = nt >> 1;  // fragment half and dk k-step of these channels
-        // L^T rows 16 nt.. = W^T K'  ->  -L fragments (mt, kq), elements 4 half .. 4 half + 3
-        // Bm columns 16 nt.. = K'^T U~ ->  Bm of value block nt
+        __syncthreads();
+        // off-diagonal blocks by distance on fp32 MFMA (16x16x4), one block per wave:
+        // X = sum_{mm=bb}^{a-1} A_a,mm T_mm,bb ;  T_a,bb = -T_aa X
+        for (int dist = 1; dist < 4; ++dist) {
+            if (wave < 4 - dist) {
+                const int a = wave + dist, bb = wave;
+                f32x4 X = {0.f, 0.f, 0.f, 0.f};
+                for (int mm = bb; mm < a; ++mm) {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            bf16x8 kpf[2];
+                    for (int kk = 0; kk < 4; ++kk)
+                        X = mfma4_f32(sm.AM[16 * a + m][16 * mm + 4 * kk + b],
+                                      ts.TM[16 * mm + 4 * kk + b][16 * bb + m], X);
+                }
+                // k order: MFMA kk takes k = 4 b + kk, which is X's own accumulator row
+                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                kpf[ks] = perm8(&sm.KPT[16 * mt + m][0], ks, b);
-            f32x4 l = {0.f, 0.f, 0.f, 0.f}, bm = {0.f, 0.f, 0.f, 0.f};
+                for (int kk = 0; kk < 4; ++kk)
+                    Y = mfma4_f32(ts.TM[16 * a + m][16 * a + 4 * b + kk], X[kk], Y);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    ts.TM[16 * a + 4 * b + i][16 * bb + m] = -Y[i];
+            }
+            __syncthreads();
+        }
+
+        // ---- phase 4: W = T X and U~ = T V for the wave's 16 channels --------------
+        const int nt = wave;                       // channels 16 nt .. 16 nt + 15
+        f32x4 accW[4], accU[4];
+        {
+            bf16x8 tf[4][2];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    bf16x8 f = {};
+                    if (ks <= (mt >> 1)) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            f[e] = (bf16)ts.TM[16 * mt + m][32 * ks + 8 * b + e];
+                    }
+                    tf[mt][ks] = f;
+                }
+            bf16x8 xf[2], vf[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                l = mfma16(wf[ks], kpf[ks], l);
-                bm = mfma16(kpf[ks], uf[ks], bm);
+                xf[ks] = lds8(&sm.XB[16 * nt + m][32 * ks + 8 * b]);
+                vf[ks] = lds8(&sm.VB[16 * nt + m][32 * ks + 8 * b]);
             }
-            *reinterpret_cast<bf16x4 *>(rec + kOffLN + (mt * 4 + kq) * kFragBytes + lane * 16 +
-                                        half * 8) = to_bf16x4(l, -1.f);
-            *reinterpret_cast<bf16x4 *>(rec + kOffBM + nt * 4096 + (mt >> 1) * 1024 + lane * 16 +
-                                        (mt & 1) * 8) = to_bf16x4(bm, 1.f);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                accW[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accU[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    if (ks <= (mt >> 1)) {
+                        accW[mt] = mfma16(tf[mt][ks], xf[ks], accW[mt]);
+                        accU[mt] = mfma16(tf[mt][ks], vf[ks], accU[mt]);
+                    }
+            }
         }
-        // Q^ = scale Q e^G - P W  (as Q^^T rows 16 nt..)  and  O0 = P U~ for value block nt
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            bf16x8 pf[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                pf[ks] = perm8(&sm.PM[16 * mt + m][0], ks, b);
-            // scale Q e^G at row 16 mt + m, channels 16 nt + 4 b .. + 3, from q e^{G - B_mt}
-            const bf16x4 qr = *reinterpret_cast<const bf16x4 *>(&sm.QR[16 * mt + m][16 * nt + 4 * b]);
-            const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[mt][16 * nt + 4 * b]);
-            f32x4 qh;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                qh[i] = -scale * (float)qr[i] * eb[i];
-            f32x4 o0 = {0.f, 0.f, 0.f, 0.f};
+
+        // ---- phase 5: L, Bm, Q^, O0 for the wave's 16 channels ----------------------
+        {
+            bf16x8 wf[2], uf[2];                   // W^T as A operand, U~ as B operand (perm k)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                qh = mfma16(wf[ks], pf[ks], qh);   // (P W)^T - (scale Q e^G)^T
-                o0 = mfma16(uf[ks], pf[ks], o0);   // (P U~)^T
+                wf[ks] = acc_to_frag(accW[2 * ks], accW[2 * ks + 1]);
+                uf[ks] = acc_to_frag(accU[2 * ks], accU[2 * ks + 1]);
             }
-            *reinterpret_cast<bf16x4 *>(rec + kOffQH + (mt * 4 + kq) * kFragBytes + lane * 16 +
-                                        half * 8) = to_bf16x4(qh, -1.f);
-            *reinterpret_cast<bf16x4 *>(rec + kOffO0 + nt * 2048 + mt * 512 + lane * 8) =
-                to_bf16x4(o0, 1.f);
+            const int half = nt & 1, kq = nt >> 1;  // fragment half and dk k-step of these channels
+            // L^T rows 16 nt.. = W^T K'  ->  -L fragments (mt, kq), elements 4 half .. 4 half + 3
+            // Bm columns 16 nt.. = K'^T U~ ->  Bm of value block nt
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                bf16x8 kpf[2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    kpf[ks] = perm8(&sm.KPT[16 * mt + m][0], ks, b);
+                f32x4 l = {0.f, 0.f, 0.f, 0.f}, bm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    l = mfma16(wf[ks], kpf[ks], l);
+                    bm = mfma16(kpf[ks], uf[ks], bm);
+                }
+                *reinterpret_cast<bf16x4 *>(rec + kOffLN + (mt * 4 + kq) * kFragBytes + lane * 16 +
+                                            half * 8) = to_bf16x4(l, -1.f);
+                *reinterpret_cast<bf16x4 *>(rec + kOffBM + nt * 4096 + (mt >> 1) * 1024 + lane * 16 +
+                                            (mt & 1) * 8) = to_bf16x4(bm, 1.f);
+            }
+            // Q^ = scale Q e^G - P W  (as Q^^T rows 16 nt..)  and  O0 = P U~ for value block nt
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                bf16x8 pf[2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    pf[ks] = perm8(&sm.PM[16 * mt + m][0], ks, b);
+                // scale Q e^G at row 16 mt + m, channels 16 nt + 4 b .. + 3, from q e^{G - B_mt}
+                const bf16x4 qr = *reinterpret_cast<const bf16x4 *>(&sm.QR[16 * mt + m][16 * nt + 4 * b]);
+                const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[mt][16 * nt + 4 * b]);
+                f32x4 qh;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    qh[i] = -scale * (float)qr[i] * eb[i];
+                f32x4 o0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    qh = mfma16(wf[ks], pf[ks], qh);   // (P W)^T - (scale Q e^G)^T
+                    o0 = mfma16(uf[ks], pf[ks], o0);   // (P U~)^T
+                }
+                *reinterpret_cast<bf16x4 *>(rec + kOffQH + (mt * 4 + kq) * kFragBytes + lane * 16 +
+                                            half * 8) = to_bf16x4(qh, -1.f);
+                *reinterpret_cast<bf16x4 *>(rec + kOffO0 + nt * 2048 + mt * 512 + lane * 8) =
+                    to_bf16x4(o0, 1.f);
+            }
         }
+        // the next task's phase 1 rewrites the LDS operands
+        __syncthreads();
     }
 }
 
 namespace {
 
-// Chain workgroup: 4 compute waves and 1 store wave.  Compute wave w keeps
-// state rows 32 w .. 32 w + 31 (two 16-row tiles) and applies
+// Chain workgroup: 8 compute waves and 1 store wave.  Compute wave w keeps
+// state rows 16 w .. 16 w + 15 (one 16-row tile) and applies
 // S' = dec S + Bm - L S chunk after chunk; the waves exchange the new state as
-// bf16 MFMA fragments through LDS.  Compute waves only ever load from global
-// memory; the store wave copies each chunk's entry state from LDS to the
-// workspace for the output kernel.  Keeping loads and stores in different
+// bf16 MFMA fragments through LDS.  The step is bound by the operand stream
+// (about 36 KiB of L, Bm and dec per chunk through one CU), and the CU's load
+// bandwidth grows with the number of waves that have loads in flight, hence
+// eight loading waves of one tile each.  Compute waves only ever load from
+// global memory; the store wave copies each chunk's entry state from LDS to
+// the workspace for the output kernel.  Keeping loads and stores in different
 // waves lets the compiler wait for exactly the prefetched stage it needs
 // (with both kinds pending it can only wait for everything).
-constexpr int kComputeWaves = 4;
+constexpr int kComputeWaves = 8;
+constexpr int kStoreWave = kComputeWaves;
 constexpr int kChainThreads = 64 * (kComputeWaves + 1);
 constexpr int kPrefetch = 4;         // chunks of operands in flight per compute wave
 
 struct ChainStage {
-    bf16x8 ln[2][4];   // -L rows of the wave's two state tiles, 4 dk k-steps each
-    bf16x8 bm;         // Bm of the wave's 32 state rows, this value block
-    f32x4 dec[2];      // e^{G_end} of the wave's state rows
+    bf16x8 ln[4];      // -L rows of the wave's state tile, 4 dk k-steps
+    bf16x4 bm;         // Bm of the wave's 16 state rows, this value block
+    float dec;         // e^{G_end} of state row 16 w + lane % 16
 };
 
-__device__ __forceinline__ void chain_load(ChainStage &st, const uint8_t *rec, int w, int lane,
-                                           int blk)
+__device__ __forceinline__ void chain_load(ChainStage &st, const uint8_t *rec_any, int w,
+                                           int lane, int blk)
 {
-    const int b = lane >> 4;
+    const gbyte *rec = uniform_gptr(rec_any);    // the record base is the same for the wave
+    const uint32_t lo = (uint32_t)lane * 16u;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            st.ln[t][ks] = *reinterpret_cast<const bf16x8 *>(
-                rec + kOffLN + ((2 * w + t) * 4 + ks) * kFragBytes + lane * 16);
-    st.bm = *reinterpret_cast<const bf16x8 *>(rec + kOffBM + blk * 4096 + w * 1024 + lane * 16);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-        st.dec[t] = *reinterpret_cast<const f32x4 *>(rec + kOffDEC + (32 * w + 16 * t + 4 * b) * 4);
+    for (int ks = 0; ks < 4; ++ks)
+        st.ln[ks] = gload<bf16x8>(rec, kOffLN + (w * 4 + ks) * kFragBytes + lo);
+    // Bm fragment of rows 32 (w / 2) + 16 (w % 2) + 4 b + i: half of a 16-byte slot
+    st.bm = gload<bf16x4>(rec, kOffBM + blk * 4096 + (w >> 1) * 1024 + lo + (w & 1) * 8);
+    // one float per lane; lanes l and l + 16 k read the same row, spread later
+    st.dec = gload<float>(rec, kOffDEC + (16 * w + (lane & 15)) * 4u);
 }
 
 }  // namespace
@@ -483,7 +574,8 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     int snap_chunks, const int32_t *__restrict__ cu, int T, int H, int units,
     uint8_t *__restrict__ ws)
 {
-    __shared__ bf16x8 sbuf[2][4][64];                 // state as 4 k-step fragments
+    // state as 4 k-step fragments; wave w writes elements 4 (w % 2) .. + 3 of k-step w / 2
+    __shared__ bf16x8 sbuf[2][4][64];
     __shared__ float snap_s[kSnap ? 2 : 1][kSnap ? kDK : 1][kVBlock];
 
     // all value blocks of one (sequence, head) land on the same XCD (blocks are
@@ -495,7 +587,8 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     if (unit >= units)
         return;
     const int n = unit / H, h = unit % H;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int m = lane & 15, b = lane >> 4;
     const SeqInfo si = seq_info(cu, n, T, kChunk);
     const int64_t nch = (si.len + kChunk - 1) / kChunk;
@@ -508,8 +601,7 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     // the chunk loop runs in rounds of kPrefetch iterations; iterations past the
     // last chunk (at most kPrefetch - 1) leave the state unchanged
     const int64_t niter = (nch + kPrefetch - 1) / kPrefetch * kPrefetch;
-    if (w == kComputeWaves) {
-        // store wave: copy the entry state of chunk jc (4 fragments, 16 B per lane each)
+    if (w == kStoreWave) {
         // snapshot jb: rows 16 i + lane / 4, channels 16 blk + 4 (lane % 4) .. + 3
         auto write_snap = [&](int64_t jb) {
             const int64_t slot =
@@ -523,6 +615,7 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
                     *reinterpret_cast<const f32x4 *>(&snap_s[jb & 1][row][4 * (lane & 3)]);
             }
         };
+        // store wave: copy the entry state of chunk jc (4 fragments, 16 B per lane each)
         __syncthreads();
         for (int64_t jc = 0; jc < niter; ++jc) {
             if (jc < nch) {
@@ -546,14 +639,18 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
 
     const int64_t sbase = (int64_t)unit * (kDK * kDV);
     const int col = kVBlock * blk + m;
-    // state tile t of this wave: rows 32 w + 16 t + 4 b + i, column col
-    f32x4 S[2];
+    const int row0 = 16 * w + 4 * b;           // the wave's rows row0 + i, column col
+    // this wave's half of k-step fragment w / 2, as 4 bf16 at byte 8 (w % 2) of a lane's slot
+    auto put_state = [&](int buf, const f32x4 &x) {
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint8_t *>(&sbuf[buf][w >> 1][lane]) +
+                                    8 * (w & 1)) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2],
+                                                          (bf16)x[3]};
+    };
+    f32x4 S;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[t][i] = init ? init[sbase + (32 * w + 16 * t + 4 * b + i) * kDV + col] : 0.f;
-    sbuf[0][w][lane] = acc_to_frag(S[0], S[1]);
+    for (int i = 0; i < 4; ++i)
+        S[i] = init ? init[sbase + (row0 + i) * kDV + col] : 0.f;
+    put_state(0, S);
     __syncthreads();
 
     // the scheduling barriers keep each stage's loads together and in stage
@@ -580,31 +677,22 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
             const int64_t jc = j0 + s;
             const ChainStage &c = st[s];
             const bf16x8 *sb = &sbuf[jc & 1][0][lane];
-            // S' = dec S + Bm - L S for the wave's 32 rows
-            f32x4 acc[2];
+            // S' = dec S + Bm - L S for the wave's 16 rows
+            f32x4 acc;
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int i = 0; i < 4; ++i)
+                acc[i] = __shfl(c.dec, 4 * b + i) * S[i] + (float)c.bm[i];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[t][i] = c.dec[t][i] * S[t][i] + (float)c.bm[4 * t + i];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 f = sb[ks * 64];
-                acc[0] = mfma16(c.ln[0][ks], f, acc[0]);
-                acc[1] = mfma16(c.ln[1][ks], f, acc[1]);
-            }
-            if (jc < nch) {
-                S[0] = acc[0];
-                S[1] = acc[1];
-            }
-            sbuf[(jc + 1) & 1][w][lane] = acc_to_frag(S[0], S[1]);
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mfma16(c.ln[ks], sb[ks * 64], acc);
+            if (jc < nch)
+                S = acc;
+            put_state((jc + 1) & 1, S);
             if constexpr (kSnap) {
                 if (snap_at(jc + 1)) {
 #pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            snap_s[(jc + 1) & 1][32 * w + 16 * t + 4 * b + i][m] = S[t][i];
+                    for (int i = 0; i < 4; ++i)
+                        snap_s[(jc + 1) & 1][row0 + i][m] = S[i];
                 }
             }
             load_stage(st[s], jc + kPrefetch);
@@ -613,10 +701,8 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     }
     if (final_state) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                final_state[sbase + (32 * w + 16 * t + 4 * b + i) * kDV + col] = S[t][i];
+        for (int i = 0; i < 4; ++i)
+            final_state[sbase + (row0 + i) * kDV + col] = S[i];
     }
 }
 
@@ -636,8 +722,12 @@ __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
     __shared__ bf16x8 sb_s[kNumVBlocks * 4][64];
     __shared__ float ot_s[4][kSub][kOutLd];
 
-    const int64_t slot = blockIdx.x;
-    const int h = blockIdx.y;
+    // slot-major 1-D grid: workgroup id = slot * H + h.  Workgroups are dealt to
+    // the 8 XCDs round-robin, so with H a multiple of 8 every chunk of head h is
+    // handled on XCD h % 8, the XCD whose chain workgroups walk head h: the
+    // record lines land in the L2 that reads them next
+    const int64_t slot = (int64_t)blockIdx.x / H;
+    const int h = (int)((int64_t)blockIdx.x % H);
     int n;
     int64_t j;
     if (!slot_to_chunk(cu, N, T, slot, n, j))
@@ -723,10 +813,21 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     });
     if (attr_err != hipSuccess)
         return attr_err;
+    int dev = 0, cus = 0;
+    hipError_t e0 = hipGetDevice(&dev);
+    if (e0 == hipSuccess)
+        e0 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e0 != hipSuccess)
+        return e0;
+    const int64_t prep_grid = cus >= 8 ? cus / 8 * 8 : 8;
     if (n_slots > 0 && H > 0) {
-        hipLaunchKernelGGL(kda_prep_bf16_kernel, dim3((unsigned)n_slots, (unsigned)H),
-                           dim3(kPrepThreads), sizeof(PrepSmem), stream, q, k, v, g, beta, cu, N,
-                           T, H, scale, static_cast<uint8_t *>(workspace));
+        // persistent prep: one workgroup per CU (its LDS allows no more), a
+        // multiple of 8 of them
+        const int64_t n_tasks = n_slots * H;
+        const int64_t grid = n_tasks < prep_grid ? n_tasks : prep_grid;
+        hipLaunchKernelGGL(kda_prep_bf16_kernel, dim3((unsigned)grid), dim3(kPrepThreads),
+                           sizeof(PrepSmem), stream, q, k, v, g, beta, cu, N, T, H, n_tasks,
+                           scale, static_cast<uint8_t *>(workspace));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -748,7 +849,7 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
             return e;
     }
     if (n_slots > 0 && H > 0) {
-        hipLaunchKernelGGL(kda_output_bf16_kernel, dim3((unsigned)n_slots, (unsigned)H), dim3(256),
+        hipLaunchKernelGGL(kda_output_bf16_kernel, dim3((unsigned)(n_slots * H)), dim3(256),
                            0, stream, gate, out, cu, N, T, H,
                            static_cast<const uint8_t *>(workspace));
         return hipGetLastError();

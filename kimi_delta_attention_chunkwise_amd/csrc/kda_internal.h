@@ -57,6 +57,36 @@ constexpr size_t kOffSB = kOffDEC + kDK * sizeof(float);
 constexpr size_t kRecBytes = kOffSB + kNumVBlocks * 4 * kFragBytes;
 static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
 
+// Global-memory pointers whose address space is explicit, so the compiler
+// emits global (not flat) memory instructions for them.
+typedef __attribute__((address_space(1))) uint8_t gbyte;
+
+// A wave-uniform pointer made visibly uniform (scalar registers), so that
+// memory accesses through it take the scalar-base + 32-bit vector-offset form
+// instead of a 64-bit address per lane, which halves the address traffic of
+// every vector memory instruction.
+__device__ __forceinline__ const gbyte *uniform_gptr(const void *p)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return reinterpret_cast<const gbyte *>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ gbyte *uniform_gptr(void *p)
+{
+    return const_cast<gbyte *>(uniform_gptr(static_cast<const void *>(p)));
+}
+
+// Load / store a T at byte offset off from a global base pointer.
+template <typename T> __device__ __forceinline__ T gload(const gbyte *base, uint32_t off)
+{
+    return *reinterpret_cast<const __attribute__((address_space(1))) T *>(base + off);
+}
+template <typename T> __device__ __forceinline__ void gstore(gbyte *base, uint32_t off, const T &v)
+{
+    *reinterpret_cast<__attribute__((address_space(1))) T *>(base + off) = v;
+}
+
 // Row of the k-step-local permutation described above.
 __host__ __device__ constexpr int perm_row(int ks, int b, int e)
 {
