@@ -151,6 +151,31 @@ kda_status kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, 
                                    kda_dtype dt, void *workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/* Fused input prologue.  Bits of `prologue` in the *_ex entry points; each
+ * applies one elementwise map to an input inside the kernels, so callers can
+ * pass raw projections without separate passes over HBM:
+ *   KDA_PRO_QK_L2NORM    q and k are divided by sqrt(sum over dk of x^2 + 1e-6)
+ *                        per (token, head), in fp32
+ *   KDA_PRO_BETA_SIGMOID beta holds logits; the write strength is sigmoid(beta)
+ *   KDA_PRO_G_SOFTPLUS   g holds pre-activations x; the log-decay is
+ *                        max(KDA_G_MIN, -softplus(x)), which always meets the
+ *                        chunked forward's g >= -5 precondition
+ * ("Kimi K3 second-pass study ledger", section 1 row Q06 for the -5 floor;
+ * the other maps are the standard ones for these inputs.)  Other bits return
+ * KDA_ERR_UNSUPPORTED. */
+#define KDA_PRO_QK_L2NORM 1u
+#define KDA_PRO_BETA_SIGMOID 2u
+#define KDA_PRO_G_SOFTPLUS 4u
+
+/* kda_chunk_fwd_snapshots plus the prologue bits (0 = exactly that call). */
+kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const void *gate, const float *init_state,
+                            void *out, float *final_state, float *snapshots,
+                            int snapshot_interval, const int32_t *cu_seqlens, int B, int T,
+                            int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
+                            unsigned prologue, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* One O(1) recurrent decode step for N independent sequences, updating the
  * state in place ("Kimi K3 second-pass study ledger", section 1 row Q07;
  * section 8 device row, fused decode): decay, prediction, correction, write,
@@ -164,6 +189,12 @@ kda_status kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *g,
                            const void *beta, const void *gate, float *state, void *out, int N,
                            int H, int dk, int dv, float scale, kda_dtype dt, hipStream_t stream);
+
+/* kda_decode_step plus the prologue bits (see KDA_PRO_*; 0 = exactly that call). */
+kda_status kda_decode_step_ex(const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, const void *gate, float *state, void *out, int N,
+                              int H, int dk, int dv, float scale, kda_dtype dt, unsigned prologue,
+                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -26,12 +26,16 @@ __all__ = [
     "KdaError", "KdaLibraryError", "chunk_fwd", "chunk_fwd_snapshots", "decode_step",
     "chunk_fwd_workspace_bytes", "snapshot_slots", "snapshot_index",
     "chunk_fwd_supported", "decode_step_supported", "library_path", "load_library",
-    "KDA_F32", "KDA_BF16", "G_MIN",
+    "KDA_F32", "KDA_BF16", "G_MIN", "PRO_QK_L2NORM", "PRO_BETA_SIGMOID", "PRO_G_SOFTPLUS",
 ]
 
 KDA_F32 = 0
 KDA_BF16 = 1
 G_MIN = -5.0
+# prologue bits (KDA_PRO_* in kda.h)
+PRO_QK_L2NORM = 1
+PRO_BETA_SIGMOID = 2
+PRO_G_SOFTPLUS = 4
 _DEFAULT_CHUNK = {KDA_F32: 16, KDA_BF16: 64}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +66,11 @@ _SIGNATURES = {
     "kda_chunk_fwd_snapshots": ([ctypes.c_void_p] * 10 + [ctypes.c_int] + [ctypes.c_void_p]
                                 + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "kda_chunk_fwd_ex": ([ctypes.c_void_p] * 10 + [ctypes.c_int] + [ctypes.c_void_p]
+                         + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int, ctypes.c_uint,
+                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "kda_decode_step_ex": ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
+                           ctypes.c_uint, ctypes.c_void_p], ctypes.c_int),
     "kda_decode_step": ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
                         ctypes.c_void_p], ctypes.c_int),
 }
@@ -165,7 +174,7 @@ def snapshot_index(lengths, interval: int, varlen: bool, T: int | None = None):
 
 
 def _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state, cu_seqlens, chunk,
-                scale, workspace, out, final_state, interval, snapshots):
+                scale, workspace, out, final_state, interval, snapshots, prologue):
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
@@ -209,29 +218,36 @@ def _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state, cu_seqle
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < nbytes:
         raise ValueError(f"workspace must be a uint8 tensor of at least {nbytes} bytes on {dev}")
-    if interval is None:
+    if interval is not None:
+        slots = snapshot_slots(B, T, N, chunk, int(interval), cu_seqlens is not None)
+        if snapshots is None:
+            snapshots = torch.empty((slots, H, dk, dv), dtype=torch.float32, device=dev)
+        else:
+            _need(snapshots, "snapshots", (slots, H, dk, dv), torch.float32, dev)
+    if prologue:
+        st = lib.kda_chunk_fwd_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate), _ptr(init_state),
+            _ptr(out), _ptr(final_state), _ptr(snapshots), int(interval or 0), _ptr(cu_seqlens),
+            B, T, N, H, dk, dv, chunk, float(scale), code, int(prologue), _ptr(workspace),
+            workspace.numel(), _stream_ptr(dev))
+    elif interval is not None:
+        st = lib.kda_chunk_fwd_snapshots(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate), _ptr(init_state),
+            _ptr(out), _ptr(final_state), _ptr(snapshots), int(interval), _ptr(cu_seqlens),
+            B, T, N, H, dk, dv, chunk, float(scale), code, _ptr(workspace), workspace.numel(),
+            _stream_ptr(dev))
+    else:
         st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
                                _ptr(init_state), _ptr(out), _ptr(final_state), _ptr(cu_seqlens),
                                B, T, N, H, dk, dv, chunk, float(scale), code, _ptr(workspace),
                                workspace.numel(), _stream_ptr(dev))
-        _check(st)
-        return out, final_state, None
-    slots = snapshot_slots(B, T, N, chunk, int(interval), cu_seqlens is not None)
-    if snapshots is None:
-        snapshots = torch.empty((slots, H, dk, dv), dtype=torch.float32, device=dev)
-    else:
-        _need(snapshots, "snapshots", (slots, H, dk, dv), torch.float32, dev)
-    st = lib.kda_chunk_fwd_snapshots(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate), _ptr(init_state), _ptr(out),
-        _ptr(final_state), _ptr(snapshots), int(interval), _ptr(cu_seqlens), B, T, N, H, dk, dv,
-        chunk, float(scale), code, _ptr(workspace), workspace.numel(), _stream_ptr(dev))
     _check(st)
     return out, final_state, snapshots
 
 
 def chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
               cu_seqlens=None, chunk=None, scale=1.0, workspace=None, out=None,
-              final_state=None):
+              final_state=None, prologue=0):
     """Chunkwise-parallel KDA forward on the GPU.
 
     q, k, g ``[B, T, H, dk]``; v, gate ``[B, T, H, dv]``; beta ``[B, T, H]``, all
@@ -240,26 +256,28 @@ def chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
     ``[N + 1]`` on the device (then B must be 1) or None (N = B).
     Optional preallocated ``workspace`` (uint8, at least
     ``chunk_fwd_workspace_bytes`` bytes), ``out`` and ``final_state``.
+    ``prologue``: PRO_* bits for raw inputs (q/k L2 norm, beta logits, g
+    pre-activations); 0 for prepared inputs.
     Returns ``(out, final_state)``; final_state is None unless requested.
     """
     out, final_state, _ = _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state,
                                       cu_seqlens, chunk, scale, workspace, out, final_state,
-                                      None, None)
+                                      None, None, prologue)
     return out, final_state
 
 
 def chunk_fwd_snapshots(q, k, v, g, beta, gate, interval, init_state=None,
                         output_final_state=True, cu_seqlens=None, chunk=None, scale=1.0,
-                        workspace=None, out=None, final_state=None, snapshots=None):
+                        workspace=None, out=None, final_state=None, snapshots=None, prologue=0):
     """``chunk_fwd`` that also returns fp32 state snapshots every ``interval``
     tokens of each sequence (a multiple of the chunk length), as
     ``[snapshot_slots(...), H, dk, dv]``; ``snapshot_index`` maps slots to
     (sequence, token count).  Returns ``(out, final_state, snapshots)``."""
     return _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state, cu_seqlens,
-                       chunk, scale, workspace, out, final_state, interval, snapshots)
+                       chunk, scale, workspace, out, final_state, interval, snapshots, prologue)
 
 
-def decode_step(q, k, v, g, beta, gate, state, scale=1.0, out=None):
+def decode_step(q, k, v, g, beta, gate, state, scale=1.0, out=None, prologue=0):
     """One recurrent KDA step on the GPU; ``state`` (fp32 ``[N, H, dk, dv]``)
     is updated in place.  q, k, g ``[N, H, dk]``; v, gate ``[N, H, dv]``;
     beta ``[N, H]``.  Returns the gated output ``[N, H, dv]``."""
@@ -280,8 +298,13 @@ def decode_step(q, k, v, g, beta, gate, state, scale=1.0, out=None):
         out = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _need(out, "out", (N, H, dv), dt, dev)
-    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
-                             _ptr(state), _ptr(out), N, H, dk, dv, float(scale), code,
-                             _stream_ptr(dev))
+    if prologue:
+        st = lib.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
+                                    _ptr(state), _ptr(out), N, H, dk, dv, float(scale), code,
+                                    int(prologue), _stream_ptr(dev))
+    else:
+        st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
+                                 _ptr(state), _ptr(out), N, H, dk, dv, float(scale), code,
+                                 _stream_ptr(dev))
     _check(st)
     return out

@@ -32,6 +32,11 @@ int64_t chunk_slots(int B, int T, int N, int chunk, int varlen)
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+constexpr unsigned kProAll = KDA_PRO_QK_L2NORM | KDA_PRO_BETA_SIGMOID | KDA_PRO_G_SOFTPLUS;
+static_assert(KDA_PRO_QK_L2NORM == kda::kProQK && KDA_PRO_BETA_SIGMOID == kda::kProBeta &&
+                  KDA_PRO_G_SOFTPLUS == kda::kProG,
+              "prologue bits agree with the kernels");
+
 }  // namespace
 
 extern "C" {
@@ -82,17 +87,17 @@ size_t kda_snapshot_slots(int B, int T, int N, int chunk, int interval, int varl
     return (size_t)B * (size_t)(T / interval);
 }
 
-kda_status kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const void *g,
-                                   const void *beta, const void *gate, const float *init_state,
-                                   void *out, float *final_state, float *snapshots,
-                                   int snapshot_interval, const int32_t *cu_seqlens, int B,
-                                   int T, int N, int H, int dk, int dv, int chunk, float scale,
-                                   kda_dtype dt, void *workspace, size_t workspace_bytes,
-                                   hipStream_t stream)
+kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const void *gate, const float *init_state,
+                            void *out, float *final_state, float *snapshots,
+                            int snapshot_interval, const int32_t *cu_seqlens, int B, int T,
+                            int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
+                            unsigned prologue, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream)
 {
     if (!valid_dtype(dt))
         return KDA_ERR_BAD_DTYPE;
-    if (!chunk_supported(dt, dk, dv, chunk))
+    if (!chunk_supported(dt, dk, dv, chunk) || (prologue & ~kProAll) != 0)
         return KDA_ERR_UNSUPPORTED;
     const int varlen = cu_seqlens != nullptr;
     if (B < 1 || T < 0 || N < 0 || H < 1)
@@ -119,12 +124,25 @@ kda_status kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, 
         return from_hip(kda::launch_chunk_f32(
             (const float *)q, (const float *)k, (const float *)v, (const float *)g,
             (const float *)beta, (const float *)gate, init_state, (float *)out, final_state,
-            snapshots, interval, cu_seqlens, N, T, H, scale, stream));
+            snapshots, interval, cu_seqlens, N, T, H, scale, prologue, stream));
     return from_hip(kda::launch_chunk_bf16(
         (const kda::bf16 *)q, (const kda::bf16 *)k, (const kda::bf16 *)v, (const kda::bf16 *)g,
         (const kda::bf16 *)beta, (const kda::bf16 *)gate, init_state, (kda::bf16 *)out,
         final_state, snapshots, interval, cu_seqlens, N, T, H,
-        chunk_slots(B, T, N, chunk, varlen), scale, workspace, stream));
+        chunk_slots(B, T, N, chunk, varlen), scale, prologue, workspace, stream));
+}
+
+kda_status kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, const void *gate, const float *init_state,
+                                   void *out, float *final_state, float *snapshots,
+                                   int snapshot_interval, const int32_t *cu_seqlens, int B,
+                                   int T, int N, int H, int dk, int dv, int chunk, float scale,
+                                   kda_dtype dt, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream)
+{
+    return kda_chunk_fwd_ex(q, k, v, g, beta, gate, init_state, out, final_state, snapshots,
+                            snapshot_interval, cu_seqlens, B, T, N, H, dk, dv, chunk, scale, dt,
+                            0u, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
@@ -133,18 +151,19 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void
                          int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
                          void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    return kda_chunk_fwd_snapshots(q, k, v, g, beta, gate, init_state, out, final_state,
-                                   nullptr, 0, cu_seqlens, B, T, N, H, dk, dv, chunk, scale, dt,
-                                   workspace, workspace_bytes, stream);
+    return kda_chunk_fwd_ex(q, k, v, g, beta, gate, init_state, out, final_state, nullptr, 0,
+                            cu_seqlens, B, T, N, H, dk, dv, chunk, scale, dt, 0u, workspace,
+                            workspace_bytes, stream);
 }
 
-kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *g,
-                           const void *beta, const void *gate, float *state, void *out, int N,
-                           int H, int dk, int dv, float scale, kda_dtype dt, hipStream_t stream)
+kda_status kda_decode_step_ex(const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, const void *gate, float *state, void *out, int N,
+                              int H, int dk, int dv, float scale, kda_dtype dt, unsigned prologue,
+                              hipStream_t stream)
 {
     if (!valid_dtype(dt))
         return KDA_ERR_BAD_DTYPE;
-    if (!decode_supported(dt, dk, dv))
+    if (!decode_supported(dt, dk, dv) || (prologue & ~kProAll) != 0)
         return KDA_ERR_UNSUPPORTED;
     if (N < 0 || H < 1)
         return KDA_ERR_BAD_SHAPE;
@@ -153,7 +172,15 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const vo
     if (!q || !k || !v || !g || !beta || !gate || !state || !out)
         return KDA_ERR_NULL_POINTER;
     return from_hip(kda::launch_decode(q, k, v, g, beta, gate, state, out, N, H, dk, dv, scale,
-                                       dt == KDA_BF16, stream));
+                                       dt == KDA_BF16, prologue, stream));
+}
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const void *gate, float *state, void *out, int N,
+                           int H, int dk, int dv, float scale, kda_dtype dt, hipStream_t stream)
+{
+    return kda_decode_step_ex(q, k, v, g, beta, gate, state, out, N, H, dk, dv, scale, dt, 0u,
+                              stream);
 }
 
 }  // extern "C"

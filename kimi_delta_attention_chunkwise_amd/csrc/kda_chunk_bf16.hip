@@ -73,6 +73,7 @@ struct PrepSmem {
     float eB[4][kDK];             // e^{B_i}
     float eGB[4][kDK];            // e^{G_end - B_i}
     float Gref[4][kDK];           // G at the end of subtiles 0, 1, 2, 3 (B_1, B_2, B_3, G_end)
+    float NRM[2][8][kChunk];      // prologue: per-wave partial sums of q^2 and k^2 per row
 };
 
 struct TSmem {                    // overlays KR after phase 2
@@ -217,10 +218,11 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const bf16 *q, const bf16 
 // task of head h runs on XCD h % 8, where the chain walks head h).  The inputs
 // of the next task are loaded into registers while the current one is in its
 // matrix phases, so only the first task of a workgroup waits for memory.
+template <bool kPro>
 __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ g, const bf16 *__restrict__ beta, const int32_t *__restrict__ cu,
-    int N, int T, int H, int64_t n_tasks, float scale, uint8_t *__restrict__ ws)
+    int N, int T, int H, int64_t n_tasks, float scale, unsigned pro, uint8_t *__restrict__ ws)
 {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
@@ -261,14 +263,43 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
             float G[4][4];                                 // [token][channel]
             float br[4];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-                br[tt] = 4 * tg + tt < pt.len ? (float)in.beta[tt] : 0.f;
+            for (int tt = 0; tt < 4; ++tt) {
+                const float bv = (float)in.beta[tt];
+                br[tt] = 4 * tg + tt < pt.len ? ((kPro && (pro & kProBeta)) ? sigmoidf_(bv) : bv) : 0.f;
+            }
+            if (kPro && (pro & kProQK)) {
+                // sums of q^2 and k^2 per row: the lane's 4 channels, then the
+                // wave's 16 (lanes 16 apart), then the 8 waves through LDS
+                float sq[4], sk[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    sq[tt] = sk[tt] = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float qv = (float)in.q[tt][c], kv = (float)in.k[tt][c];
+                        sq[tt] += qv * qv;
+                        sk[tt] += kv * kv;
+                    }
+                    sq[tt] += __shfl_xor(sq[tt], 16);
+                    sq[tt] += __shfl_xor(sq[tt], 32);
+                    sk[tt] += __shfl_xor(sk[tt], 16);
+                    sk[tt] += __shfl_xor(sk[tt], 32);
+                }
+                if (cq == 0) {
+                    *reinterpret_cast<f32x4 *>(&sm.NRM[0][wave][4 * tg]) =
+                        f32x4{sq[0], sq[1], sq[2], sq[3]};
+                    *reinterpret_cast<f32x4 *>(&sm.NRM[1][wave][4 * tg]) =
+                        f32x4{sk[0], sk[1], sk[2], sk[3]};
+                }
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 float run = 0.f;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    run += 4 * tg + tt < pt.len ? (float)in.g[tt][c] : 0.f;
+                    const float x = (float)in.g[tt][c];
+                    const float gv = (kPro && (pro & kProG)) ? log_decay_from(x) : x;
+                    run += 4 * tg + tt < pt.len ? gv : 0.f;
                     G[tt][c] = run;
                 }
                 const float excl = row_inclusive_sum(run) - run;
@@ -308,6 +339,21 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                 reinterpret_cast<float *>(rec + kOffDEC)[ch] = __expf(ge);
             }
             __syncthreads();
+            // prologue: 1 / |q| and 1 / |k| of the lane's rows (1 without it)
+            f32x4 nq = {1.f, 1.f, 1.f, 1.f}, nk = {1.f, 1.f, 1.f, 1.f};
+            if (kPro && (pro & kProQK)) {
+                f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w2 = 0; w2 < 8; ++w2) {
+                    aq += *reinterpret_cast<const f32x4 *>(&sm.NRM[0][w2][4 * tg]);
+                    ak += *reinterpret_cast<const f32x4 *>(&sm.NRM[1][w2][4 * tg]);
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    nq[tt] = __builtin_amdgcn_rsqf(aq[tt] + kNormEps);
+                    nk[tt] = __builtin_amdgcn_rsqf(ak[tt] + kNormEps);
+                }
+            }
             const f32x4 Bi = ib == 0 ? f32x4{0.f, 0.f, 0.f, 0.f}
                                      : *reinterpret_cast<const f32x4 *>(&sm.Gref[ib - 1][ch0]);
             const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[ib][ch0]);
@@ -322,8 +368,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                 for (int c = 0; c < 4; ++c) {
                     const float fr = __expf(G[tt][c] - Bi[c]);   // e^{G - B_i} in [e^-80, 1]
                     const float fc = __builtin_amdgcn_rcpf(fr);  // e^{B_i - G} in [1, e^80]
-                    const float kv = ok ? (float)in.k[tt][c] : 0.f;
-                    const float qv = ok ? (float)in.q[tt][c] : 0.f;
+                    const float kv = ok ? (float)in.k[tt][c] * nk[tt] : 0.f;
+                    const float qv = ok ? (float)in.q[tt][c] * nq[tt] : 0.f;
                     const float vv = ok ? (float)in.v[tt][c] : 0.f;
                     kr[c] = (bf16)(kv * fr);
                     qr[c] = (bf16)(qv * fr);
@@ -802,14 +848,18 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
                              const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
                              float *final_state, float *snaps, int snap_interval,
                              const int32_t *cu, int N, int T, int H, int64_t n_slots,
-                             float scale, void *workspace, hipStream_t stream)
+                             float scale, unsigned pro, void *workspace, hipStream_t stream)
 {
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(attr_once, [] {
-        attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_prep_bf16_kernel),
+        attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_prep_bf16_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sizeof(PrepSmem));
+        if (attr_err == hipSuccess)
+            attr_err = hipFuncSetAttribute(
+                reinterpret_cast<const void *>(kda_prep_bf16_kernel<true>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PrepSmem));
     });
     if (attr_err != hipSuccess)
         return attr_err;
@@ -825,9 +875,14 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
         // multiple of 8 of them
         const int64_t n_tasks = n_slots * H;
         const int64_t grid = n_tasks < prep_grid ? n_tasks : prep_grid;
-        hipLaunchKernelGGL(kda_prep_bf16_kernel, dim3((unsigned)grid), dim3(kPrepThreads),
-                           sizeof(PrepSmem), stream, q, k, v, g, beta, cu, N, T, H, n_tasks,
-                           scale, static_cast<uint8_t *>(workspace));
+        if (pro)
+            hipLaunchKernelGGL(kda_prep_bf16_kernel<true>, dim3((unsigned)grid),
+                               dim3(kPrepThreads), sizeof(PrepSmem), stream, q, k, v, g, beta, cu,
+                               N, T, H, n_tasks, scale, pro, static_cast<uint8_t *>(workspace));
+        else
+            hipLaunchKernelGGL(kda_prep_bf16_kernel<false>, dim3((unsigned)grid),
+                               dim3(kPrepThreads), sizeof(PrepSmem), stream, q, k, v, g, beta, cu,
+                               N, T, H, n_tasks, scale, 0u, static_cast<uint8_t *>(workspace));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void kda_chunk_f32_kernel(
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ gate,
     const float *__restrict__ init, float *__restrict__ out, float *__restrict__ final_state,
     float *__restrict__ snaps, int snap_interval, const int32_t *__restrict__ cu, int T, int H,
-    float scale)
+    float scale, unsigned pro)
 {
     __shared__ float sS[D][LD], sG[D][LD], sQb[D][LD], sKb[D][LD], sKc[D][LD], sKp[D][LD];
     __shared__ float sX[D][LD], sVb[D][LD], sA[D][LD], sP[D][LD], sT[D][LD], sW[D][LD];
@@ -50,13 +50,27 @@ __global__ __launch_bounds__(256) void kda_chunk_f32_kernel(
         const bool valid = r < L;
         const int64_t tok = si.bos + c0 + r;
         const int64_t off = (tok * H + h) * D + c;
-        const float qv = valid ? q[off] : 0.f;
-        const float kv = valid ? k[off] : 0.f;
+        float qv = valid ? q[off] : 0.f;
+        float kv = valid ? k[off] : 0.f;
         const float vv = valid ? v[off] : 0.f;
         const float zv = valid ? gate[off] : 0.f;
-        sG[r][c] = valid ? g[off] : 0.f;
-        if (c == 0)
-            sBeta[r] = valid ? beta[tok * H + h] : 0.f;
+        const float gx = valid ? g[off] : 0.f;
+        sG[r][c] = valid && (pro & kProG) ? log_decay_from(gx) : gx;
+        if (c == 0) {
+            const float bx = valid ? beta[tok * H + h] : 0.f;
+            sBeta[r] = valid && (pro & kProBeta) ? sigmoidf_(bx) : bx;
+        }
+        if (pro & kProQK) {
+            // row r lives in 16 consecutive lanes: reduce q^2 and k^2 across them
+            float sq = qv * qv, sk = kv * kv;
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) {
+                sq += __shfl_xor(sq, o, D);
+                sk += __shfl_xor(sk, o, D);
+            }
+            qv *= __builtin_amdgcn_rsqf(sq + kNormEps);
+            kv *= __builtin_amdgcn_rsqf(sk + kNormEps);
+        }
         __syncthreads();
         float Gr = 0.f;
         for (int u = 0; u <= r; ++u)
@@ -138,7 +152,7 @@ __global__ __launch_bounds__(256) void kda_chunk_f32_kernel(
 hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, const float *g,
                             const float *beta, const float *gate, const float *init, float *out,
                             float *final_state, float *snaps, int snap_interval,
-                            const int32_t *cu, int N, int T, int H, float scale,
+                            const int32_t *cu, int N, int T, int H, float scale, unsigned pro,
                             hipStream_t stream)
 {
     const int64_t units = (int64_t)N * H;
@@ -146,7 +160,7 @@ hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, cons
         return hipSuccess;
     hipLaunchKernelGGL(kda_chunk_f32_kernel, dim3((unsigned)units), dim3(256), 0, stream, q, k,
                        v, g, beta, gate, init, out, final_state, snaps, snap_interval, cu, T, H,
-                       scale);
+                       scale, pro);
     return hipGetLastError();
 }
 

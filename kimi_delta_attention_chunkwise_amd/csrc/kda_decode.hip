@@ -29,11 +29,13 @@ struct DecodeGeom {
     static_assert(DK % RG == 0, "rows split evenly");
 };
 
-template <typename T, int DK, int DV>
+// kPro: the prologue bits in `pro` are honoured (a separate instantiation,
+// so the plain step carries none of its registers or code)
+template <typename T, int DK, int DV, bool kPro>
 __global__ __launch_bounds__(256) void kda_decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ g, const T *__restrict__ beta, const T *__restrict__ gate,
-    float *__restrict__ state, T *__restrict__ out, float scale)
+    float *__restrict__ state, T *__restrict__ out, float scale, unsigned pro)
 {
     using Geo = DecodeGeom<T, DK, DV>;
     constexpr int CG = Geo::CG, RG = Geo::RG, RPT = Geo::RPT;
@@ -41,6 +43,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     __shared__ f32x4 red_s[RG][CG];
     __shared__ float red_kq[RG];
     __shared__ float va[DK], vk[DK], vq[DK];          // exp(g), k, q of this unit
+    __shared__ float nrm[2];                           // prologue: 1 / |k|, 1 / |q|
 
     const int64_t unit = blockIdx.x;                 // n * H + h
     const int tid = threadIdx.x;
@@ -53,11 +56,37 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     for (int m = 0; m < RPT; ++m)
         s_reg[m] = *reinterpret_cast<const f32x4 *>(S + (rg + RG * m) * DV + 4 * cg);
     for (int i = tid; i < DK; i += Geo::NT) {
-        va[i] = __expf(to_f32(gu[i]));
+        const float gx = to_f32(gu[i]);
+        va[i] = __expf((kPro && (pro & kProG)) ? log_decay_from(gx) : gx);
         vk[i] = to_f32(ku[i]);
         vq[i] = to_f32(qu[i]);
     }
     __syncthreads();
+    if (kPro && (pro & kProQK)) {
+        // wave 0 reduces |k|^2 and |q|^2 and rescales the staged vectors
+        if (tid < 64) {
+            float sk = 0.f, sq = 0.f;
+            for (int i = tid; i < DK; i += 64) {
+                sk += vk[i] * vk[i];
+                sq += vq[i] * vq[i];
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                sk += __shfl_xor(sk, o);
+                sq += __shfl_xor(sq, o);
+            }
+            if (tid == 0) {
+                nrm[0] = __builtin_amdgcn_rsqf(sk + kNormEps);
+                nrm[1] = __builtin_amdgcn_rsqf(sq + kNormEps);
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < DK; i += Geo::NT) {
+            vk[i] *= nrm[0];
+            vq[i] *= nrm[1];
+        }
+        __syncthreads();
+    }
     float kk[RPT];
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
     float kq = 0.f;
@@ -84,7 +113,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
         SQ += red_s[r][cg];
         KQ += red_kq[r];
     }
-    const float b = to_f32(beta[unit]);
+    const float b = (kPro && (pro & kProBeta)) ? sigmoidf_(to_f32(beta[unit])) : to_f32(beta[unit]);
     f32x4 u;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -108,32 +137,40 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
 template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const void *g,
                                   const void *beta, const void *gate, float *state, void *out,
-                                  int N, int H, float scale, hipStream_t stream)
+                                  int N, int H, float scale, unsigned pro, hipStream_t stream)
 {
     using Geo = DecodeGeom<T, DK, DV>;
     const int64_t units = (int64_t)N * H;
     if (units == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((kda_decode_kernel<T, DK, DV>), dim3((unsigned)units), dim3(Geo::NT), 0,
-                       stream, (const T *)q, (const T *)k, (const T *)v, (const T *)g,
-                       (const T *)beta, (const T *)gate, state, (T *)out, scale);
+    if (pro)
+        hipLaunchKernelGGL((kda_decode_kernel<T, DK, DV, true>), dim3((unsigned)units),
+                           dim3(Geo::NT), 0, stream, (const T *)q, (const T *)k, (const T *)v,
+                           (const T *)g, (const T *)beta, (const T *)gate, state, (T *)out, scale,
+                           pro);
+    else
+        hipLaunchKernelGGL((kda_decode_kernel<T, DK, DV, false>), dim3((unsigned)units),
+                           dim3(Geo::NT), 0, stream, (const T *)q, (const T *)k, (const T *)v,
+                           (const T *)g, (const T *)beta, (const T *)gate, state, (T *)out, scale,
+                           0u);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
                          const void *beta, const void *gate, float *state, void *out, int N,
-                         int H, int dk, int dv, float scale, int is_bf16, hipStream_t stream)
+                         int H, int dk, int dv, float scale, int is_bf16, unsigned pro,
+                         hipStream_t stream)
 {
     if (dk == 128 && dv == 128)
         return is_bf16 ? launch_decode_t<bf16, 128, 128>(q, k, v, g, beta, gate, state, out, N,
-                                                         H, scale, stream)
+                                                         H, scale, pro, stream)
                        : launch_decode_t<float, 128, 128>(q, k, v, g, beta, gate, state, out,
-                                                          N, H, scale, stream);
+                                                          N, H, scale, pro, stream);
     if (dk == 16 && dv == 16)
         return is_bf16 ? launch_decode_t<bf16, 16, 16>(q, k, v, g, beta, gate, state, out, N,
-                                                       H, scale, stream)
+                                                       H, scale, pro, stream)
                        : launch_decode_t<float, 16, 16>(q, k, v, g, beta, gate, state, out, N,
-                                                        H, scale, stream);
+                                                        H, scale, pro, stream);
     return hipErrorInvalidValue;
 }
 

@@ -107,6 +107,19 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// ------------------------------------------------------------- prologue
+// Optional input maps applied inside the kernels (same bits as KDA_PRO_* in
+// kda.h): q and k L2-normalised over dk per (token, head) with the epsilon
+// inside the square root, beta = sigmoid(logit), g = max(-5, -softplus(x)).
+constexpr unsigned kProQK = 1u, kProBeta = 2u, kProG = 4u;
+constexpr float kNormEps = 1e-6f;
+
+__device__ __forceinline__ float log_decay_from(float x)
+{
+    const float sp = fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));   // softplus(x)
+    return fmaxf(-5.f, -sp);
+}
+
 // Sequence bounds and first chunk slot of sequence n.  Without cu_seqlens the
 // B sequences have length T and slot = n * ceil(T / chunk) + j.  With
 // cu_seqlens, slot(n, j) = floor(cu[n] / chunk) + n + j, an injective map
@@ -148,19 +161,20 @@ __device__ __forceinline__ int64_t snap_slot0(const int32_t *cu, int n, int T, i
 // All return hipSuccess or the launch error.
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
                          const void *beta, const void *gate, float *state, void *out, int N,
-                         int H, int dk, int dv, float scale, int is_bf16, hipStream_t stream);
+                         int H, int dk, int dv, float scale, int is_bf16, unsigned pro,
+                         hipStream_t stream);
 
 // snaps / snap_interval: state snapshots (see snap_slot0); NULL / 0 for none.
 hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, const float *g,
                             const float *beta, const float *gate, const float *init,
                             float *out, float *final_state, float *snaps, int snap_interval,
-                            const int32_t *cu, int N, int T, int H, float scale,
+                            const int32_t *cu, int N, int T, int H, float scale, unsigned pro,
                             hipStream_t stream);
 
 hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                              const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
                              float *final_state, float *snaps, int snap_interval,
                              const int32_t *cu, int N, int T, int H, int64_t n_slots,
-                             float scale, void *workspace, hipStream_t stream);
+                             float scale, unsigned pro, void *workspace, hipStream_t stream);
 
 }  // namespace kda

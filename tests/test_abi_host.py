@@ -34,7 +34,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes",
-              "kda_status_str", "kda_chunk_fwd_snapshots", "kda_snapshot_slots"):
+              "kda_status_str", "kda_chunk_fwd_snapshots", "kda_snapshot_slots",
+              "kda_chunk_fwd_ex", "kda_decode_step_ex"):
         assert n in names
 
 
@@ -150,6 +151,21 @@ def test_chunk_fwd_snapshots_rejects_bad_arguments(lib):
     assert call(1, 0) == SHAPE
     assert call(1, 64, ws_bytes=REC - 1) == WS
     assert call(1, 64, B=2) == SHAPE
+
+
+def test_prologue_rejects_unknown_bits(lib):
+    p = ctypes.c_void_p
+    REC = lib.kda_chunk_fwd_workspace_bytes(1, 64, 1, 1, 128, 128, 64, 1, 0)
+
+    def chunk(pro):
+        return lib.kda_chunk_fwd_ex(p(1), p(1), p(1), p(1), p(1), p(1), None, p(1), None, None, 0,
+                                    None, 1, 64, 1, 1, 128, 128, 64, 1.0, 1, pro, p(1), REC, None)
+
+    def dec(pro):
+        return lib.kda_decode_step_ex(p(1), p(1), p(1), p(1), p(1), p(1), p(1), p(1), 1, 1, 128,
+                                      128, 1.0, 1, pro, None)
+    assert chunk(8) == UNSUP and chunk(0xFFFF) == UNSUP
+    assert dec(8) == UNSUP
 
 
 def test_decode_step_rejects_bad_arguments_before_launch(lib):
