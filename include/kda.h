@@ -196,6 +196,37 @@ kda_status kda_decode_step_ex(const void *q, const void *k, const void *v, const
                               int H, int dk, int dv, float scale, kda_dtype dt, unsigned prologue,
                               hipStream_t stream);
 
+/* Speculative decoding: verify K draft tokens, then commit the accepted
+ * prefix ("Kimi K3 plain-language guide", section 4.1: the MTP layer is tuned
+ * into an EAGLE-3 draft model whose guesses the full model verifies; the KDA
+ * state must then move past exactly the accepted tokens).
+ *
+ * kda_decode_verify runs the K tokens of each sequence, in order, on a copy of
+ * its state held on chip, and leaves `state` unchanged.  Token t of sequence
+ * n is row (n K + t) of the token-major inputs, i.e.
+ *   q, k, g  [N, K, H, dk]   v, gate, out [N, K, H, dv]   beta [N, K, H]   dt
+ *   state    [N, H, dk, dv]  fp32, read only
+ *   u_out    [N, K, H, dv]   fp32, the delta-rule correction u of every token
+ *                            (needed by kda_decode_commit; NULL = not written)
+ * out[n, t] equals what t + 1 successive kda_decode_step calls would return
+ * for that token, bit for bit.
+ *
+ * kda_decode_commit advances each state past its first accepted[n] tokens
+ * (accepted: device int32 [N], clamped to 0 .. K; 0 leaves the state as it
+ * is), from the same k and g given to the verification and its u_out:
+ *     S <- diag(exp(g_t)) S + k_t u_t^T,   t = 0 .. accepted[n] - 1
+ * The result equals accepted[n] successive kda_decode_step calls, bit for
+ * bit, at the cost of one read and one write of the state.  `prologue` must
+ * be the bits given to the verification. */
+kda_status kda_decode_verify(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, const void *gate, const float *state, void *out,
+                             float *u_out, int N, int K, int H, int dk, int dv, float scale,
+                             kda_dtype dt, unsigned prologue, hipStream_t stream);
+
+kda_status kda_decode_commit(const void *k, const void *g, const float *u,
+                             const int32_t *accepted, float *state, int N, int K, int H, int dk,
+                             int dv, kda_dtype dt, unsigned prologue, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,8 @@ Entry points (names follow the C ABI):
   chunk_fwd_snapshots(q, k, v, g, beta, gate, interval, ...)
             -> (out, final_state, snapshots)
   decode_step(q, k, v, g, beta, gate, state, scale=1.0) -> out   (state in place)
+  decode_verify(q, k, v, g, beta, gate, state, ...) -> (out, u)  (K draft tokens, state kept)
+  decode_commit(k, g, u, accepted, state, ...)                   (accepted prefix into state)
   chunk_fwd_workspace_bytes(...), snapshot_slots(...), chunk_fwd_supported(...),
   decode_step_supported(...)
 """
@@ -24,6 +26,7 @@ import torch
 
 __all__ = [
     "KdaError", "KdaLibraryError", "chunk_fwd", "chunk_fwd_snapshots", "decode_step",
+    "decode_verify", "decode_commit",
     "chunk_fwd_workspace_bytes", "snapshot_slots", "snapshot_index",
     "chunk_fwd_supported", "decode_step_supported", "library_path", "load_library",
     "KDA_F32", "KDA_BF16", "G_MIN", "PRO_QK_L2NORM", "PRO_BETA_SIGMOID", "PRO_G_SOFTPLUS",
@@ -71,6 +74,10 @@ _SIGNATURES = {
                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "kda_decode_step_ex": ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
                            ctypes.c_uint, ctypes.c_void_p], ctypes.c_int),
+    "kda_decode_verify": ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float,
+                          ctypes.c_int, ctypes.c_uint, ctypes.c_void_p], ctypes.c_int),
+    "kda_decode_commit": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_int, ctypes.c_uint,
+                          ctypes.c_void_p], ctypes.c_int),
     "kda_decode_step": ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
                         ctypes.c_void_p], ctypes.c_int),
 }
@@ -308,3 +315,61 @@ def decode_step(q, k, v, g, beta, gate, state, scale=1.0, out=None, prologue=0):
                                  _stream_ptr(dev))
     _check(st)
     return out
+
+
+def decode_verify(q, k, v, g, beta, gate, state, scale=1.0, prologue=0, out=None, u=None):
+    """Run K draft tokens per sequence from ``state`` (fp32 ``[N, H, dk, dv]``,
+    not modified).  q, k, g ``[N, K, H, dk]``; v, gate ``[N, K, H, dv]``; beta
+    ``[N, K, H]``.  Returns ``(out [N, K, H, dv], u [N, K, H, dv] fp32)``; pass
+    ``u`` and the same k, g to ``decode_commit`` once the accepted prefix is
+    known."""
+    lib = load_library()
+    if state.dim() != 4 or q.dim() != 4:
+        raise ValueError("state must be [N, H, dk, dv] and q [N, K, H, dk]")
+    N, H, dk, dv = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("kda.decode_verify runs on a HIP device; state is on " + str(dev))
+    _need(state, "state", (N, H, dk, dv), torch.float32, dev)
+    K = q.shape[1]
+    dt = q.dtype
+    code = _dtype_code(dt)
+    for name, t, shp in (("q", q, (N, K, H, dk)), ("k", k, (N, K, H, dk)),
+                         ("g", g, (N, K, H, dk)), ("v", v, (N, K, H, dv)),
+                         ("gate", gate, (N, K, H, dv)), ("beta", beta, (N, K, H))):
+        _need(t, name, shp, dt, dev)
+    if out is None:
+        out = torch.empty((N, K, H, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", (N, K, H, dv), dt, dev)
+    if u is None:
+        u = torch.empty((N, K, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _need(u, "u", (N, K, H, dv), torch.float32, dev)
+    st = lib.kda_decode_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
+                               _ptr(state), _ptr(out), _ptr(u), N, K, H, dk, dv, float(scale),
+                               code, int(prologue), _stream_ptr(dev))
+    _check(st)
+    return out, u
+
+
+def decode_commit(k, g, u, accepted, state, prologue=0):
+    """Advance ``state`` (in place) past the first ``accepted[n]`` verified
+    tokens of each sequence (``accepted``: int32 ``[N]`` on the device), using
+    the k, g and ``u`` of ``decode_verify``."""
+    lib = load_library()
+    N, H, dk, dv = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("kda.decode_commit runs on a HIP device; state is on " + str(dev))
+    _need(state, "state", (N, H, dk, dv), torch.float32, dev)
+    K = k.shape[1]
+    dt = k.dtype
+    code = _dtype_code(dt)
+    _need(k, "k", (N, K, H, dk), dt, dev)
+    _need(g, "g", (N, K, H, dk), dt, dev)
+    _need(u, "u", (N, K, H, dv), torch.float32, dev)
+    _need(accepted, "accepted", (N,), torch.int32, dev)
+    st = lib.kda_decode_commit(_ptr(k), _ptr(g), _ptr(u), _ptr(accepted), _ptr(state), N, K, H,
+                               dk, dv, code, int(prologue), _stream_ptr(dev))
+    _check(st)

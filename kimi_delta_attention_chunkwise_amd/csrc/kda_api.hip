@@ -167,11 +167,56 @@ kda_status kda_decode_step_ex(const void *q, const void *k, const void *v, const
         return KDA_ERR_UNSUPPORTED;
     if (N < 0 || H < 1)
         return KDA_ERR_BAD_SHAPE;
+    if ((int64_t)N * H > INT32_MAX)
+        return KDA_ERR_UNSUPPORTED;
     if (N == 0)
         return KDA_OK;
     if (!q || !k || !v || !g || !beta || !gate || !state || !out)
         return KDA_ERR_NULL_POINTER;
-    return from_hip(kda::launch_decode(q, k, v, g, beta, gate, state, out, N, H, dk, dv, scale,
+    return from_hip(kda::launch_decode(q, k, v, g, beta, gate, state, out, nullptr, N, 1, H, dk,
+                                       dv, scale, dt == KDA_BF16, prologue, 1, stream));
+}
+
+kda_status kda_decode_verify(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, const void *gate, const float *state, void *out,
+                             float *u_out, int N, int K, int H, int dk, int dv, float scale,
+                             kda_dtype dt, unsigned prologue, hipStream_t stream)
+{
+    if (!valid_dtype(dt))
+        return KDA_ERR_BAD_DTYPE;
+    if (!decode_supported(dt, dk, dv) || (prologue & ~kProAll) != 0)
+        return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || K < 1 || H < 1)
+        return KDA_ERR_BAD_SHAPE;
+    if ((int64_t)N * H > INT32_MAX)
+        return KDA_ERR_UNSUPPORTED;
+    if (N == 0)
+        return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !gate || !state || !out)
+        return KDA_ERR_NULL_POINTER;
+    // the state is only read (write_state = 0)
+    return from_hip(kda::launch_decode(q, k, v, g, beta, gate, const_cast<float *>(state), out,
+                                       u_out, N, K, H, dk, dv, scale, dt == KDA_BF16, prologue, 0,
+                                       stream));
+}
+
+kda_status kda_decode_commit(const void *k, const void *g, const float *u,
+                             const int32_t *accepted, float *state, int N, int K, int H, int dk,
+                             int dv, kda_dtype dt, unsigned prologue, hipStream_t stream)
+{
+    if (!valid_dtype(dt))
+        return KDA_ERR_BAD_DTYPE;
+    if (!decode_supported(dt, dk, dv) || (prologue & ~kProAll) != 0)
+        return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || K < 1 || H < 1)
+        return KDA_ERR_BAD_SHAPE;
+    if ((int64_t)N * H > INT32_MAX)
+        return KDA_ERR_UNSUPPORTED;
+    if (N == 0)
+        return KDA_OK;
+    if (!k || !g || !u || !accepted || !state)
+        return KDA_ERR_NULL_POINTER;
+    return from_hip(kda::launch_commit(k, g, u, accepted, state, N, K, H, dk, dv,
                                        dt == KDA_BF16, prologue, stream));
 }
 

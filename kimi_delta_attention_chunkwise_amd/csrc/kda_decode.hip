@@ -29,46 +29,29 @@ struct DecodeGeom {
     static_assert(DK % RG == 0, "rows split evenly");
 };
 
-// kPro: the prologue bits in `pro` are honoured (a separate instantiation,
-// so the plain step carries none of its registers or code)
-template <typename T, int DK, int DV, bool kPro>
-__global__ __launch_bounds__(256) void kda_decode_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ g, const T *__restrict__ beta, const T *__restrict__ gate,
-    float *__restrict__ state, T *__restrict__ out, float scale, unsigned pro)
+// Stage exp(g), k and (when qu is given) q of one (sequence, token, head) row
+// in LDS.  With the prologue, g is mapped to the log-decay and k, q are
+// L2-normalised (wave 0 reduces the squares).  Ends with a barrier.
+template <typename T, int DK, int NT, bool kPro>
+__device__ __forceinline__ void stage_token(const T *qu, const T *ku, const T *gu, float *va,
+                                            float *vk, float *vq, float *nrm, unsigned pro,
+                                            int tid)
 {
-    using Geo = DecodeGeom<T, DK, DV>;
-    constexpr int CG = Geo::CG, RG = Geo::RG, RPT = Geo::RPT;
-    __shared__ f32x4 red_p[RG][CG];
-    __shared__ f32x4 red_s[RG][CG];
-    __shared__ float red_kq[RG];
-    __shared__ float va[DK], vk[DK], vq[DK];          // exp(g), k, q of this unit
-    __shared__ float nrm[2];                           // prologue: 1 / |k|, 1 / |q|
-
-    const int64_t unit = blockIdx.x;                 // n * H + h
-    const int tid = threadIdx.x;
-    const int cg = tid % CG, rg = tid / CG;
-    float *S = state + unit * (int64_t)(DK * DV);
-    const T *qu = q + unit * DK, *ku = k + unit * DK, *gu = g + unit * DK;
-
-    f32x4 s_reg[RPT];
-#pragma unroll
-    for (int m = 0; m < RPT; ++m)
-        s_reg[m] = *reinterpret_cast<const f32x4 *>(S + (rg + RG * m) * DV + 4 * cg);
-    for (int i = tid; i < DK; i += Geo::NT) {
+    for (int i = tid; i < DK; i += NT) {
         const float gx = to_f32(gu[i]);
         va[i] = __expf((kPro && (pro & kProG)) ? log_decay_from(gx) : gx);
         vk[i] = to_f32(ku[i]);
-        vq[i] = to_f32(qu[i]);
+        if (qu)
+            vq[i] = to_f32(qu[i]);
     }
     __syncthreads();
     if (kPro && (pro & kProQK)) {
-        // wave 0 reduces |k|^2 and |q|^2 and rescales the staged vectors
         if (tid < 64) {
             float sk = 0.f, sq = 0.f;
             for (int i = tid; i < DK; i += 64) {
                 sk += vk[i] * vk[i];
-                sq += vq[i] * vq[i];
+                if (qu)
+                    sq += vq[i] * vq[i];
             }
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) {
@@ -81,97 +64,246 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
             }
         }
         __syncthreads();
-        for (int i = tid; i < DK; i += Geo::NT) {
+        for (int i = tid; i < DK; i += NT) {
             vk[i] *= nrm[0];
-            vq[i] *= nrm[1];
+            if (qu)
+                vq[i] *= nrm[1];
         }
         __syncthreads();
     }
-    float kk[RPT];
-    f32x4 p = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
-    float kq = 0.f;
+}
+
+// The state update of one row quad, written out so that the decode / verify
+// kernel and the commit kernel round identically: decay, then k u^T added
+// with one fused multiply-add.
+__device__ __forceinline__ f32x4 decay_row(const f32x4 &s, float a)
+{
+    return f32x4{__fmul_rn(s[0], a), __fmul_rn(s[1], a), __fmul_rn(s[2], a), __fmul_rn(s[3], a)};
+}
+__device__ __forceinline__ f32x4 write_row(const f32x4 &s, float kr, const f32x4 &u)
+{
+    return f32x4{__fmaf_rn(kr, u[0], s[0]), __fmaf_rn(kr, u[1], s[1]), __fmaf_rn(kr, u[2], s[2]),
+                 __fmaf_rn(kr, u[3], s[3])};
+}
+
+// Decode step (K = 1, state written back) and speculative verification
+// (K draft tokens run on the state in registers; the state is left as it was
+// and each token's correction u is saved for kda_commit_kernel).  Inputs of
+// token t of sequence n, head h are row (n K + t) H + h of the [N, K, H, d]
+// tensors.  kPro: the prologue bits in `pro` are honoured (a separate
+// instantiation, so the plain step carries none of its registers or code).
+// kVerify = false is the plain step: one token, the state written back, no
+// corrections saved (K, u_out and write_state are ignored).
+template <typename T, int DK, int DV, bool kPro, bool kVerify>
+__global__ __launch_bounds__(256) void kda_decode_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ g, const T *__restrict__ beta, const T *__restrict__ gate,
+    float *__restrict__ state, T *__restrict__ out, float *__restrict__ u_out, int K_arg, int H,
+    float scale, unsigned pro, int write_state_arg)
+{
+    const int K = kVerify ? K_arg : 1;
+    const bool write_state = kVerify ? write_state_arg != 0 : true;
+    using Geo = DecodeGeom<T, DK, DV>;
+    constexpr int CG = Geo::CG, RG = Geo::RG, RPT = Geo::RPT;
+    __shared__ f32x4 red_p[RG][CG];
+    __shared__ f32x4 red_s[RG][CG];
+    __shared__ float red_kq[RG];
+    __shared__ float va[DK], vk[DK], vq[DK];          // exp(g), k, q of the current token
+    __shared__ float nrm[2];                           // prologue: 1 / |k|, 1 / |q|
+
+    const int64_t unit = blockIdx.x;                 // n * H + h
+    const int64_t n = unit / H;
+    const int h = (int)(unit % H);
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    float *S = state + unit * (int64_t)(DK * DV);
+
+    f32x4 s_reg[RPT];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int row = rg + RG * m;
-        const float a = va[row], kr = vk[row], qr = vq[row];
-        kk[m] = kr;
-        s_reg[m] *= a;                                 // decay the key-channel row
-        p += s_reg[m] * kr;                            // prediction for the key
-        sq += s_reg[m] * qr;                           // decayed state read by q
-        kq += kr * qr;
-    }
-    red_p[rg][cg] = p;
-    red_s[rg][cg] = sq;
-    if (cg == 0)
-        red_kq[rg] = kq;
-    __syncthreads();
-    f32x4 P = red_p[0][cg], SQ = red_s[0][cg];
-    float KQ = red_kq[0];
+    for (int m = 0; m < RPT; ++m)
+        s_reg[m] = *reinterpret_cast<const f32x4 *>(S + (rg + RG * m) * DV + 4 * cg);
+    for (int t = 0; t < K; ++t) {
+        const int64_t row = (n * K + t) * H + h;
+        stage_token<T, DK, Geo::NT, kPro>(q + row * DK, k + row * DK, g + row * DK, va, vk, vq,
+                                          nrm, pro, tid);
+        float kk[RPT];
+        f32x4 p = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
+        float kq = 0.f;
 #pragma unroll
-    for (int r = 1; r < RG; ++r) {
-        P += red_p[r][cg];
-        SQ += red_s[r][cg];
-        KQ += red_kq[r];
-    }
-    const float b = (kPro && (pro & kProBeta)) ? sigmoidf_(to_f32(beta[unit])) : to_f32(beta[unit]);
-    f32x4 u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        u[i] = b * (to_f32(v[unit * DV + 4 * cg + i]) - P[i]);   // delta-rule correction
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int row = rg + RG * m;
-        __builtin_nontemporal_store(s_reg[m] + kk[m] * u,                  // write
-                                    reinterpret_cast<f32x4 *>(S + row * DV + 4 * cg));
-    }
-    if (rg == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = 4 * cg + i;
-            const float o = scale * (SQ[i] + KQ * u[i]);          // read after the write
-            out[unit * DV + c] = from_f32<T>(sigmoidf_(to_f32(gate[unit * DV + c])) * o);
+        for (int m = 0; m < RPT; ++m) {
+            const int r = rg + RG * m;
+            const float kr = vk[r], qr = vq[r];
+            kk[m] = kr;
+            s_reg[m] = decay_row(s_reg[m], va[r]);     // decay the key-channel row
+            p += s_reg[m] * kr;                        // prediction for the key
+            sq += s_reg[m] * qr;                       // decayed state read by q
+            kq += kr * qr;
         }
+        red_p[rg][cg] = p;
+        red_s[rg][cg] = sq;
+        if (cg == 0)
+            red_kq[rg] = kq;
+        __syncthreads();
+        f32x4 P = red_p[0][cg], SQ = red_s[0][cg];
+        float KQ = red_kq[0];
+#pragma unroll
+        for (int r = 1; r < RG; ++r) {
+            P += red_p[r][cg];
+            SQ += red_s[r][cg];
+            KQ += red_kq[r];
+        }
+        const float bx = to_f32(beta[row]);
+        const float b = (kPro && (pro & kProBeta)) ? sigmoidf_(bx) : bx;
+        f32x4 u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            u[i] = b * (to_f32(v[row * DV + 4 * cg + i]) - P[i]);   // delta-rule correction
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            s_reg[m] = write_row(s_reg[m], kk[m], u);               // write
+        if (rg == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 4 * cg + i;
+                const float o = scale * (SQ[i] + KQ * u[i]);         // read after the write
+                out[row * DV + c] = from_f32<T>(sigmoidf_(to_f32(gate[row * DV + c])) * o);
+            }
+            if (kVerify && u_out)
+                *reinterpret_cast<f32x4 *>(u_out + row * DV + 4 * cg) = u;
+        }
+        // the next token's staging and reductions overwrite LDS only after the
+        // next barrier, which every thread reaches after its reads of this one
     }
+    if (write_state) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            __builtin_nontemporal_store(s_reg[m], reinterpret_cast<f32x4 *>(
+                                                      S + (rg + RG * m) * DV + 4 * cg));
+    }
+}
+
+// Commit the first accepted[n] verified tokens of sequence n into its state:
+// S <- diag(exp(g_t)) S + k_t u_t^T with the corrections u_t saved by the
+// verification, which reproduces the verified states exactly.
+template <typename T, int DK, int DV, bool kPro>
+__global__ __launch_bounds__(256) void kda_commit_kernel(
+    const T *__restrict__ k, const T *__restrict__ g, const float *__restrict__ u,
+    const int32_t *__restrict__ accepted, float *__restrict__ state, int K, int H, unsigned pro)
+{
+    using Geo = DecodeGeom<T, DK, DV>;
+    constexpr int CG = Geo::CG, RG = Geo::RG, RPT = Geo::RPT;
+    __shared__ float va[DK], vk[DK];
+    __shared__ float nrm[2];
+
+    const int64_t unit = blockIdx.x;
+    const int64_t n = unit / H;
+    const int h = (int)(unit % H);
+    const int acc_raw = accepted[n];
+    const int acc = acc_raw < 0 ? 0 : (acc_raw > K ? K : acc_raw);
+    if (acc == 0)
+        return;                                        // the whole workgroup leaves together
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    float *S = state + unit * (int64_t)(DK * DV);
+    f32x4 s_reg[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        s_reg[m] = *reinterpret_cast<const f32x4 *>(S + (rg + RG * m) * DV + 4 * cg);
+    for (int t = 0; t < acc; ++t) {
+        const int64_t row = (n * K + t) * H + h;
+        stage_token<T, DK, Geo::NT, kPro>(nullptr, k + row * DK, g + row * DK, va, vk, nullptr,
+                                          nrm, pro, tid);
+        const f32x4 ut = *reinterpret_cast<const f32x4 *>(u + row * DV + 4 * cg);
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int r = rg + RG * m;
+            s_reg[m] = write_row(decay_row(s_reg[m], va[r]), vk[r], ut);
+        }
+        __syncthreads();                               // LDS is restaged for the next token
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        __builtin_nontemporal_store(s_reg[m],
+                                    reinterpret_cast<f32x4 *>(S + (rg + RG * m) * DV + 4 * cg));
 }
 
 template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const void *g,
                                   const void *beta, const void *gate, float *state, void *out,
-                                  int N, int H, float scale, unsigned pro, hipStream_t stream)
+                                  float *u_out, int N, int K, int H, float scale, unsigned pro,
+                                  int write_state, hipStream_t stream)
+{
+    using Geo = DecodeGeom<T, DK, DV>;
+    const int64_t units = (int64_t)N * H;
+    if (units == 0)
+        return hipSuccess;
+    const bool verify = K != 1 || !write_state || u_out;
+#define KDA_LAUNCH(PRO, VER)                                                                      \
+    hipLaunchKernelGGL((kda_decode_kernel<T, DK, DV, PRO, VER>), dim3((unsigned)units),           \
+                       dim3(Geo::NT), 0, stream, (const T *)q, (const T *)k, (const T *)v,        \
+                       (const T *)g, (const T *)beta, (const T *)gate, state, (T *)out, u_out, K, \
+                       H, scale, pro, write_state)
+    if (pro && verify)
+        KDA_LAUNCH(true, true);
+    else if (pro)
+        KDA_LAUNCH(true, false);
+    else if (verify)
+        KDA_LAUNCH(false, true);
+    else
+        KDA_LAUNCH(false, false);
+#undef KDA_LAUNCH
+    return hipGetLastError();
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_commit_t(const void *k, const void *g, const float *u,
+                                  const int32_t *accepted, float *state, int N, int K, int H,
+                                  unsigned pro, hipStream_t stream)
 {
     using Geo = DecodeGeom<T, DK, DV>;
     const int64_t units = (int64_t)N * H;
     if (units == 0)
         return hipSuccess;
     if (pro)
-        hipLaunchKernelGGL((kda_decode_kernel<T, DK, DV, true>), dim3((unsigned)units),
-                           dim3(Geo::NT), 0, stream, (const T *)q, (const T *)k, (const T *)v,
-                           (const T *)g, (const T *)beta, (const T *)gate, state, (T *)out, scale,
-                           pro);
+        hipLaunchKernelGGL((kda_commit_kernel<T, DK, DV, true>), dim3((unsigned)units),
+                           dim3(Geo::NT), 0, stream, (const T *)k, (const T *)g, u, accepted,
+                           state, K, H, pro);
     else
-        hipLaunchKernelGGL((kda_decode_kernel<T, DK, DV, false>), dim3((unsigned)units),
-                           dim3(Geo::NT), 0, stream, (const T *)q, (const T *)k, (const T *)v,
-                           (const T *)g, (const T *)beta, (const T *)gate, state, (T *)out, scale,
-                           0u);
+        hipLaunchKernelGGL((kda_commit_kernel<T, DK, DV, false>), dim3((unsigned)units),
+                           dim3(Geo::NT), 0, stream, (const T *)k, (const T *)g, u, accepted,
+                           state, K, H, 0u);
     return hipGetLastError();
 }
 
+#define KDA_DECODE_DISPATCH(CALL)                                                                 \
+    do {                                                                                          \
+        if (dk == 128 && dv == 128)                                                               \
+            return is_bf16 ? CALL(bf16, 128, 128) : CALL(float, 128, 128);                        \
+        if (dk == 16 && dv == 16)                                                                 \
+            return is_bf16 ? CALL(bf16, 16, 16) : CALL(float, 16, 16);                            \
+        return hipErrorInvalidValue;                                                              \
+    } while (0)
+
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
-                         const void *beta, const void *gate, float *state, void *out, int N,
-                         int H, int dk, int dv, float scale, int is_bf16, unsigned pro,
-                         hipStream_t stream)
+                         const void *beta, const void *gate, float *state, void *out,
+                         float *u_out, int N, int K, int H, int dk, int dv, float scale,
+                         int is_bf16, unsigned pro, int write_state, hipStream_t stream)
 {
-    if (dk == 128 && dv == 128)
-        return is_bf16 ? launch_decode_t<bf16, 128, 128>(q, k, v, g, beta, gate, state, out, N,
-                                                         H, scale, pro, stream)
-                       : launch_decode_t<float, 128, 128>(q, k, v, g, beta, gate, state, out,
-                                                          N, H, scale, pro, stream);
-    if (dk == 16 && dv == 16)
-        return is_bf16 ? launch_decode_t<bf16, 16, 16>(q, k, v, g, beta, gate, state, out, N,
-                                                       H, scale, pro, stream)
-                       : launch_decode_t<float, 16, 16>(q, k, v, g, beta, gate, state, out, N,
-                                                        H, scale, pro, stream);
-    return hipErrorInvalidValue;
+#define KDA_CALL(T, DK, DV)                                                                       \
+    launch_decode_t<T, DK, DV>(q, k, v, g, beta, gate, state, out, u_out, N, K, H, scale, pro,   \
+                               write_state, stream)
+    KDA_DECODE_DISPATCH(KDA_CALL);
+#undef KDA_CALL
+}
+
+hipError_t launch_commit(const void *k, const void *g, const float *u, const int32_t *accepted,
+                         float *state, int N, int K, int H, int dk, int dv, int is_bf16,
+                         unsigned pro, hipStream_t stream)
+{
+#define KDA_CALL(T, DK, DV)                                                                       \
+    launch_commit_t<T, DK, DV>(k, g, u, accepted, state, N, K, H, pro, stream)
+    KDA_DECODE_DISPATCH(KDA_CALL);
+#undef KDA_CALL
 }
 
 }  // namespace kda

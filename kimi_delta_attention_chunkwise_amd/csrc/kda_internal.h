@@ -159,10 +159,16 @@ __device__ __forceinline__ int64_t snap_slot0(const int32_t *cu, int n, int T, i
 
 // ------------------------------------------------------------- launchers
 // All return hipSuccess or the launch error.
+// Decode step (K = 1, write_state = 1, u_out NULL) or verification of K
+// tokens (write_state = 0, u_out = the corrections for launch_commit).
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
-                         const void *beta, const void *gate, float *state, void *out, int N,
-                         int H, int dk, int dv, float scale, int is_bf16, unsigned pro,
-                         hipStream_t stream);
+                         const void *beta, const void *gate, float *state, void *out,
+                         float *u_out, int N, int K, int H, int dk, int dv, float scale,
+                         int is_bf16, unsigned pro, int write_state, hipStream_t stream);
+
+hipError_t launch_commit(const void *k, const void *g, const float *u, const int32_t *accepted,
+                         float *state, int N, int K, int H, int dk, int dv, int is_bf16,
+                         unsigned pro, hipStream_t stream);
 
 // snaps / snap_interval: state snapshots (see snap_slot0); NULL / 0 for none.
 hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, const float *g,

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes",
               "kda_status_str", "kda_chunk_fwd_snapshots", "kda_snapshot_slots",
-              "kda_chunk_fwd_ex", "kda_decode_step_ex"):
+              "kda_chunk_fwd_ex", "kda_decode_step_ex", "kda_decode_verify",
+              "kda_decode_commit"):
         assert n in names
 
 
@@ -166,6 +167,33 @@ def test_prologue_rejects_unknown_bits(lib):
                                       128, 1.0, 1, pro, None)
     assert chunk(8) == UNSUP and chunk(0xFFFF) == UNSUP
     assert dec(8) == UNSUP
+
+
+def test_verify_and_commit_reject_bad_arguments(lib):
+    p = ctypes.c_void_p
+
+    def verify(**kw):
+        a = dict(N=2, K=3, H=1, d=128, dt=1, pro=0, state=1, out=1)
+        a.update(kw)
+        ptr = lambda x: None if x is None else p(x)
+        return lib.kda_decode_verify(p(1), p(1), p(1), p(1), p(1), p(1), ptr(a["state"]),
+                                     ptr(a["out"]), None, a["N"], a["K"], a["H"], a["d"], a["d"],
+                                     1.0, a["dt"], a["pro"], None)
+
+    def commit(**kw):
+        a = dict(N=2, K=3, H=1, d=128, dt=1, pro=0, acc=1, state=1)
+        a.update(kw)
+        ptr = lambda x: None if x is None else p(x)
+        return lib.kda_decode_commit(p(1), p(1), p(1), ptr(a["acc"]), ptr(a["state"]), a["N"],
+                                     a["K"], a["H"], a["d"], a["d"], a["dt"], a["pro"], None)
+    assert verify(K=0) == SHAPE and commit(K=0) == SHAPE
+    assert verify(H=0) == SHAPE and commit(N=-1) == SHAPE
+    assert verify(dt=9) == DTYPE and commit(dt=9) == DTYPE
+    assert verify(d=64) == UNSUP and commit(d=64) == UNSUP
+    assert verify(pro=16) == UNSUP and commit(pro=16) == UNSUP
+    assert verify(state=None) == NULLP and verify(out=None) == NULLP
+    assert commit(acc=None) == NULLP and commit(state=None) == NULLP
+    assert verify(N=0) == OK and commit(N=0) == OK
 
 
 def test_decode_step_rejects_bad_arguments_before_launch(lib):
