@@ -84,6 +84,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the snapshot / prologue / verify measurements")
     return ap.parse_args()
 
 
@@ -183,10 +185,16 @@ def main():
                  "unit": "TFLOP/s", "frac": flops_call / t_s / 1e12 / BF16_PEAK_TFLOPS,
                  "algorithmic_flops_per_call": flops_call},
     }
+    if not args.no_extras:
+        result["extras"] = {"snapshots_prologue": bench_prefill_extras(torch, kda, sets, ws, out,
+                                                                       fin, ms, args)}
     del sets
 
     if not args.no_decode:
         result["decode"] = bench_decode(torch, kda, W, dev, args)
+        if not args.no_extras:
+            result["extras"]["decode_prologue_verify"] = bench_decode_extras(torch, kda, W, dev,
+                                                                             args)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
@@ -228,6 +236,95 @@ def bench_decode(torch, kda, W, dev, args):
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "traffic": load_traffic("decode_hbm_bytes_per_step"),
                          "algorithmic_bytes_per_step": bytes_step}}
+
+
+def _time(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_prefill_extras(torch, kda, sets, ws, out, fin, ms_plain, args):
+    """The same prefill call with fp32 state snapshots every 512 tokens, and
+    with the fused prologue on raw inputs (all three maps)."""
+    n_sets = len(sets)
+    x0 = sets[0]
+    B, T, H, dk = x0["q"].shape
+    snaps = torch.empty(kda.snapshot_slots(B, T, B, CHUNK, 512, False), H, dk, DV,
+                        dtype=torch.float32, device=x0["q"].device)
+
+    def snap(i):
+        x = sets[i % n_sets]
+        kda.chunk_fwd_snapshots(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], 512,
+                                workspace=ws, out=out, final_state=fin, snapshots=snaps)
+
+    ms_snap = _time(torch, snap, max(20, args.steps // 4), 5)
+    # raw projections: unnormalised q/k, beta logits, g pre-activations
+    gen = torch.Generator(device=x0["q"].device).manual_seed(7)
+    raw = [{key: torch.randn(x0[key].shape, generator=gen, device=x0["q"].device).to(
+        torch.bfloat16) for key in ("q", "k", "g", "beta")} for _ in range(4)]
+
+    def pro(i):
+        x, r = sets[i % n_sets], raw[i % 4]
+        kda.chunk_fwd(r["q"], r["k"], x["v"], r["g"], r["beta"], x["z"], workspace=ws, out=out,
+                      final_state=fin, prologue=7)
+
+    ms_pro = _time(torch, pro, max(20, args.steps // 4), 5)
+    print(f"[bench] prefill with snapshots every 512: {ms_snap:.4f} ms; with prologue: "
+          f"{ms_pro:.4f} ms", file=sys.stderr, flush=True)
+    return {"workload": "prefill_t4096_h8", "plain_ms": ms_plain,
+            "snapshots_every_512_ms": ms_snap,
+            "snapshot_bytes_per_call": int(snaps.numel() * 4),
+            "prologue_all_ms": ms_pro,
+            "prologue_tokens_per_s": B * T / (ms_pro / 1e3)}
+
+
+def bench_decode_extras(torch, kda, W, dev, args):
+    """Decode step with the fused prologue, and speculative verification of
+    K = 4 draft tokens followed by a commit of all of them, on the decode
+    workload's 512 MiB state."""
+    w = W.WORKLOADS["decode_n256_h32"]
+    N, H, K = w.N, w.H, 4
+    state = W.decode_init_state(w, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    r = lambda *s: torch.randn(*s, generator=gen, device=dev).to(torch.bfloat16)
+    one = {"q": r(N, H, DK), "k": r(N, H, DK), "v": r(N, H, DV), "g": r(N, H, DK),
+           "beta": r(N, H), "z": r(N, H, DV)}
+    out = torch.empty(N, H, DV, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        kda.decode_step(one["q"], one["k"], one["v"], one["g"], one["beta"], one["z"], state,
+                        out=out, prologue=7)
+
+    ms_pro = _time(torch, step, 32, 4)
+    x = W.decode_inputs(w, step=0, device=dev)
+    drafts = {key: torch.stack([x[key]] * K, dim=1).contiguous() for key in x}
+    vout = torch.empty(N, K, H, DV, dtype=torch.bfloat16, device=dev)
+    u = torch.empty(N, K, H, DV, dtype=torch.float32, device=dev)
+    acc = torch.full((N,), K, dtype=torch.int32, device=dev)
+
+    def verify(i):
+        kda.decode_verify(drafts["q"], drafts["k"], drafts["v"], drafts["g"], drafts["beta"],
+                          drafts["z"], state, out=vout, u=u)
+
+    def commit(i):
+        kda.decode_commit(drafts["k"], drafts["g"], u, acc, state)
+
+    ms_ver = _time(torch, verify, 32, 4)
+    ms_com = _time(torch, commit, 32, 4)
+    print(f"[bench] decode with prologue: {ms_pro:.4f} ms; verify K={K}: {ms_ver:.4f} ms; "
+          f"commit: {ms_com:.4f} ms", file=sys.stderr, flush=True)
+    return {"workload": "decode_n256_h32", "prologue_all_step_ms": ms_pro,
+            "verify_draft_tokens": K, "verify_ms": ms_ver, "commit_all_ms": ms_com,
+            "verified_tokens_per_s": N * K / ((ms_ver + ms_com) / 1e3)}
 
 
 def cpu_baseline(w):
