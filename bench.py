@@ -196,6 +196,9 @@ def main():
             result["extras"]["decode_prologue_verify"] = bench_decode_extras(torch, kda, W, dev,
                                                                              args)
 
+    if not args.no_extras:
+        result["extras"]["long_t1m_h16"] = bench_long(torch, kda, W, dev)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
 
@@ -325,6 +328,31 @@ def bench_decode_extras(torch, kda, W, dev, args):
     return {"workload": "decode_n256_h32", "prologue_all_step_ms": ms_pro,
             "verify_draft_tokens": K, "verify_ms": ms_ver, "commit_all_ms": ms_com,
             "verified_tokens_per_s": N * K / ((ms_ver + ms_com) / 1e3)}
+
+
+def bench_long(torch, kda, W, dev, calls=3):
+    """The 1M-token workload (B=1, H=16, T=2^20, a quarter of the key channels
+    at g = -5): one kda_chunk_fwd call over the whole sequence."""
+    w = W.WORKLOADS["long_t1m_h16"]
+    x = W.prefill_inputs(w, device=dev, seed=0)
+    B, T, H = w.B, w.T, w.H
+    ws = torch.empty(kda.chunk_fwd_workspace_bytes(B, T, B, H, DK, DV, CHUNK, torch.bfloat16,
+                                                   False), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, T, H, DV, dtype=torch.bfloat16, device=dev)
+    fin = torch.empty(B, H, DK, DV, dtype=torch.float32, device=dev)
+
+    def call(i):
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], workspace=ws, out=out,
+                      final_state=fin)
+
+    ms = _time(torch, call, calls, 1)
+    token_heads = B * T * H
+    gbs = (PREFILL_BYTES_PER_TOKEN_HEAD * token_heads + B * H * STATE_BYTES) / (ms / 1e3) / 1e9
+    print(f"[bench] long_t1m_h16: {ms:.3f} ms per call", file=sys.stderr, flush=True)
+    del x, ws, out
+    return {"workload": "long_t1m_h16", "ms_per_call": ms, "tokens_per_s": B * T / (ms / 1e3),
+            "hbm_roofline": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS}}
 
 
 def cpu_baseline(w):

@@ -801,14 +801,26 @@ __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
     for (int blk = 0; blk < kNumVBlocks; ++blk)
         o0[blk] = *reinterpret_cast<const bf16x4 *>(rec + kOffO0 + blk * 2048 + t * 512 +
                                                     lane * 8);
+    // read-back mapping: lane -> row 8 p + lane / 8 of the wave's tile, channels 8 (lane % 8) ..
+    // of each 64-channel half; the gate logits of those rows are fetched now,
+    // with the other loads (rows past the chunk re-read its last row)
+    const int rq = lane >> 3, c8 = 8 * (lane & 7);
+    bf16x8 zr[2][2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int64_t row = 16 * t + 8 * p + rq;
+            const int64_t rr = row < lenc ? row : lenc - 1;
+            zr[half][p] = *reinterpret_cast<const bf16x8 *>(
+                gate + ((tok0 + rr) * H + h) * kDV + 64 * half + c8);
+        }
     bf16x8 *sbl = &sb_s[0][0];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         sbl[i * 256 + tid] = stage[i];
     __syncthreads();
 
-    // read-back mapping: lane -> row 8 p + lane / 8 of the wave's tile, channels 8 (lane % 8) ..
-    const int rq = lane >> 3, c8 = 8 * (lane & 7);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -830,14 +842,14 @@ __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
             const f32x4 hi = *reinterpret_cast<const f32x4 *>(&ot_s[t][r][c8 + 4]);
             if (row < lenc) {
                 const int64_t off = ((tok0 + row) * H + h) * kDV + 64 * half + c8;
-                const bf16x8 z = *reinterpret_cast<const bf16x8 *>(gate + off);
+                const bf16x8 z = zr[half][p];
                 bf16x8 y;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     y[i] = (bf16)(lo[i] * sigmoidf_((float)z[i]));
                     y[4 + i] = (bf16)(hi[i] * sigmoidf_((float)z[4 + i]));
                 }
-                *reinterpret_cast<bf16x8 *>(out + off) = y;
+                __builtin_nontemporal_store(y, reinterpret_cast<bf16x8 *>(out + off));
             }
         }
         __syncthreads();
