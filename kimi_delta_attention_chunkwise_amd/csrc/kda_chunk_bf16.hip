@@ -575,37 +575,34 @@ namespace {
 // Chain workgroup: 8 compute waves and 1 store wave.  Compute wave w keeps
 // state rows 16 w .. 16 w + 15 (one 16-row tile) and applies
 // S' = dec S + Bm - L S chunk after chunk; the waves exchange the new state as
-// bf16 MFMA fragments through LDS.  The step is bound by the operand stream
-// (about 36 KiB of L, Bm and dec per chunk through one CU), and the CU's load
-// bandwidth grows with the number of waves that have loads in flight, hence
-// eight loading waves of one tile each.  Compute waves only ever load from
-// global memory; the store wave copies each chunk's entry state from LDS to
-// the workspace for the output kernel.  Keeping loads and stores in different
+// bf16 MFMA fragments through LDS.  The step is bound by the CU's vector
+// memory pipeline, which costs about the same per load instruction whatever
+// its width: so the compute waves load only their 16-byte-per-lane fragments
+// of L, and a side wave fetches this value block's Bm and the decay vector
+// (5 wide loads instead of 16 narrow ones) two chunks ahead into an LDS ring.
+// The store wave copies each chunk's entry state from LDS to the workspace for
+// the output kernel.  Only the store wave issues stores: the loading waves
+// (compute and side) can then wait for exactly the loads they need.  Keeping loads and stores in different
 // waves lets the compiler wait for exactly the prefetched stage it needs
 // (with both kinds pending it can only wait for everything).
 constexpr int kComputeWaves = 8;
 constexpr int kStoreWave = kComputeWaves;
-constexpr int kChainThreads = 64 * (kComputeWaves + 1);
+constexpr int kSideWave = kComputeWaves + 1;
+constexpr int kChainThreads = 64 * (kComputeWaves + 2);
 constexpr int kPrefetch = 4;         // chunks of operands in flight per compute wave
 
 struct ChainStage {
     bf16x8 ln[4];      // -L rows of the wave's state tile, 4 dk k-steps
-    bf16x4 bm;         // Bm of the wave's 16 state rows, this value block
-    float dec;         // e^{G_end} of state row 16 w + lane % 16
 };
 
 __device__ __forceinline__ void chain_load(ChainStage &st, const uint8_t *rec_any, int w,
-                                           int lane, int blk)
+                                           int lane)
 {
     const gbyte *rec = uniform_gptr(rec_any);    // the record base is the same for the wave
     const uint32_t lo = (uint32_t)lane * 16u;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
         st.ln[ks] = gload<bf16x8>(rec, kOffLN + (w * 4 + ks) * kFragBytes + lo);
-    // Bm fragment of rows 32 (w / 2) + 16 (w % 2) + 4 b + i: half of a 16-byte slot
-    st.bm = gload<bf16x4>(rec, kOffBM + blk * 4096 + (w >> 1) * 1024 + lo + (w & 1) * 8);
-    // one float per lane; lanes l and l + 16 k read the same row, spread later
-    st.dec = gload<float>(rec, kOffDEC + (16 * w + (lane & 15)) * 4u);
 }
 
 }  // namespace
@@ -622,6 +619,10 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
 {
     // state as 4 k-step fragments; wave w writes elements 4 (w % 2) .. + 3 of k-step w / 2
     __shared__ bf16x8 sbuf[2][4][64];
+    // Bm of this value block (the record's fragment layout) and dec, per chunk,
+    // in a 2-slot ring: slot j & 1 holds chunk j
+    __shared__ bf16x8 side_bm[2][4][64];
+    __shared__ float side_dec[2][kDK];
     __shared__ float snap_s[kSnap ? 2 : 1][kSnap ? kDK : 1][kVBlock];
 
     // all value blocks of one (sequence, head) land on the same XCD (blocks are
@@ -647,6 +648,43 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     // the chunk loop runs in rounds of kPrefetch iterations; iterations past the
     // last chunk (at most kPrefetch - 1) leave the state unchanged
     const int64_t niter = (nch + kPrefetch - 1) / kPrefetch * kPrefetch;
+    if (w == kSideWave) {
+        // side operands of chunk jc (past the end: the last chunk) into register
+        // set `set`, later into ring slot jc & 1; two sets, loaded two chunks
+        // ahead, so each wait leaves the newer set's loads in flight
+        bf16x8 nbm[2][4];
+        f32x2 ndec[2];
+        auto side_load = [&](int set, int64_t jc) {
+            const gbyte *rec = uniform_gptr(rec_of(jc < nch ? jc : nch - 1));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                nbm[set][i] = gload<bf16x8>(rec, kOffBM + blk * 4096 + i * 1024 + lane * 16u);
+            ndec[set] = gload<f32x2>(rec, kOffDEC + lane * 8u);
+        };
+        auto side_store = [&](int set, int slot) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                side_bm[slot][i][lane] = nbm[set][i];
+            *reinterpret_cast<f32x2 *>(&side_dec[slot][2 * lane]) = ndec[set];
+        };
+        if (nch > 0) {
+            side_load(0, 0);
+            side_store(0, 0);
+            side_load(1, 1);
+            side_load(0, 2);
+        }
+        __syncthreads();
+        // niter is a multiple of kPrefetch, so of 2
+        for (int64_t jc = 0; jc < niter; jc += 2) {
+            side_store(1, (jc + 1) & 1);   // chunk jc + 1, read in the next iteration
+            side_load(1, jc + 3);
+            __syncthreads();
+            side_store(0, jc & 1);         // chunk jc + 2
+            side_load(0, jc + 4);
+            __syncthreads();
+        }
+        return;
+    }
     if (w == kStoreWave) {
         // snapshot jb: rows 16 i + lane / 4, channels 16 blk + 4 (lane % 4) .. + 3
         auto write_snap = [&](int64_t jb) {
@@ -707,7 +745,7 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     auto load_stage = [&](ChainStage &stage, int64_t jc) {
         const int64_t jl = jc < nch ? jc : nch - 1;
         __builtin_amdgcn_sched_barrier(0);
-        chain_load(stage, rec_of(jl), w, lane, blk);
+        chain_load(stage, rec_of(jl), w, lane);
         __builtin_amdgcn_sched_barrier(0);
     };
     ChainStage st[kPrefetch];
@@ -723,11 +761,14 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
             const int64_t jc = j0 + s;
             const ChainStage &c = st[s];
             const bf16x8 *sb = &sbuf[jc & 1][0][lane];
+            const f32x4 dec = *reinterpret_cast<const f32x4 *>(&side_dec[jc & 1][row0]);
+            const bf16x4 bm = *reinterpret_cast<const bf16x4 *>(
+                reinterpret_cast<const uint8_t *>(&side_bm[jc & 1][w >> 1][lane]) + 8 * (w & 1));
             // S' = dec S + Bm - L S for the wave's 16 rows
             f32x4 acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                acc[i] = __shfl(c.dec, 4 * b + i) * S[i] + (float)c.bm[i];
+                acc[i] = dec[i] * S[i] + (float)bm[i];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 acc = mfma16(c.ln[ks], sb[ks * 64], acc);
