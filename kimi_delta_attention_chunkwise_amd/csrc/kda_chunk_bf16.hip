@@ -521,48 +521,65 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
             }
             const int half = nt & 1, kq = nt >> 1;  // fragment half and dk k-step of these channels
             // L^T rows 16 nt.. = W^T K'  ->  -L fragments (mt, kq), elements 4 half .. 4 half + 3
-            // Bm columns 16 nt.. = K'^T U~ ->  Bm of value block nt
+            // Bm columns 16 nt.. = K'^T U~ ->  Bm of value block nt; row tiles 2 mp and
+            // 2 mp + 1 fill one 16-byte slot per lane, stored with one instruction
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                bf16x8 kpf[2];
+            for (int mp = 0; mp < 4; ++mp) {
+                f32x4 bmv[2];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    kpf[ks] = perm8(&sm.KPT[16 * mt + m][0], ks, b);
-                f32x4 l = {0.f, 0.f, 0.f, 0.f}, bm = {0.f, 0.f, 0.f, 0.f};
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int mt = 2 * mp + s2;
+                    bf16x8 kpf[2];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    l = mfma16(wf[ks], kpf[ks], l);
-                    bm = mfma16(kpf[ks], uf[ks], bm);
+                    for (int ks = 0; ks < 2; ++ks)
+                        kpf[ks] = perm8(&sm.KPT[16 * mt + m][0], ks, b);
+                    f32x4 l = {0.f, 0.f, 0.f, 0.f}, bm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        l = mfma16(wf[ks], kpf[ks], l);
+                        bm = mfma16(kpf[ks], uf[ks], bm);
+                    }
+                    *reinterpret_cast<bf16x4 *>(rec + kOffLN + (mt * 4 + kq) * kFragBytes +
+                                                lane * 16 + half * 8) = to_bf16x4(l, -1.f);
+                    bmv[s2] = bm;
                 }
-                *reinterpret_cast<bf16x4 *>(rec + kOffLN + (mt * 4 + kq) * kFragBytes + lane * 16 +
-                                            half * 8) = to_bf16x4(l, -1.f);
-                *reinterpret_cast<bf16x4 *>(rec + kOffBM + nt * 4096 + (mt >> 1) * 1024 + lane * 16 +
-                                            (mt & 1) * 8) = to_bf16x4(bm, 1.f);
+                const bf16x4 b0 = to_bf16x4(bmv[0], 1.f), b1 = to_bf16x4(bmv[1], 1.f);
+                *reinterpret_cast<bf16x8 *>(rec + kOffBM + nt * 4096 + mp * 1024 + lane * 16) =
+                    bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
             }
-            // Q^ = scale Q e^G - P W  (as Q^^T rows 16 nt..)  and  O0 = P U~ for value block nt
+            // Q^ = scale Q e^G - P W  (as Q^^T rows 16 nt..)  and  O0 = P U~ for value block nt;
+            // O0 row tiles 2 tp and 2 tp + 1 share one 16-byte slot per lane
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                bf16x8 pf[2];
+            for (int tp = 0; tp < 2; ++tp) {
+                f32x4 o0v[2];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    pf[ks] = perm8(&sm.PM[16 * mt + m][0], ks, b);
-                // scale Q e^G at row 16 mt + m, channels 16 nt + 4 b .. + 3, from q e^{G - B_mt}
-                const bf16x4 qr = *reinterpret_cast<const bf16x4 *>(&sm.QR[16 * mt + m][16 * nt + 4 * b]);
-                const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[mt][16 * nt + 4 * b]);
-                f32x4 qh;
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int mt = 2 * tp + s2;
+                    bf16x8 pf[2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    qh[i] = -scale * (float)qr[i] * eb[i];
-                f32x4 o0 = {0.f, 0.f, 0.f, 0.f};
+                    for (int ks = 0; ks < 2; ++ks)
+                        pf[ks] = perm8(&sm.PM[16 * mt + m][0], ks, b);
+                    // scale Q e^G at row 16 mt + m, channels 16 nt + 4 b .. + 3, from q e^{G - B_mt}
+                    const bf16x4 qr =
+                        *reinterpret_cast<const bf16x4 *>(&sm.QR[16 * mt + m][16 * nt + 4 * b]);
+                    const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[mt][16 * nt + 4 * b]);
+                    f32x4 qh;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    qh = mfma16(wf[ks], pf[ks], qh);   // (P W)^T - (scale Q e^G)^T
-                    o0 = mfma16(uf[ks], pf[ks], o0);   // (P U~)^T
+                    for (int i = 0; i < 4; ++i)
+                        qh[i] = -scale * (float)qr[i] * eb[i];
+                    f32x4 o0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        qh = mfma16(wf[ks], pf[ks], qh);   // (P W)^T - (scale Q e^G)^T
+                        o0 = mfma16(uf[ks], pf[ks], o0);   // (P U~)^T
+                    }
+                    *reinterpret_cast<bf16x4 *>(rec + kOffQH + (mt * 4 + kq) * kFragBytes +
+                                                lane * 16 + half * 8) = to_bf16x4(qh, -1.f);
+                    o0v[s2] = o0;
                 }
-                *reinterpret_cast<bf16x4 *>(rec + kOffQH + (mt * 4 + kq) * kFragBytes + lane * 16 +
-                                            half * 8) = to_bf16x4(qh, -1.f);
-                *reinterpret_cast<bf16x4 *>(rec + kOffO0 + nt * 2048 + mt * 512 + lane * 8) =
-                    to_bf16x4(o0, 1.f);
+                const bf16x4 a0 = to_bf16x4(o0v[0], 1.f), a1 = to_bf16x4(o0v[1], 1.f);
+                *reinterpret_cast<bf16x8 *>(rec + kOffO0 + nt * 2048 + tp * 1024 + lane * 16) =
+                    bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             }
         }
         // the next task's phase 1 rewrites the LDS operands
@@ -840,8 +857,8 @@ __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
     bf16x4 o0[kNumVBlocks];
 #pragma unroll
     for (int blk = 0; blk < kNumVBlocks; ++blk)
-        o0[blk] = *reinterpret_cast<const bf16x4 *>(rec + kOffO0 + blk * 2048 + t * 512 +
-                                                    lane * 8);
+        o0[blk] = *reinterpret_cast<const bf16x4 *>(rec + kOffO0 + blk * 2048 + (t >> 1) * 1024 +
+                                                    lane * 16 + (t & 1) * 8);
     // read-back mapping: lane -> row 8 p + lane / 8 of the wave's tile, channels 8 (lane % 8) ..
     // of each 64-channel half; the gate logits of those rows are fetched now,
     // with the other loads (rows past the chunk re-read its last row)

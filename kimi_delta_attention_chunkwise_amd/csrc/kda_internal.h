@@ -41,8 +41,8 @@ constexpr int kNumVBlocks = kDV / kVBlock;
 //   BM  : Bm per 16-wide value block, [block][wave w][lane][8]:
 //         elements 0..3 -> rows 32 w + 4 b + i, 4..7 -> rows 32 w + 16 + 4 b + i,
 //         column 16 block + lane % 16                              (32 KiB)
-//   O0  : O0 per value block, [block][row tile t][lane][4] -> row 16 t + lane % 16,
-//         columns 16 block + 4 b .. + 3
+//   O0  : O0 per value block, [block][row tile pair tp][lane][8]: elements
+//         4 s .. 4 s + 3 -> row 16 (2 tp + s) + lane % 16, columns 16 block + 4 b .. + 3
 //                                                                  (16 KiB)
 //   DEC : exp(G_end) per key channel, fp32                        (512 B)
 //   SB  : the state on entry to the chunk, per value block, as the 4 k-step
