@@ -193,24 +193,32 @@ __device__ __forceinline__ PrepTask prep_task(const int32_t *cu, int N, int T, i
     return pt;
 }
 
-// Rows past the end of the chunk re-read its last row (every load stays in
-// the sequence) and are zeroed when used.
+// Loads of token t of the lane's group (rows past the end of the chunk
+// re-read its last row, so every load stays in the sequence; they are zeroed
+// when used).
+__device__ __forceinline__ void prep_load_token(PrepIn &in, const bf16 *q, const bf16 *k,
+                                                const bf16 *v, const bf16 *g, const bf16 *beta,
+                                                const PrepTask &pt, int H, int wave, int tg,
+                                                int cq, int t)
+{
+    const int ch = 16 * wave + 4 * cq;
+    const int r = 4 * tg + t < pt.len ? 4 * tg + t : pt.len - 1;
+    const int64_t tok = pt.tok0 + r;
+    const int64_t off = (tok * H + pt.h) * (int64_t)kDK + ch;
+    in.q[t] = *reinterpret_cast<const bf16x4 *>(q + off);
+    in.k[t] = *reinterpret_cast<const bf16x4 *>(k + off);
+    in.v[t] = *reinterpret_cast<const bf16x4 *>(v + off);
+    in.g[t] = *reinterpret_cast<const bf16x4 *>(g + off);
+    in.beta[t] = beta[tok * H + pt.h];
+}
+
 __device__ __forceinline__ void prep_load(PrepIn &in, const bf16 *q, const bf16 *k, const bf16 *v,
                                           const bf16 *g, const bf16 *beta, const PrepTask &pt,
                                           int H, int wave, int tg, int cq)
 {
-    const int ch = 16 * wave + 4 * cq;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int r = 4 * tg + t < pt.len ? 4 * tg + t : pt.len - 1;
-        const int64_t tok = pt.tok0 + r;
-        const int64_t off = (tok * H + pt.h) * (int64_t)kDK + ch;
-        in.q[t] = *reinterpret_cast<const bf16x4 *>(q + off);
-        in.k[t] = *reinterpret_cast<const bf16x4 *>(k + off);
-        in.v[t] = *reinterpret_cast<const bf16x4 *>(v + off);
-        in.g[t] = *reinterpret_cast<const bf16x4 *>(g + off);
-        in.beta[t] = beta[tok * H + pt.h];
-    }
+    for (int t = 0; t < 4; ++t)
+        prep_load_token(in, q, k, v, g, beta, pt, H, wave, tg, cq, t);
 }
 
 // The prep kernel is persistent: workgroup b handles tasks b, b + G, b + 2 G,
@@ -390,9 +398,11 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
             }
         }
         __syncthreads();
-        // the registers of this task's inputs are free: fetch the next task's
+        // the registers of this task's inputs are free: fetch the next task's,
+        // one token of the lane's group before each of phases 2 to 5, so the
+        // loads do not all queue up in front of one phase
         if (load_next)
-            prep_load(in, q, k, v, g, beta, next, H, wave, tg, cq);
+            prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 0);
 
         // ---- phase 2: 16 x 16 blocks of A and P (bf16 MFMA, fp32 accumulate) -------
         for (int blk = wave; blk < 10; blk += kPrepThreads / 64) {
@@ -424,6 +434,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
         }
         __syncthreads();
 
+        if (load_next)
+            prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 1);
         // ---- phase 3: T = (I + A)^-1 ------------------------------------------------
         if (wave == 0) {
             // diagonal 16 x 16 blocks by forward substitution, one column per lane;
@@ -475,6 +487,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
             __syncthreads();
         }
 
+        if (load_next)
+            prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 2);
         // ---- phase 4: W = T X and U~ = T V for the wave's 16 channels --------------
         const int nt = wave;                       // channels 16 nt .. 16 nt + 15
         f32x4 accW[4], accU[4];
@@ -511,6 +525,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
             }
         }
 
+        if (load_next)
+            prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 3);
         // ---- phase 5: L, Bm, Q^, O0 for the wave's 16 channels ----------------------
         {
             bf16x8 wf[2], uf[2];                   // W^T as A operand, U~ as B operand (perm k)
