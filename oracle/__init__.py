@@ -8,6 +8,8 @@ Contents
   * ``forward`` / ``decode_step``: the plain token-by-token recurrence in fp64,
     in C (``kda_oracle.c``, OpenMP over (sequence, head) units), loaded with
     ctypes.  This is the oracle the GPU path is compared against.
+  * ``backward``: reverse-mode gradients of ``forward`` in fp64, token by
+    token (same C file).
   * ``oracle.chunkwise``: a second fp64 implementation in NumPy that follows
     the chunkwise-parallel form (state passed between chunks, matrices inside a
     chunk).  Used to check that the chunkwise form equals the recurrence.
@@ -64,6 +66,10 @@ def _load():
     lib.kda_oracle_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, cint, dp, dp,
                                            i64, i64, i64, i64, f64, cint]
     lib.kda_oracle_decode_step.restype = cint
+    lib.kda_oracle_backward.argtypes = [vp, vp, vp, vp, vp, vp, cint, dp, dp, dp, i64p,
+                                        i64, i64, i64, i64, f64, cint,
+                                        dp, dp, dp, dp, dp, dp, dp]
+    lib.kda_oracle_backward.restype = cint
     lib.kda_oracle_max_threads.argtypes = []
     lib.kda_oracle_max_threads.restype = cint
     _lib = lib
@@ -133,6 +139,70 @@ def forward(q, k, v, g, beta, z, init_state=None, cu_seqlens=None, scale=1.0,
         raise RuntimeError(f"kda_oracle_forward failed with {rc}")
     out = out.reshape(B, T, H, dv) if batched else out.reshape(T, H, dv)
     return out, final
+
+
+def backward(q, k, v, g, beta, z, dout, init_state=None, dfinal=None, cu_seqlens=None,
+             scale=1.0, n_threads=None):
+    """Gradients of sum(dout * out) + sum(dfinal * final_state) for ``forward``.
+
+    Same shapes and conventions as ``forward``; ``dout`` like ``out``, ``dfinal``
+    like the final state (None = zero).  Returns a dict of float64 arrays:
+    dq, dk, dv, dg, dbeta, dz (input shapes) and dinit ``[N, H, dk, dv]``."""
+    q = np.asarray(q)
+    batched = q.ndim == 4
+    if batched:
+        B, T, H, dk = q.shape
+    else:
+        B = 1
+        T, H, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    in_f32 = all(np.asarray(x).dtype == np.float32 for x in (q, k, v, g, beta, z))
+    flat = lambda x, d: _as_input(np.asarray(x).reshape(B * T, H, d) if d else
+                                  np.asarray(x).reshape(B * T, H), in_f32)
+    qf, kf, gf = flat(q, dk), flat(k, dk), flat(g, dk)
+    vf, zf = flat(v, dv), flat(z, dv)
+    bf = flat(beta, 0)
+    if cu_seqlens is None:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("cu_seqlens needs a batch dimension of 1")
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int64)
+        if cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+            raise ValueError("cu_seqlens must start at 0, end at T and be non-decreasing")
+    N = len(cu) - 1
+    init = None
+    if init_state is not None:
+        init = np.ascontiguousarray(np.asarray(init_state), dtype=np.float64)
+        if init.shape != (N, H, dk, dv):
+            raise ValueError(f"init_state shape {init.shape} != {(N, H, dk, dv)}")
+    do = np.ascontiguousarray(np.asarray(dout, dtype=np.float64).reshape(B * T, H, dv))
+    dfin = None
+    if dfinal is not None:
+        dfin = np.ascontiguousarray(np.asarray(dfinal), dtype=np.float64)
+        if dfin.shape != (N, H, dk, dv):
+            raise ValueError(f"dfinal shape {dfin.shape} != {(N, H, dk, dv)}")
+    res = {"dq": np.empty((B * T, H, dk)), "dk": np.empty((B * T, H, dk)),
+           "dv": np.empty((B * T, H, dv)), "dg": np.empty((B * T, H, dk)),
+           "dbeta": np.empty((B * T, H)), "dz": np.empty((B * T, H, dv)),
+           "dinit": np.empty((N, H, dk, dv))}
+    nt = n_threads if n_threads else max_threads()
+    rc = _load().kda_oracle_backward(
+        _ptr(qf), _ptr(kf), _ptr(vf), _ptr(gf), _ptr(bf), _ptr(zf), int(in_f32), _ptr(init),
+        _ptr(do), _ptr(dfin), _ptr(cu), N, H, dk, dv, float(scale), int(nt), _ptr(res["dq"]),
+        _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dg"]), _ptr(res["dbeta"]), _ptr(res["dz"]),
+        _ptr(res["dinit"]))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_backward failed with {rc}")
+    shape_k = (B, T, H, dk) if batched else (T, H, dk)
+    shape_v = (B, T, H, dv) if batched else (T, H, dv)
+    shape_b = (B, T, H) if batched else (T, H)
+    for key in ("dq", "dk", "dg"):
+        res[key] = res[key].reshape(shape_k)
+    for key in ("dv", "dz"):
+        res[key] = res[key].reshape(shape_v)
+    res["dbeta"] = res["dbeta"].reshape(shape_b)
+    return res
 
 
 def decode_step(q, k, v, g, beta, z, state, scale=1.0, n_threads=None):

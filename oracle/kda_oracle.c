@@ -193,6 +193,186 @@ int kda_oracle_decode_step(const void *q, const void *k, const void *v, const vo
     return failed ? -2 : 0;
 }
 
+/* Backward of the whole-sequence forward (reverse-mode, token by token, in
+ * double).  For the loss sum(dout * out) + sum(dfinal * final_state) it
+ * returns the gradients with respect to every input:
+ *   dq, dk, dg [T_total, H, dk], dv, dz [T_total, H, dv], dbeta [T_total, H],
+ *   dinit [N, H, dk, dv] (may be NULL).
+ * dfinal may be NULL (zero).  Each token's forward step is reversed in the
+ * opposite order of its operations; with S~ = diag(a) S_prev the decayed
+ * state and S_new the state after the write:
+ *   o  = scale S_new^T q,  y = sigmoid(z) o:
+ *        dz = dy o sigmoid'(z),  do = dy sigmoid(z),
+ *        dS_new += scale q do^T,  dq = scale S_new do
+ *   S_new = S~ + k u^T:   du = dS_new^T k,  dk += dS_new u,  dS~ = dS_new
+ *   u = beta (v - p):     dbeta = du . (v - p),  dv = beta du,  dp = -beta du
+ *   p = S~^T k:           dS~ += k dp^T,  dk += S~ dp
+ *   S~ = diag(a) S_prev:  dS_prev = diag(a) dS~,  dg = a * rowsum(dS~ * S_prev)
+ * States are recomputed from checkpoints taken every 32 tokens. */
+#define KDA_ORACLE_SEG 32
+int kda_oracle_backward(const void *q, const void *k, const void *v, const void *g,
+                        const void *beta, const void *z, int in_f32,
+                        const double *init_state, const double *dout, const double *dfinal,
+                        const int64_t *cu_seqlens, int64_t n_seq, int64_t H, int64_t dk,
+                        int64_t dv, double scale, int n_threads, double *dq, double *dk_out,
+                        double *dv_out, double *dg, double *dbeta, double *dz, double *dinit)
+{
+    if (!q || !k || !v || !g || !beta || !z || !cu_seqlens || !dout)
+        return -1;
+    if (!dq || !dk_out || !dv_out || !dg || !dbeta || !dz)
+        return -1;
+    if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    for (int64_t n = 0; n < n_seq; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n] || cu_seqlens[0] != 0)
+            return -1;
+    const int64_t units = n_seq * H, sd = dk * dv;
+    int failed = 0;
+    if (n_threads <= 0)
+        n_threads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+    for (int64_t unit = 0; unit < units; ++unit) {
+        const int64_t n = unit / H, h = unit % H;
+        const int64_t t0 = cu_seqlens[n], len = cu_seqlens[n + 1] - cu_seqlens[n];
+        const int64_t nseg = (len + KDA_ORACLE_SEG - 1) / KDA_ORACLE_SEG;
+        double *ck = (double *)malloc(sizeof(double) * sd * (nseg > 0 ? nseg : 1));
+        double *sb = (double *)malloc(sizeof(double) * sd * (KDA_ORACLE_SEG + 1));
+        double *dS = (double *)malloc(sizeof(double) * sd);
+        double *Sd = (double *)malloc(sizeof(double) * sd);
+        double *a = (double *)malloc(sizeof(double) * dk);
+        double *p = (double *)malloc(sizeof(double) * dv);
+        double *u = (double *)malloc(sizeof(double) * dv);
+        double *y = (double *)malloc(sizeof(double) * dv);
+        double *dov = (double *)malloc(sizeof(double) * dv);
+        double *du = (double *)malloc(sizeof(double) * dv);
+        double *dp = (double *)malloc(sizeof(double) * dv);
+        if (!ck || !sb || !dS || !Sd || !a || !p || !u || !y || !dov || !du || !dp) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            const double *S0 = init_state ? init_state + unit * sd : NULL;
+            /* forward, keeping the state on entry to every segment */
+            double *S = sb;
+            for (int64_t e = 0; e < sd; ++e)
+                S[e] = S0 ? S0[e] : 0.0;
+            for (int64_t i = 0; i < len; ++i) {
+                if (i % KDA_ORACLE_SEG == 0)
+                    memcpy(ck + (i / KDA_ORACLE_SEG) * sd, S, sizeof(double) * sd);
+                const int64_t t = t0 + i;
+                kda_token(q, k, v, g, beta, z, in_f32, (t * H + h) * dk, (t * H + h) * dv,
+                          t * H + h, dk, dv, scale, S, a, p, u, y);
+            }
+            for (int64_t e = 0; e < sd; ++e)
+                dS[e] = dfinal ? dfinal[unit * sd + e] : 0.0;
+            for (int64_t c = nseg - 1; c >= 0; --c) {
+                const int64_t i0 = c * KDA_ORACLE_SEG;
+                const int64_t nl = (len - i0) < KDA_ORACLE_SEG ? (len - i0) : KDA_ORACLE_SEG;
+                /* states of the segment: sb[i] = state before token i0 + i */
+                memcpy(sb, ck + c * sd, sizeof(double) * sd);
+                for (int64_t i = 0; i < nl; ++i) {
+                    memcpy(sb + (i + 1) * sd, sb + i * sd, sizeof(double) * sd);
+                    const int64_t t = t0 + i0 + i;
+                    kda_token(q, k, v, g, beta, z, in_f32, (t * H + h) * dk, (t * H + h) * dv,
+                              t * H + h, dk, dv, scale, sb + (i + 1) * sd, a, p, u, y);
+                }
+                for (int64_t i = nl - 1; i >= 0; --i) {
+                    const int64_t t = t0 + i0 + i;
+                    const int64_t qo = (t * H + h) * dk, vo = (t * H + h) * dv, bo = t * H + h;
+                    const double *Sp = sb + i * sd, *Sn = sb + (i + 1) * sd;
+                    const double b = rd(beta, in_f32, bo);
+                    int64_t r, j;
+                    /* recompute a, S~, p, u of this token */
+                    for (r = 0; r < dk; ++r)
+                        a[r] = exp(rd(g, in_f32, qo + r));
+                    for (r = 0; r < dk; ++r)
+                        for (j = 0; j < dv; ++j)
+                            Sd[r * dv + j] = a[r] * Sp[r * dv + j];
+                    for (j = 0; j < dv; ++j)
+                        p[j] = 0.0;
+                    for (r = 0; r < dk; ++r) {
+                        const double kr = rd(k, in_f32, qo + r);
+                        for (j = 0; j < dv; ++j)
+                            p[j] += Sd[r * dv + j] * kr;
+                    }
+                    for (j = 0; j < dv; ++j)
+                        u[j] = (rd(v, in_f32, vo + j) - p[j]) * b;
+                    /* read and gate */
+                    for (j = 0; j < dv; ++j)
+                        y[j] = 0.0;                        /* y = S_new^T q (unscaled) */
+                    for (r = 0; r < dk; ++r) {
+                        const double qr = rd(q, in_f32, qo + r);
+                        for (j = 0; j < dv; ++j)
+                            y[j] += Sn[r * dv + j] * qr;
+                    }
+                    for (j = 0; j < dv; ++j) {
+                        const double sg = sigmoid(rd(z, in_f32, vo + j));
+                        const double o = scale * y[j];
+                        dz[vo + j] = dout[vo + j] * o * sg * (1.0 - sg);
+                        dov[j] = dout[vo + j] * sg;
+                    }
+                    for (r = 0; r < dk; ++r) {
+                        const double qr = rd(q, in_f32, qo + r);
+                        double acc = 0.0;
+                        for (j = 0; j < dv; ++j) {
+                            acc += Sn[r * dv + j] * dov[j];
+                            dS[r * dv + j] += scale * qr * dov[j];
+                        }
+                        dq[qo + r] = scale * acc;
+                    }
+                    /* write: S_new = S~ + k u^T */
+                    for (j = 0; j < dv; ++j)
+                        du[j] = 0.0;
+                    for (r = 0; r < dk; ++r) {
+                        const double kr = rd(k, in_f32, qo + r);
+                        double acc = 0.0;
+                        for (j = 0; j < dv; ++j) {
+                            du[j] += dS[r * dv + j] * kr;
+                            acc += dS[r * dv + j] * u[j];
+                        }
+                        dk_out[qo + r] = acc;
+                    }
+                    /* correction: u = beta (v - p) */
+                    double db = 0.0;
+                    for (j = 0; j < dv; ++j) {
+                        const double vj = rd(v, in_f32, vo + j);
+                        db += du[j] * (vj - p[j]);
+                        dv_out[vo + j] = b * du[j];
+                        dp[j] = -b * du[j];
+                    }
+                    dbeta[bo] = db;
+                    /* prediction: p = S~^T k; then the decay S~ = diag(a) S_prev */
+                    for (r = 0; r < dk; ++r) {
+                        const double kr = rd(k, in_f32, qo + r);
+                        double acc = 0.0, da = 0.0;
+                        for (j = 0; j < dv; ++j) {
+                            acc += Sd[r * dv + j] * dp[j];
+                            const double dsd = dS[r * dv + j] + kr * dp[j];   /* dS~ */
+                            da += dsd * Sp[r * dv + j];
+                            dS[r * dv + j] = a[r] * dsd;                      /* dS_prev */
+                        }
+                        dk_out[qo + r] += acc;
+                        dg[qo + r] = a[r] * da;
+                    }
+                }
+            }
+            if (dinit)
+                memcpy(dinit + unit * sd, dS, sizeof(double) * sd);
+        }
+        free(ck);
+        free(sb);
+        free(dS);
+        free(Sd);
+        free(a);
+        free(p);
+        free(u);
+        free(y);
+        free(dov);
+        free(du);
+        free(dp);
+    }
+    return failed ? -2 : 0;
+}
+
 /* Threads OpenMP would use by default (for reporting the CPU baseline). */
 int kda_oracle_max_threads(void)
 {

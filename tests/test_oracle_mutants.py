@@ -33,6 +33,41 @@ MUTANTS = {
 }
 
 
+# planted mistakes in the backward; the backward pins have to catch them
+BACKWARD_MUTANTS = {
+    "bwd_no_prediction_term": ("const double dsd = dS[r * dv + j] + kr * dp[j];",
+                               "const double dsd = dS[r * dv + j];"),
+    "bwd_read_term_sign": ("dS[r * dv + j] += scale * qr * dov[j];",
+                           "dS[r * dv + j] -= scale * qr * dov[j];"),
+    "bwd_dg_without_decay": ("dg[qo + r] = a[r] * da;", "dg[qo + r] = da;"),
+    "bwd_dbeta_without_prediction": ("db += du[j] * (vj - p[j]);", "db += du[j] * vj;"),
+    "bwd_dk_without_prediction": ("dk_out[qo + r] += acc;", "dk_out[qo + r] += 0.0 * acc;"),
+    "bwd_dz_gate_derivative": ("dz[vo + j] = dout[vo + j] * o * sg * (1.0 - sg);",
+                               "dz[vo + j] = dout[vo + j] * o * sg;"),
+}
+
+
+def _run_pins_against(name, old, new, pin_file, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    mutant_c = tmp_path / "mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c99", "-O1", "-fopenmp", "-fPIC", "-shared", str(mutant_c),
+                    "-o", str(lib), "-lm"], check=True)
+    env = dict(os.environ, KDA_ORACLE_LIB=str(lib))
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", pin_file)],
+                          env=env, cwd=ROOT, capture_output=True, text=True, timeout=300)
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_pins_catch_planted_mistake(name, tmp_path):
+    old, new = BACKWARD_MUTANTS[name]
+    r = _run_pins_against(name, old, new, "test_oracle_backward.py", tmp_path)
+    assert r.returncode != 0, f"backward pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
     old, new = MUTANTS[name]
