@@ -227,6 +227,42 @@ kda_status kda_decode_commit(const void *k, const void *g, const float *u,
                              const int32_t *accepted, float *state, int N, int K, int H, int dk,
                              int dv, kda_dtype dt, unsigned prologue, hipStream_t stream);
 
+/* Chunkwise KDA backward for training ("Kimi K3 second-pass study ledger",
+ * section 1 row Q07: the chunkwise-parallel form serves training as well as
+ * prefill).  Given the forward's inputs and the gradients of a loss with
+ * respect to its outputs, returns the gradients with respect to every input
+ * of kda_chunk_fwd (prepared inputs: no prologue):
+ *
+ *   q, k, g, v, gate, beta, init_state, cu_seqlens, B, T, N, H, dk, dv,
+ *   chunk, scale, dt  exactly as given to kda_chunk_fwd
+ *   grad_out          [B, T, H, dv] dt: dLoss/d out
+ *   grad_final_state  [N, H, dk, dv] fp32: dLoss/d final_state, or NULL (zero)
+ *   grad_q, grad_k, grad_g [B, T, H, dk] dt     written
+ *   grad_v, grad_gate      [B, T, H, dv] dt     written (grad_gate: w.r.t. the logits)
+ *   grad_beta              [B, T, H]     dt     written
+ *   grad_init_state        [N, H, dk, dv] fp32  written, or NULL (not written);
+ *                          it may alias grad_final_state
+ * The gradient of g is the total one, through the decay of the state and
+ * through every within-chunk decay factor.  Forward quantities are recomputed
+ * inside the call (nothing is kept from a previous kda_chunk_fwd).
+ * Supported: KDA_F32 with dk = dv = 16, chunk = 16
+ * (kda_chunk_bwd_supported).  Workspace: kda_chunk_bwd_workspace_bytes(...)
+ * bytes, 256-byte aligned, contents ignored and left undefined.  Gradient
+ * outputs must not alias the inputs or each other (except as stated). */
+int kda_chunk_bwd_supported(kda_dtype dt, int dk, int dv, int chunk);
+
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv, int chunk,
+                                     kda_dtype dt, int varlen);
+
+kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const void *gate, const float *init_state,
+                         const void *grad_out, const float *grad_final_state, void *grad_q,
+                         void *grad_k, void *grad_v, void *grad_g, void *grad_beta,
+                         void *grad_gate, float *grad_init_state, const int32_t *cu_seqlens,
+                         int B, int T, int N, int H, int dk, int dv, int chunk, float scale,
+                         kda_dtype dt, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,8 +14,10 @@ Entry points (names follow the C ABI):
   decode_step(q, k, v, g, beta, gate, state, scale=1.0) -> out   (state in place)
   decode_verify(q, k, v, g, beta, gate, state, ...) -> (out, u)  (K draft tokens, state kept)
   decode_commit(k, g, u, accepted, state, ...)                   (accepted prefix into state)
-  chunk_fwd_workspace_bytes(...), snapshot_slots(...), chunk_fwd_supported(...),
-  decode_step_supported(...)
+  chunk_bwd(q, k, v, g, beta, gate, grad_out, init_state=None, grad_final_state=None, ...)
+            -> dict of gradients (training backward)
+  chunk_fwd_workspace_bytes(...), chunk_bwd_workspace_bytes(...), snapshot_slots(...),
+  chunk_fwd_supported(...), chunk_bwd_supported(...), decode_step_supported(...)
 """
 from __future__ import annotations
 
@@ -26,8 +28,8 @@ import torch
 
 __all__ = [
     "KdaError", "KdaLibraryError", "chunk_fwd", "chunk_fwd_snapshots", "decode_step",
-    "decode_verify", "decode_commit",
-    "chunk_fwd_workspace_bytes", "snapshot_slots", "snapshot_index",
+    "decode_verify", "decode_commit", "chunk_bwd", "chunk_bwd_workspace_bytes",
+    "chunk_bwd_supported", "chunk_fwd_workspace_bytes", "snapshot_slots", "snapshot_index",
     "chunk_fwd_supported", "decode_step_supported", "library_path", "load_library",
     "KDA_F32", "KDA_BF16", "G_MIN", "PRO_QK_L2NORM", "PRO_BETA_SIGMOID", "PRO_G_SOFTPLUS",
 ]
@@ -78,6 +80,10 @@ _SIGNATURES = {
                           ctypes.c_int, ctypes.c_uint, ctypes.c_void_p], ctypes.c_int),
     "kda_decode_commit": ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_int, ctypes.c_uint,
                           ctypes.c_void_p], ctypes.c_int),
+    "kda_chunk_bwd_supported": ([ctypes.c_int] * 4, ctypes.c_int),
+    "kda_chunk_bwd_workspace_bytes": ([ctypes.c_int] * 9, ctypes.c_size_t),
+    "kda_chunk_bwd": ([ctypes.c_void_p] * 17 + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
+                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "kda_decode_step": ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
                         ctypes.c_void_p], ctypes.c_int),
 }
@@ -373,3 +379,71 @@ def decode_commit(k, g, u, accepted, state, prologue=0):
     st = lib.kda_decode_commit(_ptr(k), _ptr(g), _ptr(u), _ptr(accepted), _ptr(state), N, K, H,
                                dk, dv, code, int(prologue), _stream_ptr(dev))
     _check(st)
+
+
+def chunk_bwd_supported(dtype: torch.dtype, dk: int, dv: int, chunk: int) -> bool:
+    return bool(load_library().kda_chunk_bwd_supported(_dtype_code(dtype), dk, dv, chunk))
+
+
+def chunk_bwd_workspace_bytes(B: int, T: int, N: int, H: int, dk: int, dv: int, chunk: int,
+                              dtype: torch.dtype, varlen: bool) -> int:
+    n = load_library().kda_chunk_bwd_workspace_bytes(B, T, N, H, dk, dv, chunk,
+                                                     _dtype_code(dtype), int(varlen))
+    if n == ctypes.c_size_t(-1).value:
+        raise KdaError("unsupported or invalid sizes for kda_chunk_bwd")
+    return int(n)
+
+
+def chunk_bwd(q, k, v, g, beta, gate, grad_out, init_state=None, grad_final_state=None,
+              cu_seqlens=None, chunk=None, scale=1.0, workspace=None, want_grad_init=True):
+    """Chunkwise KDA backward on the GPU: gradients of a loss with respect to
+    every input of ``chunk_fwd`` (prepared inputs), given ``grad_out`` (shape
+    and dtype of the forward's ``out``) and optionally ``grad_final_state``
+    (fp32 ``[N, H, dk, dv]``).  Returns a dict with ``q, k, v, g, beta, gate``
+    (the input dtype) and ``init_state`` (fp32, None unless ``want_grad_init``)."""
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda.chunk_bwd runs on a HIP device; tensors are on " + str(dev))
+    dt = q.dtype
+    code = _dtype_code(dt)
+    chunk = _DEFAULT_CHUNK[code] if chunk is None else int(chunk)
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)),
+                         ("g", g, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+                         ("gate", gate, (B, T, H, dv)), ("beta", beta, (B, T, H)),
+                         ("grad_out", grad_out, (B, T, H, dv))):
+        _need(t, name, shp, dt, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+        _need(cu_seqlens, "cu_seqlens", cu_seqlens.shape, torch.int32, dev)
+        if B != 1:
+            raise ValueError("cu_seqlens requires B == 1")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if init_state is not None:
+        _need(init_state, "init_state", (N, H, dk, dv), torch.float32, dev)
+    if grad_final_state is not None:
+        _need(grad_final_state, "grad_final_state", (N, H, dk, dv), torch.float32, dev)
+    nbytes = chunk_bwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < nbytes:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {nbytes} bytes on {dev}")
+    grads = {name: torch.empty_like(t) for name, t in
+             (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("gate", gate))}
+    grads["init_state"] = (torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+                           if want_grad_init else None)
+    st = lib.kda_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate), _ptr(init_state),
+        _ptr(grad_out), _ptr(grad_final_state), _ptr(grads["q"]), _ptr(grads["k"]),
+        _ptr(grads["v"]), _ptr(grads["g"]), _ptr(grads["beta"]), _ptr(grads["gate"]),
+        _ptr(grads["init_state"]), _ptr(cu_seqlens), B, T, N, H, dk, dv, chunk, float(scale),
+        code, _ptr(workspace), workspace.numel(), _stream_ptr(dev))
+    _check(st)
+    return grads

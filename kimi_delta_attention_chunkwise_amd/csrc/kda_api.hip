@@ -17,6 +17,11 @@ bool chunk_supported(kda_dtype dt, int dk, int dv, int chunk)
     return false;
 }
 
+bool bwd_supported(kda_dtype dt, int dk, int dv, int chunk)
+{
+    return dt == KDA_F32 && dk == 16 && dv == 16 && chunk == 16;
+}
+
 bool decode_supported(kda_dtype dt, int dk, int dv)
 {
     return valid_dtype(dt) && dk == dv && (dk == 16 || dk == 128);
@@ -218,6 +223,63 @@ kda_status kda_decode_commit(const void *k, const void *g, const float *u,
         return KDA_ERR_NULL_POINTER;
     return from_hip(kda::launch_commit(k, g, u, accepted, state, N, K, H, dk, dv,
                                        dt == KDA_BF16, prologue, stream));
+}
+
+int kda_chunk_bwd_supported(kda_dtype dt, int dk, int dv, int chunk)
+{
+    return bwd_supported(dt, dk, dv, chunk) ? 1 : 0;
+}
+
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv, int chunk,
+                                     kda_dtype dt, int varlen)
+{
+    if (!valid_dtype(dt) || !bwd_supported(dt, dk, dv, chunk))
+        return (size_t)-1;
+    if (B < 1 || T < 0 || N < 0 || H < 1 || (varlen && B != 1) || (!varlen && N != B))
+        return (size_t)-1;
+    // one fp32 dk x dv entry state per (chunk slot, head)
+    return (size_t)chunk_slots(B, T, N, chunk, varlen) * (size_t)H * (size_t)dk * (size_t)dv *
+           sizeof(float);
+}
+
+kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const void *gate, const float *init_state,
+                         const void *grad_out, const float *grad_final_state, void *grad_q,
+                         void *grad_k, void *grad_v, void *grad_g, void *grad_beta,
+                         void *grad_gate, float *grad_init_state, const int32_t *cu_seqlens,
+                         int B, int T, int N, int H, int dk, int dv, int chunk, float scale,
+                         kda_dtype dt, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream)
+{
+    if (!valid_dtype(dt))
+        return KDA_ERR_BAD_DTYPE;
+    if (!bwd_supported(dt, dk, dv, chunk))
+        return KDA_ERR_UNSUPPORTED;
+    const int varlen = cu_seqlens != nullptr;
+    if (B < 1 || T < 0 || N < 0 || H < 1)
+        return KDA_ERR_BAD_SHAPE;
+    if (varlen ? B != 1 : N != B)
+        return KDA_ERR_BAD_SHAPE;
+    const bool has_tokens = (int64_t)B * T > 0;
+    if (has_tokens && (!q || !k || !v || !g || !beta || !gate || !grad_out || !grad_q ||
+                       !grad_k || !grad_v || !grad_g || !grad_beta || !grad_gate))
+        return KDA_ERR_NULL_POINTER;
+    const size_t need = kda_chunk_bwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
+    if (need > 0 && !workspace)
+        return KDA_ERR_NULL_POINTER;
+    if (workspace_bytes < need)
+        return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (N == 0)
+        return KDA_OK;
+    // one workgroup per (sequence, head) on a 1-D grid
+    if ((int64_t)N * H > INT32_MAX)
+        return KDA_ERR_UNSUPPORTED;
+    return from_hip(kda::launch_chunk_bwd_f32(
+        (const float *)q, (const float *)k, (const float *)v, (const float *)g,
+        (const float *)beta, (const float *)gate, init_state, (const float *)grad_out,
+        grad_final_state, (float *)grad_q, (float *)grad_k, (float *)grad_v, (float *)grad_g,
+        (float *)grad_beta, (float *)grad_gate, grad_init_state, cu_seqlens, N, T, H, scale,
+        (float *)workspace, stream));
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *g,

@@ -178,6 +178,15 @@ hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, cons
                             const int32_t *cu, int N, int T, int H, float scale, unsigned pro,
                             hipStream_t stream);
 
+// Chunkwise backward, fp32, dk = dv = 16, 16-token chunks; ws holds one
+// 16 x 16 fp32 entry state per (chunk slot, head).
+hipError_t launch_chunk_bwd_f32(const float *q, const float *k, const float *v, const float *g,
+                                const float *beta, const float *gate, const float *init,
+                                const float *dout, const float *dfinal, float *dq, float *dk,
+                                float *dv, float *dg, float *dbeta, float *dgate, float *dinit,
+                                const int32_t *cu, int N, int T, int H, float scale, float *ws,
+                                hipStream_t stream);
+
 hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                              const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
                              float *final_state, float *snaps, int snap_interval,

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
     for n in ("kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes",
               "kda_status_str", "kda_chunk_fwd_snapshots", "kda_snapshot_slots",
               "kda_chunk_fwd_ex", "kda_decode_step_ex", "kda_decode_verify",
-              "kda_decode_commit"):
+              "kda_decode_commit", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
+              "kda_chunk_bwd_supported"):
         assert n in names
 
 
@@ -214,6 +215,39 @@ def test_decode_step_rejects_bad_arguments_before_launch(lib):
     assert call(state=None) == NULLP
     assert call(out=None) == NULLP
     assert call(N=0, q=None) == OK
+
+
+def test_chunk_bwd_sizes_and_argument_checks(lib):
+    assert lib.kda_chunk_bwd_supported(0, 16, 16, 16) == 1
+    for args in [(1, 128, 128, 64), (0, 16, 16, 64), (0, 128, 128, 16), (2, 16, 16, 16)]:
+        assert lib.kda_chunk_bwd_supported(*args) == 0
+    ws = lib.kda_chunk_bwd_workspace_bytes
+    bad = ctypes.c_size_t(-1).value
+    # one fp32 16 x 16 entry state per (16-token chunk slot, head)
+    assert ws(2, 37, 2, 3, 16, 16, 16, 0, 0) == 2 * 3 * 3 * 1024
+    assert ws(1, 55, 5, 2, 16, 16, 16, 0, 1) == (55 // 16 + 5) * 2 * 1024
+    assert ws(1, 0, 1, 2, 16, 16, 16, 0, 0) == 0
+    assert ws(2, 64, 1, 1, 16, 16, 16, 0, 0) == bad
+    assert ws(1, 64, 1, 1, 128, 128, 64, 1, 0) == bad
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(**kw):
+        a = dict(q=1, gq=1, B=1, T=64, N=1, H=2, d=16, chunk=16, dt=0, cu=None, ws=1,
+                 ws_bytes=10 ** 9)
+        a.update(kw)
+        return lib.kda_chunk_bwd(p(a["q"]), p(1), p(1), p(1), p(1), p(1), None, p(1), None,
+                                 p(a["gq"]), p(1), p(1), p(1), p(1), p(1), None, p(a["cu"]),
+                                 a["B"], a["T"], a["N"], a["H"], a["d"], a["d"], a["chunk"], 1.0,
+                                 a["dt"], p(a["ws"]), a["ws_bytes"], None)
+    assert call(dt=4) == DTYPE
+    assert call(dt=1, d=128, chunk=64) == UNSUP
+    assert call(chunk=64) == UNSUP
+    assert call(H=0) == SHAPE and call(T=-1) == SHAPE and call(B=2) == SHAPE
+    assert call(cu=1, B=2, N=2) == SHAPE
+    assert call(q=None) == NULLP and call(gq=None) == NULLP
+    assert call(ws=None) == NULLP
+    assert call(ws_bytes=2 * 4 * 1024 - 1) == WS
+    assert call(cu=1, N=0, T=0, q=None, gq=None) == OK
 
 
 def test_python_binding_refuses_cpu_tensors(lib):
