@@ -245,8 +245,10 @@ kda_status kda_decode_commit(const void *k, const void *g, const float *u,
  * The gradient of g is the total one, through the decay of the state and
  * through every within-chunk decay factor.  Forward quantities are recomputed
  * inside the call (nothing is kept from a previous kda_chunk_fwd).
- * Supported: KDA_F32 with dk = dv = 16, chunk = 16
- * (kda_chunk_bwd_supported).  Workspace: kda_chunk_bwd_workspace_bytes(...)
+ * Supported: the same (dt, dk, dv, chunk) as kda_chunk_fwd
+ * (kda_chunk_bwd_supported): KDA_BF16 with dk = dv = 128, chunk = 64
+ * (gradients rounded to bf16, state gradients carried in fp32), and KDA_F32
+ * with dk = dv = 16, chunk = 16.  Workspace: kda_chunk_bwd_workspace_bytes(...)
  * bytes, 256-byte aligned, contents ignored and left undefined.  Gradient
  * outputs must not alias the inputs or each other (except as stated). */
 int kda_chunk_bwd_supported(kda_dtype dt, int dk, int dv, int chunk);

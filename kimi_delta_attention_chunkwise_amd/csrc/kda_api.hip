@@ -19,7 +19,7 @@ bool chunk_supported(kda_dtype dt, int dk, int dv, int chunk)
 
 bool bwd_supported(kda_dtype dt, int dk, int dv, int chunk)
 {
-    return dt == KDA_F32 && dk == 16 && dv == 16 && chunk == 16;
+    return chunk_supported(dt, dk, dv, chunk);
 }
 
 bool decode_supported(kda_dtype dt, int dk, int dv)
@@ -237,9 +237,10 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
         return (size_t)-1;
     if (B < 1 || T < 0 || N < 0 || H < 1 || (varlen && B != 1) || (!varlen && N != B))
         return (size_t)-1;
-    // one fp32 dk x dv entry state per (chunk slot, head)
-    return (size_t)chunk_slots(B, T, N, chunk, varlen) * (size_t)H * (size_t)dk * (size_t)dv *
-           sizeof(float);
+    const size_t units = (size_t)chunk_slots(B, T, N, chunk, varlen) * (size_t)H;
+    if (dt == KDA_F32)   // one fp32 dk x dv entry state per (chunk slot, head)
+        return units * (size_t)dk * (size_t)dv * sizeof(float);
+    return 2 * units * kda::kRecBytes;   // forward and backward records
 }
 
 kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
@@ -271,9 +272,18 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const void
         return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (N == 0)
         return KDA_OK;
-    // one workgroup per (sequence, head) on a 1-D grid
-    if ((int64_t)N * H > INT32_MAX)
+    // 1-D grids: one workgroup per (sequence, head) or per (chunk slot, head)
+    if ((int64_t)N * H > INT32_MAX ||
+        (dt == KDA_BF16 && chunk_slots(B, T, N, chunk, varlen) * (int64_t)H > INT32_MAX))
         return KDA_ERR_UNSUPPORTED;
+    if (dt == KDA_BF16)
+        return from_hip(kda::launch_chunk_bwd_bf16(
+            (const kda::bf16 *)q, (const kda::bf16 *)k, (const kda::bf16 *)v,
+            (const kda::bf16 *)g, (const kda::bf16 *)beta, (const kda::bf16 *)gate, init_state,
+            (const kda::bf16 *)grad_out, grad_final_state, (kda::bf16 *)grad_q,
+            (kda::bf16 *)grad_k, (kda::bf16 *)grad_v, (kda::bf16 *)grad_g,
+            (kda::bf16 *)grad_beta, (kda::bf16 *)grad_gate, grad_init_state, cu_seqlens, N, T,
+            H, chunk_slots(B, T, N, chunk, varlen), scale, workspace, stream));
     return from_hip(kda::launch_chunk_bwd_f32(
         (const float *)q, (const float *)k, (const float *)v, (const float *)g,
         (const float *)beta, (const float *)gate, init_state, (const float *)grad_out,

@@ -83,33 +83,11 @@ static_assert(sizeof(TSmem) <= sizeof(bf16) * kChunk * kRowLd, "T overlay fits")
 
 __device__ __forceinline__ int pair_index(int i, int j) { return (i * (i - 1)) / 2 + j; }
 
-__device__ __forceinline__ bf16x8 lds8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-
-// 8 bf16 in perm order from a row with the k index contiguous:
-// elements 0..3 <- p[32 ks + 4 b + 0..3], 4..7 <- p[32 ks + 16 + 4 b + 0..3]
-__device__ __forceinline__ bf16x8 perm8(const bf16 *row, int ks, int b)
-{
-    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row + 32 * ks + 4 * b);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(row + 32 * ks + 16 + 4 * b);
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// accumulator tiles (2 ks, 2 ks + 1) -> one perm-order fragment
-__device__ __forceinline__ bf16x8 acc_to_frag(const f32x4 &lo, const f32x4 &hi)
-{
-    return bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
-                  (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
-}
-
 __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4 &a, float s)
 {
     return bf16x4{(bf16)(s * a[0]), (bf16)(s * a[1]), (bf16)(s * a[2]), (bf16)(s * a[3])};
 }
 
-__device__ __forceinline__ f32x4 mfma4_f32(float a, float b, const f32x4 &c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 // DPP lane move (as int bits) with every lane active; lanes whose source is
 // out of range (bound_ctrl) or whose row is masked off read 0
@@ -129,29 +107,6 @@ __device__ __forceinline__ float row_inclusive_sum(float x)
     x += dpp_add_src<0x114, 0xf, true>(x);
     x += dpp_add_src<0x118, 0xf, true>(x);
     return x;
-}
-
-// Chunk slot -> (sequence, chunk index).  Returns false for an unused slot.
-__device__ __forceinline__ bool slot_to_chunk(const int32_t *cu, int N, int T, int64_t slot,
-                                              int &n, int64_t &j)
-{
-    if (cu) {
-        int lo = 0, hi = N - 1;
-        while (lo < hi) {                       // largest n with cu[n]/C + n <= slot
-            const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)cu[mid] / kChunk + mid <= slot)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        n = lo;
-        j = slot - ((int64_t)cu[n] / kChunk + n);
-        return (int64_t)cu[n + 1] - cu[n] > j * kChunk;
-    }
-    const int64_t nck = (T + kChunk - 1) / kChunk;
-    n = (int)(slot / nck);
-    j = slot % nck;
-    return n < N;
 }
 
 }  // namespace
@@ -930,11 +885,13 @@ __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
     }
 }
 
-hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
-                             const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
-                             float *final_state, float *snaps, int snap_interval,
-                             const int32_t *cu, int N, int T, int H, int64_t n_slots,
-                             float scale, unsigned pro, void *workspace, hipStream_t stream)
+namespace {
+
+// Persistent prep over every (chunk slot, head) task: one workgroup per CU
+// (its LDS allows no more), a multiple of 8 of them.
+hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
+                       const bf16 *beta, const int32_t *cu, int N, int T, int H, int64_t n_slots,
+                       float scale, unsigned pro, uint8_t *ws, hipStream_t stream)
 {
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
@@ -949,6 +906,8 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     });
     if (attr_err != hipSuccess)
         return attr_err;
+    if (n_slots <= 0)
+        return hipSuccess;
     int dev = 0, cus = 0;
     hipError_t e0 = hipGetDevice(&dev);
     if (e0 == hipSuccess)
@@ -956,39 +915,52 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     if (e0 != hipSuccess)
         return e0;
     const int64_t prep_grid = cus >= 8 ? cus / 8 * 8 : 8;
-    if (n_slots > 0 && H > 0) {
-        // persistent prep: one workgroup per CU (its LDS allows no more), a
-        // multiple of 8 of them
-        const int64_t n_tasks = n_slots * H;
-        const int64_t grid = n_tasks < prep_grid ? n_tasks : prep_grid;
-        if (pro)
-            hipLaunchKernelGGL(kda_prep_bf16_kernel<true>, dim3((unsigned)grid),
-                               dim3(kPrepThreads), sizeof(PrepSmem), stream, q, k, v, g, beta, cu,
-                               N, T, H, n_tasks, scale, pro, static_cast<uint8_t *>(workspace));
-        else
-            hipLaunchKernelGGL(kda_prep_bf16_kernel<false>, dim3((unsigned)grid),
-                               dim3(kPrepThreads), sizeof(PrepSmem), stream, q, k, v, g, beta, cu,
-                               N, T, H, n_tasks, scale, 0u, static_cast<uint8_t *>(workspace));
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
+    const int64_t n_tasks = n_slots * H;
+    const int64_t grid = n_tasks < prep_grid ? n_tasks : prep_grid;
+    if (pro)
+        hipLaunchKernelGGL(kda_prep_bf16_kernel<true>, dim3((unsigned)grid), dim3(kPrepThreads),
+                           sizeof(PrepSmem), stream, q, k, v, g, beta, cu, N, T, H, n_tasks,
+                           scale, pro, ws);
+    else
+        hipLaunchKernelGGL(kda_prep_bf16_kernel<false>, dim3((unsigned)grid), dim3(kPrepThreads),
+                           sizeof(PrepSmem), stream, q, k, v, g, beta, cu, N, T, H, n_tasks,
+                           scale, 0u, ws);
+    return hipGetLastError();
+}
+
+// The chain over the records in ws, one workgroup per (sequence, head, value block).
+hipError_t launch_chain(const float *init, float *final_state, float *snaps, int snap_interval,
+                        const int32_t *cu, int N, int T, int H, uint8_t *ws, hipStream_t stream)
+{
     const int64_t units = (int64_t)N * H;
-    if (units > 0) {
-        const int64_t blocks = (units + 7) / 8 * 8 * kNumVBlocks;
-        if (snaps)
-            hipLaunchKernelGGL(kda_chain_bf16_kernel<true>, dim3((unsigned)blocks),
-                               dim3(kChainThreads), 0, stream, init, final_state, snaps,
-                               snap_interval / kChunk, cu, T, H, (int)units,
-                               static_cast<uint8_t *>(workspace));
-        else
-            hipLaunchKernelGGL(kda_chain_bf16_kernel<false>, dim3((unsigned)blocks),
-                               dim3(kChainThreads), 0, stream, init, final_state, snaps, 1, cu, T,
-                               H, (int)units, static_cast<uint8_t *>(workspace));
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
+    if (units <= 0)
+        return hipSuccess;
+    const int64_t blocks = (units + 7) / 8 * 8 * kNumVBlocks;
+    if (snaps)
+        hipLaunchKernelGGL(kda_chain_bf16_kernel<true>, dim3((unsigned)blocks),
+                           dim3(kChainThreads), 0, stream, init, final_state, snaps,
+                           snap_interval / kChunk, cu, T, H, (int)units, ws);
+    else
+        hipLaunchKernelGGL(kda_chain_bf16_kernel<false>, dim3((unsigned)blocks),
+                           dim3(kChainThreads), 0, stream, init, final_state, snaps, 1, cu, T, H,
+                           (int)units, ws);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
+                             const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
+                             float *final_state, float *snaps, int snap_interval,
+                             const int32_t *cu, int N, int T, int H, int64_t n_slots,
+                             float scale, unsigned pro, void *workspace, hipStream_t stream)
+{
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    hipError_t e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, pro, ws, stream);
+    if (e == hipSuccess)
+        e = launch_chain(init, final_state, snaps, snap_interval, cu, N, T, H, ws, stream);
+    if (e != hipSuccess)
+        return e;
     if (n_slots > 0 && H > 0) {
         hipLaunchKernelGGL(kda_output_bf16_kernel, dim3((unsigned)(n_slots * H)), dim3(256),
                            0, stream, gate, out, cu, N, T, H,
@@ -996,6 +968,32 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
         return hipGetLastError();
     }
     return hipSuccess;
+}
+
+// Backward: forward records (prep + chain give every chunk's entry state),
+// backward records in reverse chunk order (-L^T, Q^^T dO, dec), the same chain
+// over them from dS_final (the state gradient on exit of every chunk, and
+// dS_0), then the per-chunk gradients.
+hipError_t launch_chunk_bwd_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
+                                 const bf16 *beta, const bf16 *gate, const float *init,
+                                 const bf16 *dout, const float *dfinal, bf16 *dq, bf16 *dk,
+                                 bf16 *dv, bf16 *dg, bf16 *dbeta, bf16 *dgate, float *dinit,
+                                 const int32_t *cu, int N, int T, int H, int64_t n_slots,
+                                 float scale, void *workspace, hipStream_t stream)
+{
+    uint8_t *ws_f = static_cast<uint8_t *>(workspace);
+    uint8_t *ws_b = ws_f + (size_t)n_slots * (size_t)H * kRecBytes;
+    hipError_t e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, 0u, ws_f, stream);
+    if (e == hipSuccess)
+        e = launch_chain(init, nullptr, nullptr, 0, cu, N, T, H, ws_f, stream);
+    if (e == hipSuccess)
+        e = launch_bwd_prep_bf16(gate, dout, cu, N, T, H, n_slots, ws_f, ws_b, stream);
+    if (e == hipSuccess)
+        e = launch_chain(dfinal, dinit, nullptr, 0, cu, N, T, H, ws_b, stream);
+    if (e == hipSuccess)
+        e = launch_grad_bf16(q, k, v, g, beta, gate, dout, dq, dk, dv, dg, dbeta, dgate, cu, N,
+                             T, H, n_slots, scale, ws_f, ws_b, stream);
+    return e;
 }
 
 }  // namespace kda

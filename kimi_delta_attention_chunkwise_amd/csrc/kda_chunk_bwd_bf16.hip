@@ -1,0 +1,760 @@
+// kda_chunk_bwd_bf16.hip -- chunkwise KDA backward for bf16 inputs,
+// dk = dv = 128, 64-token chunks, fp32 state and gradients of the state.
+//
+// Source: "Kimi K3 second-pass study ledger" (llm-atlas K3_RESEARCH.md),
+// section 1 row Q07 (the chunkwise-parallel form serves training as well as
+// prefill) and row Q06 (g >= -5 bounds the decay inside a 16-token subtile).
+//
+// The forward maps the state on entry to chunk j to the next one with
+//     S_{j+1} = (diag(dec) - L) S_j + Bm,      O_j = Q^ S_j + O0
+// (the records of the forward prep).  Its adjoint walks the chunks backward:
+//     dS_j = (diag(dec) - L^T) dS_{j+1} + Q^^T dO_j,    dO = dY sigmoid(Z),
+// which is the same recurrence with L^T for L and Q^^T dO for Bm.  So:
+//   1. forward prep + chain: every chunk's entry state S_j (record SB);
+//   2. backward prep (here): records with -L^T, Q^^T dO and dec, stored in
+//      reverse chunk order, so that
+//   3. the unchanged chain kernel, started from dS_final, yields dS_{j+1} for
+//      every chunk (record SB) and dS_0;
+//   4. gradient kernel (here): one workgroup per (chunk, head) recomputes the
+//      chunk subtile by subtile (16 tokens, so every decay factor stays within
+//      exp(+-40) around the subtile midpoint and fp32 / bf16 never overflow):
+//      a forward sweep gives the states on entry to subtiles 1..3, a backward
+//      sweep from dS_{j+1} gives the gradients of the chunk's tokens.
+//
+// Algebra of one 16-token subtile with entry state S (r, s its rows; G the
+// cumulative log-decay from the subtile start including the row; Ge = G of
+// row 15; B = G of row 7):
+//   Qs = scale Q e^G, Ks = K e^G, Kp = K e^{Ge-G}, Qr = scale Q e^{G-B},
+//   Kr = K e^{G-B}, Kc = K e^{B-G};  M = Kr Kc^T, A = strict_lower(diag(beta) M),
+//   P = lower_incl(Qr Kc^T), T = (I + A)^-1, W = T diag(beta) Ks,
+//   U~ = T diag(beta) V, U = U~ - W S, O = Qs S + P U, S' = diag(e^Ge) S + Kp^T U.
+// Backward, given dS' and dO:
+//   dU = Kp dS' + P^T dO,  dS = diag(e^Ge) dS' + Qs^T dO - W^T dU,
+//   dKp = U dS'^T, dQs = dO S^T, dW = -dU S^T, dP = lower_incl(dO U^T),
+//   dT = dW (diag(beta) Ks)^T + dU (diag(beta) V)^T, dA = strict_lower(-T^T dT T^T),
+//   dKs = diag(beta) T^T dW, dV = diag(beta) T^T dU, dKr = diag(beta) dA Kc,
+//   dKc = dA^T diag(beta) Kr + dP^T Qr, dQr = dP Kc,
+//   dbeta = rowsum((T^T dW) Ks + (T^T dU) V + dA M),
+//   dQ = scale (e^G dQs + e^{G-B} dQr), dK = e^G dKs + e^{G-B} dKr + e^{B-G} dKc + e^{Ge-G} dKp,
+//   dG = dQs Qs + dQr Qr + dKs Ks + dKr Kr - dKc Kc - dKp Kp,
+//   dGe = colsum(dKp Kp) + e^Ge rowsum(dS' S),  dg_u = sum_{r >= u} dG_r + dGe.
+// B cancels inside M and P, so it carries no gradient.
+#include "kda_internal.h"
+
+#include <mutex>
+
+namespace kda {
+
+namespace {
+
+// ------------------------------------------------------------ backward prep
+constexpr int kBpThreads = 512;
+
+struct BwdPrepSmem {
+    bf16 L[kDK][kDK + 8];           // -L, row-major
+    bf16 QT[kDK][kChunk + 8];       // Q^^T  [dk][token]
+    bf16 OT[kDV][kChunk + 8];       // dO^T  [dv][token]
+};
+
+__global__ __launch_bounds__(kBpThreads) void kda_bwd_prep_bf16_kernel(
+    const bf16 *__restrict__ gate, const bf16 *__restrict__ dout, const int32_t *__restrict__ cu,
+    int N, int T, int H, const uint8_t *__restrict__ ws_f, uint8_t *__restrict__ ws_b)
+{
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    BwdPrepSmem &sm = *reinterpret_cast<BwdPrepSmem *>(smem_raw);
+    const int64_t slot = (int64_t)blockIdx.x / H;
+    const int h = (int)((int64_t)blockIdx.x % H);
+    int n;
+    int64_t j;
+    if (!slot_to_chunk(cu, N, T, slot, n, j))
+        return;
+    const SeqInfo si = seq_info(cu, n, T, kChunk);
+    const int64_t nch = (si.len + kChunk - 1) / kChunk;
+    const int64_t tok0 = si.bos + j * kChunk;
+    const int len = (int)((si.len - j * kChunk) < kChunk ? (si.len - j * kChunk) : kChunk);
+    const uint8_t *rf = ws_f + (slot * H + h) * (int64_t)kRecBytes;
+    uint8_t *rb = ws_b + ((si.slot0 + nch - 1 - j) * H + h) * (int64_t)kRecBytes;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int m = lane & 15, b = lane >> 4;
+
+    // -L fragments (row 16 mt + m, perm k order) -> dense rows; 4 lane slots per thread
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int idx = it * kBpThreads + tid;
+        const int f = idx >> 6, l = idx & 63;
+        const int mt = f >> 2, ks = f & 3, fb = l >> 4, fm = l & 15;
+        const bf16x8 x = *reinterpret_cast<const bf16x8 *>(rf + kOffLN + f * kFragBytes + l * 16);
+        bf16 *row = &sm.L[16 * mt + fm][0];
+        *reinterpret_cast<bf16x4 *>(row + 32 * ks + 4 * fb) = bf16x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<bf16x4 *>(row + 32 * ks + 16 + 4 * fb) = bf16x4{x[4], x[5], x[6], x[7]};
+    }
+    // Q^ fragments (token row 16 mt + m, perm dk order) -> Q^^T
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int idx = it * kBpThreads + tid;
+        const int f = idx >> 6, l = idx & 63;
+        const int mt = f >> 2, ks = f & 3, fb = l >> 4, fm = l & 15;
+        const bf16x8 x = *reinterpret_cast<const bf16x8 *>(rf + kOffQH + f * kFragBytes + l * 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            sm.QT[perm_row(ks, fb, e)][16 * mt + fm] = x[e];
+    }
+    // dO = dY sigmoid(Z) of token r, channels c0 .. c0 + 15, transposed; zero past the chunk
+    {
+        const int r = tid >> 3, c0 = 16 * (tid & 7);
+        bf16x8 dy[2] = {}, z[2] = {};
+        if (r < len) {
+            const int64_t off = ((tok0 + r) * H + h) * (int64_t)kDV + c0;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                dy[p] = *reinterpret_cast<const bf16x8 *>(dout + off + 8 * p);
+                z[p] = *reinterpret_cast<const bf16x8 *>(gate + off + 8 * p);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sm.OT[c0 + 8 * p + e][r] =
+                    (bf16)(r < len ? (float)dy[p][e] * sigmoidf_((float)z[p][e]) : 0.f);
+    }
+    if (tid < kDK / 4)
+        *reinterpret_cast<f32x4 *>(rb + kOffDEC + tid * 16) =
+            *reinterpret_cast<const f32x4 *>(rf + kOffDEC + tid * 16);
+    __syncthreads();
+
+    // -L^T fragments of row tile w: element e of lane (b, m) = -L[perm_row(ks, b, e)][16 w + m]
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            x[e] = sm.L[perm_row(ks, b, e)][16 * w + m];
+        *reinterpret_cast<bf16x8 *>(rb + kOffLN + (w * 4 + ks) * kFragBytes + lane * 16) = x;
+    }
+    // Q^^T dO for value block w, in the record's Bm layout: fragment i2 holds row
+    // tiles 2 i2 (elements 0..3) and 2 i2 + 1 (elements 4..7)
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+        f32x4 acc[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int t = 2 * i2 + s2;
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                a = mfma16(lds8(&sm.QT[16 * t + m][32 * ks + 8 * b]),
+                           lds8(&sm.OT[16 * w + m][32 * ks + 8 * b]), a);
+            acc[s2] = a;
+        }
+        *reinterpret_cast<bf16x8 *>(rb + kOffBM + w * 4096 + i2 * 1024 + lane * 16) =
+            acc_to_frag(acc[0], acc[1]);
+    }
+}
+
+// ------------------------------------------------------------ gradient kernel
+constexpr int kGThreads = 512;
+constexpr int kRL = kDK + 8;     // bf16 row stride of [16][128] and [128][128] tiles
+constexpr int kFL = kDK + 4;     // fp32 row stride of [16][128] tiles
+constexpr int kTL = kSub + 8;    // bf16 row stride of transposed [128][16] tiles
+constexpr int kSL = kSub + 1;    // fp32 row stride of 16 x 16 matrices
+
+typedef float Sq[kSub][kSL];
+
+struct GradSmem {
+    // small and often-read arrays first, so that their addresses fit the
+    // 16-bit offsets of LDS instructions
+    Sq M, A, Tm, P, dP, dTu, dT, X, dA;
+    alignas(16) float Bref[kDK];
+    alignas(16) float Ge[kDK];
+    alignas(16) float dec[kDK];
+    alignas(16) float dGeD[kDK];        // e^Ge rowsum(dS' S)
+    alignas(16) float beta[kSub];
+    alignas(16) float dbp[kGThreads / 64][kSub];   // per-wave partial sums of dbeta
+    alignas(16) float G[kSub][kFL];     // cumulative log-decay within the subtile
+    alignas(16) bf16 Kin[kSub][kRL];    // k and q as given (bf16, exact); the pair
+    alignas(16) bf16 Qin[kSub][kRL];    // factors Kr, Kc, Qr are formed from them in fp32
+    alignas(16) bf16 Ks[kSub][kRL];
+    alignas(16) bf16 V[kSub][kRL];
+    alignas(16) bf16 U[kSub][kRL];
+    alignas(16) bf16 dO[kSub][kRL];
+    alignas(16) bf16 dU[kSub][kRL];
+    union {
+        struct {                         // operands of the state products
+            alignas(16) bf16 W[kSub][kRL];
+            alignas(16) bf16 Qs[kSub][kRL];
+            alignas(16) bf16 Kp[kSub][kRL];
+            alignas(16) bf16 WT[kDK][kTL];
+            alignas(16) bf16 QsT[kDK][kTL];
+            alignas(16) bf16 KpT[kDK][kTL];
+        } a;
+        struct {
+            alignas(16) float dW[kSub][kFL];
+        } b;
+        struct {                         // for the reverse cumulative sum of dG
+            alignas(16) float dG[kSub][kFL];
+            alignas(16) float kpk[kSub][kFL];
+        } c;
+    } u;
+    alignas(16) bf16 Sb[kDK][kRL];      // S on entry to the subtile, [dk][dv]
+    alignas(16) bf16 dSb[kDK][kRL];     // dS' on exit of the subtile, [dk][dv]
+};
+static_assert(sizeof(GradSmem) <= 160 * 1024, "gradient kernel LDS fits one CU");
+
+// D += A B with a 16-wide k: lane (b, m) gives A[m][4 b + e] and B[4 b + e][m]
+// (e = 0..3).  Issued as the 16x16x32 product with elements 4..7 of both
+// operands zero (k = 8 b + e then stands for 4 b + e on both sides), so that
+// every bf16 matrix instruction of the kernel has one shape: a 16x16x16
+// accumulating directly onto a chain of 16x16x32 products has been seen to
+// read part of its accumulator input stale on gfx950.
+__device__ __forceinline__ f32x4 mfma16k16(const bf16x4 &a, const bf16x4 &b, const f32x4 &c)
+{
+    const bf16 z = (bf16)0.f;
+    return mfma16(bf16x8{a[0], a[1], a[2], a[3], z, z, z, z},
+                  bf16x8{b[0], b[1], b[2], b[3], z, z, z, z}, c);
+}
+
+__device__ __forceinline__ bf16x4 bf4(const f32x4 &x)
+{
+    return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+
+// Layout of the per-wave tiles below: wave w owns key (or value) channels
+// 16 w .. 16 w + 15; lane (b, m) = (lane / 16, lane % 16) holds rows 4 b + i
+// (i = 0..3) of channel 16 w + m, the accumulator layout of the 16x16 MFMAs.
+__global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ g, const bf16 *__restrict__ beta, const bf16 *__restrict__ gate,
+    const bf16 *__restrict__ dout, bf16 *__restrict__ dq, bf16 *__restrict__ dk,
+    bf16 *__restrict__ dv, bf16 *__restrict__ dg, bf16 *__restrict__ dbeta,
+    bf16 *__restrict__ dgate, const int32_t *__restrict__ cu, int N, int T, int H, float scale,
+    uint8_t *__restrict__ ws_f, const uint8_t *__restrict__ ws_b)
+{
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    GradSmem &sm = *reinterpret_cast<GradSmem *>(smem_raw);
+    const int64_t slot = (int64_t)blockIdx.x / H;
+    const int h = (int)((int64_t)blockIdx.x % H);
+    int n;
+    int64_t j;
+    if (!slot_to_chunk(cu, N, T, slot, n, j))
+        return;
+    const SeqInfo si = seq_info(cu, n, T, kChunk);
+    const int64_t nch = (si.len + kChunk - 1) / kChunk;
+    const int64_t tok0 = si.bos + j * kChunk;
+    const int len = (int)((si.len - j * kChunk) < kChunk ? (si.len - j * kChunk) : kChunk);
+    const int nsub = (len + kSub - 1) / kSub;
+    uint8_t *rf = ws_f + (slot * H + h) * (int64_t)kRecBytes;
+    const uint8_t *rb = ws_b + ((si.slot0 + nch - 1 - j) * H + h) * (int64_t)kRecBytes;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m = lane & 15, b = lane >> 4;
+    const int col = kVBlock * w + m;                          // the lane's channel
+    const int er = tid >> 5, ec = 4 * (tid & 31);            // elementwise: row, 4 channels
+
+    // The state on entry to subtile i as this wave's B fragments (perm order):
+    // subtile 0 from the forward record's SB; subtiles 1..3 are parked in the
+    // same record's first 96 KiB (LN, QH, BM, O0, no longer read once the
+    // backward records exist), 32 KiB per subtile, each lane reading back only
+    // the 16-byte slots it wrote.
+    static_assert(kOffDEC >= 3 * 32768, "three parked states fit before DEC");
+    auto sfrag_ptr = [&](int i, int ks) -> uint8_t * {
+        return i == 0 ? rf + kOffSB + w * 4096 + ks * 1024 + lane * 16
+                      : rf + (i - 1) * 32768 + w * 4096 + ks * 1024 + lane * 16;
+    };
+
+    float zr[4], dyr[4];
+    f32x4 ut;                        // U~ of the wave's value channels
+    // Loads subtile i and forms its operands: G, the factored K / Q tiles, M,
+    // A (and P for the backward), T, W and U~.
+    auto prep_subtile = [&](int i, bool bwd) {
+        const int r0 = kSub * i;
+        {
+            const bool ev = r0 + er < len;
+            const int64_t etok = tok0 + r0 + er;
+            const int64_t eoff = (etok * H + h) * (int64_t)kDK + ec;
+            bf16x4 g4 = {}, v4 = {}, k4 = {}, q4 = {};
+            if (ev) {
+                k4 = *reinterpret_cast<const bf16x4 *>(k + eoff);
+                g4 = *reinterpret_cast<const bf16x4 *>(g + eoff);
+                v4 = *reinterpret_cast<const bf16x4 *>(v + eoff);
+                if (bwd)
+                    q4 = *reinterpret_cast<const bf16x4 *>(q + eoff);
+            }
+            if ((tid & 31) == 0)
+                sm.beta[er] = ev ? (float)beta[etok * H + h] : 0.f;
+            *reinterpret_cast<f32x4 *>(&sm.G[er][ec]) =
+                f32x4{(float)g4[0], (float)g4[1], (float)g4[2], (float)g4[3]};
+            *reinterpret_cast<bf16x4 *>(&sm.V[er][ec]) = v4;
+            *reinterpret_cast<bf16x4 *>(&sm.Kin[er][ec]) = k4;
+            *reinterpret_cast<bf16x4 *>(&sm.Qin[er][ec]) = q4;
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+                const int row = r0 + 4 * b + i2;
+                zr[i2] = dyr[i2] = 0.f;
+                if (bwd && row < len) {
+                    const int64_t off = ((tok0 + row) * H + h) * (int64_t)kDV + col;
+                    zr[i2] = (float)gate[off];
+                    dyr[i2] = (float)dout[off];
+                }
+            }
+            __syncthreads();
+            if (tid < kDK) {
+                float acc = 0.f;
+#pragma unroll
+                for (int r = 0; r < kSub; ++r) {
+                    acc += sm.G[r][tid];
+                    sm.G[r][tid] = acc;
+                    if (r == kSub / 2 - 1)
+                        sm.Bref[tid] = acc;
+                }
+                sm.Ge[tid] = acc;
+                sm.dec[tid] = __expf(acc);
+            }
+            __syncthreads();
+            bf16x4 ks, kp, qs;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int x = ec + e;
+                const float G = sm.G[er][x], Ge = sm.Ge[x];
+                const float eG = __expf(G), eP = __expf(Ge - G);
+                const float kv = (float)k4[e], qv = scale * (float)q4[e];
+                ks[e] = (bf16)(kv * eG);
+                kp[e] = (bf16)(kv * eP);
+                qs[e] = (bf16)(qv * eG);
+                sm.u.a.KpT[x][er] = kp[e];
+                if (bwd)
+                    sm.u.a.QsT[x][er] = qs[e];
+            }
+            *reinterpret_cast<bf16x4 *>(&sm.Ks[er][ec]) = ks;
+            *reinterpret_cast<bf16x4 *>(&sm.u.a.Kp[er][ec]) = kp;
+            if (bwd)
+                *reinterpret_cast<bf16x4 *>(&sm.u.a.Qs[er][ec]) = qs;
+        }
+        __syncthreads();
+        // M = Kr Kc^T and A (wave 0); P = lower_incl(Qr Kc^T) (wave 1); the
+        // operands Kr = K e^{G-B}, Qr = scale Q e^{G-B}, Kc = K e^{B-G} of row m
+        // are formed here and rounded to bf16 for the product
+        if (w == 0 || (bwd && w == 1)) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const bf16 *xr = w == 0 ? &sm.Kin[m][0] : &sm.Qin[m][0];
+            const float xs = w == 0 ? 1.f : scale;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int x0 = 32 * ks + 8 * b;
+                const bf16x8 xv = lds8(xr + x0), kv = lds8(&sm.Kin[m][x0]);
+                bf16x8 af, bfr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = sm.G[m][x0 + e] - sm.Bref[x0 + e];
+                    af[e] = (bf16)(xs * (float)xv[e] * __expf(d));
+                    bfr[e] = (bf16)((float)kv[e] * __expf(-d));
+                }
+                acc = mfma16(af, bfr, acc);
+            }
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+                const int r = 4 * b + i2;
+                if (w == 0) {
+                    sm.M[r][m] = acc[i2];
+                    sm.A[r][m] = m < r ? sm.beta[r] * acc[i2] : 0.f;
+                } else {
+                    sm.P[r][m] = m <= r ? acc[i2] : 0.f;
+                }
+            }
+        }
+        // T = (I + A)^-1 by forward substitution in column form: once row s is
+        // final it updates every later row; thread (r, c) owns T[r][c]
+        if (tid < kSub * kSub)
+            sm.Tm[tid >> 4][tid & 15] = (tid >> 4) == (tid & 15) ? 1.f : 0.f;
+        __syncthreads();
+        for (int s = 0; s < kSub - 1; ++s) {
+            const int r = tid >> 4, c = tid & 15;
+            if (tid < kSub * kSub && r > s)
+                sm.Tm[r][c] -= sm.A[r][s] * sm.Tm[s][c];
+            __syncthreads();
+        }
+        // W = T diag(beta) Ks and U~ = T diag(beta) V on the wave's channels (fp32 MFMA)
+        f32x4 wt = {0.f, 0.f, 0.f, 0.f}, u = wt;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int s = 4 * kk + b;
+            const float t = sm.Tm[m][s], bs = sm.beta[s];
+            wt = mfma4_f32(t, bs * (float)sm.Ks[s][col], wt);
+            u = mfma4_f32(t, bs * (float)sm.V[s][col], u);
+        }
+        ut = u;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+            sm.u.a.W[4 * b + i2][col] = (bf16)wt[i2];
+            sm.u.a.WT[col][4 * b + i2] = (bf16)wt[i2];
+        }
+        __syncthreads();
+    };
+
+    // ---------------- forward sweep: states on entry to subtiles 1 .. nsub - 1
+    if (nsub > 1) {
+        f32x4 S[8];
+        bf16x8 sf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(0, ks));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                S[2 * ks][i] = (float)sf[ks][i];
+                S[2 * ks + 1][i] = (float)sf[ks][4 + i];
+            }
+        }
+#pragma unroll 1
+        for (int i = 0; i + 1 < nsub; ++i) {
+            prep_subtile(i, false);
+            f32x4 ws = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                ws = mfma16(perm8(&sm.u.a.W[m][0], ks, b), sf[ks], ws);
+            const bf16x4 ub = bf4(ut - ws);
+            // S' = diag(e^Ge) S + Kp^T U
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const f32x4 dc = *reinterpret_cast<const f32x4 *>(&sm.dec[16 * t + 4 * b]);
+                S[t] = S[t] * dc;
+                S[t] = mfma16k16(*reinterpret_cast<const bf16x4 *>(&sm.u.a.KpT[16 * t + m][4 * b]),
+                                 ub, S[t]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                sf[ks] = acc_to_frag(S[2 * ks], S[2 * ks + 1]);
+                *reinterpret_cast<bf16x8 *>(sfrag_ptr(i + 1, ks)) = sf[ks];
+            }
+            __syncthreads();
+        }
+    }
+
+    // gradient of the state on exit of the current subtile, accumulator tiles
+    // (rows 16 t + 4 b + i of the wave's value channels)
+    f32x4 dS[8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 d = *reinterpret_cast<const bf16x8 *>(rb + kOffSB + w * 4096 + ks * 1024 +
+                                                           lane * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dS[2 * ks][i] = (float)d[i];
+            dS[2 * ks + 1][i] = (float)d[4 + i];
+        }
+    }
+
+    // ---------------- backward sweep over the subtiles, last to first
+#pragma unroll 1
+    for (int i = nsub - 1; i >= 0; --i) {
+        prep_subtile(i, true);
+        const int r0 = kSub * i;
+        bf16x8 sf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(i, ks));
+        // U = U~ - W S and O = Qs S + P U on the wave's value channels
+        f32x4 ws = {0.f, 0.f, 0.f, 0.f}, o = ws;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            ws = mfma16(perm8(&sm.u.a.W[m][0], ks, b), sf[ks], ws);
+            o = mfma16(perm8(&sm.u.a.Qs[m][0], ks, b), sf[ks], o);
+        }
+        const bf16x4 ub = bf4(ut - ws);
+        {
+            bf16x4 pa;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pa[e] = (bf16)sm.P[m][4 * b + e];
+            o = mfma16k16(pa, ub, o);
+        }
+        // gate: dZ, and dO = dY sigmoid(Z)
+        f32x4 dOv;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+            const int row = r0 + 4 * b + i2;
+            const float sg = sigmoidf_(zr[i2]);
+            if (row < len)
+                dgate[((tok0 + row) * H + h) * (int64_t)kDV + col] =
+                    (bf16)(dyr[i2] * o[i2] * sg * (1.f - sg));
+            dOv[i2] = dyr[i2] * sg;
+        }
+        const bf16x4 dob = bf4(dOv);
+        // dU = Kp dS' + P^T dO
+        f32x4 du = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            du = mfma16(perm8(&sm.u.a.Kp[m][0], ks, b), acc_to_frag(dS[2 * ks], dS[2 * ks + 1]),
+                        du);
+        {
+            bf16x4 pt;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pt[e] = (bf16)sm.P[4 * b + e][m];
+            du = mfma16k16(pt, dob, du);
+        }
+        const bf16x4 dub = bf4(du);
+        // U, dO, dU, S and dS' of the wave's value channels into LDS
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+            const int r = 4 * b + i2;
+            sm.U[r][col] = ub[i2];
+            sm.dO[r][col] = dob[i2];
+            sm.dU[r][col] = dub[i2];
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sm.Sb[perm_row(ks, b, e)][col] = sf[ks][e];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2)
+                sm.dSb[16 * t + 4 * b + i2][col] = (bf16)dS[t][i2];
+        // dS on entry to the subtile: diag(e^Ge) dS' + Qs^T dO - W^T dU
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            const bf16x4 ndub = bf16x4{(bf16)(-du[0]), (bf16)(-du[1]), (bf16)(-du[2]),
+                                       (bf16)(-du[3])};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const f32x4 dc = *reinterpret_cast<const f32x4 *>(&sm.dec[16 * t + 4 * b]);
+                f32x4 x = dS[t] * dc;
+                x = mfma16k16(*reinterpret_cast<const bf16x4 *>(&sm.u.a.QsT[16 * t + m][4 * b]),
+                              dob, x);
+                dS[t] = mfma16k16(*reinterpret_cast<const bf16x4 *>(&sm.u.a.WT[16 * t + m][4 * b]),
+                                  ndub, x);
+            }
+        }
+        __syncthreads();
+
+        // sums over the value channels on the wave's key channels col:
+        // dKp = U dS'^T, dQs = dO S^T, dW = -dU S^T
+        f32x4 dkp = {0.f, 0.f, 0.f, 0.f}, dqs = dkp, dw = dkp;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kc = 32 * ks + 8 * b;
+            const bf16x8 srow = lds8(&sm.Sb[col][kc]);
+            dkp = mfma16(lds8(&sm.U[m][kc]), lds8(&sm.dSb[col][kc]), dkp);
+            dqs = mfma16(lds8(&sm.dO[m][kc]), srow, dqs);
+            dw = mfma16(lds8(&sm.dU[m][kc]), srow, dw);
+        }
+        dw = -dw;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2)
+            sm.u.b.dW[4 * b + i2][col] = dw[i2];
+        {
+            // e^Ge rowsum(dS' S) of key channel col, 32 value channels per lane group
+            float pr = 0.f;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const bf16x8 sv = lds8(&sm.Sb[col][32 * b + 8 * p]);
+                const bf16x8 dv8 = lds8(&sm.dSb[col][32 * b + 8 * p]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pr += (float)sv[e] * (float)dv8[e];
+            }
+            pr += __shfl_xor(pr, 16);
+            pr += __shfl_xor(pr, 32);
+            if (b == 0)
+                sm.dGeD[col] = sm.dec[col] * pr;
+        }
+        if (w == 0 || w == 1) {
+            // wave 0: dP = lower_incl(dO U^T); wave 1: dU (diag(beta) V)^T
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const bf16 *ar = w == 0 ? &sm.dO[m][0] : &sm.dU[m][0];
+            const bf16 *br = w == 0 ? &sm.U[m][0] : &sm.V[m][0];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mfma16(lds8(ar + 32 * ks + 8 * b), lds8(br + 32 * ks + 8 * b), acc);
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+                const int r = 4 * b + i2;
+                if (w == 0)
+                    sm.dP[r][m] = m <= r ? acc[i2] : 0.f;
+                else
+                    sm.dTu[r][m] = sm.beta[m] * acc[i2];
+            }
+        }
+        __syncthreads();
+        // dT = dW (diag(beta) Ks)^T + dU (diag(beta) V)^T  (fp32 MFMA over the 128 key channels)
+        if (w == 0) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int kk = 0; kk < kDK / 4; ++kk) {
+                const int x = 4 * kk + b;
+                acc = mfma4_f32(sm.u.b.dW[m][x], (float)sm.Ks[m][x], acc);
+            }
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+                const int r = 4 * b + i2;
+                sm.dT[r][m] = sm.beta[m] * acc[i2] + sm.dTu[r][m];
+            }
+        }
+        __syncthreads();
+        // dA = strict_lower(-T^T dT T^T)
+        if (tid < kSub * kSub) {
+            const int r = tid >> 4, c = tid & 15;
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < kSub; ++s)
+                acc += sm.Tm[s][r] * sm.dT[s][c];
+            sm.X[r][c] = acc;
+        }
+        __syncthreads();
+        if (tid < kSub * kSub) {
+            const int r = tid >> 4, c = tid & 15;
+            float acc = 0.f;
+#pragma unroll
+            for (int x = 0; x < kSub; ++x)
+                acc += sm.X[r][x] * sm.Tm[c][x];
+            sm.dA[r][c] = c < r ? -acc : 0.f;
+        }
+        __syncthreads();
+
+        // the contractions over the subtile's 16 tokens, on the wave's channels:
+        // T^T dW, T^T dU, dP^T Qr + dA^T diag(beta) Kr, dA Kc, dP Kc.  Kr, Kc and
+        // Qr enter in fp32: every pair (r, s) of A and P adds a term to dG_r and
+        // its negative to dG_s, and the two cancel in the reverse cumulative sum
+        // that gives dg, so both must be formed from the same fp32 factors.
+        f32x4 tdw = {0.f, 0.f, 0.f, 0.f}, tdu = tdw, dkc = tdw, dkr = tdw, dqr = tdw;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int s = 4 * kk + b;
+            const float t_ms = sm.Tm[s][m];
+            const float d = sm.G[s][col] - sm.Bref[col];
+            const float egb = __expf(d), ebg = __expf(-d);
+            const float ks_ = (float)sm.Kin[s][col];
+            const float kc_s = ks_ * ebg, kr_s = ks_ * egb;
+            const float qr_s = scale * (float)sm.Qin[s][col] * egb;
+            tdw = mfma4_f32(t_ms, sm.u.b.dW[s][col], tdw);
+            tdu = mfma4_f32(t_ms, (float)sm.dU[s][col], tdu);
+            dkc = mfma4_f32(sm.dP[s][m], qr_s, dkc);
+            dkc = mfma4_f32(sm.dA[s][m] * sm.beta[s], kr_s, dkc);
+            dkr = mfma4_f32(sm.dA[m][s], kc_s, dkr);
+            dqr = mfma4_f32(sm.dP[m][s], kc_s, dqr);
+        }
+        // per element: row r = 4 b + i2, channel col
+        float dGv[4], kpk[4];
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+            const int r = 4 * b + i2;
+            const bool valid = r0 + r < len;
+            const int64_t tok = tok0 + r0 + r;
+            const int64_t off = (tok * H + h) * (int64_t)kDK + col;
+            const float kv = (float)sm.Kin[r][col];
+            const float qv = scale * (float)sm.Qin[r][col];
+            const float G = sm.G[r][col], d = G - sm.Bref[col], Ge = sm.Ge[col];
+            const float eG = __expf(G), eGB = __expf(d), eBG = __expf(-d), eP = __expf(Ge - G);
+            const float br = sm.beta[r];
+            const float dks = br * tdw[i2], dkr_ = br * dkr[i2];
+            if (valid) {
+                dq[off] = (bf16)(scale * (eG * dqs[i2] + eGB * dqr[i2]));
+                dk[off] = (bf16)(eG * dks + eGB * dkr_ + eBG * dkc[i2] + eP * dkp[i2]);
+                dv[off] = (bf16)(br * tdu[i2]);
+            }
+            dGv[i2] = dqs[i2] * qv * eG + dqr[i2] * qv * eGB + dks * kv * eG + dkr_ * kv * eGB -
+                      dkc[i2] * kv * eBG - dkp[i2] * kv * eP;
+            kpk[i2] = dkp[i2] * kv * eP;
+            // dbeta terms of this element, summed over the wave's 16 channels
+            float pb = tdw[i2] * kv * eG + tdu[i2] * (float)sm.V[r][col];
+            pb += __shfl_xor(pb, 8, 16);
+            pb += __shfl_xor(pb, 4, 16);
+            pb += __shfl_xor(pb, 2, 16);
+            pb += __shfl_xor(pb, 1, 16);
+            if (m == 0)
+                sm.dbp[w][r] = pb;
+        }
+        // dG and dKp Kp of the wave's channels; the wave read only its own
+        // channels of dW, which dG overlays
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+            sm.u.c.dG[4 * b + i2][col] = dGv[i2];
+            sm.u.c.kpk[4 * b + i2][col] = kpk[i2];
+        }
+        __syncthreads();
+        if (tid < kSub && r0 + tid < len) {
+            float acc = 0.f;
+#pragma unroll
+            for (int x = 0; x < kGThreads / 64; ++x)
+                acc += sm.dbp[x][tid];
+#pragma unroll
+            for (int s = 0; s < kSub; ++s)
+                acc += sm.dA[tid][s] * sm.M[tid][s];
+            dbeta[(tok0 + r0 + tid) * H + h] = (bf16)acc;
+        }
+        {
+            float dge = sm.dGeD[col];
+#pragma unroll
+            for (int r = 0; r < kSub; ++r)
+                dge += sm.u.c.kpk[r][col];
+            // dg_u = sum_{r >= u} dG_r + dGe, for the lane's rows 4 b + i2
+            float suf[kSub];
+            float acc = dge;
+#pragma unroll
+            for (int r = kSub - 1; r >= 0; --r) {
+                acc += sm.u.c.dG[r][col];
+                suf[r] = acc;
+            }
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+                const int r = 4 * b + i2;
+                float val = suf[0];
+#pragma unroll
+                for (int rr = 1; rr < kSub; ++rr)
+                    val = (r == rr) ? suf[rr] : val;
+                if (r0 + r < len)
+                    dg[((tok0 + r0 + r) * H + h) * (int64_t)kDK + col] = (bf16)val;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep_bf16(const bf16 *gate, const bf16 *dout, const int32_t *cu, int N,
+                                int T, int H, int64_t n_slots, const uint8_t *ws_f,
+                                uint8_t *ws_b, hipStream_t stream)
+{
+    static std::once_flag once;
+    static hipError_t err = hipSuccess;
+    std::call_once(once, [] {
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_bwd_prep_bf16_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)sizeof(BwdPrepSmem));
+    });
+    if (err != hipSuccess)
+        return err;
+    if (n_slots <= 0 || H <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(kda_bwd_prep_bf16_kernel, dim3((unsigned)(n_slots * H)), dim3(kBpThreads),
+                       sizeof(BwdPrepSmem), stream, gate, dout, cu, N, T, H, ws_f, ws_b);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
+                            const bf16 *beta, const bf16 *gate, const bf16 *dout, bf16 *dq,
+                            bf16 *dk, bf16 *dv, bf16 *dg, bf16 *dbeta, bf16 *dgate,
+                            const int32_t *cu, int N, int T, int H, int64_t n_slots, float scale,
+                            uint8_t *ws_f, const uint8_t *ws_b, hipStream_t stream)
+{
+    static std::once_flag once;
+    static hipError_t err = hipSuccess;
+    std::call_once(once, [] {
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_grad_bf16_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)sizeof(GradSmem));
+    });
+    if (err != hipSuccess)
+        return err;
+    if (n_slots <= 0 || H <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(kda_grad_bf16_kernel, dim3((unsigned)(n_slots * H)), dim3(kGThreads),
+                       sizeof(GradSmem), stream, q, k, v, g, beta, gate, dout, dq, dk, dv, dg,
+                       dbeta, dgate, cu, N, T, H, scale, ws_f, ws_b);
+    return hipGetLastError();
+}
+
+}  // namespace kda

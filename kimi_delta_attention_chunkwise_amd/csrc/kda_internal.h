@@ -99,6 +99,30 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ bf16x8 lds8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// 8 bf16 in perm order from a row with the k index contiguous:
+// elements 0..3 <- p[32 ks + 4 b + 0..3], 4..7 <- p[32 ks + 16 + 4 b + 0..3]
+__device__ __forceinline__ bf16x8 perm8(const bf16 *row, int ks, int b)
+{
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row + 32 * ks + 4 * b);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(row + 32 * ks + 16 + 4 * b);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// accumulator tiles (2 ks, 2 ks + 1) -> one perm-order fragment
+__device__ __forceinline__ bf16x8 acc_to_frag(const f32x4 &lo, const f32x4 &hi)
+{
+    return bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+                  (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+}
+
+// fp32 16x16x4: lane l gives A[l % 16][l / 16] and B[l / 16][l % 16]
+__device__ __forceinline__ f32x4 mfma4_f32(float a, float b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 
@@ -147,6 +171,30 @@ __device__ __forceinline__ SeqInfo seq_info(const int32_t *cu, int n, int T, int
     return s;
 }
 
+// Chunk slot -> (sequence, chunk index).  Returns false for an unused slot.
+__device__ __forceinline__ bool slot_to_chunk(const int32_t *cu, int N, int T, int64_t slot,
+                                              int &n, int64_t &j)
+{
+    if (cu) {
+        int lo = 0, hi = N - 1;
+        while (lo < hi) {                       // largest n with cu[n]/C + n <= slot
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)cu[mid] / kChunk + mid <= slot)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        n = lo;
+        j = slot - ((int64_t)cu[n] / kChunk + n);
+        return (int64_t)cu[n + 1] - cu[n] > j * kChunk;
+    }
+    const int64_t nck = (T + kChunk - 1) / kChunk;
+    n = (int)(slot / nck);
+    j = slot % nck;
+    return n < N;
+}
+
+
 // First snapshot slot of sequence n for snapshots every `interval` tokens
 // (a multiple of the chunk length).  Snapshot m = 1 .. floor(len / interval)
 // of sequence n, the state after its first m * interval tokens, goes to slot
@@ -192,5 +240,31 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
                              float *final_state, float *snaps, int snap_interval,
                              const int32_t *cu, int N, int T, int H, int64_t n_slots,
                              float scale, unsigned pro, void *workspace, hipStream_t stream);
+
+// Chunkwise backward, bf16, dk = dv = 128, 64-token chunks; the workspace
+// holds two record arrays of n_slots * H records each (forward, backward).
+hipError_t launch_chunk_bwd_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
+                                 const bf16 *beta, const bf16 *gate, const float *init,
+                                 const bf16 *dout, const float *dfinal, bf16 *dq, bf16 *dk,
+                                 bf16 *dv, bf16 *dg, bf16 *dbeta, bf16 *dgate, float *dinit,
+                                 const int32_t *cu, int N, int T, int H, int64_t n_slots,
+                                 float scale, void *workspace, hipStream_t stream);
+
+// Backward records: for chunk j of a sequence with nch chunks, record
+// slot0 + nch - 1 - j of ws_b gets LN = -L^T, BM = Q^^T dO (dO = dY sigmoid(Z))
+// and DEC of the forward record of chunk j in ws_f, so that the chain walks
+// the chunks last to first.
+hipError_t launch_bwd_prep_bf16(const bf16 *gate, const bf16 *dout, const int32_t *cu, int N,
+                                int T, int H, int64_t n_slots, const uint8_t *ws_f,
+                                uint8_t *ws_b, hipStream_t stream);
+
+// Per-chunk gradients from the entry states (SB of ws_f) and the exit state
+// gradients (SB of the reversed records of ws_b); overwrites the LN, QH, BM
+// and O0 parts of the forward records.
+hipError_t launch_grad_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
+                            const bf16 *beta, const bf16 *gate, const bf16 *dout, bf16 *dq,
+                            bf16 *dk, bf16 *dv, bf16 *dg, bf16 *dbeta, bf16 *dgate,
+                            const int32_t *cu, int N, int T, int H, int64_t n_slots, float scale,
+                            uint8_t *ws_f, const uint8_t *ws_b, hipStream_t stream);
 
 }  // namespace kda

@@ -219,7 +219,8 @@ def test_decode_step_rejects_bad_arguments_before_launch(lib):
 
 def test_chunk_bwd_sizes_and_argument_checks(lib):
     assert lib.kda_chunk_bwd_supported(0, 16, 16, 16) == 1
-    for args in [(1, 128, 128, 64), (0, 16, 16, 64), (0, 128, 128, 16), (2, 16, 16, 16)]:
+    assert lib.kda_chunk_bwd_supported(1, 128, 128, 64) == 1
+    for args in [(1, 128, 128, 16), (0, 16, 16, 64), (0, 128, 128, 16), (2, 16, 16, 16)]:
         assert lib.kda_chunk_bwd_supported(*args) == 0
     ws = lib.kda_chunk_bwd_workspace_bytes
     bad = ctypes.c_size_t(-1).value
@@ -228,7 +229,11 @@ def test_chunk_bwd_sizes_and_argument_checks(lib):
     assert ws(1, 55, 5, 2, 16, 16, 16, 0, 1) == (55 // 16 + 5) * 2 * 1024
     assert ws(1, 0, 1, 2, 16, 16, 16, 0, 0) == 0
     assert ws(2, 64, 1, 1, 16, 16, 16, 0, 0) == bad
-    assert ws(1, 64, 1, 1, 128, 128, 64, 1, 0) == bad
+    # bf16: a forward and a backward record per (64-token chunk slot, head)
+    REC = lib.kda_chunk_fwd_workspace_bytes(1, 64, 1, 1, 128, 128, 64, 1, 0)
+    assert ws(1, 4096, 1, 8, 128, 128, 64, 1, 0) == 2 * 64 * 8 * REC
+    assert ws(1, 1000, 3, 2, 128, 128, 64, 1, 1) == 2 * (1000 // 64 + 3) * 2 * REC
+    assert ws(1, 64, 1, 1, 128, 128, 16, 1, 0) == bad
     p = lambda x: None if x is None else ctypes.c_void_p(x)
 
     def call(**kw):
@@ -240,8 +245,9 @@ def test_chunk_bwd_sizes_and_argument_checks(lib):
                                  a["B"], a["T"], a["N"], a["H"], a["d"], a["d"], a["chunk"], 1.0,
                                  a["dt"], p(a["ws"]), a["ws_bytes"], None)
     assert call(dt=4) == DTYPE
-    assert call(dt=1, d=128, chunk=64) == UNSUP
+    assert call(dt=1, d=128, chunk=16) == UNSUP
     assert call(chunk=64) == UNSUP
+    assert call(dt=1, d=128, chunk=64, ws_bytes=REC) == WS
     assert call(H=0) == SHAPE and call(T=-1) == SHAPE and call(B=2) == SHAPE
     assert call(cu=1, B=2, N=2) == SHAPE
     assert call(q=None) == NULLP and call(gq=None) == NULLP

@@ -90,3 +90,63 @@ def test_f32_backward_empty(dev):
     torch.cuda.synchronize()
     assert gr["q"].numel() == 0
     assert torch.equal(gr["init_state"].cpu(), dfin)
+
+
+# ------------------------------------------------------------------ bf16 path
+# Gradients are outputs of the backward and the initial-state gradient is a
+# state: the bf16 tolerances of the forward (2e-2 on outputs, 1e-2 on states)
+# apply to them.
+TOL_BF16_GRAD, TOL_BF16_DSTATE = 2e-2, 1e-2
+
+
+def run_bf16_case(dev, x, dy, dfin, scale, label):
+    xd = to(x, dev)
+    gr = kda.chunk_bwd(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["z"], dy.to(dev),
+                       init_state=xd.get("init_state"),
+                       grad_final_state=None if dfin is None else dfin.to(dev),
+                       cu_seqlens=xd.get("cu_seqlens"), scale=scale)
+    torch.cuda.synchronize()
+    cu = x.get("cu_seqlens")
+    ref = oracle.backward(np32(x["q"]), np32(x["k"]), np32(x["v"]), np32(x["g"]),
+                          np32(x["beta"]), np32(x["z"]), np32(dy),
+                          init_state=np32(x.get("init_state")), dfinal=np32(dfin),
+                          cu_seqlens=None if cu is None else cu.numpy(), scale=scale)
+    errs = {name: rel(np32(gr[name]), ref[key]) for name, key in GRADS}
+    es = rel(np32(gr["init_state"]), ref["dinit"])
+    say(f"backward bf16 {label}: " + ", ".join(f"d{k} {e:.2e}" for k, e in errs.items()) +
+        f", dinit {es:.2e}")
+    for name, _ in GRADS:
+        assert np.all(np.isfinite(np32(gr[name]))), f"{label}: non-finite d{name}"
+    bad = {k: e for k, e in errs.items() if e > TOL_BF16_GRAD}
+    assert not bad, f"{label}: gradient errors above {TOL_BF16_GRAD}: {bad}"
+    assert es <= TOL_BF16_DSTATE, f"{label}: initial-state gradient error {es}"
+
+
+@pytest.mark.parametrize("case", ["ragged_batch", "varlen_edges", "pinned_floor", "floor_decay",
+                                  "zero_decay"])
+def test_bf16_backward_cases(dev, case):
+    say(f"backward bf16 case {case}")
+    bf = torch.bfloat16
+    if case == "ragged_batch":
+        x = small_inputs(bf, 2, 200, 2, 128, 128, 31, init_std=0.02)
+    elif case == "varlen_edges":
+        x = small_inputs(bf, 1, 0, 3, 128, 128, 32, lengths=[0, 1, 15, 17, 63, 64, 65, 129, 0],
+                         init_std=0.02)
+    elif case == "pinned_floor":
+        x = small_inputs(bf, 1, 300, 2, 128, 128, 33, init_std=0.02, g_mode="pinned")
+    elif case == "floor_decay":
+        x = small_inputs(bf, 1, 150, 2, 128, 128, 34, init_std=0.02)
+        x["g"] = torch.full_like(x["g"], -5.0)
+    else:
+        x = small_inputs(bf, 1, 130, 2, 128, 128, 35, init_std=0.02, g_mode="zero")
+    dy, dfin = cotangents(x, 800, 0.05)
+    run_bf16_case(dev, x, dy, dfin, 0.5 if case == "varlen_edges" else 1.0, case)
+
+
+def test_bf16_backward_prefill_t4096_h8(dev):
+    """The prefill workload's shape (B=1, H=8, T=4096, dk=dv=128), compared in full."""
+    w = W.WORKLOADS["prefill_t4096_h8"]
+    say("backward bf16 prefill_t4096_h8 B=1 H=8 T=4096")
+    x = W.prefill_inputs(w, seed=0)
+    dy, dfin = cotangents(x, 900, 0.05)
+    run_bf16_case(dev, x, dy, dfin, 1.0, "prefill_t4096_h8")
