@@ -43,7 +43,8 @@ CHUNK = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_prefill_t4096_h8_traffic.json")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "kimi_delta_attention_chunkwise_amd", "csrc", f)
-    for f in ("kda_chunk_bf16.hip", "kda_decode.hip", "kda_internal.h", "kda_api.hip")
+    for f in ("kda_chunk_bf16.hip", "kda_decode.hip", "kda_internal.h", "kda_api.hip",
+              "kda_chunk_bwd_bf16.hip")
 ]
 
 
@@ -84,6 +85,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--extras", default="snapshots_prologue,backward,decode_prologue_verify,long",
+                    help="comma-separated extra measurements to run (default: all)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the snapshot / prologue / verify measurements")
     return ap.parse_args()
@@ -185,18 +188,22 @@ def main():
                  "unit": "TFLOP/s", "frac": flops_call / t_s / 1e12 / BF16_PEAK_TFLOPS,
                  "algorithmic_flops_per_call": flops_call},
     }
-    if not args.no_extras:
-        result["extras"] = {"snapshots_prologue": bench_prefill_extras(torch, kda, sets, ws, out,
-                                                                       fin, ms, args)}
+    extras = set() if args.no_extras else set(args.extras.split(","))
+    result["extras"] = {}
+    if "snapshots_prologue" in extras:
+        result["extras"]["snapshots_prologue"] = bench_prefill_extras(torch, kda, sets, ws, out,
+                                                                      fin, ms, args)
+    if "backward" in extras:
+        result["extras"]["backward_prefill_t4096_h8"] = bench_backward(torch, kda, sets, ms, args)
     del sets
 
     if not args.no_decode:
         result["decode"] = bench_decode(torch, kda, W, dev, args)
-        if not args.no_extras:
+        if "decode_prologue_verify" in extras:
             result["extras"]["decode_prologue_verify"] = bench_decode_extras(torch, kda, W, dev,
                                                                              args)
 
-    if not args.no_extras:
+    if "long" in extras:
         result["extras"]["long_t1m_h16"] = bench_long(torch, kda, W, dev)
 
     if not args.no_cpu_baseline:
@@ -288,6 +295,53 @@ def bench_prefill_extras(torch, kda, sets, ws, out, fin, ms_plain, args):
             "snapshot_bytes_per_call": int(snaps.numel() * 4),
             "prologue_all_ms": ms_pro,
             "prologue_tokens_per_s": B * T / (ms_pro / 1e3)}
+
+
+def bench_backward(torch, kda, sets, ms_fwd, args):
+    """kda_chunk_bwd on the prefill workload: gradients of every input and of
+    the initial state from dY ~ N(0, 1) and a zero dS_final, all buffers
+    preallocated, rotating over the same input sets as the forward."""
+    x0 = sets[0]
+    B, T, H, _ = x0["q"].shape
+    dev = x0["q"].device
+    gen = torch.Generator(device=dev).manual_seed(77)
+    dys = [torch.randn(x0["v"].shape, generator=gen, device=dev).to(torch.bfloat16)
+           for _ in range(2)]
+    ws = torch.empty(kda.chunk_bwd_workspace_bytes(B, T, B, H, DK, DV, CHUNK, torch.bfloat16,
+                                                   False), dtype=torch.uint8, device=dev)
+    grads = {n: torch.empty_like(x0[src]) for n, src in
+             (("q", "q"), ("k", "k"), ("v", "v"), ("g", "g"), ("beta", "beta"), ("gate", "z"))}
+    grads["init_state"] = torch.empty(B, H, DK, DV, dtype=torch.float32, device=dev)
+    n_sets = len(sets)
+
+    def call(i):
+        x = sets[i % n_sets]
+        kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], dys[i % 2],
+                      workspace=ws, grads=grads)
+
+    steps = max(5, args.steps // 2)
+    ms = _time(torch, call, steps, max(3, args.warmup // 2))
+    print(f"[bench] backward prefill_t4096_h8: {ms:.4f} ms per call", file=sys.stderr,
+          flush=True)
+    token_heads = B * T * H
+    # reads q, k, v, g, z, dY (256 B each) and beta; writes dq, dk, dv, dg, dz and dbeta;
+    # the fp32 dS_0
+    bytes_call = (6 * 256 + 2 + 5 * 256 + 2) * token_heads + B * H * STATE_BYTES
+    flops_call = 3 * flops_per_token_head() * token_heads
+    t_s = ms / 1e3
+    del ws, grads
+    return {"workload": "prefill_t4096_h8", "ms_per_call": ms, "tokens_per_s": B * T / t_s,
+            "ratio_to_forward": ms / ms_fwd, "steps": steps,
+            "kernels": "forward prep + chain, backward prep, chain, gradient kernel",
+            "roofline": {"bound": "hbm", "achieved": bytes_call / t_s / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": bytes_call / t_s / 1e9 / HBM_PEAK_GBS,
+                         "algorithmic_bytes_per_call": bytes_call},
+            "mfma": {"achieved": flops_call / t_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops_call / t_s / 1e12 / BF16_PEAK_TFLOPS,
+                     "algorithmic_flops_per_call": flops_call,
+                     "flops_rule": "3 x the forward's: the recompute plus two products of "
+                                   "the same size for the adjoint of each product"}}
 
 
 def bench_decode_extras(torch, kda, W, dev, args):

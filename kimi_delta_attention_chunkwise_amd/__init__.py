@@ -395,12 +395,14 @@ def chunk_bwd_workspace_bytes(B: int, T: int, N: int, H: int, dk: int, dv: int, 
 
 
 def chunk_bwd(q, k, v, g, beta, gate, grad_out, init_state=None, grad_final_state=None,
-              cu_seqlens=None, chunk=None, scale=1.0, workspace=None, want_grad_init=True):
+              cu_seqlens=None, chunk=None, scale=1.0, workspace=None, want_grad_init=True,
+              grads=None):
     """Chunkwise KDA backward on the GPU: gradients of a loss with respect to
     every input of ``chunk_fwd`` (prepared inputs), given ``grad_out`` (shape
     and dtype of the forward's ``out``) and optionally ``grad_final_state``
     (fp32 ``[N, H, dk, dv]``).  Returns a dict with ``q, k, v, g, beta, gate``
-    (the input dtype) and ``init_state`` (fp32, None unless ``want_grad_init``)."""
+    (the input dtype) and ``init_state`` (fp32, None unless ``want_grad_init``).
+    ``grads``: an optional dict of preallocated outputs with those keys."""
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
@@ -435,10 +437,16 @@ def chunk_bwd(q, k, v, g, beta, gate, grad_out, init_state=None, grad_final_stat
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < nbytes:
         raise ValueError(f"workspace must be a uint8 tensor of at least {nbytes} bytes on {dev}")
-    grads = {name: torch.empty_like(t) for name, t in
-             (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("gate", gate))}
-    grads["init_state"] = (torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-                           if want_grad_init else None)
+    if grads is None:
+        grads = {name: torch.empty_like(t) for name, t in
+                 (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("gate", gate))}
+        grads["init_state"] = (torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+                               if want_grad_init else None)
+    else:
+        for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("gate", gate)):
+            _need(grads[name], "grads['" + name + "']", t.shape, dt, dev)
+        if grads.get("init_state") is not None:
+            _need(grads["init_state"], "grads['init_state']", (N, H, dk, dv), torch.float32, dev)
     st = lib.kda_chunk_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate), _ptr(init_state),
         _ptr(grad_out), _ptr(grad_final_state), _ptr(grads["q"]), _ptr(grads["k"]),
