@@ -352,28 +352,44 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                 }
                 acc = mfma16(af, bfr, acc);
             }
+            if (w == 0) {
+                // lane (b, m) holds A[4 b + i2][m]
+                f32x4 a;
 #pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-                const int r = 4 * b + i2;
-                if (w == 0) {
+                for (int i2 = 0; i2 < 4; ++i2) {
+                    const int r = 4 * b + i2;
+                    a[i2] = m < r ? sm.beta[r] * acc[i2] : 0.f;
                     sm.M[r][m] = acc[i2];
-                    sm.A[r][m] = m < r ? sm.beta[r] * acc[i2] : 0.f;
-                } else {
+                }
+                // T = (I + A)^-1 by forward substitution in column form, inside the
+                // wave: lane (b, m) owns T[4 b + i2][m]; once row s is final it
+                // updates every later row, row s and A[.][s] arrive by lane shuffles
+                f32x4 t;
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2)
+                    t[i2] = (4 * b + i2 == m) ? 1.f : 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < kSub - 1; ++s2) {
+                    const float ts = __shfl(t[s2 & 3], m + 16 * (s2 >> 2));
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2) {
+                        const float ars = __shfl(a[i2], s2 + 16 * b);   // A[4 b + i2][s2]
+                        if (4 * b + i2 > s2)
+                            t[i2] -= ars * ts;
+                    }
+                }
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2)
+                    sm.Tm[4 * b + i2][m] = t[i2];
+            } else {
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2) {
+                    const int r = 4 * b + i2;
                     sm.P[r][m] = m <= r ? acc[i2] : 0.f;
                 }
             }
         }
-        // T = (I + A)^-1 by forward substitution in column form: once row s is
-        // final it updates every later row; thread (r, c) owns T[r][c]
-        if (tid < kSub * kSub)
-            sm.Tm[tid >> 4][tid & 15] = (tid >> 4) == (tid & 15) ? 1.f : 0.f;
         __syncthreads();
-        for (int s = 0; s < kSub - 1; ++s) {
-            const int r = tid >> 4, c = tid & 15;
-            if (tid < kSub * kSub && r > s)
-                sm.Tm[r][c] -= sm.A[r][s] * sm.Tm[s][c];
-            __syncthreads();
-        }
         // W = T diag(beta) Ks and U~ = T diag(beta) V on the wave's channels (fp32 MFMA)
         f32x4 wt = {0.f, 0.f, 0.f, 0.f}, u = wt;
 #pragma unroll
@@ -578,7 +594,9 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             }
         }
         __syncthreads();
-        // dT = dW (diag(beta) Ks)^T + dU (diag(beta) V)^T  (fp32 MFMA over the 128 key channels)
+        // dT = dW (diag(beta) Ks)^T + dU (diag(beta) V)^T (fp32 MFMA over the 128 key
+        // channels), then dA = strict_lower(-T^T dT T^T), all in wave 0; lanes
+        // exchange the intermediate tiles through LDS, ordered by wavefront fences
         if (w == 0) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
@@ -591,25 +609,28 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                 const int r = 4 * b + i2;
                 sm.dT[r][m] = sm.beta[m] * acc[i2] + sm.dTu[r][m];
             }
-        }
-        __syncthreads();
-        // dA = strict_lower(-T^T dT T^T)
-        if (tid < kSub * kSub) {
-            const int r = tid >> 4, c = tid & 15;
-            float acc = 0.f;
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            f32x4 x1 = {0.f, 0.f, 0.f, 0.f};       // T^T dT
 #pragma unroll
-            for (int s = 0; s < kSub; ++s)
-                acc += sm.Tm[s][r] * sm.dT[s][c];
-            sm.X[r][c] = acc;
-        }
-        __syncthreads();
-        if (tid < kSub * kSub) {
-            const int r = tid >> 4, c = tid & 15;
-            float acc = 0.f;
+            for (int kk = 0; kk < 4; ++kk) {
+                const int s2 = 4 * kk + b;
+                x1 = mfma4_f32(sm.Tm[s2][m], sm.dT[s2][m], x1);
+            }
 #pragma unroll
-            for (int x = 0; x < kSub; ++x)
-                acc += sm.X[r][x] * sm.Tm[c][x];
-            sm.dA[r][c] = c < r ? -acc : 0.f;
+            for (int i2 = 0; i2 < 4; ++i2)
+                sm.X[4 * b + i2][m] = x1[i2];
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            f32x4 x2 = {0.f, 0.f, 0.f, 0.f};       // (T^T dT) T^T
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int s2 = 4 * kk + b;
+                x2 = mfma4_f32(sm.X[m][s2], sm.Tm[m][s2], x2);
+            }
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+                const int r = 4 * b + i2;
+                sm.dA[r][m] = m < r ? -x2[i2] : 0.f;
+            }
         }
         __syncthreads();
 
