@@ -154,6 +154,7 @@ __global__ __launch_bounds__(kBpThreads) void kda_bwd_prep_bf16_kernel(
 
 // ------------------------------------------------------------ gradient kernel
 constexpr int kGThreads = 512;
+constexpr int kGWaves = kGThreads / 64;
 constexpr int kRL = kDK + 8;     // bf16 row stride of [16][128] and [128][128] tiles
 constexpr int kFL = kDK + 4;     // fp32 row stride of [16][128] tiles
 constexpr int kTL = kSub + 8;    // bf16 row stride of transposed [128][16] tiles
@@ -164,16 +165,16 @@ typedef float Sq[kSub][kSL];
 struct GradSmem {
     // small and often-read arrays first, so that their addresses fit the
     // 16-bit offsets of LDS instructions
-    Sq M, A, Tm, P, dP, dTu, dT, X, dA;
+    Sq M, Tm, P, dP, dTu, dT, X, dA;
     alignas(16) float Bref[kDK];
     alignas(16) float Ge[kDK];
     alignas(16) float dec[kDK];
     alignas(16) float dGeD[kDK];        // e^Ge rowsum(dS' S)
     alignas(16) float beta[kSub];
-    alignas(16) float dbp[kGThreads / 64][kSub];   // per-wave partial sums of dbeta
+    alignas(16) float dbp[kGWaves][kSub];   // per-wave partial sums of dbeta
     alignas(16) float G[kSub][kFL];     // cumulative log-decay within the subtile
-    alignas(16) bf16 Kin[kSub][kRL];    // k and q as given (bf16, exact); the pair
-    alignas(16) bf16 Qin[kSub][kRL];    // factors Kr, Kc, Qr are formed from them in fp32
+    alignas(16) bf16 Kin[kSub][kRL];    // k and q as given (bf16, exact); the pair factors
+    alignas(16) bf16 Qin[kSub][kRL];    // of the 16-token contractions are formed from them
     alignas(16) bf16 Ks[kSub][kRL];
     alignas(16) bf16 V[kSub][kRL];
     alignas(16) bf16 U[kSub][kRL];
@@ -181,23 +182,35 @@ struct GradSmem {
     alignas(16) bf16 dU[kSub][kRL];
     union {
         struct {                         // operands of the state products
-            alignas(16) bf16 W[kSub][kRL];
             alignas(16) bf16 Qs[kSub][kRL];
             alignas(16) bf16 Kp[kSub][kRL];
-            alignas(16) bf16 WT[kDK][kTL];
             alignas(16) bf16 QsT[kDK][kTL];
             alignas(16) bf16 KpT[kDK][kTL];
+            union {
+                struct {                 // bf16 operands of M and P
+                    alignas(16) bf16 Kr[kSub][kRL];
+                    alignas(16) bf16 Kc[kSub][kRL];
+                    alignas(16) bf16 Qr[kSub][kRL];
+                } mp;
+                struct {                 // written once T exists
+                    alignas(16) bf16 W[kSub][kRL];
+                    alignas(16) bf16 WT[kDK][kTL];
+                } w;
+            } x;
         } a;
         struct {
             alignas(16) float dW[kSub][kFL];
         } b;
-        struct {                         // for the reverse cumulative sum of dG
-            alignas(16) float dG[kSub][kFL];
-            alignas(16) float kpk[kSub][kFL];
-        } c;
     } u;
-    alignas(16) bf16 Sb[kDK][kRL];      // S on entry to the subtile, [dk][dv]
-    alignas(16) bf16 dSb[kDK][kRL];     // dS' on exit of the subtile, [dk][dv]
+    union {
+        struct {
+            alignas(16) bf16 Sb[kDK][kRL];      // S on entry to the subtile, [dk][dv]
+            alignas(16) bf16 dSb[kDK][kRL];     // dS' on exit of the subtile, [dk][dv]
+        } s;
+        // once the sums over the value channels are done: the subtile's token
+        // gradients dq, dk, dv, dg, dz, staged for row-contiguous stores
+        alignas(16) bf16 out[5][kSub][kRL];
+    } v;
 };
 static_assert(sizeof(GradSmem) <= 160 * 1024, "gradient kernel LDS fits one CU");
 
@@ -219,9 +232,42 @@ __device__ __forceinline__ bf16x4 bf4(const f32x4 &x)
     return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
 }
 
+// Zero, hidden from the optimizer (an empty asm statement that only claims to
+// modify the value; no instruction is emitted).  Adding it to the LDS base at
+// the top of every pass keeps the compiler from hoisting the several dozen
+// loop-invariant LDS addresses of a pass out of the pass loops, where they
+// would hold registers for the whole kernel and force spills; recomputing
+// them costs a few integer adds per pass.
+__device__ __forceinline__ uint32_t opaque_zero()
+{
+    uint32_t z = 0;
+    asm volatile("" : "+s"(z));
+    return z;
+}
+
+// Inputs of one subtile pass, loaded a pass ahead: row er, channels ec..ec+3
+// of k, g, v, q and beta of row er (elementwise mapping), and the gate logits
+// and dY of rows 4 b + i, channel col (the wave's mapping).
+// The 16-bit values are kept as raw bits, one per register, and converted
+// where used: packing or converting them right after the load would make the
+// compiler wait for every load in flight.
+struct GradIn {
+    bf16x4 k, g, v, q;
+    uint16_t beta;
+    uint16_t z[4], dy[4];
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t x)
+{
+    return __uint_as_float((uint32_t)x << 16);
+}
+
 // Layout of the per-wave tiles below: wave w owns key (or value) channels
 // 16 w .. 16 w + 15; lane (b, m) = (lane / 16, lane % 16) holds rows 4 b + i
 // (i = 0..3) of channel 16 w + m, the accumulator layout of the 16x16 MFMAs.
+// A chunk is worked in passes over its 16-token subtiles: forward passes
+// 0 .. nsub - 2 (states on entry to subtiles 1 .. nsub - 1), then backward
+// passes nsub - 1 .. 0.
 __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ g, const bf16 *__restrict__ beta, const bf16 *__restrict__ gate,
@@ -231,7 +277,8 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
     uint8_t *__restrict__ ws_f, const uint8_t *__restrict__ ws_b)
 {
     extern __shared__ __align__(16) uint8_t smem_raw[];
-    GradSmem &sm = *reinterpret_cast<GradSmem *>(smem_raw);
+    // re-derived from an opaque zero at the top of every pass (see opaque_zero)
+    GradSmem *smp = reinterpret_cast<GradSmem *>(smem_raw);
     const int64_t slot = (int64_t)blockIdx.x / H;
     const int h = (int)((int64_t)blockIdx.x % H);
     int n;
@@ -243,6 +290,7 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
     const int64_t tok0 = si.bos + j * kChunk;
     const int len = (int)((si.len - j * kChunk) < kChunk ? (si.len - j * kChunk) : kChunk);
     const int nsub = (len + kSub - 1) / kSub;
+    const int npass = 2 * nsub - 1;
     uint8_t *rf = ws_f + (slot * H + h) * (int64_t)kRecBytes;
     const uint8_t *rb = ws_b + ((si.slot0 + nch - 1 - j) * H + h) * (int64_t)kRecBytes;
 
@@ -253,8 +301,8 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
     const int er = tid >> 5, ec = 4 * (tid & 31);            // elementwise: row, 4 channels
 
     // The state on entry to subtile i as this wave's B fragments (perm order):
-    // subtile 0 from the forward record's SB; subtiles 1..3 are parked in the
-    // same record's first 96 KiB (LN, QH, BM, O0, no longer read once the
+    // subtile 0 from the forward record's SB; subtiles 1..nsub-2 are parked in
+    // the same record's first 96 KiB (LN, QH, BM, O0, no longer read once the
     // backward records exist), 32 KiB per subtile, each lane reading back only
     // the 16-byte slots it wrote.
     static_assert(kOffDEC >= 3 * 32768, "three parked states fit before DEC");
@@ -262,108 +310,134 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
         return i == 0 ? rf + kOffSB + w * 4096 + ks * 1024 + lane * 16
                       : rf + (i - 1) * 32768 + w * 4096 + ks * 1024 + lane * 16;
     };
+    auto pass_sub = [&](int p) { return p < nsub - 1 ? p : 2 * nsub - 2 - p; };
 
-    float zr[4], dyr[4];
-    f32x4 ut;                        // U~ of the wave's value channels
-    // Loads subtile i and forms its operands: G, the factored K / Q tiles, M,
-    // A (and P for the backward), T, W and U~.
-    auto prep_subtile = [&](int i, bool bwd) {
+    auto load_in = [&](GradIn &in, int i, bool bwd) {
         const int r0 = kSub * i;
-        {
-            const bool ev = r0 + er < len;
-            const int64_t etok = tok0 + r0 + er;
-            const int64_t eoff = (etok * H + h) * (int64_t)kDK + ec;
-            bf16x4 g4 = {}, v4 = {}, k4 = {}, q4 = {};
-            if (ev) {
-                k4 = *reinterpret_cast<const bf16x4 *>(k + eoff);
-                g4 = *reinterpret_cast<const bf16x4 *>(g + eoff);
-                v4 = *reinterpret_cast<const bf16x4 *>(v + eoff);
-                if (bwd)
-                    q4 = *reinterpret_cast<const bf16x4 *>(q + eoff);
-            }
+        const int64_t etok = tok0 + r0 + er;
+        const int64_t eoff = (etok * H + h) * (int64_t)kDK + ec;
+        in.k = in.g = in.v = in.q = bf16x4{};
+        in.beta = 0;
+        if (r0 + er < len) {
+            in.k = *reinterpret_cast<const bf16x4 *>(k + eoff);
+            in.g = *reinterpret_cast<const bf16x4 *>(g + eoff);
+            in.v = *reinterpret_cast<const bf16x4 *>(v + eoff);
+            if (bwd)
+                in.q = *reinterpret_cast<const bf16x4 *>(q + eoff);
             if ((tid & 31) == 0)
-                sm.beta[er] = ev ? (float)beta[etok * H + h] : 0.f;
-            *reinterpret_cast<f32x4 *>(&sm.G[er][ec]) =
-                f32x4{(float)g4[0], (float)g4[1], (float)g4[2], (float)g4[3]};
-            *reinterpret_cast<bf16x4 *>(&sm.V[er][ec]) = v4;
-            *reinterpret_cast<bf16x4 *>(&sm.Kin[er][ec]) = k4;
-            *reinterpret_cast<bf16x4 *>(&sm.Qin[er][ec]) = q4;
+                in.beta = reinterpret_cast<const uint16_t *>(beta)[etok * H + h];
+        }
 #pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-                const int row = r0 + 4 * b + i2;
-                zr[i2] = dyr[i2] = 0.f;
-                if (bwd && row < len) {
-                    const int64_t off = ((tok0 + row) * H + h) * (int64_t)kDV + col;
-                    zr[i2] = (float)gate[off];
-                    dyr[i2] = (float)dout[off];
-                }
+        for (int i2 = 0; i2 < 4; ++i2) {
+            const int row = r0 + 4 * b + i2;
+            in.z[i2] = in.dy[i2] = 0;
+            if (bwd && row < len) {
+                const int64_t off = ((tok0 + row) * H + h) * (int64_t)kDV + col;
+                in.z[i2] = reinterpret_cast<const uint16_t *>(gate)[off];
+                in.dy[i2] = reinterpret_cast<const uint16_t *>(dout)[off];
             }
-            __syncthreads();
-            if (tid < kDK) {
-                float acc = 0.f;
+        }
+    };
+
+    // Each pass's inputs are loaded at the end of the pass before it, ahead of
+    // that pass's global stores (loads and stores share one in-order counter, so
+    // loads issued after stores would wait for the stores).
+    GradIn cur;
+    bf16x8 sf[4];                    // state fragments of the current subtile
 #pragma unroll
-                for (int r = 0; r < kSub; ++r) {
-                    acc += sm.G[r][tid];
-                    sm.G[r][tid] = acc;
-                    if (r == kSub / 2 - 1)
-                        sm.Bref[tid] = acc;
-                }
-                sm.Ge[tid] = acc;
-                sm.dec[tid] = __expf(acc);
+    for (int ks = 0; ks < 4; ++ks)
+        sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(0, ks));
+    load_in(cur, pass_sub(0), npass == 1);
+
+    // Row-contiguous stores of the token gradients of subtile i staged in LDS
+    // (16 bytes per lane: array a, row r, channels 8 c8 ..).  Issued once the
+    // next pass's inputs have been consumed, so that no load waits behind them.
+    auto store_staged = [&](int i) {
+        bf16 *const dst[5] = {dq, dk, dv, dg, dgate};
+        const int r0 = kSub * i;
+        for (int idx = tid; idx < 5 * kSub * 16; idx += kGThreads) {
+            const int a = idx / (kSub * 16), r = (idx / 16) % kSub, c8 = idx % 16;
+            if (r0 + r < len)
+                *reinterpret_cast<bf16x8 *>(dst[a] + ((tok0 + r0 + r) * H + h) * (int64_t)kDK +
+                                            8 * c8) = lds8(&smp->v.out[a][r][8 * c8]);
+        }
+    };
+
+    // Operands of the subtile of pass p: G, factored K / Q tiles, M, A (P), T,
+    // W and U~ (returned).  A backward pass after the first also stores the
+    // previous pass's staged gradients (subtile i + 1).
+    auto prep_pass = [&](int p, bool bwd, int i) -> f32x4 {
+        if ((tid & 31) == 0)
+            smp->beta[er] = bf16_bits_to_f32(cur.beta);
+        *reinterpret_cast<f32x4 *>(&smp->G[er][ec]) =
+            f32x4{(float)cur.g[0], (float)cur.g[1], (float)cur.g[2], (float)cur.g[3]};
+        *reinterpret_cast<bf16x4 *>(&smp->V[er][ec]) = cur.v;
+        *reinterpret_cast<bf16x4 *>(&smp->Kin[er][ec]) = cur.k;
+        *reinterpret_cast<bf16x4 *>(&smp->Qin[er][ec]) = cur.q;
+        if (bwd && p > nsub - 1)
+            store_staged(i + 1);
+        __syncthreads();
+        if (tid < kDK) {
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < kSub; ++r) {
+                acc += smp->G[r][tid];
+                smp->G[r][tid] = acc;
+                if (r == kSub / 2 - 1)
+                    smp->Bref[tid] = acc;
             }
-            __syncthreads();
-            bf16x4 ks, kp, qs;
+            smp->Ge[tid] = acc;
+            smp->dec[tid] = __expf(acc);
+        }
+        __syncthreads();
+        {
+            bf16x4 ks, kp, qs, kr, kc, qr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int x = ec + e;
-                const float G = sm.G[er][x], Ge = sm.Ge[x];
-                const float eG = __expf(G), eP = __expf(Ge - G);
-                const float kv = (float)k4[e], qv = scale * (float)q4[e];
+                const float G = smp->G[er][x], d = G - smp->Bref[x], Ge = smp->Ge[x];
+                const float eG = __expf(G), eP = __expf(Ge - G), eGB = __expf(d), eBG = __expf(-d);
+                const float kv = (float)smp->Kin[er][x], qv = scale * (float)smp->Qin[er][x];
                 ks[e] = (bf16)(kv * eG);
                 kp[e] = (bf16)(kv * eP);
                 qs[e] = (bf16)(qv * eG);
-                sm.u.a.KpT[x][er] = kp[e];
+                kr[e] = (bf16)(kv * eGB);
+                kc[e] = (bf16)(kv * eBG);
+                qr[e] = (bf16)(qv * eGB);
+                smp->u.a.KpT[x][er] = kp[e];
                 if (bwd)
-                    sm.u.a.QsT[x][er] = qs[e];
+                    smp->u.a.QsT[x][er] = qs[e];
             }
-            *reinterpret_cast<bf16x4 *>(&sm.Ks[er][ec]) = ks;
-            *reinterpret_cast<bf16x4 *>(&sm.u.a.Kp[er][ec]) = kp;
-            if (bwd)
-                *reinterpret_cast<bf16x4 *>(&sm.u.a.Qs[er][ec]) = qs;
+            *reinterpret_cast<bf16x4 *>(&smp->Ks[er][ec]) = ks;
+            *reinterpret_cast<bf16x4 *>(&smp->u.a.Kp[er][ec]) = kp;
+            *reinterpret_cast<bf16x4 *>(&smp->u.a.x.mp.Kr[er][ec]) = kr;
+            *reinterpret_cast<bf16x4 *>(&smp->u.a.x.mp.Kc[er][ec]) = kc;
+            if (bwd) {
+                *reinterpret_cast<bf16x4 *>(&smp->u.a.Qs[er][ec]) = qs;
+                *reinterpret_cast<bf16x4 *>(&smp->u.a.x.mp.Qr[er][ec]) = qr;
+            }
         }
         __syncthreads();
-        // M = Kr Kc^T and A (wave 0); P = lower_incl(Qr Kc^T) (wave 1); the
-        // operands Kr = K e^{G-B}, Qr = scale Q e^{G-B}, Kc = K e^{B-G} of row m
-        // are formed here and rounded to bf16 for the product
+        // M = Kr Kc^T, A and T = (I + A)^-1 (wave 0); P = lower_incl(Qr Kc^T) (wave 1)
         if (w == 0 || (bwd && w == 1)) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const bf16 *xr = w == 0 ? &sm.Kin[m][0] : &sm.Qin[m][0];
-            const float xs = w == 0 ? 1.f : scale;
+            const bf16 *xr = w == 0 ? &smp->u.a.x.mp.Kr[m][0] : &smp->u.a.x.mp.Qr[m][0];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int x0 = 32 * ks + 8 * b;
-                const bf16x8 xv = lds8(xr + x0), kv = lds8(&sm.Kin[m][x0]);
-                bf16x8 af, bfr;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float d = sm.G[m][x0 + e] - sm.Bref[x0 + e];
-                    af[e] = (bf16)(xs * (float)xv[e] * __expf(d));
-                    bfr[e] = (bf16)((float)kv[e] * __expf(-d));
-                }
-                acc = mfma16(af, bfr, acc);
-            }
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mfma16(lds8(xr + 32 * ks + 8 * b), lds8(&smp->u.a.x.mp.Kc[m][32 * ks + 8 * b]),
+                             acc);
             if (w == 0) {
                 // lane (b, m) holds A[4 b + i2][m]
                 f32x4 a;
 #pragma unroll
                 for (int i2 = 0; i2 < 4; ++i2) {
                     const int r = 4 * b + i2;
-                    a[i2] = m < r ? sm.beta[r] * acc[i2] : 0.f;
-                    sm.M[r][m] = acc[i2];
+                    a[i2] = m < r ? smp->beta[r] * acc[i2] : 0.f;
+                    smp->M[r][m] = acc[i2];
                 }
-                // T = (I + A)^-1 by forward substitution in column form, inside the
-                // wave: lane (b, m) owns T[4 b + i2][m]; once row s is final it
-                // updates every later row, row s and A[.][s] arrive by lane shuffles
+                // forward substitution in column form inside the wave: lane (b, m)
+                // owns T[4 b + i2][m]; once row s is final it updates every later
+                // row; row s and A[.][s] arrive by lane shuffles
                 f32x4 t;
 #pragma unroll
                 for (int i2 = 0; i2 < 4; ++i2)
@@ -380,75 +454,81 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                 }
 #pragma unroll
                 for (int i2 = 0; i2 < 4; ++i2)
-                    sm.Tm[4 * b + i2][m] = t[i2];
+                    smp->Tm[4 * b + i2][m] = t[i2];
             } else {
 #pragma unroll
                 for (int i2 = 0; i2 < 4; ++i2) {
                     const int r = 4 * b + i2;
-                    sm.P[r][m] = m <= r ? acc[i2] : 0.f;
+                    smp->P[r][m] = m <= r ? acc[i2] : 0.f;
                 }
             }
         }
         __syncthreads();
         // W = T diag(beta) Ks and U~ = T diag(beta) V on the wave's channels (fp32 MFMA)
-        f32x4 wt = {0.f, 0.f, 0.f, 0.f}, u = wt;
+        f32x4 ut;
+        {
+            f32x4 wt = {0.f, 0.f, 0.f, 0.f}, u = wt;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int s = 4 * kk + b;
-            const float t = sm.Tm[m][s], bs = sm.beta[s];
-            wt = mfma4_f32(t, bs * (float)sm.Ks[s][col], wt);
-            u = mfma4_f32(t, bs * (float)sm.V[s][col], u);
-        }
-        ut = u;
+            for (int kk = 0; kk < 4; ++kk) {
+                const int s = 4 * kk + b;
+                const float t = smp->Tm[m][s], bs = smp->beta[s];
+                wt = mfma4_f32(t, bs * (float)smp->Ks[s][col], wt);
+                u = mfma4_f32(t, bs * (float)smp->V[s][col], u);
+            }
+            ut = u;
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-            sm.u.a.W[4 * b + i2][col] = (bf16)wt[i2];
-            sm.u.a.WT[col][4 * b + i2] = (bf16)wt[i2];
+            for (int i2 = 0; i2 < 4; ++i2) {
+                smp->u.a.x.w.W[4 * b + i2][col] = (bf16)wt[i2];
+                smp->u.a.x.w.WT[col][4 * b + i2] = (bf16)wt[i2];
+            }
         }
         __syncthreads();
+        return ut;
     };
 
-    // ---------------- forward sweep: states on entry to subtiles 1 .. nsub - 1
+    // ---------------- forward passes: states on entry to subtiles 1 .. nsub - 1
     if (nsub > 1) {
-        f32x4 S[8];
-        bf16x8 sf[4];
+        f32x4 S[8];                  // the fp32 state of the wave's value channels
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(0, ks));
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 S[2 * ks][i] = (float)sf[ks][i];
                 S[2 * ks + 1][i] = (float)sf[ks][4 + i];
             }
-        }
 #pragma unroll 1
-        for (int i = 0; i + 1 < nsub; ++i) {
-            prep_subtile(i, false);
+        for (int p = 0; p < nsub - 1; ++p) {
+            const int i = p;
+            smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
+            const f32x4 ut = prep_pass(p, false, i);
+            // S' = diag(e^Ge) S + Kp^T U, U = U~ - W S
             f32x4 ws = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                ws = mfma16(perm8(&sm.u.a.W[m][0], ks, b), sf[ks], ws);
+                ws = mfma16(perm8(&smp->u.a.x.w.W[m][0], ks, b), sf[ks], ws);
             const bf16x4 ub = bf4(ut - ws);
-            // S' = diag(e^Ge) S + Kp^T U
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const f32x4 dc = *reinterpret_cast<const f32x4 *>(&sm.dec[16 * t + 4 * b]);
+                const f32x4 dc = *reinterpret_cast<const f32x4 *>(&smp->dec[16 * t + 4 * b]);
                 S[t] = S[t] * dc;
-                S[t] = mfma16k16(*reinterpret_cast<const bf16x4 *>(&sm.u.a.KpT[16 * t + m][4 * b]),
+                S[t] = mfma16k16(*reinterpret_cast<const bf16x4 *>(&smp->u.a.KpT[16 * t + m][4 * b]),
                                  ub, S[t]);
             }
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < 4; ++ks)
                 sf[ks] = acc_to_frag(S[2 * ks], S[2 * ks + 1]);
-                *reinterpret_cast<bf16x8 *>(sfrag_ptr(i + 1, ks)) = sf[ks];
-            }
             __syncthreads();
+            load_in(cur, pass_sub(p + 1), p + 1 >= nsub - 1);
+            if (i + 1 < nsub - 1) {       // S_{nsub-1} stays in registers for the first backward pass
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    *reinterpret_cast<bf16x8 *>(sfrag_ptr(i + 1, ks)) = sf[ks];
+            }
         }
     }
 
-    // gradient of the state on exit of the current subtile, accumulator tiles
-    // (rows 16 t + 4 b + i of the wave's value channels)
-    f32x4 dS[8];
+    // ---------------- backward passes over the subtiles, last to first
+    f32x4 dS[8];                     // dS' of the wave's value channels, from the backward record
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 d = *reinterpret_cast<const bf16x8 *>(rb + kOffSB + w * 4096 + ks * 1024 +
@@ -459,54 +539,49 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             dS[2 * ks + 1][i] = (float)d[4 + i];
         }
     }
-
-    // ---------------- backward sweep over the subtiles, last to first
 #pragma unroll 1
-    for (int i = nsub - 1; i >= 0; --i) {
-        prep_subtile(i, true);
+    for (int p = nsub - 1; p < npass; ++p) {
+        const int i = pass_sub(p);
         const int r0 = kSub * i;
-        bf16x8 sf[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(i, ks));
-        // U = U~ - W S and O = Qs S + P U on the wave's value channels
+        smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
+        const f32x4 ut = prep_pass(p, true, i);
+        // U and O on the wave's value channels
         f32x4 ws = {0.f, 0.f, 0.f, 0.f}, o = ws;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            ws = mfma16(perm8(&sm.u.a.W[m][0], ks, b), sf[ks], ws);
-            o = mfma16(perm8(&sm.u.a.Qs[m][0], ks, b), sf[ks], o);
+            ws = mfma16(perm8(&smp->u.a.x.w.W[m][0], ks, b), sf[ks], ws);
+            o = mfma16(perm8(&smp->u.a.Qs[m][0], ks, b), sf[ks], o);
         }
         const bf16x4 ub = bf4(ut - ws);
         {
             bf16x4 pa;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                pa[e] = (bf16)sm.P[m][4 * b + e];
+                pa[e] = (bf16)smp->P[m][4 * b + e];
             o = mfma16k16(pa, ub, o);
         }
-        // gate: dZ, and dO = dY sigmoid(Z)
+        // gate: dZ (kept until the outputs are staged), and dO = dY sigmoid(Z)
         f32x4 dOv;
+        bf16x4 dz4;
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2) {
-            const int row = r0 + 4 * b + i2;
-            const float sg = sigmoidf_(zr[i2]);
-            if (row < len)
-                dgate[((tok0 + row) * H + h) * (int64_t)kDV + col] =
-                    (bf16)(dyr[i2] * o[i2] * sg * (1.f - sg));
-            dOv[i2] = dyr[i2] * sg;
+            const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-bf16_bits_to_f32(cur.z[i2])));
+            const float dyv = bf16_bits_to_f32(cur.dy[i2]);
+            dz4[i2] = (bf16)(dyv * o[i2] * sg * (1.f - sg));
+            dOv[i2] = dyv * sg;
         }
         const bf16x4 dob = bf4(dOv);
         // dU = Kp dS' + P^T dO
         f32x4 du = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            du = mfma16(perm8(&sm.u.a.Kp[m][0], ks, b), acc_to_frag(dS[2 * ks], dS[2 * ks + 1]),
+            du = mfma16(perm8(&smp->u.a.Kp[m][0], ks, b), acc_to_frag(dS[2 * ks], dS[2 * ks + 1]),
                         du);
         {
             bf16x4 pt;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                pt[e] = (bf16)sm.P[4 * b + e][m];
+                pt[e] = (bf16)smp->P[4 * b + e][m];
             du = mfma16k16(pt, dob, du);
         }
         const bf16x4 dub = bf4(du);
@@ -514,20 +589,20 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2) {
             const int r = 4 * b + i2;
-            sm.U[r][col] = ub[i2];
-            sm.dO[r][col] = dob[i2];
-            sm.dU[r][col] = dub[i2];
+            smp->U[r][col] = ub[i2];
+            smp->dO[r][col] = dob[i2];
+            smp->dU[r][col] = dub[i2];
         }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                sm.Sb[perm_row(ks, b, e)][col] = sf[ks][e];
+                smp->v.s.Sb[perm_row(ks, b, e)][col] = sf[ks][e];
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2)
-                sm.dSb[16 * t + 4 * b + i2][col] = (bf16)dS[t][i2];
+                smp->v.s.dSb[16 * t + 4 * b + i2][col] = (bf16)dS[t][i2];
         // dS on entry to the subtile: diag(e^Ge) dS' + Qs^T dO - W^T dU
         __builtin_amdgcn_sched_barrier(0);
         {
@@ -535,12 +610,12 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                                        (bf16)(-du[3])};
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const f32x4 dc = *reinterpret_cast<const f32x4 *>(&sm.dec[16 * t + 4 * b]);
+                const f32x4 dc = *reinterpret_cast<const f32x4 *>(&smp->dec[16 * t + 4 * b]);
                 f32x4 x = dS[t] * dc;
-                x = mfma16k16(*reinterpret_cast<const bf16x4 *>(&sm.u.a.QsT[16 * t + m][4 * b]),
+                x = mfma16k16(*reinterpret_cast<const bf16x4 *>(&smp->u.a.QsT[16 * t + m][4 * b]),
                               dob, x);
-                dS[t] = mfma16k16(*reinterpret_cast<const bf16x4 *>(&sm.u.a.WT[16 * t + m][4 * b]),
-                                  ndub, x);
+                dS[t] = mfma16k16(
+                    *reinterpret_cast<const bf16x4 *>(&smp->u.a.x.w.WT[16 * t + m][4 * b]), ndub, x);
             }
         }
         __syncthreads();
@@ -551,22 +626,22 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kc = 32 * ks + 8 * b;
-            const bf16x8 srow = lds8(&sm.Sb[col][kc]);
-            dkp = mfma16(lds8(&sm.U[m][kc]), lds8(&sm.dSb[col][kc]), dkp);
-            dqs = mfma16(lds8(&sm.dO[m][kc]), srow, dqs);
-            dw = mfma16(lds8(&sm.dU[m][kc]), srow, dw);
+            const bf16x8 srow = lds8(&smp->v.s.Sb[col][kc]);
+            dkp = mfma16(lds8(&smp->U[m][kc]), lds8(&smp->v.s.dSb[col][kc]), dkp);
+            dqs = mfma16(lds8(&smp->dO[m][kc]), srow, dqs);
+            dw = mfma16(lds8(&smp->dU[m][kc]), srow, dw);
         }
         dw = -dw;
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2)
-            sm.u.b.dW[4 * b + i2][col] = dw[i2];
+            smp->u.b.dW[4 * b + i2][col] = dw[i2];
         {
             // e^Ge rowsum(dS' S) of key channel col, 32 value channels per lane group
             float pr = 0.f;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const bf16x8 sv = lds8(&sm.Sb[col][32 * b + 8 * p]);
-                const bf16x8 dv8 = lds8(&sm.dSb[col][32 * b + 8 * p]);
+            for (int pp = 0; pp < 4; ++pp) {
+                const bf16x8 sv = lds8(&smp->v.s.Sb[col][32 * b + 8 * pp]);
+                const bf16x8 dv8 = lds8(&smp->v.s.dSb[col][32 * b + 8 * pp]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     pr += (float)sv[e] * (float)dv8[e];
@@ -574,13 +649,13 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             pr += __shfl_xor(pr, 16);
             pr += __shfl_xor(pr, 32);
             if (b == 0)
-                sm.dGeD[col] = sm.dec[col] * pr;
+                smp->dGeD[col] = smp->dec[col] * pr;
         }
         if (w == 0 || w == 1) {
             // wave 0: dP = lower_incl(dO U^T); wave 1: dU (diag(beta) V)^T
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const bf16 *ar = w == 0 ? &sm.dO[m][0] : &sm.dU[m][0];
-            const bf16 *br = w == 0 ? &sm.U[m][0] : &sm.V[m][0];
+            const bf16 *ar = w == 0 ? &smp->dO[m][0] : &smp->dU[m][0];
+            const bf16 *br = w == 0 ? &smp->U[m][0] : &smp->V[m][0];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 acc = mfma16(lds8(ar + 32 * ks + 8 * b), lds8(br + 32 * ks + 8 * b), acc);
@@ -588,48 +663,50 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             for (int i2 = 0; i2 < 4; ++i2) {
                 const int r = 4 * b + i2;
                 if (w == 0)
-                    sm.dP[r][m] = m <= r ? acc[i2] : 0.f;
+                    smp->dP[r][m] = m <= r ? acc[i2] : 0.f;
                 else
-                    sm.dTu[r][m] = sm.beta[m] * acc[i2];
+                    smp->dTu[r][m] = smp->beta[m] * acc[i2];
             }
         }
         __syncthreads();
-        // dT = dW (diag(beta) Ks)^T + dU (diag(beta) V)^T (fp32 MFMA over the 128 key
-        // channels), then dA = strict_lower(-T^T dT T^T), all in wave 0; lanes
-        // exchange the intermediate tiles through LDS, ordered by wavefront fences
+        // dT = dW (diag(beta) Ks)^T + dU (diag(beta) V)^T, then
+        // dA = strict_lower(-T^T dT T^T), all in wave 0; lanes exchange the
+        // intermediate tiles through LDS, ordered by wavefront fences
         if (w == 0) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int kk = 0; kk < kDK / 4; ++kk) {
-                const int x = 4 * kk + b;
-                acc = mfma4_f32(sm.u.b.dW[m][x], (float)sm.Ks[m][x], acc);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int kc = 32 * ks + 8 * b;
+                const f32x4 lo = *reinterpret_cast<const f32x4 *>(&smp->u.b.dW[m][kc]);
+                const f32x4 hi = *reinterpret_cast<const f32x4 *>(&smp->u.b.dW[m][kc + 4]);
+                acc = mfma16(acc_to_frag(lo, hi), lds8(&smp->Ks[m][kc]), acc);
             }
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2) {
                 const int r = 4 * b + i2;
-                sm.dT[r][m] = sm.beta[m] * acc[i2] + sm.dTu[r][m];
+                smp->dT[r][m] = smp->beta[m] * acc[i2] + smp->dTu[r][m];
             }
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             f32x4 x1 = {0.f, 0.f, 0.f, 0.f};       // T^T dT
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int s2 = 4 * kk + b;
-                x1 = mfma4_f32(sm.Tm[s2][m], sm.dT[s2][m], x1);
+                x1 = mfma4_f32(smp->Tm[s2][m], smp->dT[s2][m], x1);
             }
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2)
-                sm.X[4 * b + i2][m] = x1[i2];
+                smp->X[4 * b + i2][m] = x1[i2];
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             f32x4 x2 = {0.f, 0.f, 0.f, 0.f};       // (T^T dT) T^T
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int s2 = 4 * kk + b;
-                x2 = mfma4_f32(sm.X[m][s2], sm.Tm[m][s2], x2);
+                x2 = mfma4_f32(smp->X[m][s2], smp->Tm[m][s2], x2);
             }
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2) {
                 const int r = 4 * b + i2;
-                sm.dA[r][m] = m < r ? -x2[i2] : 0.f;
+                smp->dA[r][m] = m < r ? -x2[i2] : 0.f;
             }
         }
         __syncthreads();
@@ -643,94 +720,85 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int s = 4 * kk + b;
-            const float t_ms = sm.Tm[s][m];
-            const float d = sm.G[s][col] - sm.Bref[col];
+            const float t_ms = smp->Tm[s][m];
+            const float d = smp->G[s][col] - smp->Bref[col];
             const float egb = __expf(d), ebg = __expf(-d);
-            const float ks_ = (float)sm.Kin[s][col];
+            const float ks_ = (float)smp->Kin[s][col];
             const float kc_s = ks_ * ebg, kr_s = ks_ * egb;
-            const float qr_s = scale * (float)sm.Qin[s][col] * egb;
-            tdw = mfma4_f32(t_ms, sm.u.b.dW[s][col], tdw);
-            tdu = mfma4_f32(t_ms, (float)sm.dU[s][col], tdu);
-            dkc = mfma4_f32(sm.dP[s][m], qr_s, dkc);
-            dkc = mfma4_f32(sm.dA[s][m] * sm.beta[s], kr_s, dkc);
-            dkr = mfma4_f32(sm.dA[m][s], kc_s, dkr);
-            dqr = mfma4_f32(sm.dP[m][s], kc_s, dqr);
+            const float qr_s = scale * (float)smp->Qin[s][col] * egb;
+            tdw = mfma4_f32(t_ms, smp->u.b.dW[s][col], tdw);
+            tdu = mfma4_f32(t_ms, (float)smp->dU[s][col], tdu);
+            dkc = mfma4_f32(smp->dP[s][m], qr_s, dkc);
+            dkc = mfma4_f32(smp->dA[s][m] * smp->beta[s], kr_s, dkc);
+            dkr = mfma4_f32(smp->dA[m][s], kc_s, dkr);
+            dqr = mfma4_f32(smp->dP[m][s], kc_s, dqr);
         }
         // per element: row r = 4 b + i2, channel col
-        float dGv[4], kpk[4];
+        float dGv[4], kpk = 0.f;
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2) {
             const int r = 4 * b + i2;
-            const bool valid = r0 + r < len;
-            const int64_t tok = tok0 + r0 + r;
-            const int64_t off = (tok * H + h) * (int64_t)kDK + col;
-            const float kv = (float)sm.Kin[r][col];
-            const float qv = scale * (float)sm.Qin[r][col];
-            const float G = sm.G[r][col], d = G - sm.Bref[col], Ge = sm.Ge[col];
+            const float kv = (float)smp->Kin[r][col];
+            const float qv = scale * (float)smp->Qin[r][col];
+            const float G = smp->G[r][col], d = G - smp->Bref[col], Ge = smp->Ge[col];
             const float eG = __expf(G), eGB = __expf(d), eBG = __expf(-d), eP = __expf(Ge - G);
-            const float br = sm.beta[r];
+            const float br = smp->beta[r];
             const float dks = br * tdw[i2], dkr_ = br * dkr[i2];
-            if (valid) {
-                dq[off] = (bf16)(scale * (eG * dqs[i2] + eGB * dqr[i2]));
-                dk[off] = (bf16)(eG * dks + eGB * dkr_ + eBG * dkc[i2] + eP * dkp[i2]);
-                dv[off] = (bf16)(br * tdu[i2]);
-            }
+            smp->v.out[0][r][col] = (bf16)(scale * (eG * dqs[i2] + eGB * dqr[i2]));
+            smp->v.out[1][r][col] = (bf16)(eG * dks + eGB * dkr_ + eBG * dkc[i2] + eP * dkp[i2]);
+            smp->v.out[2][r][col] = (bf16)(br * tdu[i2]);
+            smp->v.out[4][r][col] = dz4[i2];
             dGv[i2] = dqs[i2] * qv * eG + dqr[i2] * qv * eGB + dks * kv * eG + dkr_ * kv * eGB -
                       dkc[i2] * kv * eBG - dkp[i2] * kv * eP;
-            kpk[i2] = dkp[i2] * kv * eP;
-            // dbeta terms of this element, summed over the wave's 16 channels
-            float pb = tdw[i2] * kv * eG + tdu[i2] * (float)sm.V[r][col];
+            kpk += dkp[i2] * kv * eP;
+            // dbeta terms of this element, summed over the wave's 16 channels; wave 0
+            // adds the dA M term of row r (its lane m is the column of A)
+            float pb = tdw[i2] * kv * eG + tdu[i2] * (float)smp->V[r][col];
+            if (w == 0)
+                pb += smp->dA[r][m] * smp->M[r][m];
             pb += __shfl_xor(pb, 8, 16);
             pb += __shfl_xor(pb, 4, 16);
             pb += __shfl_xor(pb, 2, 16);
             pb += __shfl_xor(pb, 1, 16);
             if (m == 0)
-                sm.dbp[w][r] = pb;
+                smp->dbp[w][r] = pb;
         }
-        // dG and dKp Kp of the wave's channels; the wave read only its own
-        // channels of dW, which dG overlays
+        // dg_u = sum_{r >= u} dG_r + dGe with dGe = dGeD + colsum(dKp Kp): the rows of
+        // channel col are spread over the four lane groups b
+        {
+            kpk += __shfl_xor(kpk, 16);
+            kpk += __shfl_xor(kpk, 32);
+            float suf[4];
+            suf[3] = dGv[3];
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-            sm.u.c.dG[4 * b + i2][col] = dGv[i2];
-            sm.u.c.kpk[4 * b + i2][col] = kpk[i2];
+            for (int i2 = 2; i2 >= 0; --i2)
+                suf[i2] = suf[i2 + 1] + dGv[i2];
+            const float t1 = __shfl(suf[0], m + 16 * ((b + 1) & 3));
+            const float t2 = __shfl(suf[0], m + 16 * ((b + 2) & 3));
+            const float t3 = __shfl(suf[0], m + 16 * ((b + 3) & 3));
+            const float later = (b < 3 ? t1 : 0.f) + (b < 2 ? t2 : 0.f) + (b < 1 ? t3 : 0.f);
+            const float dge = smp->dGeD[col] + kpk + later;
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2)
+                smp->v.out[3][4 * b + i2][col] = (bf16)(dge + suf[i2]);
         }
         __syncthreads();
         if (tid < kSub && r0 + tid < len) {
             float acc = 0.f;
 #pragma unroll
-            for (int x = 0; x < kGThreads / 64; ++x)
-                acc += sm.dbp[x][tid];
-#pragma unroll
-            for (int s = 0; s < kSub; ++s)
-                acc += sm.dA[tid][s] * sm.M[tid][s];
+            for (int x = 0; x < kGWaves; ++x)
+                acc += smp->dbp[x][tid];
             dbeta[(tok0 + r0 + tid) * H + h] = (bf16)acc;
         }
-        {
-            float dge = sm.dGeD[col];
+        // the next pass's inputs (tokens and state fragments of subtile i - 1)
+        if (i >= 1) {
+            load_in(cur, i - 1, true);
 #pragma unroll
-            for (int r = 0; r < kSub; ++r)
-                dge += sm.u.c.kpk[r][col];
-            // dg_u = sum_{r >= u} dG_r + dGe, for the lane's rows 4 b + i2
-            float suf[kSub];
-            float acc = dge;
-#pragma unroll
-            for (int r = kSub - 1; r >= 0; --r) {
-                acc += sm.u.c.dG[r][col];
-                suf[r] = acc;
-            }
-#pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-                const int r = 4 * b + i2;
-                float val = suf[0];
-#pragma unroll
-                for (int rr = 1; rr < kSub; ++rr)
-                    val = (r == rr) ? suf[rr] : val;
-                if (r0 + r < len)
-                    dg[((tok0 + r0 + r) * H + h) * (int64_t)kDK + col] = (bf16)val;
-            }
+            for (int ks = 0; ks < 4; ++ks)
+                sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(i - 1, ks));
         }
-        __syncthreads();
     }
+    store_staged(0);
 }
 
 }  // namespace
