@@ -323,15 +323,34 @@ def bench_backward(torch, kda, sets, ms_fwd, args):
     ms = _time(torch, call, steps, max(3, args.warmup // 2))
     print(f"[bench] backward prefill_t4096_h8: {ms:.4f} ms per call", file=sys.stderr,
           flush=True)
+    # a training step: the forward, then the backward reusing the forward's records
+    ws_fwd = torch.empty(kda.chunk_fwd_workspace_bytes(B, T, B, H, DK, DV, CHUNK,
+                                                       torch.bfloat16, False),
+                         dtype=torch.uint8, device=dev)
+    ws_half = torch.empty(ws.numel() - ws_fwd.numel(), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x0["v"])
+
+    def train_step(i):
+        x = sets[i % n_sets]
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], workspace=ws_fwd,
+                      out=out, output_final_state=False)
+        kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], dys[i % 2],
+                      workspace=ws_half, grads=grads, fwd_workspace=ws_fwd)
+
+    ms_train = _time(torch, train_step, steps, max(3, args.warmup // 2))
+    print(f"[bench] forward + backward on the forward's records: {ms_train:.4f} ms",
+          file=sys.stderr, flush=True)
     token_heads = B * T * H
     # reads q, k, v, g, z, dY (256 B each) and beta; writes dq, dk, dv, dg, dz and dbeta;
     # the fp32 dS_0
     bytes_call = (6 * 256 + 2 + 5 * 256 + 2) * token_heads + B * H * STATE_BYTES
     flops_call = 3 * flops_per_token_head() * token_heads
     t_s = ms / 1e3
-    del ws, grads
+    del ws, grads, ws_fwd, ws_half
     return {"workload": "prefill_t4096_h8", "ms_per_call": ms, "tokens_per_s": B * T / t_s,
             "ratio_to_forward": ms / ms_fwd, "steps": steps,
+            "train_step_ms": ms_train, "train_step_tokens_per_s": B * T / (ms_train / 1e3),
+            "train_step": "kda_chunk_fwd, then kda_chunk_bwd_ex on its records",
             "kernels": "forward prep + chain, backward prep, chain, gradient kernel",
             "roofline": {"bound": "hbm", "achieved": bytes_call / t_s / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -265,6 +265,24 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const void
                          kda_dtype dt, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* kda_chunk_bwd reusing the forward's work (training: forward, then backward
+ * on the same inputs).  fwd_records = the workspace of a kda_chunk_fwd (or
+ * _snapshots) call with KDA_BF16, prologue 0 and the same q, k, v, g, beta,
+ * init_state, cu_seqlens, sizes and scale, left untouched since that call;
+ * fwd_records_bytes its size.  The backward then skips recomputing every
+ * chunk's entry state, and needs only kda_chunk_fwd_workspace_bytes(...) bytes
+ * of `workspace`.  The records are consumed: their contents are undefined
+ * afterwards.  fwd_records NULL = exactly kda_chunk_bwd; fwd_records with
+ * KDA_F32 returns KDA_ERR_UNSUPPORTED (that path keeps no records). */
+kda_status kda_chunk_bwd_ex(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const void *gate, const float *init_state,
+                            const void *grad_out, const float *grad_final_state, void *grad_q,
+                            void *grad_k, void *grad_v, void *grad_g, void *grad_beta,
+                            void *grad_gate, float *grad_init_state, const int32_t *cu_seqlens,
+                            int B, int T, int N, int H, int dk, int dv, int chunk, float scale,
+                            kda_dtype dt, void *fwd_records, size_t fwd_records_bytes,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

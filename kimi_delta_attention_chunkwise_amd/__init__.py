@@ -84,6 +84,9 @@ _SIGNATURES = {
     "kda_chunk_bwd_workspace_bytes": ([ctypes.c_int] * 9, ctypes.c_size_t),
     "kda_chunk_bwd": ([ctypes.c_void_p] * 17 + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "kda_chunk_bwd_ex": ([ctypes.c_void_p] * 17 + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
+                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                         ctypes.c_void_p], ctypes.c_int),
     "kda_decode_step": ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
                         ctypes.c_void_p], ctypes.c_int),
 }
@@ -396,13 +399,15 @@ def chunk_bwd_workspace_bytes(B: int, T: int, N: int, H: int, dk: int, dv: int, 
 
 def chunk_bwd(q, k, v, g, beta, gate, grad_out, init_state=None, grad_final_state=None,
               cu_seqlens=None, chunk=None, scale=1.0, workspace=None, want_grad_init=True,
-              grads=None):
+              grads=None, fwd_workspace=None):
     """Chunkwise KDA backward on the GPU: gradients of a loss with respect to
     every input of ``chunk_fwd`` (prepared inputs), given ``grad_out`` (shape
     and dtype of the forward's ``out``) and optionally ``grad_final_state``
     (fp32 ``[N, H, dk, dv]``).  Returns a dict with ``q, k, v, g, beta, gate``
     (the input dtype) and ``init_state`` (fp32, None unless ``want_grad_init``).
-    ``grads``: an optional dict of preallocated outputs with those keys."""
+    ``grads``: an optional dict of preallocated outputs with those keys.
+    ``fwd_workspace``: the workspace of a ``chunk_fwd`` call on the same inputs
+    (bf16, no prologue), untouched since; its records are reused and consumed."""
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
@@ -433,6 +438,11 @@ def chunk_bwd(q, k, v, g, beta, gate, grad_out, init_state=None, grad_final_stat
     if grad_final_state is not None:
         _need(grad_final_state, "grad_final_state", (N, H, dk, dv), torch.float32, dev)
     nbytes = chunk_bwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, cu_seqlens is not None)
+    if fwd_workspace is not None:
+        if fwd_workspace.device != dev or fwd_workspace.dtype != torch.uint8:
+            raise ValueError(f"fwd_workspace must be a uint8 tensor on {dev}")
+        nbytes -= chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt,
+                                            cu_seqlens is not None)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < nbytes:
@@ -447,11 +457,12 @@ def chunk_bwd(q, k, v, g, beta, gate, grad_out, init_state=None, grad_final_stat
             _need(grads[name], "grads['" + name + "']", t.shape, dt, dev)
         if grads.get("init_state") is not None:
             _need(grads["init_state"], "grads['init_state']", (N, H, dk, dv), torch.float32, dev)
-    st = lib.kda_chunk_bwd(
+    st = lib.kda_chunk_bwd_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate), _ptr(init_state),
         _ptr(grad_out), _ptr(grad_final_state), _ptr(grads["q"]), _ptr(grads["k"]),
         _ptr(grads["v"]), _ptr(grads["g"]), _ptr(grads["beta"]), _ptr(grads["gate"]),
         _ptr(grads["init_state"]), _ptr(cu_seqlens), B, T, N, H, dk, dv, chunk, float(scale),
-        code, _ptr(workspace), workspace.numel(), _stream_ptr(dev))
+        code, _ptr(fwd_workspace), 0 if fwd_workspace is None else fwd_workspace.numel(),
+        _ptr(workspace), workspace.numel(), _stream_ptr(dev))
     _check(st)
     return grads

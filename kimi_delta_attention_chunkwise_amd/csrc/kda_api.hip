@@ -243,18 +243,20 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
     return 2 * units * kda::kRecBytes;   // forward and backward records
 }
 
-kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
-                         const void *beta, const void *gate, const float *init_state,
-                         const void *grad_out, const float *grad_final_state, void *grad_q,
-                         void *grad_k, void *grad_v, void *grad_g, void *grad_beta,
-                         void *grad_gate, float *grad_init_state, const int32_t *cu_seqlens,
-                         int B, int T, int N, int H, int dk, int dv, int chunk, float scale,
-                         kda_dtype dt, void *workspace, size_t workspace_bytes,
-                         hipStream_t stream)
+kda_status kda_chunk_bwd_ex(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const void *gate, const float *init_state,
+                            const void *grad_out, const float *grad_final_state, void *grad_q,
+                            void *grad_k, void *grad_v, void *grad_g, void *grad_beta,
+                            void *grad_gate, float *grad_init_state, const int32_t *cu_seqlens,
+                            int B, int T, int N, int H, int dk, int dv, int chunk, float scale,
+                            kda_dtype dt, void *fwd_records, size_t fwd_records_bytes,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (!valid_dtype(dt))
         return KDA_ERR_BAD_DTYPE;
     if (!bwd_supported(dt, dk, dv, chunk))
+        return KDA_ERR_UNSUPPORTED;
+    if (fwd_records && dt != KDA_BF16)
         return KDA_ERR_UNSUPPORTED;
     const int varlen = cu_seqlens != nullptr;
     if (B < 1 || T < 0 || N < 0 || H < 1)
@@ -265,7 +267,14 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const void
     if (has_tokens && (!q || !k || !v || !g || !beta || !gate || !grad_out || !grad_q ||
                        !grad_k || !grad_v || !grad_g || !grad_beta || !grad_gate))
         return KDA_ERR_NULL_POINTER;
-    const size_t need = kda_chunk_bwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
+    size_t need = kda_chunk_bwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
+    if (fwd_records) {
+        // the forward records stand in for the first of the two record arrays
+        const size_t rec = kda_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
+        if (fwd_records_bytes < rec)
+            return KDA_ERR_WORKSPACE_TOO_SMALL;
+        need -= rec;
+    }
     if (need > 0 && !workspace)
         return KDA_ERR_NULL_POINTER;
     if (workspace_bytes < need)
@@ -283,13 +292,28 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const void
             (const kda::bf16 *)grad_out, grad_final_state, (kda::bf16 *)grad_q,
             (kda::bf16 *)grad_k, (kda::bf16 *)grad_v, (kda::bf16 *)grad_g,
             (kda::bf16 *)grad_beta, (kda::bf16 *)grad_gate, grad_init_state, cu_seqlens, N, T,
-            H, chunk_slots(B, T, N, chunk, varlen), scale, workspace, stream));
+            H, chunk_slots(B, T, N, chunk, varlen), scale, fwd_records, workspace, stream));
     return from_hip(kda::launch_chunk_bwd_f32(
         (const float *)q, (const float *)k, (const float *)v, (const float *)g,
         (const float *)beta, (const float *)gate, init_state, (const float *)grad_out,
         grad_final_state, (float *)grad_q, (float *)grad_k, (float *)grad_v, (float *)grad_g,
         (float *)grad_beta, (float *)grad_gate, grad_init_state, cu_seqlens, N, T, H, scale,
         (float *)workspace, stream));
+}
+
+kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, const void *gate, const float *init_state,
+                         const void *grad_out, const float *grad_final_state, void *grad_q,
+                         void *grad_k, void *grad_v, void *grad_g, void *grad_beta,
+                         void *grad_gate, float *grad_init_state, const int32_t *cu_seqlens,
+                         int B, int T, int N, int H, int dk, int dv, int chunk, float scale,
+                         kda_dtype dt, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream)
+{
+    return kda_chunk_bwd_ex(q, k, v, g, beta, gate, init_state, grad_out, grad_final_state,
+                            grad_q, grad_k, grad_v, grad_g, grad_beta, grad_gate, grad_init_state,
+                            cu_seqlens, B, T, N, H, dk, dv, chunk, scale, dt, nullptr, 0,
+                            workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *g,

@@ -970,22 +970,30 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     return hipSuccess;
 }
 
-// Backward: forward records (prep + chain give every chunk's entry state),
-// backward records in reverse chunk order (-L^T, Q^^T dO, dec), the same chain
-// over them from dS_final (the state gradient on exit of every chunk, and
-// dS_0), then the per-chunk gradients.
+// Backward: forward records (prep + chain give every chunk's entry state, or
+// the caller passes those of its kda_chunk_fwd call), backward records in
+// reverse chunk order (-L^T, Q^^T dO, dec), the same chain over them from
+// dS_final (the state gradient on exit of every chunk, and dS_0), then the
+// per-chunk gradients.
 hipError_t launch_chunk_bwd_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                                  const bf16 *beta, const bf16 *gate, const float *init,
                                  const bf16 *dout, const float *dfinal, bf16 *dq, bf16 *dk,
                                  bf16 *dv, bf16 *dg, bf16 *dbeta, bf16 *dgate, float *dinit,
                                  const int32_t *cu, int N, int T, int H, int64_t n_slots,
-                                 float scale, void *workspace, hipStream_t stream)
+                                 float scale, void *fwd_records, void *workspace,
+                                 hipStream_t stream)
 {
-    uint8_t *ws_f = static_cast<uint8_t *>(workspace);
-    uint8_t *ws_b = ws_f + (size_t)n_slots * (size_t)H * kRecBytes;
-    hipError_t e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, 0u, ws_f, stream);
-    if (e == hipSuccess)
-        e = launch_chain(init, nullptr, nullptr, 0, cu, N, T, H, ws_f, stream);
+    const size_t rec_bytes = (size_t)n_slots * (size_t)H * kRecBytes;
+    uint8_t *ws_f = fwd_records ? static_cast<uint8_t *>(fwd_records)
+                                : static_cast<uint8_t *>(workspace);
+    uint8_t *ws_b = fwd_records ? static_cast<uint8_t *>(workspace)
+                                : static_cast<uint8_t *>(workspace) + rec_bytes;
+    hipError_t e = hipSuccess;
+    if (!fwd_records) {
+        e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, 0u, ws_f, stream);
+        if (e == hipSuccess)
+            e = launch_chain(init, nullptr, nullptr, 0, cu, N, T, H, ws_f, stream);
+    }
     if (e == hipSuccess)
         e = launch_bwd_prep_bf16(gate, dout, cu, N, T, H, n_slots, ws_f, ws_b, stream);
     if (e == hipSuccess)

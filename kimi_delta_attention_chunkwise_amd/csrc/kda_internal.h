@@ -242,13 +242,15 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
                              float scale, unsigned pro, void *workspace, hipStream_t stream);
 
 // Chunkwise backward, bf16, dk = dv = 128, 64-token chunks; the workspace
-// holds two record arrays of n_slots * H records each (forward, backward).
+// holds two record arrays of n_slots * H records each (forward, backward), or
+// only the backward one when fwd_records holds a forward call's records.
 hipError_t launch_chunk_bwd_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                                  const bf16 *beta, const bf16 *gate, const float *init,
                                  const bf16 *dout, const float *dfinal, bf16 *dq, bf16 *dk,
                                  bf16 *dv, bf16 *dg, bf16 *dbeta, bf16 *dgate, float *dinit,
                                  const int32_t *cu, int N, int T, int H, int64_t n_slots,
-                                 float scale, void *workspace, hipStream_t stream);
+                                 float scale, void *fwd_records, void *workspace,
+                                 hipStream_t stream);
 
 // Backward records: for chunk j of a sequence with nch chunks, record
 // slot0 + nch - 1 - j of ws_b gets LN = -L^T, BM = Q^^T dO (dO = dY sigmoid(Z))

@@ -37,6 +37,7 @@ def test_header_declares_the_entry_points():
               "kda_status_str", "kda_chunk_fwd_snapshots", "kda_snapshot_slots",
               "kda_chunk_fwd_ex", "kda_decode_step_ex", "kda_decode_verify",
               "kda_decode_commit", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
+              "kda_chunk_bwd_ex",
               "kda_chunk_bwd_supported"):
         assert n in names
 
@@ -254,6 +255,18 @@ def test_chunk_bwd_sizes_and_argument_checks(lib):
     assert call(ws=None) == NULLP
     assert call(ws_bytes=2 * 4 * 1024 - 1) == WS
     assert call(cu=1, N=0, T=0, q=None, gq=None) == OK
+
+    def call_ex(fwd, fwd_bytes, ws_bytes, dt=1, d=128, chunk=64):
+        return lib.kda_chunk_bwd_ex(p(1), p(1), p(1), p(1), p(1), p(1), None, p(1), None,
+                                    p(1), p(1), p(1), p(1), p(1), p(1), None, None, 1, 64, 1, 2,
+                                    d, d, chunk, 1.0, dt, p(fwd), fwd_bytes, p(1), ws_bytes, None)
+    # (only calls that fail validation: nothing may launch with these fake pointers)
+    # H = 2: a record array is 2 REC; the backward alone needs two arrays, with the
+    # forward's records one array
+    assert call_ex(None, 0, 4 * REC - 1) == WS
+    assert call_ex(1, 2 * REC - 1, 10 ** 9) == WS           # forward records too small
+    assert call_ex(1, 2 * REC, 2 * REC - 1) == WS           # below one record array
+    assert call_ex(1, 10 ** 9, 10 ** 9, dt=0, d=16, chunk=16) == UNSUP   # fp32 keeps no records
 
 
 def test_python_binding_refuses_cpu_tensors(lib):

@@ -150,3 +150,29 @@ def test_bf16_backward_prefill_t4096_h8(dev):
     x = W.prefill_inputs(w, seed=0)
     dy, dfin = cotangents(x, 900, 0.05)
     run_bf16_case(dev, x, dy, dfin, 1.0, "prefill_t4096_h8")
+
+
+def test_bf16_backward_reusing_forward_records(dev):
+    """kda_chunk_bwd_ex on the workspace of the forward call: the same gradients
+    bit for bit as the backward alone, and within tolerance of the oracle."""
+    say("backward bf16 reusing the forward's records (varlen, init state)")
+    x = small_inputs(torch.bfloat16, 1, 0, 2, 128, 128, 36, lengths=[70, 0, 200, 64, 5],
+                     init_std=0.02)
+    dy, dfin = cotangents(x, 901, 0.05)
+    xd = to(x, dev)
+    ws_f = torch.empty(kda.chunk_fwd_workspace_bytes(1, int(x["q"].shape[1]), 5, 2, 128, 128, 64,
+                                                     torch.bfloat16, True),
+                       dtype=torch.uint8, device=dev)
+    kda.chunk_fwd(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["z"],
+                  init_state=xd["init_state"], cu_seqlens=xd["cu_seqlens"], workspace=ws_f,
+                  scale=0.5)
+    kw = dict(init_state=xd["init_state"], grad_final_state=dfin.to(dev),
+              cu_seqlens=xd["cu_seqlens"], scale=0.5)
+    reused = kda.chunk_bwd(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["z"], dy.to(dev),
+                           fwd_workspace=ws_f, **kw)
+    alone = kda.chunk_bwd(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["z"], dy.to(dev),
+                          **kw)
+    torch.cuda.synchronize()
+    for key in ("q", "k", "v", "g", "beta", "gate", "init_state"):
+        assert torch.equal(reused[key], alone[key]), f"d{key} differs with reused records"
+    run_bf16_case(dev, x, dy, dfin, 0.5, "reused records")
