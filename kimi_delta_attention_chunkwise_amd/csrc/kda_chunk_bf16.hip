@@ -30,19 +30,21 @@
 // column factor is formed as e^{B_j - G_s} e^{B_i - B_j}.
 //
 // Three kernels, in stream order:
-//   prep   (512 threads per (chunk slot, head); all chunks in parallel):
-//          G, A and P (bf16 MFMA), T (fp32 substitution and fp32 MFMA), W and
-//          U~ (MFMA), then L, Bm, Q^ and O0 (MFMA) written to the chunk's
-//          workspace record as the later kernels' operand fragments.
-//   chain  (320 threads per (sequence, head, 16-wide value block)): walks the
-//          chunks in order and carries only the state.  Compute wave w keeps
-//          rows 32 w .. 32 w + 31 of the fp32 state slice in its accumulators
-//          and computes those rows of S' = dec S + Bm - L S; the four compute
-//          waves exchange the new state as bf16 MFMA fragments through LDS,
-//          one barrier per chunk, with the operands of the next chunks
-//          prefetched into registers.  A fifth wave copies each chunk's entry
-//          state fragments from LDS to the record, so no wave has both loads
-//          and stores in flight.
+//   prep   (persistent, 512 threads per CU, over the (chunk slot, head)
+//          tasks; all chunks in parallel): G, A and P (bf16 MFMA), T (fp32
+//          substitution and fp32 MFMA), W and U~ (MFMA), then L, Bm, Q^ and O0
+//          (MFMA) written to the chunk's workspace record as the later kernels'
+//          operand fragments.
+//   chain  (640 threads per (sequence, head, 16-wide value block)): walks the
+//          chunks in order and carries only the state.  Compute wave w (of 8)
+//          keeps rows 16 w .. 16 w + 15 of the fp32 state slice in its
+//          accumulators and computes those rows of S' = dec S + Bm - L S; the
+//          compute waves exchange the new state as bf16 MFMA fragments through
+//          LDS, one barrier per chunk, with their rows of L for the next chunks
+//          prefetched into registers.  A side wave loads Bm and the decay of
+//          the chunks ahead into LDS, and a store wave copies each chunk's entry
+//          state fragments from LDS to the record, so no wave has both loads and
+//          stores in flight.
 //   output (256 threads per (chunk slot, head)): O = Q^ S + O0 from the
 //          record, gated by sigmoid(z), rounded to bf16; all chunks in parallel.
 #include "kda_internal.h"
