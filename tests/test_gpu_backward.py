@@ -176,3 +176,13 @@ def test_bf16_backward_reusing_forward_records(dev):
     for key in ("q", "k", "v", "g", "beta", "gate", "init_state"):
         assert torch.equal(reused[key], alone[key]), f"d{key} differs with reused records"
     run_bf16_case(dev, x, dy, dfin, 0.5, "reused records")
+
+
+def test_bf16_backward_varlen_4seq_h32_full(dev):
+    """The packed varlen workload at full size (4 sequences, lengths up to 32K, H=32,
+    non-zero initial state), every gradient against the oracle's backward."""
+    w = W.WORKLOADS["varlen_4seq_h32"]
+    say(f"backward bf16 varlen_4seq_h32: lengths {W.varlen_lengths(w, 0)}")
+    x = W.prefill_inputs(w, seed=0)
+    dy, dfin = cotangents(x, 902, 0.02)
+    run_bf16_case(dev, x, dy, dfin, 1.0, "varlen_4seq_h32")
