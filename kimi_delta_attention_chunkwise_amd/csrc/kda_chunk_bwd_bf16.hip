@@ -172,6 +172,7 @@ struct GradSmem {
     alignas(16) float dGeD[kDK];        // e^Ge rowsum(dS' S)
     alignas(16) float beta[kSub];
     alignas(16) float dbp[kGWaves][kSub];   // per-wave partial sums of dbeta
+    alignas(16) bf16 dbst[kSub];        // dbeta of the subtile, staged for its store
     alignas(16) float G[kSub][kFL];     // cumulative log-decay within the subtile
     alignas(16) bf16 Kin[kSub][kRL];    // k and q as given (bf16, exact); the pair factors
     alignas(16) bf16 Qin[kSub][kRL];    // of the 16-token contractions are formed from them
@@ -312,7 +313,8 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
     };
     auto pass_sub = [&](int p) { return p < nsub - 1 ? p : 2 * nsub - 2 - p; };
 
-    auto load_in = [&](GradIn &in, int i, bool bwd) {
+    // token inputs of subtile i (q only for a backward pass)
+    auto load_tok = [&](GradIn &in, int i, bool bwd) {
         const int r0 = kSub * i;
         const int64_t etok = tok0 + r0 + er;
         const int64_t eoff = (etok * H + h) * (int64_t)kDK + ec;
@@ -327,31 +329,38 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             if ((tid & 31) == 0)
                 in.beta = reinterpret_cast<const uint16_t *>(beta)[etok * H + h];
         }
+    };
+    // gate and output gradient of subtile i on the lane's value channel.  A row
+    // past the end reads the last row of the chunk (always in range) and is
+    // masked where it is used: branch-free loads, so that nothing that depends
+    // on a loaded value is scheduled next to its load.
+    auto load_gate = [&](GradIn &in, int i) {
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2) {
-            const int row = r0 + 4 * b + i2;
-            in.z[i2] = in.dy[i2] = 0;
-            if (bwd && row < len) {
-                const int64_t off = ((tok0 + row) * H + h) * (int64_t)kDV + col;
-                in.z[i2] = reinterpret_cast<const uint16_t *>(gate)[off];
-                in.dy[i2] = reinterpret_cast<const uint16_t *>(dout)[off];
-            }
+            const int row = min(kSub * i + 4 * b + i2, len - 1);
+            const int64_t off = ((tok0 + row) * H + h) * (int64_t)kDV + col;
+            in.z[i2] = reinterpret_cast<const uint16_t *>(gate)[off];
+            in.dy[i2] = reinterpret_cast<const uint16_t *>(dout)[off];
         }
     };
 
-    // Each pass's inputs are loaded at the end of the pass before it, ahead of
-    // that pass's global stores (loads and stores share one in-order counter, so
-    // loads issued after stores would wait for the stores).
+    // A pass's token inputs are loaded one pass ahead, as soon as the pass
+    // before it has copied its own into LDS; a backward pass's gate, output
+    // gradient and state fragments (first needed after the operand set-up) right
+    // after that, at the top of the pass itself.  All global stores come after
+    // these loads and none at the end of a pass: loads and stores share one
+    // in-order counter, so a wait for a load also waits for every store issued
+    // before it.
     GradIn cur;
     bf16x8 sf[4];                    // state fragments of the current subtile
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
         sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(0, ks));
-    load_in(cur, pass_sub(0), npass == 1);
+    load_tok(cur, pass_sub(0), npass == 1);
 
     // Row-contiguous stores of the token gradients of subtile i staged in LDS
-    // (16 bytes per lane: array a, row r, channels 8 c8 ..).  Issued once the
-    // next pass's inputs have been consumed, so that no load waits behind them.
+    // (16 bytes per lane: array a, row r, channels 8 c8 ..) and of its dbeta.
+    // Issued after the next pass's loads, so that no load waits behind them.
     auto store_staged = [&](int i) {
         bf16 *const dst[5] = {dq, dk, dv, dg, dgate};
         const int r0 = kSub * i;
@@ -361,11 +370,15 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                 *reinterpret_cast<bf16x8 *>(dst[a] + ((tok0 + r0 + r) * H + h) * (int64_t)kDK +
                                             8 * c8) = lds8(&smp->v.out[a][r][8 * c8]);
         }
+        if (tid < kSub && r0 + tid < len)
+            dbeta[(tok0 + r0 + tid) * H + h] = smp->dbst[tid];
     };
 
     // Operands of the subtile of pass p: G, factored K / Q tiles, M, A (P), T,
-    // W and U~ (returned).  A backward pass after the first also stores the
-    // previous pass's staged gradients (subtile i + 1).
+    // W and U~ (returned).  Issues the next pass's token loads once this pass's
+    // tokens are in LDS, then a backward pass's own gate and state loads; a
+    // backward pass after the first then stores the previous pass's staged
+    // gradients (subtile i + 1).
     auto prep_pass = [&](int p, bool bwd, int i) -> f32x4 {
         if ((tid & 31) == 0)
             smp->beta[er] = bf16_bits_to_f32(cur.beta);
@@ -374,8 +387,17 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
         *reinterpret_cast<bf16x4 *>(&smp->V[er][ec]) = cur.v;
         *reinterpret_cast<bf16x4 *>(&smp->Kin[er][ec]) = cur.k;
         *reinterpret_cast<bf16x4 *>(&smp->Qin[er][ec]) = cur.q;
-        if (bwd && p > nsub - 1)
-            store_staged(i + 1);
+        if (p + 1 < npass)
+            load_tok(cur, pass_sub(p + 1), p + 1 >= nsub - 1);
+        if (bwd) {
+            load_gate(cur, i);
+            if (p > nsub - 1) {      // the first backward pass has S_{nsub-1} in registers
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(i, ks));
+                store_staged(i + 1);
+            }
+        }
         __syncthreads();
         if (tid < kDK) {
             float acc = 0.f;
@@ -518,7 +540,6 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             for (int ks = 0; ks < 4; ++ks)
                 sf[ks] = acc_to_frag(S[2 * ks], S[2 * ks + 1]);
             __syncthreads();
-            load_in(cur, pass_sub(p + 1), p + 1 >= nsub - 1);
             if (i + 1 < nsub - 1) {       // S_{nsub-1} stays in registers for the first backward pass
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
@@ -566,7 +587,7 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2) {
             const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-bf16_bits_to_f32(cur.z[i2])));
-            const float dyv = bf16_bits_to_f32(cur.dy[i2]);
+            const float dyv = r0 + 4 * b + i2 < len ? bf16_bits_to_f32(cur.dy[i2]) : 0.f;
             dz4[i2] = (bf16)(dyv * o[i2] * sg * (1.f - sg));
             dOv[i2] = dyv * sg;
         }
@@ -733,8 +754,9 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             dkr = mfma4_f32(smp->dA[m][s], kc_s, dkr);
             dqr = mfma4_f32(smp->dP[m][s], kc_s, dqr);
         }
-        // per element: row r = 4 b + i2, channel col
-        float dGv[4], kpk = 0.f;
+        // per element: row r = 4 b + i2, channel col (all reads first, stores last)
+        float dGv[4], pb[4], kpk = 0.f;
+        bf16x4 oq, ok, ov;
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2) {
             const int r = 4 * b + i2;
@@ -744,24 +766,38 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             const float eG = __expf(G), eGB = __expf(d), eBG = __expf(-d), eP = __expf(Ge - G);
             const float br = smp->beta[r];
             const float dks = br * tdw[i2], dkr_ = br * dkr[i2];
-            smp->v.out[0][r][col] = (bf16)(scale * (eG * dqs[i2] + eGB * dqr[i2]));
-            smp->v.out[1][r][col] = (bf16)(eG * dks + eGB * dkr_ + eBG * dkc[i2] + eP * dkp[i2]);
-            smp->v.out[2][r][col] = (bf16)(br * tdu[i2]);
-            smp->v.out[4][r][col] = dz4[i2];
+            oq[i2] = (bf16)(scale * (eG * dqs[i2] + eGB * dqr[i2]));
+            ok[i2] = (bf16)(eG * dks + eGB * dkr_ + eBG * dkc[i2] + eP * dkp[i2]);
+            ov[i2] = (bf16)(br * tdu[i2]);
             dGv[i2] = dqs[i2] * qv * eG + dqr[i2] * qv * eGB + dks * kv * eG + dkr_ * kv * eGB -
                       dkc[i2] * kv * eBG - dkp[i2] * kv * eP;
             kpk += dkp[i2] * kv * eP;
-            // dbeta terms of this element, summed over the wave's 16 channels; wave 0
-            // adds the dA M term of row r (its lane m is the column of A)
-            float pb = tdw[i2] * kv * eG + tdu[i2] * (float)smp->V[r][col];
+            // dbeta terms of this element; wave 0 adds the dA M term of row r (its lane
+            // m is the column of A)
+            pb[i2] = tdw[i2] * kv * eG + tdu[i2] * (float)smp->V[r][col];
             if (w == 0)
-                pb += smp->dA[r][m] * smp->M[r][m];
-            pb += __shfl_xor(pb, 8, 16);
-            pb += __shfl_xor(pb, 4, 16);
-            pb += __shfl_xor(pb, 2, 16);
-            pb += __shfl_xor(pb, 1, 16);
-            if (m == 0)
-                smp->dbp[w][r] = pb;
+                pb[i2] += smp->dA[r][m] * smp->M[r][m];
+        }
+        // sums of pb over the wave's 16 channels for the lane group's four rows, as
+        // a butterfly that also spreads the rows: afterwards lanes with m % 4 == 0
+        // hold the sum of row 4 b + 2 ((m >> 3) & 1) + ((m >> 2) & 1)
+        {
+            const bool hi = (m & 8) != 0, mid = (m & 4) != 0;
+            const float a0 = (hi ? pb[2] : pb[0]) + __shfl_xor(hi ? pb[0] : pb[2], 8);
+            const float a1 = (hi ? pb[3] : pb[1]) + __shfl_xor(hi ? pb[1] : pb[3], 8);
+            float c = (mid ? a1 : a0) + __shfl_xor(mid ? a0 : a1, 4);
+            c += __shfl_xor(c, 2);
+            c += __shfl_xor(c, 1);
+            if ((m & 3) == 0)
+                smp->dbp[w][4 * b + 2 * (hi ? 1 : 0) + (mid ? 1 : 0)] = c;
+        }
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+            const int r = 4 * b + i2;
+            smp->v.out[0][r][col] = oq[i2];
+            smp->v.out[1][r][col] = ok[i2];
+            smp->v.out[2][r][col] = ov[i2];
+            smp->v.out[4][r][col] = dz4[i2];
         }
         // dg_u = sum_{r >= u} dG_r + dGe with dGe = dGeD + colsum(dKp Kp): the rows of
         // channel col are spread over the four lane groups b
@@ -783,19 +819,12 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                 smp->v.out[3][4 * b + i2][col] = (bf16)(dge + suf[i2]);
         }
         __syncthreads();
-        if (tid < kSub && r0 + tid < len) {
+        if (tid < kSub) {
             float acc = 0.f;
 #pragma unroll
             for (int x = 0; x < kGWaves; ++x)
                 acc += smp->dbp[x][tid];
-            dbeta[(tok0 + r0 + tid) * H + h] = (bf16)acc;
-        }
-        // the next pass's inputs (tokens and state fragments of subtile i - 1)
-        if (i >= 1) {
-            load_in(cur, i - 1, true);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(i - 1, ks));
+            smp->dbst[tid] = (bf16)acc;
         }
     }
     store_staged(0);
