@@ -162,6 +162,16 @@ constexpr int kSL = kSub + 1;    // fp32 row stride of 16 x 16 matrices
 
 typedef float Sq[kSub][kSL];
 
+// Column of element [x][r] of a transposed [128][16] tile: the four groups of
+// four tokens of a row are XOR-permuted by bits 3..4 of the channel x.  A
+// group stays contiguous for the 8-byte MFMA operand reads, while the
+// transposed 2-byte writes of 32 consecutive-by-4 channels spread over eight
+// banks instead of two.
+__device__ __forceinline__ int tcol(int x, int r)
+{
+    return 4 * ((r >> 2) ^ ((x >> 3) & 3)) + (r & 3);
+}
+
 struct GradSmem {
     // small and often-read arrays first, so that their addresses fit the
     // 16-bit offsets of LDS instructions
@@ -426,9 +436,9 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                 kr[e] = (bf16)(kv * eGB);
                 kc[e] = (bf16)(kv * eBG);
                 qr[e] = (bf16)(qv * eGB);
-                smp->u.a.KpT[x][er] = kp[e];
+                smp->u.a.KpT[x][tcol(x, er)] = kp[e];
                 if (bwd)
-                    smp->u.a.QsT[x][er] = qs[e];
+                    smp->u.a.QsT[x][tcol(x, er)] = qs[e];
             }
             *reinterpret_cast<bf16x4 *>(&smp->Ks[er][ec]) = ks;
             *reinterpret_cast<bf16x4 *>(&smp->u.a.Kp[er][ec]) = kp;
@@ -501,7 +511,7 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2) {
                 smp->u.a.x.w.W[4 * b + i2][col] = (bf16)wt[i2];
-                smp->u.a.x.w.WT[col][4 * b + i2] = (bf16)wt[i2];
+                smp->u.a.x.w.WT[col][tcol(col, 4 * b + i2)] = (bf16)wt[i2];
             }
         }
         __syncthreads();
@@ -533,7 +543,8 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             for (int t = 0; t < 8; ++t) {
                 const f32x4 dc = *reinterpret_cast<const f32x4 *>(&smp->dec[16 * t + 4 * b]);
                 S[t] = S[t] * dc;
-                S[t] = mfma16k16(*reinterpret_cast<const bf16x4 *>(&smp->u.a.KpT[16 * t + m][4 * b]),
+                S[t] = mfma16k16(*reinterpret_cast<const bf16x4 *>(
+                                     &smp->u.a.KpT[16 * t + m][tcol(16 * t + m, 4 * b)]),
                                  ub, S[t]);
             }
 #pragma unroll
@@ -633,10 +644,12 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             for (int t = 0; t < 8; ++t) {
                 const f32x4 dc = *reinterpret_cast<const f32x4 *>(&smp->dec[16 * t + 4 * b]);
                 f32x4 x = dS[t] * dc;
-                x = mfma16k16(*reinterpret_cast<const bf16x4 *>(&smp->u.a.QsT[16 * t + m][4 * b]),
+                x = mfma16k16(*reinterpret_cast<const bf16x4 *>(
+                                  &smp->u.a.QsT[16 * t + m][tcol(16 * t + m, 4 * b)]),
                               dob, x);
                 dS[t] = mfma16k16(
-                    *reinterpret_cast<const bf16x4 *>(&smp->u.a.x.w.WT[16 * t + m][4 * b]), ndub, x);
+                    *reinterpret_cast<const bf16x4 *>(
+                        &smp->u.a.x.w.WT[16 * t + m][tcol(16 * t + m, 4 * b)]), ndub, x);
             }
         }
         __syncthreads();
