@@ -85,6 +85,19 @@ static_assert(sizeof(TSmem) <= sizeof(bf16) * kChunk * kRowLd, "T overlay fits")
 
 __device__ __forceinline__ int pair_index(int i, int j) { return (i * (i - 1)) / 2 + j; }
 
+// KR, QR and KCD store the 16-byte slot o (channels 8 o .. 8 o + 7) of row r at
+// slot o ^ ((r >> 4) & 3).  Phase 1 writes 8 bytes of 16 rows four apart per 16
+// lanes; unpermuted, the 68-dword row stride puts them in two LDS banks,
+// permuted in eight.  Reads of a whole slot, by rows of one 16-row tile, are
+// unaffected.  Column of channel group c4 (channels 4 c4 .. 4 c4 + 3) of row r:
+__device__ __forceinline__ int rq(int r, int c4) { return 4 * (c4 ^ ((r >> 3) & 6)); }
+
+// channels 8 o .. 8 o + 7 of row r of such a tile
+__device__ __forceinline__ bf16x8 lds8_rq(const bf16 (*t)[kRowLd], int r, int o)
+{
+    return lds8(&t[r][8 * (o ^ ((r >> 4) & 3))]);
+}
+
 __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4 &a, float s)
 {
     return bf16x4{(bf16)(s * a[0]), (bf16)(s * a[1]), (bf16)(s * a[2]), (bf16)(s * a[3])};
@@ -343,9 +356,9 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                     vb[c][tt] = (bf16)(br[tt] * vv);                   // beta v
                     kp[c][tt] = (bf16)(kv * (egb[c] * fc));            // k e^{G_end - G}
                 }
-                *reinterpret_cast<bf16x4 *>(&sm.KR[r][ch0]) = kr;
-                *reinterpret_cast<bf16x4 *>(&sm.QR[r][ch0]) = qr;
-                *reinterpret_cast<bf16x4 *>(&sm.KCD[r][ch0]) = kc;
+                *reinterpret_cast<bf16x4 *>(&sm.KR[r][rq(r, ch0 >> 2)]) = kr;
+                *reinterpret_cast<bf16x4 *>(&sm.QR[r][rq(r, ch0 >> 2)]) = qr;
+                *reinterpret_cast<bf16x4 *>(&sm.KCD[r][rq(r, ch0 >> 2)]) = kc;
             }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -370,9 +383,9 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int ch = 32 * ks + 8 * b;
-                const bf16x8 ar = lds8(&sm.KR[16 * i + m][ch]);
-                const bf16x8 aq = lds8(&sm.QR[16 * i + m][ch]);
-                bf16x8 bc = lds8(&sm.KCD[16 * jb + m][ch]);
+                const bf16x8 ar = lds8_rq(sm.KR, 16 * i + m, 4 * ks + b);
+                const bf16x8 aq = lds8_rq(sm.QR, 16 * i + m, 4 * ks + b);
+                bf16x8 bc = lds8_rq(sm.KCD, 16 * jb + m, 4 * ks + b);
                 if (jb < i) {
                     const float *f = &sm.F[pair_index(i, jb)][ch];
 #pragma unroll
@@ -534,7 +547,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                         pf[ks] = perm8(&sm.PM[16 * mt + m][0], ks, b);
                     // scale Q e^G at row 16 mt + m, channels 16 nt + 4 b .. + 3, from q e^{G - B_mt}
                     const bf16x4 qr =
-                        *reinterpret_cast<const bf16x4 *>(&sm.QR[16 * mt + m][16 * nt + 4 * b]);
+                        *reinterpret_cast<const bf16x4 *>(&sm.QR[16 * mt + m][rq(16 * mt + m, 4 * nt + b)]);
                     const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[mt][16 * nt + 4 * b]);
                     f32x4 qh;
 #pragma unroll
