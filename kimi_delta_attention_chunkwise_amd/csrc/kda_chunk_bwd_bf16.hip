@@ -99,9 +99,11 @@ __global__ __launch_bounds__(kBpThreads) void kda_bwd_prep_bf16_kernel(
         for (int e = 0; e < 8; ++e)
             sm.QT[perm_row(ks, fb, e)][16 * mt + fm] = x[e];
     }
-    // dO = dY sigmoid(Z) of token r, channels c0 .. c0 + 15, transposed; zero past the chunk
+    // dO = dY sigmoid(Z) of token r = lane, channels 16 w .. 16 w + 15, transposed;
+    // zero past the chunk.  Lanes take consecutive tokens so that the 2-byte
+    // transposed writes of a wave fill consecutive LDS words.
     {
-        const int r = tid >> 3, c0 = 16 * (tid & 7);
+        const int r = lane, c0 = 16 * w;
         bf16x8 dy[2] = {}, z[2] = {};
         if (r < len) {
             const int64_t off = ((tok0 + r) * H + h) * (int64_t)kDV + c0;
