@@ -50,6 +50,9 @@ namespace {
 // ------------------------------------------------------------ backward prep
 constexpr int kBpThreads = 512;
 
+// column of token r in row c of OT (see the dO staging below)
+__device__ __forceinline__ int ot_col(int c, int r) { return 8 * ((r >> 3) ^ ((c >> 4) & 7)) + (r & 7); }
+
 struct BwdPrepSmem {
     bf16 L[kDK][kDK + 8];           // -L, row-major
     bf16 QT[kDK][kChunk + 8];       // Q^^T  [dk][token]
@@ -99,11 +102,12 @@ __global__ __launch_bounds__(kBpThreads) void kda_bwd_prep_bf16_kernel(
         for (int e = 0; e < 8; ++e)
             sm.QT[perm_row(ks, fb, e)][16 * mt + fm] = x[e];
     }
-    // dO = dY sigmoid(Z) of token r = lane, channels 16 w .. 16 w + 15, transposed;
-    // zero past the chunk.  Lanes take consecutive tokens so that the 2-byte
-    // transposed writes of a wave fill consecutive LDS words.
+    // dO = dY sigmoid(Z) of token r, channels c0 .. c0 + 15, transposed; zero past
+    // the chunk.  OT keeps the 8-token group of row c at group ^ ((c >> 4) & 7)
+    // (ot_col): the rows a wave writes at once are 16 apart, which without the
+    // permutation would all share one LDS bank.
     {
-        const int r = lane, c0 = 16 * w;
+        const int r = tid >> 3, c0 = 16 * (tid & 7);
         bf16x8 dy[2] = {}, z[2] = {};
         if (r < len) {
             const int64_t off = ((tok0 + r) * H + h) * (int64_t)kDV + c0;
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(kBpThreads) void kda_bwd_prep_bf16_kernel(
         for (int p = 0; p < 2; ++p)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                sm.OT[c0 + 8 * p + e][r] =
+                sm.OT[c0 + 8 * p + e][ot_col(c0 + 8 * p + e, r)] =
                     (bf16)(r < len ? (float)dy[p][e] * sigmoidf_((float)z[p][e]) : 0.f);
     }
     if (tid < kDK / 4)
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(kBpThreads) void kda_bwd_prep_bf16_kernel(
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 a = mfma16(lds8(&sm.QT[16 * t + m][32 * ks + 8 * b]),
-                           lds8(&sm.OT[16 * w + m][32 * ks + 8 * b]), a);
+                           lds8(&sm.OT[16 * w + m][8 * ((4 * ks + b) ^ w)]), a);
             acc[s2] = a;
         }
         *reinterpret_cast<bf16x8 *>(rb + kOffBM + w * 4096 + i2 * 1024 + lane * 16) =
