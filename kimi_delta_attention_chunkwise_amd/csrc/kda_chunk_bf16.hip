@@ -58,7 +58,8 @@ namespace {
 constexpr int kPrepThreads = 512;
 constexpr int kRowLd = 136;   // bf16 row stride of row-major 64 x 128 tiles
 constexpr int kColLd = 72;    // bf16 row stride of channel-major 128 x 64 tiles
-constexpr int kALd = 65;      // fp32 row stride of A and T
+constexpr int kALd = 68;      // fp32 row stride of A and T: 16-byte rows, and the column
+                              // reads of phases 2 and 4 spread over all LDS banks
 
 struct PrepSmem {
     // -- live in phases 1-2 only; T reuses this space afterwards
@@ -470,9 +471,14 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                 for (int ks = 0; ks < 2; ++ks) {
                     bf16x8 f = {};
                     if (ks <= (mt >> 1)) {
+                        const float *t = &ts.TM[16 * mt + m][32 * ks + 8 * b];
+                        const f32x4 lo = *reinterpret_cast<const f32x4 *>(t);
+                        const f32x4 hi = *reinterpret_cast<const f32x4 *>(t + 4);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            f[e] = (bf16)ts.TM[16 * mt + m][32 * ks + 8 * b + e];
+                        for (int e = 0; e < 4; ++e) {
+                            f[e] = (bf16)lo[e];
+                            f[4 + e] = (bf16)hi[e];
+                        }
                     }
                     tf[mt][ks] = f;
                 }
