@@ -73,9 +73,11 @@ struct PrepSmem {
     bf16 KPT[kDK][kColLd];        // K' = k e^{G_end - G}, channel-major
     bf16 PM[kChunk][kColLd];      // scale P, lower incl., zero above
     float AM[kChunk][kALd];       // diag(beta) A, strict lower
-    float eB[4][kDK];             // e^{B_i}
-    float eGB[4][kDK];            // e^{G_end - B_i}
-    float Gref[4][kDK];           // G at the end of subtiles 0, 1, 2, 3 (B_1, B_2, B_3, G_end)
+    // per-subtile channel constants; rows padded to 132 floats so that the
+    // 16-byte reads of four rows by one 16-lane group use different LDS banks
+    float eB[4][kDK + 4];         // e^{B_i}
+    float eGB[4][kDK + 4];        // e^{G_end - B_i}
+    float Gref[4][kDK + 4];       // G at the end of subtiles 0, 1, 2, 3 (B_1, B_2, B_3, G_end)
     float NRM[2][8][kChunk];      // prologue: per-wave partial sums of q^2 and k^2 per row
 };
 

@@ -375,26 +375,28 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
     load_tok(cur, pass_sub(0), npass == 1);
 
     // Row-contiguous stores of the token gradients of subtile i staged in LDS
-    // (16 bytes per lane: array a, row r, channels 8 c8 ..) and of its dbeta.
-    // Issued after the next pass's loads, so that no load waits behind them.
-    auto store_staged = [&](int i) {
+    // (16 bytes per lane: array a, row r, channels 8 c8 ..) and of its dbeta, by
+    // the nthr threads rt = 0 .. nthr - 1.  In a backward pass they are issued by
+    // waves 2..7 while waves 0 and 1 form M, A, T and P, after the pass's loads,
+    // so that no load waits behind them.
+    auto store_staged = [&](int i, int rt, int nthr) {
         bf16 *const dst[5] = {dq, dk, dv, dg, dgate};
         const int r0 = kSub * i;
-        for (int idx = tid; idx < 5 * kSub * 16; idx += kGThreads) {
+        for (int idx = rt; idx < 5 * kSub * 16; idx += nthr) {
             const int a = idx / (kSub * 16), r = (idx / 16) % kSub, c8 = idx % 16;
             if (r0 + r < len)
                 *reinterpret_cast<bf16x8 *>(dst[a] + ((tok0 + r0 + r) * H + h) * (int64_t)kDK +
                                             8 * c8) = lds8(&smp->v.out[a][r][8 * c8]);
         }
-        if (tid < kSub && r0 + tid < len)
-            dbeta[(tok0 + r0 + tid) * H + h] = smp->dbst[tid];
+        if (rt < kSub && r0 + rt < len)
+            dbeta[(tok0 + r0 + rt) * H + h] = smp->dbst[rt];
     };
 
     // Operands of the subtile of pass p: G, factored K / Q tiles, M, A (P), T,
     // W and U~ (returned).  Issues the next pass's token loads once this pass's
-    // tokens are in LDS, then a backward pass's own gate and state loads; a
-    // backward pass after the first then stores the previous pass's staged
-    // gradients (subtile i + 1).
+    // tokens are in LDS, then a backward pass's own gate and state loads; in a
+    // backward pass after the first, waves 2..7 store the previous pass's staged
+    // gradients (subtile i + 1) during the M / A / T / P step.
     auto prep_pass = [&](int p, bool bwd, int i) -> f32x4 {
         if ((tid & 31) == 0)
             smp->beta[er] = bf16_bits_to_f32(cur.beta);
@@ -411,7 +413,6 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
                     sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(i, ks));
-                store_staged(i + 1);
             }
         }
         __syncthreads();
@@ -500,6 +501,9 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                     smp->P[r][m] = m <= r ? acc[i2] : 0.f;
                 }
             }
+        } else if (bwd && p > nsub - 1) {
+            // waves 2..7; the staging area is next written in this pass's U / O step
+            store_staged(i + 1, tid - 2 * 64, kGThreads - 2 * 64);
         }
         __syncthreads();
         // W = T diag(beta) Ks and U~ = T diag(beta) V on the wave's channels (fp32 MFMA)
@@ -846,7 +850,7 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             smp->dbst[tid] = (bf16)acc;
         }
     }
-    store_staged(0);
+    store_staged(0, tid, kGThreads);
 }
 
 }  // namespace
