@@ -42,6 +42,7 @@
 #include "kda_internal.h"
 
 #include <mutex>
+#include <utility>
 
 namespace kda {
 
@@ -167,6 +168,38 @@ constexpr int kTL = kSub + 8;    // bf16 row stride of transposed [128][16] tile
 constexpr int kSL = kSub + 1;    // fp32 row stride of 16 x 16 matrices
 
 typedef float Sq[kSub][kSL];
+
+// Lane kS of the caller's 16-lane row, to every lane of that row (DPP
+// row_newbcast: a VALU move, no LDS traffic).
+template <int kS>
+__device__ __forceinline__ float row_bcast(float x)
+{
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + kS, 0xf, 0xf, false));
+}
+
+// Step kS of the in-wave forward substitution for T = (I + A)^-1 in column
+// form: lane (b, m) owns T[4 b + i2][m] and A[4 b + i2][m]; once row kS of T is
+// final it updates every later row.  Row kS of T comes from row group kS / 4
+// by a lane shuffle, A[4 b + i2][kS] from lane kS of the lane's own row.
+template <int kS>
+__device__ __forceinline__ void tsolve_step(f32x4 &t, const f32x4 &a, int b, int m)
+{
+    const float ts = __shfl(t[kS & 3], m + 16 * (kS >> 2));
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+        const float ars = row_bcast<kS>(a[i2]);
+        if (4 * b + i2 > kS)
+            t[i2] -= ars * ts;
+    }
+}
+
+template <int... kS>
+__device__ __forceinline__ void tsolve(f32x4 &t, const f32x4 &a, int b, int m,
+                                       std::integer_sequence<int, kS...>)
+{
+    (tsolve_step<kS>(t, a, b, m), ...);
+}
 
 // Column of element [x][r] of a transposed [128][16] tile: the four groups of
 // four tokens of a row are XOR-permuted by bits 3..4 of the channel x.  A
@@ -474,23 +507,12 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                     a[i2] = m < r ? smp->beta[r] * acc[i2] : 0.f;
                     smp->M[r][m] = acc[i2];
                 }
-                // forward substitution in column form inside the wave: lane (b, m)
-                // owns T[4 b + i2][m]; once row s is final it updates every later
-                // row; row s and A[.][s] arrive by lane shuffles
+                // T = (I + A)^-1 by forward substitution inside the wave
                 f32x4 t;
 #pragma unroll
                 for (int i2 = 0; i2 < 4; ++i2)
                     t[i2] = (4 * b + i2 == m) ? 1.f : 0.f;
-#pragma unroll
-                for (int s2 = 0; s2 < kSub - 1; ++s2) {
-                    const float ts = __shfl(t[s2 & 3], m + 16 * (s2 >> 2));
-#pragma unroll
-                    for (int i2 = 0; i2 < 4; ++i2) {
-                        const float ars = __shfl(a[i2], s2 + 16 * b);   // A[4 b + i2][s2]
-                        if (4 * b + i2 > s2)
-                            t[i2] -= ars * ts;
-                    }
-                }
+                tsolve(t, a, b, m, std::make_integer_sequence<int, kSub - 1>{});
 #pragma unroll
                 for (int i2 = 0; i2 < 4; ++i2)
                     smp->Tm[4 * b + i2][m] = t[i2];
