@@ -214,7 +214,7 @@ __device__ __forceinline__ int tcol(int x, int r)
 struct GradSmem {
     // small and often-read arrays first, so that their addresses fit the
     // 16-bit offsets of LDS instructions
-    Sq M, Tm, P, dP, dTu, dT, X, dA;
+    Sq M, Tm, P, dP, dTu, dA;
     alignas(16) float Bref[kDK];
     alignas(16) float Ge[kDK];
     alignas(16) float dec[kDK];
@@ -736,39 +736,34 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
         }
         __syncthreads();
         // dT = dW (diag(beta) Ks)^T + dU (diag(beta) V)^T, then
-        // dA = strict_lower(-T^T dT T^T), all in wave 0; lanes exchange the
-        // intermediate tiles through LDS, ordered by wavefront fences
+        // dA = strict_lower(-T^T (dT T^T)), all in wave 0 and in registers: an
+        // accumulator tile (lane (b, n) holds D[4 b + i][n]) is used directly as
+        // the next 16x16x4 product's operand, with the contraction index of step
+        // kk taken as k = 4 b + kk on both sides
         if (w == 0) {
+            // dT^T: lane (b, m) holds dT[m][4 b + i]
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int kc = 32 * ks + 8 * b;
                 const f32x4 lo = *reinterpret_cast<const f32x4 *>(&smp->u.b.dW[m][kc]);
                 const f32x4 hi = *reinterpret_cast<const f32x4 *>(&smp->u.b.dW[m][kc + 4]);
-                acc = mfma16(acc_to_frag(lo, hi), lds8(&smp->Ks[m][kc]), acc);
+                acc = mfma16(lds8(&smp->Ks[m][kc]), acc_to_frag(lo, hi), acc);
             }
-#pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-                const int r = 4 * b + i2;
-                smp->dT[r][m] = smp->beta[m] * acc[i2] + smp->dTu[r][m];
-            }
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            f32x4 x1 = {0.f, 0.f, 0.f, 0.f};       // T^T dT
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int s2 = 4 * kk + b;
-                x1 = mfma4_f32(smp->Tm[s2][m], smp->dT[s2][m], x1);
-            }
+            f32x4 dtt;
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2)
-                smp->X[4 * b + i2][m] = x1[i2];
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            f32x4 x2 = {0.f, 0.f, 0.f, 0.f};       // (T^T dT) T^T
+                dtt[i2] = smp->beta[4 * b + i2] * acc[i2] + smp->dTu[m][4 * b + i2];
+            // Y = dT T^T: A[m][k] = dT[m][k] is dtt[kk], B[k][n] = T[n][k]
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int s2 = 4 * kk + b;
-                x2 = mfma4_f32(smp->X[m][s2], smp->Tm[m][s2], x2);
-            }
+            for (int kk = 0; kk < 4; ++kk)
+                y = mfma4_f32(dtt[kk], smp->Tm[m][4 * b + kk], y);
+            // T^T Y: A[m][k] = T[k][m], B[k][n] = Y[k][n] is y[kk]
+            f32x4 x2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                x2 = mfma4_f32(smp->Tm[4 * b + kk][m], y[kk], x2);
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2) {
                 const int r = 4 * b + i2;
