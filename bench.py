@@ -107,7 +107,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the KDA path here is single-GPU; see the sharding notes in DESIGN.md)",
+              "(the KDA path here runs on one GPU)",
               file=sys.stderr, flush=True)
         return 2
     import torch
@@ -188,6 +188,12 @@ def main():
                  "unit": "TFLOP/s", "frac": flops_call / t_s / 1e12 / BF16_PEAK_TFLOPS,
                  "algorithmic_flops_per_call": flops_call},
     }
+    executed = load_traffic("mfma_executed_bf16_flops_per_call")
+    if executed is not None:
+        # bf16 MFMA flops the kernels execute (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512),
+        # masked and folded products included, over the same call time
+        result["mfma"]["executed_flops_per_call"] = executed
+        result["mfma"]["executed_frac"] = executed / t_s / 1e12 / BF16_PEAK_TFLOPS
     extras = set() if args.no_extras else set(args.extras.split(","))
     result["extras"] = {}
     if "snapshots_prologue" in extras:
