@@ -23,10 +23,13 @@
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library allocates no device or host memory and keeps no global state;
- *     calls are re-entrant.
+ *     library allocates no device memory; calls are re-entrant.  Its only
+ *     state is one auxiliary HIP stream and a few events per device, created
+ *     at the first kda_chunk_fwd over a long single sequence (see there) and
+ *     kept until the process ends.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
- *     returns without synchronising.  Arguments are validated on the host
+ *     returns without synchronising; work forked to the auxiliary stream is
+ *     joined back into `stream` before the call's last kernel.  Arguments are validated on the host
  *     before anything is launched: on any error a status code is returned and
  *     nothing is written.  A failed launch returns KDA_ERR_HIP.
  *   - Layouts are row-major and contiguous.  Element types: `dt` gives the
@@ -116,6 +119,13 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
  *               bytes, 256-byte aligned; contents on entry are ignored and
  *               left undefined.  May be NULL when the size is 0.
  * Overlapping calls that share a workspace race; out must not alias any input.
+ *
+ * Long single sequences (KDA_BF16, cu_seqlens NULL, B = 1, at least 1,024
+ * chunks, final_state not NULL, no snapshots): the serial part runs in
+ * segments of at least 512 chunks on the auxiliary stream, each segment
+ * starting from the fp32 state the previous one left in final_state, while
+ * `stream` computes each finished segment's outputs.  The result is bitwise
+ * that of one unsegmented pass; final_state is written during the call.
  */
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                          const void *beta, const void *gate, const float *init_state,

@@ -1,6 +1,7 @@
 // kda_api.hip -- the extern "C" entry points of libkda.so: host-side argument
 // validation, workspace sizing and dispatch to the gfx950 kernels.  Nothing
-// here allocates memory or keeps state between calls.
+// here allocates memory or keeps state between calls (the one auxiliary
+// stream of the long-sequence forward lives with its launcher).
 #include "kda.h"
 #include "kda_internal.h"
 

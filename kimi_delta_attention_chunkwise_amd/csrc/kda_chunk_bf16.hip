@@ -952,22 +952,111 @@ hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *
 }
 
 // The chain over the records in ws, one workgroup per (sequence, head, value block).
+// With own_cu each workgroup also reserves LDS it does not use, so that no
+// workgroup of a kernel running beside it shares its CU (and the CU's memory
+// pipeline, which bounds the chain's step).
+constexpr int kChainOwnCuLds = 152 * 1024;   // static + reserved LDS per chain workgroup
+
 hipError_t launch_chain(const float *init, float *final_state, float *snaps, int snap_interval,
-                        const int32_t *cu, int N, int T, int H, uint8_t *ws, hipStream_t stream)
+                        const int32_t *cu, int N, int T, int H, uint8_t *ws, hipStream_t stream,
+                        bool own_cu = false)
 {
+    // the reserved (dynamic) part: kChainOwnCuLds less the kernel's static LDS
+    static std::once_flag attr_once;
+    static hipError_t attr_err = hipSuccess;
+    static size_t reserve = 0;
+    std::call_once(attr_once, [] {
+        const void *fn = reinterpret_cast<const void *>(kda_chain_bf16_kernel<false>);
+        hipFuncAttributes fa{};
+        attr_err = hipFuncGetAttributes(&fa, fn);
+        if (attr_err == hipSuccess && fa.sharedSizeBytes < (size_t)kChainOwnCuLds) {
+            reserve = kChainOwnCuLds - fa.sharedSizeBytes;
+            attr_err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)reserve);
+        }
+    });
     const int64_t units = (int64_t)N * H;
     if (units <= 0)
         return hipSuccess;
     const int64_t blocks = (units + 7) / 8 * 8 * kNumVBlocks;
-    if (snaps)
+    if (snaps) {
         hipLaunchKernelGGL(kda_chain_bf16_kernel<true>, dim3((unsigned)blocks),
                            dim3(kChainThreads), 0, stream, init, final_state, snaps,
                            snap_interval / kChunk, cu, T, H, (int)units, ws);
-    else
+    } else {
+        size_t dyn = 0;
+        if (own_cu) {
+            if (attr_err != hipSuccess)
+                return attr_err;
+            dyn = reserve;
+        }
         hipLaunchKernelGGL(kda_chain_bf16_kernel<false>, dim3((unsigned)blocks),
-                           dim3(kChainThreads), 0, stream, init, final_state, snaps, 1, cu, T, H,
-                           (int)units, ws);
+                           dim3(kChainThreads), dyn, stream, init, final_state, snaps, 1, cu, T,
+                           H, (int)units, ws);
+    }
     return hipGetLastError();
+}
+
+hipError_t launch_output(const bf16 *gate, bf16 *out, const int32_t *cu, int N, int T, int H,
+                         int64_t n_slots, const uint8_t *ws, hipStream_t stream)
+{
+    if (n_slots <= 0 || H <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(kda_output_bf16_kernel, dim3((unsigned)(n_slots * H)), dim3(256), 0,
+                       stream, gate, out, cu, N, T, H, ws);
+    return hipGetLastError();
+}
+
+// ---- long single sequences: output beside the chain ---------------------------
+//
+// On one long sequence the chain walks thousands of chunks on H * 8
+// workgroups while the rest of the device idles.  The chain then runs on a
+// second stream in segments of kSegSlots chunks, each starting from the
+// previous segment's final state (fp32, written to final_state and read back
+// unchanged, so the result is bitwise that of one chain), and the caller's
+// stream runs the output kernel of each segment as soon as that segment's
+// chain is done, beside the chain of the next.  Records, inputs and outputs
+// of a segment are addressed by offsetting the base pointers, so the kernels
+// see an ordinary one-sequence call.
+//
+// The second stream and a pool of events are created once per device, at the
+// first such call, and kept until the process ends; a mutex orders the
+// record / wait / launch sequences of concurrent host threads.
+constexpr int64_t kSegSlots = 512;
+constexpr int64_t kMinSegmentedSlots = 2 * kSegSlots;
+constexpr int kMaxSegments = 32;
+
+struct AuxStream {
+    bool ready = false;
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr;
+    hipEvent_t seg[kMaxSegments] = {};
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_aux_mutex;
+AuxStream g_aux[kMaxDevices];
+
+hipError_t aux_stream(AuxStream *&out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    AuxStream &a = g_aux[dev];
+    if (!a.ready) {
+        e = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming);
+        for (int i = 0; i < kMaxSegments && e == hipSuccess; ++i)
+            e = hipEventCreateWithFlags(&a.seg[i], hipEventDisableTiming);
+        if (e != hipSuccess)
+            return e;
+        a.ready = true;
+    }
+    out = &a;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -980,17 +1069,44 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
 {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     hipError_t e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, pro, ws, stream);
-    if (e == hipSuccess)
-        e = launch_chain(init, final_state, snaps, snap_interval, cu, N, T, H, ws, stream);
     if (e != hipSuccess)
         return e;
-    if (n_slots > 0 && H > 0) {
-        hipLaunchKernelGGL(kda_output_bf16_kernel, dim3((unsigned)(n_slots * H)), dim3(256),
-                           0, stream, gate, out, cu, N, T, H,
-                           static_cast<const uint8_t *>(workspace));
-        return hipGetLastError();
+    // segments need one sequence without cu_seqlens, no snapshots and a final
+    // state buffer to hand the state over in
+    const bool segmented = !cu && N == 1 && !snaps && final_state && n_slots >= kMinSegmentedSlots;
+    if (!segmented) {
+        e = launch_chain(init, final_state, snaps, snap_interval, cu, N, T, H, ws, stream);
+        if (e == hipSuccess)
+            e = launch_output(gate, out, cu, N, T, H, n_slots, ws, stream);
+        return e;
     }
-    return hipSuccess;
+    int64_t seg = (n_slots + kMaxSegments - 1) / kMaxSegments;
+    seg = seg < kSegSlots ? kSegSlots : seg;
+    const int64_t nseg = (n_slots + seg - 1) / seg;
+    std::lock_guard<std::mutex> lock(g_aux_mutex);
+    AuxStream *aux = nullptr;
+    e = aux_stream(aux);
+    if (e == hipSuccess)
+        e = hipEventRecord(aux->fork, stream);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(aux->stream, aux->fork, 0);
+    for (int64_t s = 0; s < nseg && e == hipSuccess; ++s) {
+        const int64_t slot0 = s * seg;
+        const int64_t ns = n_slots - slot0 < seg ? n_slots - slot0 : seg;
+        const int64_t tok0 = slot0 * kChunk;
+        const int Ts = (int)(T - tok0 < ns * kChunk ? T - tok0 : ns * kChunk);
+        uint8_t *wss = ws + slot0 * H * (int64_t)kRecBytes;
+        e = launch_chain(s == 0 ? init : final_state, final_state, nullptr, 0, nullptr, 1, Ts, H,
+                         wss, aux->stream, true);
+        if (e == hipSuccess)
+            e = hipEventRecord(aux->seg[s], aux->stream);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(stream, aux->seg[s], 0);
+        if (e == hipSuccess)
+            e = launch_output(gate + tok0 * H * kDV, out + tok0 * H * kDV, nullptr, 1, Ts, H, ns,
+                              wss, stream);
+    }
+    return e;
 }
 
 // Backward: forward records (prep + chain give every chunk's entry state, or

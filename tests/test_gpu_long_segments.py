@@ -1,0 +1,55 @@
+"""GPU: a long single sequence, whose chain runs in segments on a second stream.
+
+From 1,024 chunks on, ``kda_chunk_fwd`` over one sequence (no cu_seqlens, no
+snapshots, a final state wanted) runs the chain in segments of at least 512
+chunks on a second stream, handing the fp32 state from segment to segment,
+while the caller's stream runs each segment's output kernel.  The state passes
+through memory unchanged, so the result must be bitwise that of calls too
+short to be segmented, chained by hand; and it must match the oracle.
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import kimi_delta_attention_chunkwise_amd as kda
+
+from test_gpu_parity import check, run_oracle, small_inputs, to
+
+pytestmark = pytest.mark.gpu
+KEYS = ("q", "k", "v", "g", "beta", "z")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    kda.load_library()
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"[gpu-long-segments] {msg}", flush=True)
+
+
+def test_segmented_chain_equals_short_calls_and_oracle(dev):
+    T, H, cut = 70_000, 2, 32_768          # 1,094 chunks: segments of 512, 512 and 70
+    say(f"B=1 H={H} T={T}: one call against two calls of {cut} and {T - cut} tokens")
+    x = small_inputs(torch.bfloat16, 1, T, H, 128, 128, 77, init_std=0.02)
+    xd = to(x, dev)
+    out, fin = kda.chunk_fwd(*[xd[k] for k in KEYS], init_state=xd["init_state"])
+    a = [xd[k][:, :cut].contiguous() for k in KEYS]
+    b = [xd[k][:, cut:].contiguous() for k in KEYS]
+    o1, s1 = kda.chunk_fwd(*a, init_state=xd["init_state"])
+    o2, s2 = kda.chunk_fwd(*b, init_state=s1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.cat([o1, o2], dim=1)), "outputs differ from the short calls"
+    assert torch.equal(fin, s2), "final state differs from the short calls"
+    # the same call with the final state written over the initial state
+    st = xd["init_state"].clone()
+    out3, _ = kda.chunk_fwd(*[xd[k] for k in KEYS], init_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(out3, out) and torch.equal(st, fin), "in-place state differs"
+    say("oracle comparison, both heads over all tokens")
+    ro, rf = run_oracle(x)
+    check(out, fin, ro, rf, 2e-2, 1e-2, f"long segments T={T}")
