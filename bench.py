@@ -246,12 +246,45 @@ def bench_decode(torch, kda, W, dev, args):
           file=sys.stderr, flush=True)
     bytes_step = N * H * (2 * STATE_BYTES + PREFILL_BYTES_PER_TOKEN_HEAD)
     gbs = bytes_step / (ms / 1e3) / 1e9
+    measured = measured_bandwidth(torch, state)
     return {"workload": "decode_n256_h32", "N": N, "H": H, "steps": args.decode_steps,
             "ms_per_step": ms, "steps_per_s": 1e3 / ms, "tokens_per_s": N * 1e3 / ms,
             "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "traffic": load_traffic("decode_hbm_bytes_per_step"),
-                         "algorithmic_bytes_per_step": bytes_step}}
+                         "algorithmic_bytes_per_step": bytes_step},
+            "measured_bandwidth": dict(measured, decode_frac_of_inplace=gbs / measured["inplace_gbs"])}
+
+
+def measured_bandwidth(torch, state):
+    """Secondary denominators measured on this device with torch's own kernels:
+    a 1 GiB device-to-device copy, and an in-place multiply over a buffer the
+    size of the decode state (512 MiB fp32, read and written like the state).
+    Read plus write bytes per second."""
+    def rate(fn, nbytes, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return nbytes / (e0.elapsed_time(e1) / reps / 1e3) / 1e9
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=state.device)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    copy_gbs = rate(lambda: dst.copy_(src), 2 * n)
+    del src, dst
+    buf = torch.ones_like(state)
+    inplace_gbs = rate(lambda: buf.mul_(0.999), 2 * buf.numel() * 4)
+    del buf
+    return {"copy_1GiB_gbs": copy_gbs, "inplace_gbs": inplace_gbs,
+            "inplace_bytes": int(state.numel() * 4)}
 
 
 def _time(torch, fn, steps, warmup):
