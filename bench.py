@@ -85,7 +85,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--extras", default="snapshots_prologue,backward,decode_prologue_verify,long",
+    ap.add_argument("--extras", default="snapshots_prologue,backward,decode_prologue_verify,long,varlen",
                     help="comma-separated extra measurements to run (default: all)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the snapshot / prologue / verify measurements")
@@ -211,6 +211,8 @@ def main():
 
     if "long" in extras:
         result["extras"]["long_t1m_h16"] = bench_long(torch, kda, W, dev)
+    if "varlen" in extras:
+        result["extras"]["varlen_4seq_h32"] = bench_varlen(torch, kda, W, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
@@ -465,6 +467,37 @@ def bench_long(torch, kda, W, dev, calls=3):
     return {"workload": "long_t1m_h16", "ms_per_call": ms, "tokens_per_s": B * T / (ms / 1e3),
             "hbm_roofline": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": gbs / HBM_PEAK_GBS}}
+
+
+def bench_varlen(torch, kda, W, dev, calls=10):
+    """The packed varlen workload: 4 sequences (lengths drawn uniform in
+    [1024, 32768], seed 0) in one cu_seqlens call, H=32, fp32 initial state
+    N(0, 0.02^2), final state written."""
+    w = W.WORKLOADS["varlen_4seq_h32"]
+    x = W.prefill_inputs(w, device=dev, seed=0)
+    lens = W.varlen_lengths(w, 0)
+    T, H, N = int(sum(lens)), w.H, len(lens)
+    ws = torch.empty(kda.chunk_fwd_workspace_bytes(1, T, N, H, DK, DV, CHUNK, torch.bfloat16,
+                                                   True), dtype=torch.uint8, device=dev)
+    out = torch.empty(1, T, H, DV, dtype=torch.bfloat16, device=dev)
+    fin = torch.empty(N, H, DK, DV, dtype=torch.float32, device=dev)
+
+    def call(i):
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"],
+                      init_state=x["init_state"], cu_seqlens=x["cu_seqlens"], workspace=ws,
+                      out=out, final_state=fin)
+
+    ms = _time(torch, call, calls, 2)
+    token_heads = T * H
+    nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * token_heads + 2 * N * H * STATE_BYTES
+    gbs = nbytes / (ms / 1e3) / 1e9
+    print(f"[bench] varlen_4seq_h32 (lengths {lens}): {ms:.3f} ms per call", file=sys.stderr,
+          flush=True)
+    del x, ws, out
+    return {"workload": "varlen_4seq_h32", "lengths": lens, "ms_per_call": ms,
+            "tokens_per_s": T / (ms / 1e3),
+            "hbm_roofline": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes}}
 
 
 def cpu_baseline(w):
