@@ -599,7 +599,10 @@ namespace {
 constexpr int kComputeWaves = 8;
 constexpr int kStoreWave = kComputeWaves;
 constexpr int kSideWave = kComputeWaves + 1;
-constexpr int kChainThreads = 64 * (kComputeWaves + 2);
+// with kNB value blocks per workgroup (see the kernel), side waves of at most
+// two blocks each
+template <int kNB> constexpr int chain_side_waves() { return kNB <= 2 ? 1 : kNB / 2; }
+template <int kNB> constexpr int chain_threads() { return 64 * (kComputeWaves + 1 + chain_side_waves<kNB>()); }
 constexpr int kPrefetch = 4;         // chunks of operands in flight per compute wave
 
 struct ChainStage {
@@ -622,26 +625,36 @@ __device__ __forceinline__ void chain_load(ChainStage &st, const uint8_t *rec_an
 // chunks (see snap_slot0): the compute waves park the state in LDS at a
 // snapshot boundary and the store wave writes it out in the next iteration, so
 // the compute waves still issue no stores inside the loop.
-template <bool kSnap>
-__global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
+//
+// kNB value blocks per workgroup (1, 2 or 4; kNB > 1 only without snapshots):
+// the waves apply every step to kNB adjacent 16-column blocks with the same L
+// fragments, so a (sequence, head) takes 8 / kNB workgroups, which stream L
+// once for kNB blocks.  Each side wave fetches Bm for two blocks at most.
+template <bool kSnap, int kNB = 1>
+__global__ __launch_bounds__(chain_threads<kNB>()) void kda_chain_bf16_kernel(
     const float *__restrict__ init, float *__restrict__ final_state, float *__restrict__ snaps,
     int snap_chunks, const int32_t *__restrict__ cu, int T, int H, int units,
     uint8_t *__restrict__ ws)
 {
-    // state as 4 k-step fragments; wave w writes elements 4 (w % 2) .. + 3 of k-step w / 2
-    __shared__ bf16x8 sbuf[2][4][64];
-    // Bm of this value block (the record's fragment layout) and dec, per chunk,
-    // in a 2-slot ring: slot j & 1 holds chunk j
-    __shared__ bf16x8 side_bm[2][4][64];
+    static_assert(kNB == 1 || kNB == 2 || kNB == 4, "1, 2 or 4 value blocks per workgroup");
+    static_assert(!kSnap || kNB == 1, "snapshots with one value block per workgroup");
+    constexpr int kSideBlocks = kNB == 1 ? 1 : 2;   // value blocks per side wave
+    // state as 4 k-step fragments per value block; wave w writes elements
+    // 4 (w % 2) .. + 3 of k-step w / 2
+    __shared__ bf16x8 sbuf[2][kNB][4][64];
+    // Bm of these value blocks (the record's fragment layout) and dec, per
+    // chunk, in a 2-slot ring: slot j & 1 holds chunk j
+    __shared__ bf16x8 side_bm[2][kNB][4][64];
     __shared__ float side_dec[2][kDK];
     __shared__ float snap_s[kSnap ? 2 : 1][kSnap ? kDK : 1][kVBlock];
 
     // all value blocks of one (sequence, head) land on the same XCD (blocks are
     // dealt to the 8 XCDs round-robin), so they share that XCD's L2
+    constexpr int kWgPerUnit = kNumVBlocks / kNB;
     const int id = blockIdx.x;
     const int xcd = id & 7, qid = id >> 3;
-    const int unit = (qid >> 3) * 8 + xcd;
-    const int blk = qid & 7;
+    const int unit = (int)((unsigned)qid / kWgPerUnit) * 8 + xcd;
+    const int blk = (int)((unsigned)qid % kWgPerUnit) * kNB;   // first value block of the workgroup
     if (unit >= units)
         return;
     const int n = unit / H, h = unit % H;
@@ -659,24 +672,35 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     // the chunk loop runs in rounds of kPrefetch iterations; iterations past the
     // last chunk (at most kPrefetch - 1) leave the state unchanged
     const int64_t niter = (nch + kPrefetch - 1) / kPrefetch * kPrefetch;
-    if (w == kSideWave) {
+    if (chain_side_waves<kNB>() == 1 ? w == kSideWave : w >= kSideWave) {
         // side operands of chunk jc (past the end: the last chunk) into register
         // set `set`, later into ring slot jc & 1; two sets, loaded two chunks
-        // ahead, so each wait leaves the newer set's loads in flight
-        bf16x8 nbm[2][4];
+        // ahead, so each wait leaves the newer set's loads in flight.  Side
+        // wave sw fetches Bm of blocks sw * kSideBlocks .. + kSideBlocks - 1
+        // (of the workgroup's), and side wave 0 the decay vector too.
+        constexpr bool kOneSide = chain_side_waves<kNB>() == 1;
+        const int sb0 = kOneSide ? 0 : (w - kSideWave) * kSideBlocks;
+        bf16x8 nbm[2][kSideBlocks][4];
         f32x2 ndec[2];
         auto side_load = [&](int set, int64_t jc) {
             const gbyte *rec = uniform_gptr(rec_of(jc < nch ? jc : nch - 1));
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                nbm[set][i] = gload<bf16x8>(rec, kOffBM + blk * 4096 + i * 1024 + lane * 16u);
-            ndec[set] = gload<f32x2>(rec, kOffDEC + lane * 8u);
+            for (int vb = 0; vb < kSideBlocks; ++vb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    nbm[set][vb][i] = gload<bf16x8>(
+                        rec, kOffBM + (blk + sb0 + vb) * 4096 + i * 1024 + lane * 16u);
+            if (kOneSide || sb0 == 0)
+                ndec[set] = gload<f32x2>(rec, kOffDEC + lane * 8u);
         };
         auto side_store = [&](int set, int slot) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                side_bm[slot][i][lane] = nbm[set][i];
-            *reinterpret_cast<f32x2 *>(&side_dec[slot][2 * lane]) = ndec[set];
+            for (int vb = 0; vb < kSideBlocks; ++vb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    side_bm[slot][sb0 + vb][i][lane] = nbm[set][vb][i];
+            if (kOneSide || sb0 == 0)
+                *reinterpret_cast<f32x2 *>(&side_dec[slot][2 * lane]) = ndec[set];
         };
         if (nch > 0) {
             side_load(0, 0);
@@ -714,10 +738,14 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
         __syncthreads();
         for (int64_t jc = 0; jc < niter; ++jc) {
             if (jc < nch) {
-                bf16x8 *dst = reinterpret_cast<bf16x8 *>(rec_of(jc) + kOffSB + blk * 4096) + lane;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    dst[ks * 64] = sbuf[jc & 1][ks][lane];
+                for (int vb = 0; vb < kNB; ++vb) {
+                    bf16x8 *dst =
+                        reinterpret_cast<bf16x8 *>(rec_of(jc) + kOffSB + (blk + vb) * 4096) + lane;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        dst[ks * 64] = sbuf[jc & 1][vb][ks][lane];
+                }
             }
             if constexpr (kSnap) {
                 if (snap_at(jc))
@@ -733,19 +761,23 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     }
 
     const int64_t sbase = (int64_t)unit * (kDK * kDV);
-    const int col = kVBlock * blk + m;
+    const int col = kVBlock * blk + m;         // column in the first block (+16 per block)
     const int row0 = 16 * w + 4 * b;           // the wave's rows row0 + i, column col
-    // this wave's half of k-step fragment w / 2, as 4 bf16 at byte 8 (w % 2) of a lane's slot
-    auto put_state = [&](int buf, const f32x4 &x) {
-        *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint8_t *>(&sbuf[buf][w >> 1][lane]) +
+    // this wave's half of k-step fragment w / 2 of block vb, as 4 bf16 at byte
+    // 8 (w % 2) of a lane's slot
+    auto put_state = [&](int buf, int vb, const f32x4 &x) {
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint8_t *>(&sbuf[buf][vb][w >> 1][lane]) +
                                     8 * (w & 1)) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2],
                                                           (bf16)x[3]};
     };
-    f32x4 S;
+    f32x4 S[kNB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        S[i] = init ? init[sbase + (row0 + i) * kDV + col] : 0.f;
-    put_state(0, S);
+    for (int vb = 0; vb < kNB; ++vb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[vb][i] = init ? init[sbase + (row0 + i) * kDV + col + kVBlock * vb] : 0.f;
+        put_state(0, vb, S[vb]);
+    }
     __syncthreads();
 
     // the scheduling barriers keep each stage's loads together and in stage
@@ -771,26 +803,30 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
         for (int s = 0; s < kPrefetch; ++s) {
             const int64_t jc = j0 + s;
             const ChainStage &c = st[s];
-            const bf16x8 *sb = &sbuf[jc & 1][0][lane];
             const f32x4 dec = *reinterpret_cast<const f32x4 *>(&side_dec[jc & 1][row0]);
-            const bf16x4 bm = *reinterpret_cast<const bf16x4 *>(
-                reinterpret_cast<const uint8_t *>(&side_bm[jc & 1][w >> 1][lane]) + 8 * (w & 1));
-            // S' = dec S + Bm - L S for the wave's 16 rows
-            f32x4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[i] = dec[i] * S[i] + (float)bm[i];
+            for (int vb = 0; vb < kNB; ++vb) {
+                const bf16x8 *sb = &sbuf[jc & 1][vb][0][lane];
+                const bf16x4 bm = *reinterpret_cast<const bf16x4 *>(
+                    reinterpret_cast<const uint8_t *>(&side_bm[jc & 1][vb][w >> 1][lane]) +
+                    8 * (w & 1));
+                // S' = dec S + Bm - L S for the wave's 16 rows
+                f32x4 acc;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                acc = mfma16(c.ln[ks], sb[ks * 64], acc);
-            if (jc < nch)
-                S = acc;
-            put_state((jc + 1) & 1, S);
+                for (int i = 0; i < 4; ++i)
+                    acc[i] = dec[i] * S[vb][i] + (float)bm[i];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    acc = mfma16(c.ln[ks], sb[ks * 64], acc);
+                if (jc < nch)
+                    S[vb] = acc;
+                put_state((jc + 1) & 1, vb, S[vb]);
+            }
             if constexpr (kSnap) {
                 if (snap_at(jc + 1)) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        snap_s[(jc + 1) & 1][row0 + i][m] = S[i];
+                        snap_s[(jc + 1) & 1][row0 + i][m] = S[0][i];
                 }
             }
             load_stage(st[s], jc + kPrefetch);
@@ -799,8 +835,10 @@ __global__ __launch_bounds__(kChainThreads) void kda_chain_bf16_kernel(
     }
     if (final_state) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            final_state[sbase + (row0 + i) * kDV + col] = S[i];
+        for (int vb = 0; vb < kNB; ++vb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                final_state[sbase + (row0 + i) * kDV + col + kVBlock * vb] = S[vb][i];
     }
 }
 
@@ -951,22 +989,26 @@ hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *
     return hipGetLastError();
 }
 
-// The chain over the records in ws, one workgroup per (sequence, head, value block).
-// With own_cu each workgroup also reserves LDS it does not use, so that no
-// workgroup of a kernel running beside it shares its CU (and the CU's memory
-// pipeline, which bounds the chain's step).
+// The chain over the records in ws, one workgroup per (sequence, head, kNB
+// value blocks).  With own_cu each workgroup also reserves LDS it does not
+// use, so that no workgroup of a kernel running beside it shares its CU (and
+// the CU's memory pipeline, which bounds the chain's step).
 constexpr int kChainOwnCuLds = 152 * 1024;   // static + reserved LDS per chain workgroup
 
-hipError_t launch_chain(const float *init, float *final_state, float *snaps, int snap_interval,
-                        const int32_t *cu, int N, int T, int H, uint8_t *ws, hipStream_t stream,
-                        bool own_cu = false)
+// Workgroups of the chain for `units` (sequence, head) units: units rounded up
+// to 8 (one per XCD), times the workgroups per unit.
+int64_t chain_workgroups(int64_t units, int nb) { return (units + 7) / 8 * 8 * (kNumVBlocks / nb); }
+
+template <int kNB>
+hipError_t launch_chain_nb(const float *init, float *final_state, const int32_t *cu, int N,
+                           int T, int H, uint8_t *ws, hipStream_t stream, bool own_cu)
 {
     // the reserved (dynamic) part: kChainOwnCuLds less the kernel's static LDS
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
     static size_t reserve = 0;
     std::call_once(attr_once, [] {
-        const void *fn = reinterpret_cast<const void *>(kda_chain_bf16_kernel<false>);
+        const void *fn = reinterpret_cast<const void *>(kda_chain_bf16_kernel<false, kNB>);
         hipFuncAttributes fa{};
         attr_err = hipFuncGetAttributes(&fa, fn);
         if (attr_err == hipSuccess && fa.sharedSizeBytes < (size_t)kChainOwnCuLds) {
@@ -978,23 +1020,47 @@ hipError_t launch_chain(const float *init, float *final_state, float *snaps, int
     const int64_t units = (int64_t)N * H;
     if (units <= 0)
         return hipSuccess;
-    const int64_t blocks = (units + 7) / 8 * 8 * kNumVBlocks;
-    if (snaps) {
-        hipLaunchKernelGGL(kda_chain_bf16_kernel<true>, dim3((unsigned)blocks),
-                           dim3(kChainThreads), 0, stream, init, final_state, snaps,
-                           snap_interval / kChunk, cu, T, H, (int)units, ws);
-    } else {
-        size_t dyn = 0;
-        if (own_cu) {
-            if (attr_err != hipSuccess)
-                return attr_err;
-            dyn = reserve;
-        }
-        hipLaunchKernelGGL(kda_chain_bf16_kernel<false>, dim3((unsigned)blocks),
-                           dim3(kChainThreads), dyn, stream, init, final_state, snaps, 1, cu, T,
-                           H, (int)units, ws);
+    size_t dyn = 0;
+    if (own_cu) {
+        if (attr_err != hipSuccess)
+            return attr_err;
+        dyn = reserve;
     }
+    hipLaunchKernelGGL((kda_chain_bf16_kernel<false, kNB>),
+                       dim3((unsigned)chain_workgroups(units, kNB)), dim3(chain_threads<kNB>()),
+                       dyn, stream, init, final_state, nullptr, 1, cu, T, H, (int)units, ws);
     return hipGetLastError();
+}
+
+// The chain over all units.  When its one-block workgroups outnumber the CUs
+// the chain is bound by the operand stream through the device, not by its
+// serial depth, and workgroups of 4 (or 2) value blocks stream L once for all
+// of them, as long as they still fill the device.
+hipError_t launch_chain(const float *init, float *final_state, float *snaps, int snap_interval,
+                        const int32_t *cu, int N, int T, int H, uint8_t *ws, hipStream_t stream,
+                        bool own_cu = false)
+{
+    const int64_t units = (int64_t)N * H;
+    if (units <= 0)
+        return hipSuccess;
+    if (snaps) {
+        hipLaunchKernelGGL((kda_chain_bf16_kernel<true, 1>),
+                           dim3((unsigned)chain_workgroups(units, 1)), dim3(chain_threads<1>()),
+                           0, stream, init, final_state, snaps, snap_interval / kChunk, cu, T, H,
+                           (int)units, ws);
+        return hipGetLastError();
+    }
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    if (!own_cu && chain_workgroups(units, 4) >= cus)
+        return launch_chain_nb<4>(init, final_state, cu, N, T, H, ws, stream, false);
+    if (!own_cu && chain_workgroups(units, 2) >= cus)
+        return launch_chain_nb<2>(init, final_state, cu, N, T, H, ws, stream, false);
+    return launch_chain_nb<1>(init, final_state, cu, N, T, H, ws, stream, own_cu);
 }
 
 hipError_t launch_output(const bf16 *gate, bf16 *out, const int32_t *cu, int N, int T, int H,
