@@ -85,7 +85,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--extras", default="snapshots_prologue,backward,decode_prologue_verify,long,varlen",
+    ap.add_argument("--extras",
+                    default="snapshots_prologue,backward,decode_prologue_verify,long,varlen",
                     help="comma-separated extra measurements to run (default: all)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the snapshot / prologue / verify measurements")
