@@ -184,16 +184,22 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
 
 // Commit the first accepted[n] verified tokens of sequence n into its state:
 // S <- diag(exp(g_t)) S + k_t u_t^T with the corrections u_t saved by the
-// verification, which reproduces the verified states exactly.
+// verification, which reproduces the verified states exactly.  Tokens are
+// staged kCommitGroup at a time (one load phase and one barrier per group;
+// with the prologue, wave w reduces 1 / |k| of tokens w, w + waves, ...), each
+// with the same arithmetic as a staged decode step.
+constexpr int kCommitGroup = 4;
+
 template <typename T, int DK, int DV, bool kPro>
 __global__ __launch_bounds__(256) void kda_commit_kernel(
     const T *__restrict__ k, const T *__restrict__ g, const float *__restrict__ u,
     const int32_t *__restrict__ accepted, float *__restrict__ state, int K, int H, unsigned pro)
 {
     using Geo = DecodeGeom<T, DK, DV>;
-    constexpr int CG = Geo::CG, RG = Geo::RG, RPT = Geo::RPT;
-    __shared__ float va[DK], vk[DK];
-    __shared__ float nrm[2];
+    constexpr int CG = Geo::CG, RG = Geo::RG, RPT = Geo::RPT, NT = Geo::NT;
+    static_assert(NT % 64 == 0, "whole waves");
+    __shared__ float va[kCommitGroup][DK], vk[kCommitGroup][DK];
+    __shared__ float nrm[kCommitGroup];
 
     const int64_t unit = blockIdx.x;
     const int64_t n = unit / H;
@@ -209,17 +215,51 @@ __global__ __launch_bounds__(256) void kda_commit_kernel(
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
         s_reg[m] = *reinterpret_cast<const f32x4 *>(S + (rg + RG * m) * DV + 4 * cg);
-    for (int t = 0; t < acc; ++t) {
-        const int64_t row = (n * K + t) * H + h;
-        stage_token<T, DK, Geo::NT, kPro>(nullptr, k + row * DK, g + row * DK, va, vk, nullptr,
-                                          nrm, pro, tid);
-        const f32x4 ut = *reinterpret_cast<const f32x4 *>(u + row * DV + 4 * cg);
-#pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int r = rg + RG * m;
-            s_reg[m] = write_row(decay_row(s_reg[m], va[r]), vk[r], ut);
+    for (int t0 = 0; t0 < acc; t0 += kCommitGroup) {
+        const int nt = acc - t0 < kCommitGroup ? acc - t0 : kCommitGroup;
+        const int64_t row0 = (n * K + t0) * H + h;     // token t0 + tt is row row0 + tt H
+        for (int i = tid; i < nt * DK; i += NT) {
+            const int tt = i / DK, c = i % DK;
+            const int64_t row = row0 + (int64_t)tt * H;
+            const float gx = to_f32(g[row * DK + c]);
+            va[tt][c] = __expf((kPro && (pro & kProG)) ? log_decay_from(gx) : gx);
+            vk[tt][c] = to_f32(k[row * DK + c]);
         }
-        __syncthreads();                               // LDS is restaged for the next token
+        f32x4 ut[kCommitGroup];
+#pragma unroll
+        for (int tt = 0; tt < kCommitGroup; ++tt)
+            if (tt < nt)
+                ut[tt] = *reinterpret_cast<const f32x4 *>(u + (row0 + (int64_t)tt * H) * DV +
+                                                          4 * cg);
+        __syncthreads();
+        if (kPro && (pro & kProQK)) {
+            const int l = tid & 63;
+            for (int tt = tid >> 6; tt < nt; tt += NT / 64) {
+                float sk = 0.f;
+                for (int i = l; i < DK; i += 64)
+                    sk += vk[tt][i] * vk[tt][i];
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1)
+                    sk += __shfl_xor(sk, o);
+                if (l == 0)
+                    nrm[tt] = __builtin_amdgcn_rsqf(sk + kNormEps);
+            }
+            __syncthreads();
+            for (int i = tid; i < nt * DK; i += NT)
+                vk[i / DK][i % DK] *= nrm[i / DK];
+            __syncthreads();
+        }
+#pragma unroll
+        for (int tt = 0; tt < kCommitGroup; ++tt) {
+            if (tt < nt) {
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const int r = rg + RG * m;
+                    s_reg[m] = write_row(decay_row(s_reg[m], va[tt][r]), vk[tt][r], ut[tt]);
+                }
+            }
+        }
+        __syncthreads();                               // LDS is restaged for the next group
     }
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
