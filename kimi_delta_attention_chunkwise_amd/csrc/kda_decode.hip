@@ -86,6 +86,143 @@ __device__ __forceinline__ f32x4 write_row(const f32x4 &s, float kr, const f32x4
                  __fmaf_rn(kr, u[3], s[3])};
 }
 
+// The K draft tokens of a verification, on the state in registers: the
+// tokens are staged kVerifyGroup at a time (q, k and exp(g) in LDS, v, beta and
+// the gate logits in registers: one load phase per group), the reductions of
+// token t go to LDS buffer t & 1 (one barrier per token), and each token takes
+// exactly the arithmetic of a decode step.
+constexpr int kVerifyGroup = 4;
+
+template <typename T, int DK, int DV, bool kPro>
+__device__ __forceinline__ void verify_tokens(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ g, const T *__restrict__ beta, const T *__restrict__ gate,
+    T *__restrict__ out, float *__restrict__ u_out, f32x4 *s_reg, int64_t n, int h, int K,
+    int H, float scale, unsigned pro, int tid)
+{
+    using Geo = DecodeGeom<T, DK, DV>;
+    constexpr int CG = Geo::CG, RG = Geo::RG, RPT = Geo::RPT, NT = Geo::NT;
+    constexpr int kG = kVerifyGroup;
+    static_assert(NT % 64 == 0, "whole waves");
+    __shared__ float va[kG][DK], vk[kG][DK], vq[kG][DK];
+    __shared__ float nrm[kG][2];
+    __shared__ f32x4 red_p[2][RG][CG];
+    __shared__ f32x4 red_s[2][RG][CG];
+    __shared__ float red_kq[2][RG];
+    const int cg = tid % CG, rg = tid / CG;
+    for (int t0 = 0; t0 < K; t0 += kG) {
+        const int nt = K - t0 < kG ? K - t0 : kG;
+        const int64_t row0 = (n * K + t0) * H + h;   // token t0 + tt is row row0 + tt H
+        for (int i = tid; i < nt * DK; i += NT) {
+            const int tt = i / DK, c = i % DK;
+            const int64_t row = row0 + (int64_t)tt * H;
+            const float gx = to_f32(g[row * DK + c]);
+            va[tt][c] = __expf((kPro && (pro & kProG)) ? log_decay_from(gx) : gx);
+            vk[tt][c] = to_f32(k[row * DK + c]);
+            vq[tt][c] = to_f32(q[row * DK + c]);
+        }
+        float vb[kG][4], bx[kG], zb[kG][4];
+#pragma unroll
+        for (int tt = 0; tt < kG; ++tt) {
+            if (tt < nt) {
+                const int64_t row = row0 + (int64_t)tt * H;
+                bx[tt] = to_f32(beta[row]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vb[tt][i] = to_f32(v[row * DV + 4 * cg + i]);
+                if (rg == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        zb[tt][i] = to_f32(gate[row * DV + 4 * cg + i]);
+                }
+            }
+        }
+        __syncthreads();
+        if (kPro && (pro & kProQK)) {
+            // 1 / |k| and 1 / |q| of each token, summed as in a decode step
+            const int l = tid & 63;
+            for (int tt = tid >> 6; tt < nt; tt += NT / 64) {
+                float sk = 0.f, sq = 0.f;
+                for (int i = l; i < DK; i += 64) {
+                    sk += vk[tt][i] * vk[tt][i];
+                    sq += vq[tt][i] * vq[tt][i];
+                }
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) {
+                    sk += __shfl_xor(sk, o);
+                    sq += __shfl_xor(sq, o);
+                }
+                if (l == 0) {
+                    nrm[tt][0] = __builtin_amdgcn_rsqf(sk + kNormEps);
+                    nrm[tt][1] = __builtin_amdgcn_rsqf(sq + kNormEps);
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < nt * DK; i += NT) {
+                const int tt = i / DK, c = i % DK;
+                vk[tt][c] *= nrm[tt][0];
+                vq[tt][c] *= nrm[tt][1];
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int tt = 0; tt < kG; ++tt) {
+            if (tt < nt) {
+                const int64_t row = row0 + (int64_t)tt * H;
+                const int par = (t0 + tt) & 1;
+                float kk[RPT];
+                f32x4 p = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
+                float kq = 0.f;
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const int r = rg + RG * m;
+                    const float kr = vk[tt][r], qr = vq[tt][r];
+                    kk[m] = kr;
+                    s_reg[m] = decay_row(s_reg[m], va[tt][r]);
+                    p += s_reg[m] * kr;
+                    sq += s_reg[m] * qr;
+                    kq += kr * qr;
+                }
+                red_p[par][rg][cg] = p;
+                red_s[par][rg][cg] = sq;
+                if (cg == 0)
+                    red_kq[par][rg] = kq;
+                // buffer par is written again for token t + 2 only after every
+                // thread has passed this barrier and the next one
+                __syncthreads();
+                f32x4 P = red_p[par][0][cg], SQ = red_s[par][0][cg];
+                float KQ = red_kq[par][0];
+#pragma unroll
+                for (int r = 1; r < RG; ++r) {
+                    P += red_p[par][r][cg];
+                    SQ += red_s[par][r][cg];
+                    KQ += red_kq[par][r];
+                }
+                const float b = (kPro && (pro & kProBeta)) ? sigmoidf_(bx[tt]) : bx[tt];
+                f32x4 u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    u[i] = b * (vb[tt][i] - P[i]);
+#pragma unroll
+                for (int m = 0; m < RPT; ++m)
+                    s_reg[m] = write_row(s_reg[m], kk[m], u);
+                if (rg == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = 4 * cg + i;
+                        const float o = scale * (SQ[i] + KQ * u[i]);
+                        out[row * DV + c] = from_f32<T>(sigmoidf_(zb[tt][i]) * o);
+                    }
+                    if (u_out)
+                        *reinterpret_cast<f32x4 *>(u_out + row * DV + 4 * cg) = u;
+                }
+            }
+        }
+        if (t0 + kG < K)
+            __syncthreads();                           // LDS is restaged for the next group
+    }
+}
+
 // Decode step (K = 1, state written back) and speculative verification
 // (K draft tokens run on the state in registers; the state is left as it was
 // and each token's correction u is saved for kda_commit_kernel).  Inputs of
@@ -122,6 +259,10 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
         s_reg[m] = *reinterpret_cast<const f32x4 *>(S + (rg + RG * m) * DV + 4 * cg);
+    if constexpr (kVerify) {
+        verify_tokens<T, DK, DV, kPro>(q, k, v, g, beta, gate, out, u_out, s_reg, n, h, K, H,
+                                       scale, pro, tid);
+    } else {
     for (int t = 0; t < K; ++t) {
         const int64_t row = (n * K + t) * H + h;
         stage_token<T, DK, Geo::NT, kPro>(q + row * DK, k + row * DK, g + row * DK, va, vk, vq,
@@ -173,6 +314,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
         }
         // the next token's staging and reductions overwrite LDS only after the
         // next barrier, which every thread reaches after its reads of this one
+    }
     }
     if (write_state) {
 #pragma unroll
