@@ -518,11 +518,26 @@ def cpu_baseline(w):
         elapsed += time.perf_counter() - t0
         reps += 1
     per_call = elapsed / reps
+    # one thread, for the per-core rate: about 3 s of the same calls
+    reps1, elapsed1 = 0, 0.0
+    while elapsed1 < 3.0 and reps1 < 5000:
+        t0 = time.perf_counter()
+        oracle.forward(*arrs, n_threads=1)
+        elapsed1 += time.perf_counter() - t0
+        reps1 += 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     del np
     return {"value": w.B * w.T / per_call, "unit": "tokens/s", "cores": min(threads, units),
             "kind": "oracle",
             "sample": f"full prefill_t4096_h8 call (B=1, H=8, T=4096) repeated {reps}x, "
-                      f"{elapsed:.1f} s total; OpenMP over the {units} (sequence, head) units"}
+                      f"{elapsed:.1f} s total; OpenMP over the {units} (sequence, head) units",
+            "single_thread_value": w.B * w.T / (elapsed1 / reps1),
+            "host_cpus": os.cpu_count(), "cpu_model": model}
 
 
 if __name__ == "__main__":

@@ -35,11 +35,14 @@ def draft_inputs(dtype, N, K, H, d, seed, raw):
     return {key: val.to(dtype) for key, val in d_.items()}
 
 
-@pytest.mark.parametrize("dtype,d,pro", [(torch.bfloat16, 128, 0), (torch.float32, 16, 0),
-                                         (torch.bfloat16, 128, 7), (torch.float32, 128, 0)])
-def test_verify_and_commit(dev, dtype, d, pro):
-    N, K, H = 6, 5, 3
-    x = draft_inputs(dtype, N, K, H, d, 80 + d + pro, raw=bool(pro))
+# K = 5 and 9 leave a ragged last group of the four-token staging; K = 1 and 8 do not
+@pytest.mark.parametrize("dtype,d,pro,K", [(torch.bfloat16, 128, 0, 5), (torch.float32, 16, 0, 5),
+                                           (torch.bfloat16, 128, 7, 5), (torch.float32, 128, 0, 5),
+                                           (torch.bfloat16, 128, 0, 1), (torch.bfloat16, 128, 7, 8),
+                                           (torch.float32, 16, 7, 9)])
+def test_verify_and_commit(dev, dtype, d, pro, K):
+    N, H = 6, 3
+    x = draft_inputs(dtype, N, K, H, d, 80 + d + pro + 100 * K, raw=bool(pro))
     xd = {key: val.to(dev) for key, val in x.items()}
     gen = torch.Generator().manual_seed(81)
     st0 = (torch.randn(N, H, d, d, generator=gen) * 0.05).to(dev)
@@ -73,7 +76,7 @@ def test_verify_and_commit(dev, dtype, d, pro):
         worst = max(worst, rel(np32(out[:, t]), ry))
         ref_states.append(ref.copy())
     tol_out = TOL_BF16_OUT if dtype == torch.bfloat16 else 1e-5
-    say(f"verify {dtype} d={d} prologue={pro}: worst out rel err {worst:.3e}")
+    say(f"verify {dtype} d={d} prologue={pro} K={K}: worst out rel err {worst:.3e}")
     assert worst <= tol_out
 
     # commit: accepted prefix lengths 0 .. K (and out-of-range values clamp)
@@ -86,5 +89,5 @@ def test_verify_and_commit(dev, dtype, d, pro):
         a = min(max(int(acc[n_]), 0), K)
         assert torch.equal(committed[n_], states[a][n_]), f"sequence {n_}: commit of {a} tokens"
         worst_s = max(worst_s, rel(np32(committed[n_]), ref_states[a][n_]))
-    say(f"commit {dtype} d={d} prologue={pro}: worst state rel err {worst_s:.3e}")
+    say(f"commit {dtype} d={d} prologue={pro} K={K}: worst state rel err {worst_s:.3e}")
     assert worst_s <= 1e-4
