@@ -994,6 +994,7 @@ hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *
 // use, so that no workgroup of a kernel running beside it shares its CU (and
 // the CU's memory pipeline, which bounds the chain's step).
 constexpr int kChainOwnCuLds = 152 * 1024;   // static + reserved LDS per chain workgroup
+constexpr int kMaxDevices = 64;              // devices with per-device library state
 
 // Workgroups of the chain for `units` (sequence, head) units: units rounded up
 // to 8 (one per XCD), times the workgroups per unit.
@@ -1003,28 +1004,35 @@ template <int kNB>
 hipError_t launch_chain_nb(const float *init, float *final_state, const int32_t *cu, int N,
                            int T, int H, uint8_t *ws, hipStream_t stream, bool own_cu)
 {
-    // the reserved (dynamic) part: kChainOwnCuLds less the kernel's static LDS
-    static std::once_flag attr_once;
-    static hipError_t attr_err = hipSuccess;
-    static size_t reserve = 0;
-    std::call_once(attr_once, [] {
-        const void *fn = reinterpret_cast<const void *>(kda_chain_bf16_kernel<false, kNB>);
-        hipFuncAttributes fa{};
-        attr_err = hipFuncGetAttributes(&fa, fn);
-        if (attr_err == hipSuccess && fa.sharedSizeBytes < (size_t)kChainOwnCuLds) {
-            reserve = kChainOwnCuLds - fa.sharedSizeBytes;
-            attr_err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)reserve);
-        }
-    });
     const int64_t units = (int64_t)N * H;
     if (units <= 0)
         return hipSuccess;
     size_t dyn = 0;
     if (own_cu) {
-        if (attr_err != hipSuccess)
-            return attr_err;
-        dyn = reserve;
+        // the reserved (dynamic) part: kChainOwnCuLds less the kernel's static
+        // LDS, allowed once per device
+        static std::once_flag attr_once[kMaxDevices];
+        static hipError_t attr_err[kMaxDevices];
+        static size_t reserve[kMaxDevices];
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess)
+            return e;
+        if (dev < 0 || dev >= kMaxDevices)
+            return hipErrorInvalidDevice;
+        std::call_once(attr_once[dev], [dev] {
+            const void *fn = reinterpret_cast<const void *>(kda_chain_bf16_kernel<false, kNB>);
+            hipFuncAttributes fa{};
+            attr_err[dev] = hipFuncGetAttributes(&fa, fn);
+            if (attr_err[dev] == hipSuccess && fa.sharedSizeBytes < (size_t)kChainOwnCuLds) {
+                reserve[dev] = kChainOwnCuLds - fa.sharedSizeBytes;
+                attr_err[dev] = hipFuncSetAttribute(
+                    fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)reserve[dev]);
+            }
+        });
+        if (attr_err[dev] != hipSuccess)
+            return attr_err[dev];
+        dyn = reserve[dev];
     }
     hipLaunchKernelGGL((kda_chain_bf16_kernel<false, kNB>),
                        dim3((unsigned)chain_workgroups(units, kNB)), dim3(chain_threads<kNB>()),
@@ -1095,10 +1103,9 @@ constexpr int kMaxSegments = 32;
 struct AuxStream {
     bool ready = false;
     hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
     hipEvent_t seg[kMaxSegments] = {};
 };
-constexpr int kMaxDevices = 64;
 std::mutex g_aux_mutex;
 AuxStream g_aux[kMaxDevices];
 
@@ -1115,10 +1122,28 @@ hipError_t aux_stream(AuxStream *&out)
         e = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking);
         if (e == hipSuccess)
             e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&a.join, hipEventDisableTiming);
         for (int i = 0; i < kMaxSegments && e == hipSuccess; ++i)
             e = hipEventCreateWithFlags(&a.seg[i], hipEventDisableTiming);
-        if (e != hipSuccess)
+        if (e != hipSuccess) {
+            // release what was created, so that a later call starts afresh
+            for (hipEvent_t &ev : a.seg)
+                if (ev) {
+                    (void)hipEventDestroy(ev);
+                    ev = nullptr;
+                }
+            for (hipEvent_t *ev : {&a.fork, &a.join})
+                if (*ev) {
+                    (void)hipEventDestroy(*ev);
+                    *ev = nullptr;
+                }
+            if (a.stream) {
+                (void)hipStreamDestroy(a.stream);
+                a.stream = nullptr;
+            }
             return e;
+        }
         a.ready = true;
     }
     out = &a;
@@ -1152,10 +1177,12 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     std::lock_guard<std::mutex> lock(g_aux_mutex);
     AuxStream *aux = nullptr;
     e = aux_stream(aux);
-    if (e == hipSuccess)
-        e = hipEventRecord(aux->fork, stream);
-    if (e == hipSuccess)
-        e = hipStreamWaitEvent(aux->stream, aux->fork, 0);
+    if (e != hipSuccess)
+        return e;
+    e = hipEventRecord(aux->fork, stream);
+    if (e != hipSuccess)
+        return e;
+    e = hipStreamWaitEvent(aux->stream, aux->fork, 0);
     for (int64_t s = 0; s < nseg && e == hipSuccess; ++s) {
         const int64_t slot0 = s * seg;
         const int64_t ns = n_slots - slot0 < seg ? n_slots - slot0 : seg;
@@ -1171,6 +1198,12 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
         if (e == hipSuccess)
             e = launch_output(gate + tok0 * H * kDV, out + tok0 * H * kDV, nullptr, 1, Ts, H, ns,
                               wss, stream);
+    }
+    if (e != hipSuccess) {
+        // after a failure part way, still order the caller's stream after
+        // whatever reached the second stream, which reads the workspace
+        if (hipEventRecord(aux->join, aux->stream) == hipSuccess)
+            (void)hipStreamWaitEvent(stream, aux->join, 0);
     }
     return e;
 }
