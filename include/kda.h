@@ -34,6 +34,11 @@
  *     nothing is written.  A failed launch returns KDA_ERR_HIP.
  *   - Layouts are row-major and contiguous.  Element types: `dt` gives the
  *     type of q, k, v, g, beta, gate and out; the state is always fp32.
+ *   - Alignment: every tensor pointer 16 bytes, except beta and grad_beta
+ *     (their element size) and cu_seqlens / accepted (4 bytes); workspaces
+ *     and forward records 256 bytes.  A pointer below its alignment returns
+ *     KDA_ERR_MISALIGNED, checked after the other arguments.  Tensors from a
+ *     device allocator, and views of them at whole-token offsets, meet it.
  *   - Values are not range-checked on the device.  Documented preconditions:
  *     beta in [0, 1]; for the chunked forward g must be finite with
  *     g >= -5 (KDA_G_MIN), which bounds the reciprocal of the cumulative decay
@@ -63,7 +68,8 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = 4,        /* (dt, dk, dv, chunk) outside the supported set, or
                                        more than 2^31 - 1 (chunk slot, head) pairs */
     KDA_ERR_WORKSPACE_TOO_SMALL = 5,/* workspace_bytes below the required size    */
-    KDA_ERR_HIP = 6                 /* a HIP launch or runtime call failed        */
+    KDA_ERR_HIP = 6,                /* a HIP launch or runtime call failed        */
+    KDA_ERR_MISALIGNED = 7          /* a pointer below its required alignment     */
 } kda_status;
 
 typedef enum {

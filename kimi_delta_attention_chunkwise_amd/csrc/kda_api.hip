@@ -5,6 +5,8 @@
 #include "kda.h"
 #include "kda_internal.h"
 
+#include <initializer_list>
+
 namespace {
 
 bool valid_dtype(kda_dtype dt) { return dt == KDA_F32 || dt == KDA_BF16; }
@@ -38,6 +40,19 @@ int64_t chunk_slots(int B, int T, int N, int chunk, int varlen)
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+// Alignment the kernels' vector accesses rely on (NULL passes): tensors 16
+// bytes, beta its element, cu_seqlens / accepted 4 bytes, workspaces 256.
+constexpr uintptr_t kTensorAlign = 16, kWorkspaceAlign = 256;
+bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool tensors_aligned(std::initializer_list<const void *> ps)
+{
+    for (const void *p : ps)
+        if (!aligned_to(p, kTensorAlign))
+            return false;
+    return true;
+}
+uintptr_t elem_bytes(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
+
 constexpr unsigned kProAll = KDA_PRO_QK_L2NORM | KDA_PRO_BETA_SIGMOID | KDA_PRO_G_SOFTPLUS;
 static_assert(KDA_PRO_QK_L2NORM == kda::kProQK && KDA_PRO_BETA_SIGMOID == kda::kProBeta &&
                   KDA_PRO_G_SOFTPLUS == kda::kProG,
@@ -57,6 +72,7 @@ const char *kda_status_str(kda_status s)
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
     case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
     case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED";
     }
     return "KDA_ERR_UNKNOWN";
 }
@@ -125,6 +141,10 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const v
     // one workgroup per (chunk slot, head) on a 1-D grid
     if (dt == KDA_BF16 && chunk_slots(B, T, N, chunk, varlen) * (int64_t)H > INT32_MAX)
         return KDA_ERR_UNSUPPORTED;
+    if (!tensors_aligned({q, k, v, g, gate, out, init_state, final_state, snapshots}) ||
+        !aligned_to(beta, elem_bytes(dt)) || !aligned_to(cu_seqlens, 4) ||
+        !aligned_to(workspace, kWorkspaceAlign))
+        return KDA_ERR_MISALIGNED;
     const int interval = snapshots ? snapshot_interval : 0;
     if (dt == KDA_F32)
         return from_hip(kda::launch_chunk_f32(
@@ -179,6 +199,8 @@ kda_status kda_decode_step_ex(const void *q, const void *k, const void *v, const
         return KDA_OK;
     if (!q || !k || !v || !g || !beta || !gate || !state || !out)
         return KDA_ERR_NULL_POINTER;
+    if (!tensors_aligned({q, k, v, g, gate, state, out}) || !aligned_to(beta, elem_bytes(dt)))
+        return KDA_ERR_MISALIGNED;
     return from_hip(kda::launch_decode(q, k, v, g, beta, gate, state, out, nullptr, N, 1, H, dk,
                                        dv, scale, dt == KDA_BF16, prologue, 1, stream));
 }
@@ -200,6 +222,9 @@ kda_status kda_decode_verify(const void *q, const void *k, const void *v, const 
         return KDA_OK;
     if (!q || !k || !v || !g || !beta || !gate || !state || !out)
         return KDA_ERR_NULL_POINTER;
+    if (!tensors_aligned({q, k, v, g, gate, state, out, u_out}) ||
+        !aligned_to(beta, elem_bytes(dt)))
+        return KDA_ERR_MISALIGNED;
     // the state is only read (write_state = 0)
     return from_hip(kda::launch_decode(q, k, v, g, beta, gate, const_cast<float *>(state), out,
                                        u_out, N, K, H, dk, dv, scale, dt == KDA_BF16, prologue, 0,
@@ -222,6 +247,8 @@ kda_status kda_decode_commit(const void *k, const void *g, const float *u,
         return KDA_OK;
     if (!k || !g || !u || !accepted || !state)
         return KDA_ERR_NULL_POINTER;
+    if (!tensors_aligned({k, g, u, state}) || !aligned_to(accepted, 4))
+        return KDA_ERR_MISALIGNED;
     return from_hip(kda::launch_commit(k, g, u, accepted, state, N, K, H, dk, dv,
                                        dt == KDA_BF16, prologue, stream));
 }
@@ -286,6 +313,12 @@ kda_status kda_chunk_bwd_ex(const void *q, const void *k, const void *v, const v
     if ((int64_t)N * H > INT32_MAX ||
         (dt == KDA_BF16 && chunk_slots(B, T, N, chunk, varlen) * (int64_t)H > INT32_MAX))
         return KDA_ERR_UNSUPPORTED;
+    if (!tensors_aligned({q, k, v, g, gate, init_state, grad_out, grad_final_state, grad_q,
+                          grad_k, grad_v, grad_g, grad_gate, grad_init_state}) ||
+        !aligned_to(beta, elem_bytes(dt)) || !aligned_to(grad_beta, elem_bytes(dt)) ||
+        !aligned_to(cu_seqlens, 4) || !aligned_to(fwd_records, kWorkspaceAlign) ||
+        !aligned_to(workspace, kWorkspaceAlign))
+        return KDA_ERR_MISALIGNED;
     if (dt == KDA_BF16)
         return from_hip(kda::launch_chunk_bwd_bf16(
             (const kda::bf16 *)q, (const kda::bf16 *)k, (const kda::bf16 *)v,

@@ -15,7 +15,8 @@ import kimi_delta_attention_chunkwise_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULLP, SHAPE, DTYPE, UNSUP, WS, HIP = range(7)
+OK, NULLP, SHAPE, DTYPE, UNSUP, WS, HIP, MISAL = range(8)
+A = 1 << 20            # a fake device address with every alignment
 
 
 def declared_functions():
@@ -50,7 +51,8 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     for code, name in enumerate(["KDA_OK", "KDA_ERR_NULL_POINTER", "KDA_ERR_BAD_SHAPE",
                                  "KDA_ERR_BAD_DTYPE", "KDA_ERR_UNSUPPORTED",
-                                 "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_HIP"]):
+                                 "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_HIP",
+                                 "KDA_ERR_MISALIGNED"]):
         assert lib.kda_status_str(code).decode() == name
     assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
 
@@ -115,6 +117,35 @@ def test_chunk_fwd_rejects_bad_arguments_before_launch(lib):
     # nothing to do: zero sequences
     assert _chunk(lib, cu=1, N=0, T=0, q=None, k=None, v=None, g=None, beta=None, gate=None,
                   out=None) == OK
+
+
+def test_misaligned_pointers_are_rejected_before_launch(lib):
+    """Tensors need 16 bytes, beta its element, cu_seqlens 4 bytes and the
+    workspace 256; each case has exactly one pointer below its alignment."""
+    REC = lib.kda_chunk_fwd_workspace_bytes(1, 64, 1, 2, 128, 128, 64, 1, 0)
+    ok = dict(q=A, k=A, v=A, g=A, beta=A, gate=A, out=A, ws=A, ws_bytes=REC)
+    for name, off in [("q", 8), ("k", 2), ("v", 4), ("g", 8), ("gate", 8), ("out", 8),
+                      ("init", 8), ("final", 4), ("beta", 1), ("ws", 128)]:
+        kw = dict(ok, init=A, final=A)
+        kw[name] = A + off
+        assert _chunk(lib, **kw) == MISAL, name
+    assert _chunk(lib, **dict(ok, cu=A + 2, ws_bytes=4 * REC)) == MISAL
+    # checked after the other arguments
+    assert _chunk(lib, **dict(ok, q=A + 8, ws_bytes=REC - 1)) == WS
+    p = ctypes.c_void_p
+
+    def step(**kw):
+        a = dict(q=A, k=A, v=A, g=A, beta=A, gate=A, state=A, out=A)
+        a.update(kw)
+        return lib.kda_decode_step(*[p(a[n]) for n in ("q", "k", "v", "g", "beta", "gate",
+                                                        "state", "out")],
+                                   4, 2, 128, 128, 1.0, 1, None)
+    for name, off in [("q", 8), ("v", 8), ("gate", 8), ("state", 8), ("out", 2), ("beta", 1)]:
+        assert step(**{name: A + off}) == MISAL, name
+    assert lib.kda_decode_commit(p(A), p(A), p(A), p(A + 2), p(A), 2, 3, 1, 128, 128, 1, 0,
+                                 None) == MISAL
+    assert lib.kda_decode_verify(p(A), p(A), p(A), p(A), p(A), p(A), p(A), p(A), p(A + 8), 2, 3,
+                                 1, 128, 128, 1.0, 1, 0, None) == MISAL
 
 
 def test_snapshot_slots(lib):
