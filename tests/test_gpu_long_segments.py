@@ -53,3 +53,45 @@ def test_segmented_chain_equals_short_calls_and_oracle(dev):
     say("oracle comparison, both heads over all tokens")
     ro, rf = run_oracle(x)
     check(out, fin, ro, rf, 2e-2, 1e-2, f"long segments T={T}")
+
+
+def test_segmented_calls_from_two_threads(dev):
+    """Two host threads, each on its own stream, run segmented forwards at the
+    same time (they share the library's second stream and its events): each
+    result must be bitwise that of the same call made alone."""
+    import threading
+
+    T, H = 66_000, 2                       # 1,032 chunks: two segments
+    say(f"two threads, B=1 H={H} T={T} each, on two streams")
+    xs = [to(small_inputs(torch.bfloat16, 1, T, H, 128, 128, 78 + i, init_std=0.02), dev)
+          for i in range(2)]
+    alone = []
+    for x in xs:
+        alone.append(kda.chunk_fwd(*[x[k] for k in KEYS], init_state=x["init_state"]))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in xs]   # default priority
+    results = [None, None]
+    errors = []
+
+    def work(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                got = []
+                for _ in range(3):
+                    x = xs[i]
+                    got.append(kda.chunk_fwd(*[x[k] for k in KEYS], init_state=x["init_state"]))
+                results[i] = got
+        except Exception as exc:  # reported below, in the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for out, fin in results[i]:
+            assert torch.equal(out, alone[i][0]) and torch.equal(fin, alone[i][1]), (
+                f"thread {i}: result differs from the call made alone")
