@@ -215,6 +215,7 @@ def main():
     if "varlen" in extras:
         result["extras"]["varlen_4seq_h32"] = bench_varlen(torch, kda, W, dev)
 
+    result["device"] = device_info(torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
 
@@ -499,6 +500,25 @@ def bench_varlen(torch, kda, W, dev, calls=10):
             "tokens_per_s": T / (ms / 1e3),
             "hbm_roofline": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes}}
+
+
+def device_info(torch, dev):
+    """The device the numbers were taken on: name, architecture, compute units,
+    peak shader clock (HIP's hipDeviceAttributeClockRate, enum value 5, kHz)
+    and memory, against which the peaks above are quoted."""
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1), "peak_clock_mhz": None}
+    try:
+        import ctypes
+        # by soname: the HIP runtime torch has already loaded, not a second copy
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        khz = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, dev.index or 0) == 0:
+            info["peak_clock_mhz"] = khz.value / 1000.0
+    except OSError:
+        pass
+    return info
 
 
 def cpu_baseline(w):
