@@ -178,6 +178,21 @@ def test_empty_sequences(dev):
     assert torch.count_nonzero(fin) == 0
 
 
+def test_misaligned_input_is_refused(dev):
+    """A contiguous q that starts one element into its buffer is below the
+    16-byte alignment: the call is refused on the host and writes nothing."""
+    say("misaligned q: refused before launch")
+    x = to(small_inputs(torch.bfloat16, 1, 64, 2, 128, 128, 18), dev)
+    flat = torch.empty(x["q"].numel() + 8, dtype=torch.bfloat16, device=dev)
+    q = flat[1:1 + x["q"].numel()].view(x["q"].shape)
+    q.copy_(x["q"])
+    out = torch.full_like(x["v"], 7.0)
+    with pytest.raises(kda.KdaError, match="KDA_ERR_MISALIGNED"):
+        kda.chunk_fwd(q, x["k"], x["v"], x["g"], x["beta"], x["z"], out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
 def test_bf16_split_equals_single_call(dev):
     say("bf16 split at T/2 (aligned) and at an unaligned point")
     x = small_inputs(torch.bfloat16, 1, 512, 2, 128, 128, 18, init_std=0.02)
