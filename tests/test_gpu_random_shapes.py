@@ -79,3 +79,50 @@ def test_backward_random_shape(dev, dtype, d, seed):
         run_bf16_case(dev, x, dy, dfin, scale, name)
     else:
         run_case(dev, x, dy, dfin, scale, name, TOL_F32)
+
+
+@pytest.mark.parametrize("dtype,d,seed", [(torch.bfloat16, 128, 0), (torch.float32, 16, 1),
+                                         (torch.bfloat16, 16, 2), (torch.float32, 128, 3)])
+def test_decode_random_shape(dev, dtype, d, seed):
+    """A few decode steps on a random (N, H) with random prologue bits, against
+    the oracle's decode step (outputs and the state after every step)."""
+    import numpy as np_
+
+    import oracle
+    from oracle import prologue as P
+    from test_gpu_parity import np32, rel
+    import kimi_delta_attention_chunkwise_amd as kda_
+
+    r = np_.random.default_rng([7801, seed])
+    N, H, steps = int(r.integers(1, 40)), int(r.choice([1, 3, 8, 13])), 3
+    pro = int(r.choice([0, 1, 6, 7]))
+    say(f"decode {dtype} d={d} seed {seed}: N={N} H={H} prologue={pro}, {steps} steps")
+    gen = torch.Generator().manual_seed(7900 + seed)
+    st = torch.randn(N, H, d, d, generator=gen) * 0.05
+    ref = st.double().numpy().copy()
+    state = st.to(dev)
+    worst_o = worst_s = 0.0
+    for t in range(steps):
+        x = {key: torch.randn(*shape, generator=gen) for key, shape in
+             (("q", (N, H, d)), ("k", (N, H, d)), ("v", (N, H, d)), ("g", (N, H, d)),
+              ("beta", (N, H)), ("z", (N, H, d)))}
+        if not pro & P.QK_L2NORM:
+            x["q"] = x["q"] / x["q"].norm(dim=-1, keepdim=True)
+            x["k"] = x["k"] / x["k"].norm(dim=-1, keepdim=True)
+        if not pro & P.BETA_SIGMOID:
+            x["beta"] = torch.sigmoid(x["beta"])
+        if not pro & P.G_SOFTPLUS:
+            x["g"] = torch.clamp(-torch.nn.functional.softplus(x["g"]), min=-5.0)
+        x = {key: val.to(dtype) for key, val in x.items()}
+        out = kda_.decode_step(*[x[key].to(dev) for key in ("q", "k", "v", "g", "beta", "z")],
+                               state, prologue=pro)
+        torch.cuda.synchronize()
+        xs = {key: np32(val) for key, val in x.items()}
+        q, k, beta, g = P.apply(xs["q"], xs["k"], xs["beta"], xs["g"], pro)
+        ry = oracle.decode_step(q, k, xs["v"].astype(np_.float64), g, beta,
+                                xs["z"].astype(np_.float64), ref)
+        worst_o = max(worst_o, rel(np32(out), ry))
+        worst_s = max(worst_s, rel(np32(state), ref))
+    say(f"decode seed {seed}: worst out rel err {worst_o:.3e}, state {worst_s:.3e}")
+    tol = TOL_BF16_OUT if dtype == torch.bfloat16 else 1e-5
+    assert worst_o <= tol and worst_s <= 1e-4
