@@ -1,25 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the KDA hot path on one MI355X.
 
-One step = one ``kda_chunk_fwd`` call (prep, chain and output kernels) over one batch of
-the prefill workload (B=1, H=8, T=4096, dk=dv=128, bf16 inputs, fp32 state,
-64-token chunks).  Inputs are resident in HBM before timing starts; the steps
-rotate over several independent input sets whose total size exceeds the
-256 MB Infinity Cache, so every step reads cold inputs.  The decode workload
-(256 sequences x 32 heads, 512 MiB fp32 state updated in place, 128 steps) is
-timed the same way and reported under "decode".
+One step = one ``kda_chunk_fwd`` call (prep, chain and output kernels) over the
+whole long-context prefill workload: B=1, H=16, T=1,048,576 tokens,
+dk=dv=128, bf16 inputs, fp32 state, 64-token chunks, a quarter of the key
+channels at the log-decay floor g = -5 (the largest configuration that fits one
+GPU).  Inputs are resident in HBM before timing starts; at 4 GiB per tensor
+they are far larger than the 256 MB Infinity Cache, so every step reads them
+from HBM.
 
 Prints one JSON line:
-  value      prefill tokens/s (B * T per call / seconds per call)
-  roofline   the prefill call against the HBM roof: algorithmic bytes per call
-             (1,538 B per token-head + the fp32 final state) / call time,
-             over 8 TB/s; traffic is the HBM bytes from rocprofv3 counters when
-             a summary taken on the current kernel sources exists in profiles/
+  value      prefill tokens/s of that workload (T per call / seconds per call)
+  roofline   the call against the HBM roof: algorithmic bytes per call
+             (1,538 B per token-head + the fp32 final state) / call time, over
+             8 TB/s; traffic = HBM bytes per call from rocprofv3 FETCH_SIZE /
+             WRITE_SIZE counters, when the committed summary was taken on the
+             current kernel sources
   mfma       algorithmic flops per call / call time over the bf16 dense peak
-  cpu_baseline  the fp64 oracle on the same workload on the host cores
-  decode     steps/s, tokens/s and HBM GB/s of the decode step
+             (and the executed bf16 MFMA flops from counters, when current)
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on
+             the host cores
+Named blocks, timed the same way: prefill_t4096_h8 (B=1, H=8, T=4096),
+varlen_4seq_h32 (4 packed sequences, H=32), decode (256 sequences x 32 heads,
+512 MiB fp32 state in place, 128 steps), backward_prefill_t4096_h8; extras:
+snapshots, the fused prologue, speculative verify / commit.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--workloads long,prefill,varlen,decode,backward,extras]
        python bench.py --copy-calibration   (a 1 GiB device copy, for counters)
 """
 from __future__ import annotations
@@ -40,12 +47,13 @@ PREFILL_BYTES_PER_TOKEN_HEAD = 1538      # q, k, g, v, z, out at 256 B each + be
 STATE_BYTES = 128 * 128 * 4              # one fp32 state slice
 DK = DV = 128
 CHUNK = 64
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_prefill_t4096_h8_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_hbm_traffic.json")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "kimi_delta_attention_chunkwise_amd", "csrc", f)
     for f in ("kda_chunk_bf16.hip", "kda_decode.hip", "kda_internal.h", "kda_api.hip",
               "kda_chunk_bwd_bf16.hip")
 ]
+ALL_WORKLOADS = "long,prefill,varlen,decode,backward,extras"
 
 
 def flops_per_token_head(C=CHUNK, dk=DK, dv=DV):
@@ -62,10 +70,10 @@ def source_digest(paths=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(key):
-    """HBM bytes (``hbm_bytes_per_call`` for prefill, ``decode_hbm_bytes_per_step``
-    for decode) from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel sources; else None."""
+def load_traffic(workload, key):
+    """A figure of ``workload`` (``hbm_bytes_per_call``, ``hbm_bytes_per_step``,
+    ``mfma_executed_bf16_flops_per_call``) from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
@@ -73,23 +81,21 @@ def load_traffic(key):
         return None
     if t.get("source_digest") != source_digest():
         return None
-    return float(t[key])
+    v = t.get("workloads", {}).get(workload, {}).get(key)
+    return None if v is None else float(v)
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed calls of the headline workload (about 25 ms each)")
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--extras",
-                    default="snapshots_prologue,backward,decode_prologue_verify,long,varlen",
-                    help="comma-separated extra measurements to run (default: all)")
-    ap.add_argument("--no-extras", action="store_true",
-                    help="skip the snapshot / prologue / verify measurements")
+    ap.add_argument("--workloads", default=ALL_WORKLOADS,
+                    help=f"comma-separated subset of {ALL_WORKLOADS} (default: all)")
     return ap.parse_args()
 
 
@@ -124,11 +130,104 @@ def main():
         return 0
     dev = torch.device("cuda:0")
     kda.load_library()
+    todo = set(args.workloads.split(","))
+    result = {
+        "metric": "KDA prefill tokens/s + decode steps/s; % bf16 MFMA peak / % HBM GB/s peak",
+        "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+    }
+    if "long" in todo:
+        long = bench_long(torch, kda, W, dev, args)
+        result.update(value=long.pop("tokens_per_s"), ms_per_step=long.pop("ms_per_call"))
+        result.update(long)
+    else:
+        result["config"] = {"workload": "long_t1m_h16", "skipped": True}
+    if "prefill" in todo:
+        result["prefill_t4096_h8"] = bench_prefill(torch, kda, W, dev, args,
+                                                   with_extras="extras" in todo)
+    if "backward" in todo:
+        result["backward_prefill_t4096_h8"] = bench_backward(torch, kda, W, dev, args)
+    if "varlen" in todo:
+        result["varlen_4seq_h32"] = bench_varlen(torch, kda, W, dev)
+    if "decode" in todo:
+        result["decode"] = bench_decode(torch, kda, W, dev, args)
+        if "extras" in todo:
+            result.setdefault("extras", {})["decode_prologue_verify"] = bench_decode_extras(
+                torch, kda, W, dev, args)
+    result["device"] = device_info(torch, dev)
+    if not args.no_cpu_baseline and "long" in todo:
+        result["cpu_baseline"] = cpu_baseline(torch, W, dev)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def prefill_roofline(workload, ms, token_heads, states, kernels):
+    """Roofline and MFMA blocks of one forward call: algorithmic bytes (1,538 B per
+    token-head + ``states`` fp32 state slices) and flops per call over the event-timed
+    call time; HBM traffic and executed MFMA flops from the committed counters when
+    they were taken on the current sources."""
+    t_s = ms / 1e3
+    nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * token_heads + states * STATE_BYTES
+    flops = flops_per_token_head() * token_heads
+    achieved = nbytes / t_s / 1e9
+    roof = {"bound": "hbm", "kernel": kernels, "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": load_traffic(workload, "hbm_bytes_per_call"),
+            "algorithmic_bytes_per_call": nbytes}
+    mfma = {"achieved": flops / t_s / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": flops / t_s / 1e12 / BF16_PEAK_TFLOPS, "algorithmic_flops_per_call": flops}
+    executed = load_traffic(workload, "mfma_executed_bf16_flops_per_call")
+    if executed is not None:
+        # bf16 MFMA flops the kernels execute (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512),
+        # masked and folded products included, over the same call time
+        mfma["executed_flops_per_call"] = executed
+        mfma["executed_frac"] = executed / t_s / 1e12 / BF16_PEAK_TFLOPS
+    return roof, mfma
+
+
+def bench_long(torch, kda, W, dev, args):
+    """The headline: one kda_chunk_fwd call over the 1M-token workload (B=1,
+    H=16, T=2^20, a quarter of the key channels at g = -5, zero initial state,
+    final state written), timed over K calls after W warm-up calls."""
+    w = W.WORKLOADS["long_t1m_h16"]
+    x = W.prefill_inputs(w, device=dev, seed=0)
+    B, T, H = w.B, w.T, w.H
+    ws = torch.empty(kda.chunk_fwd_workspace_bytes(B, T, B, H, DK, DV, CHUNK, torch.bfloat16,
+                                                   False), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, T, H, DV, dtype=torch.bfloat16, device=dev)
+    fin = torch.empty(B, H, DK, DV, dtype=torch.float32, device=dev)
+
+    def call(i):
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], workspace=ws, out=out,
+                      final_state=fin)
+
+    w0 = time.perf_counter()
+    ms = _time(torch, call, args.steps, args.warmup)
+    wall = time.perf_counter() - w0
+    print(f"[bench] long_t1m_h16: {args.steps} calls, {ms:.3f} ms per call "
+          f"(wall {wall:.2f} s with {args.warmup} warm-up calls)", file=sys.stderr, flush=True)
+    roof, mfma = prefill_roofline("long_t1m_h16", ms, B * T * H, B * H,
+                                  "kda_chunk_fwd call (prep + chain + output kernels)")
+    res = {"ms_per_call": ms, "tokens_per_s": B * T / (ms / 1e3),
+           "config": {"workload": "long_t1m_h16", "B": B, "T": T, "H": H, "dk": DK, "dv": DV,
+                      "chunk": CHUNK, "global_batch": B, "seq_len": T, "parallelism": "none",
+                      "state": "fp32, zero init, final state written",
+                      "pinned_channels": "a quarter of the key channels at g = -5",
+                      "workspace_bytes": int(ws.numel())},
+           "roofline": roof, "mfma": mfma}
+    del x, ws, out, fin
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(torch, kda, W, dev, args, with_extras=True):
+    """prefill_t4096_h8 (B=1, H=8, T=4096): the calls rotate over enough input
+    sets (> 600 MiB) that every call reads inputs that are not cache-resident."""
     w = W.WORKLOADS["prefill_t4096_h8"]
     B, T, H = w.B, w.T, w.H
-    in_bytes_per_set = B * T * H * (5 * 256 + 2)
-    n_sets = max(2, -(-600 * 2 ** 20 // in_bytes_per_set))      # > 2x the 256 MB MALL
-    sets = [W.prefill_inputs(w, device=dev, seed=s) for s in range(n_sets)]
+    sets = prefill_sets(W, dev)
+    n_sets = len(sets)
     ws = torch.empty(kda.chunk_fwd_workspace_bytes(B, T, B, H, DK, DV, CHUNK, torch.bfloat16,
                                                    False), dtype=torch.uint8, device=dev)
     out = torch.empty(B, T, H, DV, dtype=torch.bfloat16, device=dev)
@@ -139,88 +238,19 @@ def main():
         kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], workspace=ws, out=out,
                       final_state=fin)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    print(f"[bench] prefill warmup done ({args.warmup} steps, {n_sets} input sets)",
-          file=sys.stderr, flush=True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] prefill timed: {args.steps} steps, {ms:.4f} ms/step (wall {wall:.3f} s)",
-          file=sys.stderr, flush=True)
-
-    tokens = B * T
-    token_heads = tokens * H
-    bytes_call = PREFILL_BYTES_PER_TOKEN_HEAD * token_heads + B * H * STATE_BYTES
-    flops_call = flops_per_token_head() * token_heads
-    t_s = ms / 1e3
-    achieved = bytes_call / t_s / 1e9
-    traffic = load_traffic("hbm_bytes_per_call")
-    result = {
-        "metric": "KDA prefill tokens/s + decode steps/s; % bf16 MFMA peak / % HBM GB/s peak",
-        "value": tokens / t_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "prefill_t4096_h8", "B": B, "T": T, "H": H, "dk": DK, "dv": DV,
-                   "chunk": CHUNK, "global_batch": B, "seq_len": T, "parallelism": "none",
-                   "state": "fp32, zero init, final state written", "input_sets": n_sets},
-        "roofline": {"bound": "hbm", "kernel": "kda_chunk_fwd call (prep + chain + output kernels)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_call": bytes_call},
-        "mfma": {"achieved": flops_call / t_s / 1e12, "peak": BF16_PEAK_TFLOPS,
-                 "unit": "TFLOP/s", "frac": flops_call / t_s / 1e12 / BF16_PEAK_TFLOPS,
-                 "algorithmic_flops_per_call": flops_call},
-    }
-    executed = load_traffic("mfma_executed_bf16_flops_per_call")
-    if executed is not None:
-        # bf16 MFMA flops the kernels execute (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512),
-        # masked and folded products included, over the same call time
-        result["mfma"]["executed_flops_per_call"] = executed
-        result["mfma"]["executed_frac"] = executed / t_s / 1e12 / BF16_PEAK_TFLOPS
-    extras = set() if args.no_extras else set(args.extras.split(","))
-    result["extras"] = {}
-    if "snapshots_prologue" in extras:
-        result["extras"]["snapshots_prologue"] = bench_prefill_extras(torch, kda, sets, ws, out,
-                                                                      fin, ms, args)
-    if "backward" in extras:
-        result["extras"]["backward_prefill_t4096_h8"] = bench_backward(torch, kda, sets, ms, args)
-    del sets
-
-    if not args.no_decode:
-        result["decode"] = bench_decode(torch, kda, W, dev, args)
-        if "decode_prologue_verify" in extras:
-            result["extras"]["decode_prologue_verify"] = bench_decode_extras(torch, kda, W, dev,
-                                                                             args)
-
-    if "long" in extras:
-        result["extras"]["long_t1m_h16"] = bench_long(torch, kda, W, dev)
-    if "varlen" in extras:
-        result["extras"]["varlen_4seq_h32"] = bench_varlen(torch, kda, W, dev)
-
-    result["device"] = device_info(torch, dev)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w)
-
-    print(json.dumps(result), flush=True)
-    return 0
+    steps = max(args.steps, 100)
+    ms = _time(torch, step, steps, max(args.warmup, 10))
+    print(f"[bench] prefill_t4096_h8: {steps} calls, {ms:.4f} ms per call", file=sys.stderr,
+          flush=True)
+    roof, mfma = prefill_roofline("prefill_t4096_h8", ms, B * T * H, B * H,
+                                  "kda_chunk_fwd call (prep + chain + output kernels)")
+    res = {"workload": "prefill_t4096_h8", "B": B, "T": T, "H": H, "input_sets": n_sets,
+           "steps": steps, "ms_per_call": ms, "tokens_per_s": B * T / (ms / 1e3),
+           "workspace_bytes": int(ws.numel()), "roofline": roof, "mfma": mfma}
+    if with_extras:
+        res["snapshots_prologue"] = bench_prefill_extras(torch, kda, sets, ws, out, fin, ms, args)
+    del sets, ws, out, fin
+    return res
 
 
 def bench_decode(torch, kda, W, dev, args):
@@ -255,7 +285,7 @@ def bench_decode(torch, kda, W, dev, args):
             "ms_per_step": ms, "steps_per_s": 1e3 / ms, "tokens_per_s": N * 1e3 / ms,
             "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": load_traffic("decode_hbm_bytes_per_step"),
+                         "traffic": load_traffic("decode_n256_h32", "hbm_bytes_per_step"),
                          "algorithmic_bytes_per_step": bytes_step},
             "measured_bandwidth": dict(measured, decode_frac_of_inplace=gbs / measured["inplace_gbs"])}
 
@@ -340,10 +370,20 @@ def bench_prefill_extras(torch, kda, sets, ws, out, fin, ms_plain, args):
             "prologue_tokens_per_s": B * T / (ms_pro / 1e3)}
 
 
-def bench_backward(torch, kda, sets, ms_fwd, args):
+def prefill_sets(W, dev):
+    """Input sets of prefill_t4096_h8, enough of them (> 600 MiB in all) that
+    calls rotating over them read inputs that are not cache-resident."""
+    w = W.WORKLOADS["prefill_t4096_h8"]
+    in_bytes_per_set = w.B * w.T * w.H * (5 * 256 + 2)
+    n_sets = max(2, -(-600 * 2 ** 20 // in_bytes_per_set))      # > 2x the 256 MB MALL
+    return [W.prefill_inputs(w, device=dev, seed=s) for s in range(n_sets)]
+
+
+def bench_backward(torch, kda, W, dev, args):
     """kda_chunk_bwd on the prefill workload: gradients of every input and of
     the initial state from dY ~ N(0, 1) and a zero dS_final, all buffers
-    preallocated, rotating over the same input sets as the forward."""
+    preallocated, rotating over the prefill input sets."""
+    sets = prefill_sets(W, dev)
     x0 = sets[0]
     B, T, H, _ = x0["q"].shape
     dev = x0["q"].device
@@ -381,6 +421,13 @@ def bench_backward(torch, kda, sets, ms_fwd, args):
                       workspace=ws_half, grads=grads, fwd_workspace=ws_fwd)
 
     ms_train = _time(torch, train_step, steps, max(3, args.warmup // 2))
+
+    def fwd(i):
+        x = sets[i % n_sets]
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], workspace=ws_fwd,
+                      out=out, output_final_state=False)
+
+    ms_fwd = _time(torch, fwd, max(20, steps), 5)
     print(f"[bench] forward + backward on the forward's records: {ms_train:.4f} ms",
           file=sys.stderr, flush=True)
     token_heads = B * T * H
@@ -389,18 +436,22 @@ def bench_backward(torch, kda, sets, ms_fwd, args):
     bytes_call = (6 * 256 + 2 + 5 * 256 + 2) * token_heads + B * H * STATE_BYTES
     flops_call = 3 * flops_per_token_head() * token_heads
     t_s = ms / 1e3
-    del ws, grads, ws_fwd, ws_half
+    del ws, grads, ws_fwd, ws_half, sets
     return {"workload": "prefill_t4096_h8", "ms_per_call": ms, "tokens_per_s": B * T / t_s,
-            "ratio_to_forward": ms / ms_fwd, "steps": steps,
+            "forward_ms": ms_fwd, "ratio_to_forward": ms / ms_fwd, "steps": steps,
             "train_step_ms": ms_train, "train_step_tokens_per_s": B * T / (ms_train / 1e3),
             "train_step": "kda_chunk_fwd, then kda_chunk_bwd_ex on its records",
             "kernels": "forward prep + chain, backward prep, chain, gradient kernel",
             "roofline": {"bound": "hbm", "achieved": bytes_call / t_s / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": bytes_call / t_s / 1e9 / HBM_PEAK_GBS,
+                         "traffic": load_traffic("backward_prefill_t4096_h8",
+                                                 "hbm_bytes_per_call"),
                          "algorithmic_bytes_per_call": bytes_call},
             "mfma": {"achieved": flops_call / t_s / 1e12, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops_call / t_s / 1e12 / BF16_PEAK_TFLOPS,
+                     "executed_flops_per_call": load_traffic("backward_prefill_t4096_h8",
+                                                             "mfma_executed_bf16_flops_per_call"),
                      "algorithmic_flops_per_call": flops_call,
                      "flops_rule": "3 x the forward's: the recompute plus two products of "
                                    "the same size for the adjoint of each product"}}
@@ -446,31 +497,6 @@ def bench_decode_extras(torch, kda, W, dev, args):
             "verified_tokens_per_s": N * K / ((ms_ver + ms_com) / 1e3)}
 
 
-def bench_long(torch, kda, W, dev, calls=3):
-    """The 1M-token workload (B=1, H=16, T=2^20, a quarter of the key channels
-    at g = -5): one kda_chunk_fwd call over the whole sequence."""
-    w = W.WORKLOADS["long_t1m_h16"]
-    x = W.prefill_inputs(w, device=dev, seed=0)
-    B, T, H = w.B, w.T, w.H
-    ws = torch.empty(kda.chunk_fwd_workspace_bytes(B, T, B, H, DK, DV, CHUNK, torch.bfloat16,
-                                                   False), dtype=torch.uint8, device=dev)
-    out = torch.empty(B, T, H, DV, dtype=torch.bfloat16, device=dev)
-    fin = torch.empty(B, H, DK, DV, dtype=torch.float32, device=dev)
-
-    def call(i):
-        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], workspace=ws, out=out,
-                      final_state=fin)
-
-    ms = _time(torch, call, calls, 1)
-    token_heads = B * T * H
-    gbs = (PREFILL_BYTES_PER_TOKEN_HEAD * token_heads + B * H * STATE_BYTES) / (ms / 1e3) / 1e9
-    print(f"[bench] long_t1m_h16: {ms:.3f} ms per call", file=sys.stderr, flush=True)
-    del x, ws, out
-    return {"workload": "long_t1m_h16", "ms_per_call": ms, "tokens_per_s": B * T / (ms / 1e3),
-            "hbm_roofline": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": gbs / HBM_PEAK_GBS}}
-
-
 def bench_varlen(torch, kda, W, dev, calls=10):
     """The packed varlen workload: 4 sequences (lengths drawn uniform in
     [1024, 32768], seed 0) in one cu_seqlens call, H=32, fp32 initial state
@@ -490,16 +516,16 @@ def bench_varlen(torch, kda, W, dev, calls=10):
                       out=out, final_state=fin)
 
     ms = _time(torch, call, calls, 2)
-    token_heads = T * H
-    nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * token_heads + 2 * N * H * STATE_BYTES
-    gbs = nbytes / (ms / 1e3) / 1e9
     print(f"[bench] varlen_4seq_h32 (lengths {lens}): {ms:.3f} ms per call", file=sys.stderr,
           flush=True)
+    # state I/O: the fp32 initial state is read and the final state written
+    roof, mfma = prefill_roofline("varlen_4seq_h32", ms, T * H, 2 * N * H,
+                                  "kda_chunk_fwd call (prep + chain + output kernels)")
+    nbytes = int(ws.numel())
     del x, ws, out
-    return {"workload": "varlen_4seq_h32", "lengths": lens, "ms_per_call": ms,
-            "tokens_per_s": T / (ms / 1e3),
-            "hbm_roofline": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes}}
+    return {"workload": "varlen_4seq_h32", "lengths": lens, "calls": calls, "ms_per_call": ms,
+            "tokens_per_s": T / (ms / 1e3), "workspace_bytes": nbytes, "roofline": roof,
+            "mfma": mfma}
 
 
 def device_info(torch, dev):
@@ -521,37 +547,46 @@ def device_info(torch, dev):
     return info
 
 
-def cpu_baseline(w):
-    """The fp64 oracle (as it stands) on the same prefill workload, host cores."""
+def cpu_baseline(torch, W, dev):
+    """The fp64 oracle (as it stands) on a bounded sample of the headline
+    workload: the first tokens of long_t1m_h16, all 16 heads, in consecutive
+    segments of 32,768 tokens (the same inputs the GPU ran, widened exactly
+    from bf16 to float32 on the host), the state carried from segment to
+    segment, until about 10 s have passed; OpenMP over the 16 heads.  Also the
+    one-thread rate on one head, and the oracle's decode rate."""
     import numpy as np
 
     import oracle
-    import workloads as W
-    x = W.prefill_inputs(w, device="cpu", seed=0)
-    arrs = [x[k].float().numpy() for k in ("q", "k", "v", "g", "beta", "z")]
+    w = W.WORKLOADS["long_t1m_h16"]
+    x = W.prefill_inputs(w, device=dev, seed=0)
+    keys = ("q", "k", "v", "g", "beta", "z")
     threads = max(1, min(os.cpu_count() or 1, 16))
-    units = w.B * w.H
-    reps, elapsed = 0, 0.0
-    while elapsed < 10.0 and reps < 5000:
+    seg = 32768
+    state = None
+    tokens, elapsed = 0, 0.0
+    while elapsed < 10.0 and tokens + seg <= w.T:
+        arrs = [x[k][:, tokens:tokens + seg].float().cpu().numpy() for k in keys]
         t0 = time.perf_counter()
-        oracle.forward(*arrs, n_threads=threads)
+        _, state = oracle.forward(*arrs, init_state=state, n_threads=threads)
         elapsed += time.perf_counter() - t0
-        reps += 1
-    per_call = elapsed / reps
-    # one thread, for the per-core rate: about 3 s of the same calls
-    reps1, elapsed1 = 0, 0.0
-    while elapsed1 < 3.0 and reps1 < 5000:
+        tokens += seg
+    # one thread, one head, about 3 s
+    one = [x[k][:, :seg, :1].float().cpu().numpy() for k in keys]
+    t1, e1 = 0, 0.0
+    while e1 < 3.0 and t1 < 64:
         t0 = time.perf_counter()
-        oracle.forward(*arrs, n_threads=1)
-        elapsed1 += time.perf_counter() - t0
-        reps1 += 1
+        oracle.forward(*one, n_threads=1)
+        e1 += time.perf_counter() - t0
+        t1 += 1
+    del x, one
+    torch.cuda.empty_cache()
     # decode_n256_h32 (256 sequences x 32 heads, fp64 state in place): a few steps
     wd = W.WORKLOADS["decode_n256_h32"]
     st = W.decode_init_state(wd, device="cpu", seed=0).double().numpy()
     dins = []
     for i in range(8):
         xd = W.decode_inputs(wd, i, device="cpu", seed=0)
-        dins.append([xd[k].float().numpy() for k in ("q", "k", "v", "g", "beta", "z")])
+        dins.append([xd[k].float().numpy() for k in keys])
     dsteps, delapsed = 0, 0.0
     while delapsed < 4.0 and dsteps < 4096:
         t0 = time.perf_counter()
@@ -566,11 +601,14 @@ def cpu_baseline(w):
     except OSError:
         pass
     del np
-    return {"value": w.B * w.T / per_call, "unit": "tokens/s", "cores": min(threads, units),
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": min(threads, w.H),
             "kind": "oracle",
-            "sample": f"full prefill_t4096_h8 call (B=1, H=8, T=4096) repeated {reps}x, "
-                      f"{elapsed:.1f} s total; OpenMP over the {units} (sequence, head) units",
-            "single_thread_value": w.B * w.T / (elapsed1 / reps1),
+            "sample": f"long_t1m_h16: the first {tokens:,} of its {w.T:,} tokens, all {w.H} heads, "
+                      f"in segments of {seg:,} tokens with the state carried, {elapsed:.1f} s; "
+                      f"OpenMP over the {w.H} heads with {min(threads, w.H)} threads",
+            "single_thread_value": t1 * seg / e1,
+            "single_thread_sample": f"one head, {seg:,} tokens, {t1} calls, one thread; "
+                                    "tokens/s of that head alone",
             "decode_steps_per_s": dsteps / delapsed,
             "decode_sample": f"decode_n256_h32, {dsteps} steps (8 input sets in turn) of the "
                              f"fp64 oracle on the full state, {delapsed:.1f} s, OpenMP over the "

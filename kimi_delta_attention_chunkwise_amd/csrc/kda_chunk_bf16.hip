@@ -1150,6 +1150,18 @@ hipError_t aux_stream(AuxStream *&out)
     return hipSuccess;
 }
 
+// True when `stream` is recording a graph capture (or when that cannot be
+// told, so that the single-stream schedule, correct everywhere, is taken).
+bool stream_capturing(hipStream_t stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
 }  // namespace
 
 hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
@@ -1163,8 +1175,11 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     if (e != hipSuccess)
         return e;
     // segments need one sequence without cu_seqlens, no snapshots and a final
-    // state buffer to hand the state over in
-    const bool segmented = !cu && N == 1 && !snaps && final_state && n_slots >= kMinSegmentedSlots;
+    // state buffer to hand the state over in; a stream that is being captured
+    // into a graph keeps the single-stream schedule, so that no work of the
+    // shared auxiliary stream is pulled into the capture
+    const bool segmented = !cu && N == 1 && !snaps && final_state &&
+                           n_slots >= kMinSegmentedSlots && !stream_capturing(stream);
     if (!segmented) {
         e = launch_chain(init, final_state, snaps, snap_interval, cu, N, T, H, ws, stream);
         if (e == hipSuccess)

@@ -8,6 +8,10 @@ Contents
   * ``forward`` / ``decode_step``: the plain token-by-token recurrence in fp64,
     in C (``kda_oracle.c``, OpenMP over (sequence, head) units), loaded with
     ctypes.  This is the oracle the GPU path is compared against.
+  * ``forward_compare``: the same recurrence compared on the fly with an
+    output computed elsewhere (per (sequence, head) maximum errors), for
+    inputs too long to hold a float64 output; bfloat16 inputs are widened
+    exactly.
   * ``backward``: reverse-mode gradients of ``forward`` in fp64, token by
     token (same C file).
   * ``oracle.chunkwise``: a second fp64 implementation in NumPy that follows
@@ -36,7 +40,7 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile kda_oracle.c into liboracle.so with gcc (OpenMP, -O2)."""
+    """Compile kda_oracle.c into liboracle.so with gcc (OpenMP, -O3)."""
     if not force and os.path.exists(_LIB_PATH):
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp"
@@ -70,6 +74,9 @@ def _load():
                                         i64, i64, i64, i64, f64, cint,
                                         dp, dp, dp, dp, dp, dp, dp]
     lib.kda_oracle_backward.restype = cint
+    lib.kda_oracle_forward_compare.argtypes = [vp, vp, vp, vp, vp, vp, cint, dp, vp, cint, i64p,
+                                               i64, i64, i64, i64, f64, cint, dp, dp, dp]
+    lib.kda_oracle_forward_compare.restype = cint
     lib.kda_oracle_max_threads.argtypes = []
     lib.kda_oracle_max_threads.restype = cint
     _lib = lib
@@ -139,6 +146,60 @@ def forward(q, k, v, g, beta, z, init_state=None, cu_seqlens=None, scale=1.0,
         raise RuntimeError(f"kda_oracle_forward failed with {rc}")
     out = out.reshape(B, T, H, dv) if batched else out.reshape(T, H, dv)
     return out, final
+
+
+def forward_compare(q, k, v, g, beta, z, x, init_state=None, cu_seqlens=None, scale=1.0,
+                    bf16=False, n_threads=None):
+    """``forward`` compared on the fly with an output ``x`` computed elsewhere.
+
+    Needs no float64 output array, so it serves inputs too long to hold one
+    (a million tokens x 16 heads).  Inputs are float32 arrays, or with
+    ``bf16=True`` uint16 arrays holding bfloat16 bit patterns (widened exactly);
+    ``x`` is float32 or, with ``bf16=True``, bfloat16 bits, laid out like the
+    output.  Shapes as in ``forward``.  Returns ``(err, ref, final)``: per
+    (sequence, head) ``err[n, h] = max |x - y|`` and ``ref[n, h] = max |y|`` over
+    that sequence's tokens and value channels (``y`` = the recurrence's output),
+    and the final state ``[N, H, dk, dv]`` float64."""
+    q = np.asarray(q)
+    if q.ndim == 4:
+        B, T, H, dk = q.shape
+    else:
+        B = 1
+        T, H, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    want = np.uint16 if bf16 else np.float32
+    arrs = [np.asarray(a) for a in (q, k, v, g, beta, z, x)]
+    for a in arrs:
+        if a.dtype != want or not a.flags["C_CONTIGUOUS"]:
+            raise TypeError(f"forward_compare wants C-contiguous {np.dtype(want).name} arrays")
+    if arrs[6].size != B * T * H * dv:
+        raise ValueError("x must have the output's size")
+    if cu_seqlens is None:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("cu_seqlens needs a batch dimension of 1")
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int64)
+        if cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+            raise ValueError("cu_seqlens must start at 0, end at T and be non-decreasing")
+    N = len(cu) - 1
+    init = None
+    if init_state is not None:
+        init = np.ascontiguousarray(np.asarray(init_state), dtype=np.float64)
+        if init.shape != (N, H, dk, dv):
+            raise ValueError(f"init_state shape {init.shape} != {(N, H, dk, dv)}")
+    err = np.empty((N, H), dtype=np.float64)
+    ref = np.empty((N, H), dtype=np.float64)
+    final = np.empty((N, H, dk, dv), dtype=np.float64)
+    code = 2 if bf16 else 1
+    nt = n_threads if n_threads else max_threads()
+    rc = _load().kda_oracle_forward_compare(*(_ptr(a) for a in arrs[:6]), code, _ptr(init),
+                                            _ptr(arrs[6]), code, _ptr(cu), N, H, dk, dv,
+                                            float(scale), int(nt), _ptr(err), _ptr(ref),
+                                            _ptr(final))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_forward_compare failed with {rc}")
+    return err, ref, final
 
 
 def backward(q, k, v, g, beta, z, dout, init_state=None, dfinal=None, cu_seqlens=None,

@@ -41,8 +41,8 @@
  *   q, k, g    [T_total, H, dk]      v, z, out  [T_total, H, dv]
  *   beta       [T_total, H]          state      [N, H, dk, dv]
  *   cu_seqlens [N + 1], int64, cu[0] = 0, non-decreasing, cu[N] = T_total.
- * Inputs are either double or float (in_f32 = 1); float inputs are widened
- * exactly to double on read.
+ * Inputs are double (in_type = 0), float (1) or bfloat16 bit patterns (2,
+ * uint16); float and bfloat16 inputs are widened exactly to double on read.
  */
 #include <math.h>
 #include <stdint.h>
@@ -52,9 +52,19 @@
 #include <omp.h>
 #endif
 
-static double rd(const void *p, int in_f32, int64_t i)
+/* Element i of an input: in_type 0 = double, 1 = float, 2 = bfloat16 (the
+ * upper 16 bits of an IEEE single, widened exactly). */
+static double rd(const void *p, int in_type, int64_t i)
 {
-    return in_f32 ? (double)((const float *)p)[i] : ((const double *)p)[i];
+    if (in_type == 1)
+        return (double)((const float *)p)[i];
+    if (in_type == 2) {
+        uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return ((const double *)p)[i];
 }
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
@@ -63,14 +73,14 @@ static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
  * qo, ko, vo, bo: element offsets of this token-head in the inputs.
  * a, p, u: scratch of length dk, dv, dv.  Writes dv outputs to y. */
 static void kda_token(const void *q, const void *k, const void *v, const void *g,
-                      const void *beta, const void *z, int in_f32,
+                      const void *beta, const void *z, int in_type,
                       int64_t qo, int64_t vo, int64_t bo, int64_t dk, int64_t dv,
                       double scale, double *S, double *a, double *p, double *u,
                       double *y)
 {
     int64_t i, j;
     for (i = 0; i < dk; ++i)
-        a[i] = exp(rd(g, in_f32, qo + i));
+        a[i] = exp(rd(g, in_type, qo + i));
     /* decay: every row i (key channel) scales by a[i] */
     for (i = 0; i < dk; ++i)
         for (j = 0; j < dv; ++j)
@@ -79,17 +89,17 @@ static void kda_token(const void *q, const void *k, const void *v, const void *g
     for (j = 0; j < dv; ++j)
         p[j] = 0.0;
     for (i = 0; i < dk; ++i) {
-        double ki = rd(k, in_f32, qo + i);
+        double ki = rd(k, in_type, qo + i);
         for (j = 0; j < dv; ++j)
             p[j] += S[i * dv + j] * ki;
     }
     /* delta-rule correction */
-    double b = rd(beta, in_f32, bo);
+    double b = rd(beta, in_type, bo);
     for (j = 0; j < dv; ++j)
-        u[j] = b * (rd(v, in_f32, vo + j) - p[j]);
+        u[j] = b * (rd(v, in_type, vo + j) - p[j]);
     /* write */
     for (i = 0; i < dk; ++i) {
-        double ki = rd(k, in_f32, qo + i);
+        double ki = rd(k, in_type, qo + i);
         for (j = 0; j < dv; ++j)
             S[i * dv + j] += ki * u[j];
     }
@@ -97,19 +107,19 @@ static void kda_token(const void *q, const void *k, const void *v, const void *g
     for (j = 0; j < dv; ++j)
         p[j] = 0.0;
     for (i = 0; i < dk; ++i) {
-        double qi = rd(q, in_f32, qo + i);
+        double qi = rd(q, in_type, qo + i);
         for (j = 0; j < dv; ++j)
             p[j] += S[i * dv + j] * qi;
     }
     for (j = 0; j < dv; ++j)
-        y[j] = sigmoid(rd(z, in_f32, vo + j)) * (scale * p[j]);
+        y[j] = sigmoid(rd(z, in_type, vo + j)) * (scale * p[j]);
 }
 
 /* Whole-sequence forward.  init_state may be NULL (zeros); final_state may
  * be NULL (not written); out may be NULL (not written).
  * Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
 int kda_oracle_forward(const void *q, const void *k, const void *v, const void *g,
-                       const void *beta, const void *z, int in_f32,
+                       const void *beta, const void *z, int in_type,
                        const double *init_state, double *out, double *final_state,
                        const int64_t *cu_seqlens, int64_t n_seq, int64_t H,
                        int64_t dk, int64_t dv, double scale, int n_threads)
@@ -142,7 +152,7 @@ int kda_oracle_forward(const void *q, const void *k, const void *v, const void *
                 S[e] = S0 ? S0[e] : 0.0;
             for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
                 int64_t qo = (t * H + h) * dk, vo = (t * H + h) * dv, bo = t * H + h;
-                kda_token(q, k, v, g, beta, z, in_f32, qo, vo, bo, dk, dv, scale,
+                kda_token(q, k, v, g, beta, z, in_type, qo, vo, bo, dk, dv, scale,
                           S, a, p, u, y);
                 if (out)
                     memcpy(out + vo, y, sizeof(double) * dv);
@@ -159,11 +169,77 @@ int kda_oracle_forward(const void *q, const void *k, const void *v, const void *
     return failed ? -2 : 0;
 }
 
+/* The same forward as kda_oracle_forward, compared on the fly with an output
+ * x computed elsewhere (x_type 1 = float, 2 = bfloat16 bits, layout of out),
+ * so that long inputs need no double-precision output array.  For every
+ * (sequence, head) unit: err[unit] = max |x - y| and ref[unit] = max |y| over
+ * the unit's tokens and value channels, y the recurrence's output (0 for an
+ * empty sequence).  final_state as in kda_oracle_forward (may be NULL). */
+int kda_oracle_forward_compare(const void *q, const void *k, const void *v, const void *g,
+                               const void *beta, const void *z, int in_type,
+                               const double *init_state, const void *x, int x_type,
+                               const int64_t *cu_seqlens, int64_t n_seq, int64_t H,
+                               int64_t dk, int64_t dv, double scale, int n_threads,
+                               double *err, double *ref, double *final_state)
+{
+    if (!q || !k || !v || !g || !beta || !z || !cu_seqlens || !x || !err || !ref)
+        return -1;
+    if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0 || (x_type != 1 && x_type != 2))
+        return -1;
+    for (int64_t n = 0; n < n_seq; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n] || cu_seqlens[0] != 0)
+            return -1;
+    int64_t units = n_seq * H;
+    int failed = 0;
+    if (n_threads <= 0)
+        n_threads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+    for (int64_t unit = 0; unit < units; ++unit) {
+        int64_t n = unit / H, h = unit % H;
+        double *S = (double *)malloc(sizeof(double) * dk * dv);
+        double *a = (double *)malloc(sizeof(double) * dk);
+        double *p = (double *)malloc(sizeof(double) * dv);
+        double *u = (double *)malloc(sizeof(double) * dv);
+        double *y = (double *)malloc(sizeof(double) * dv);
+        double e_max = 0.0, r_max = 0.0;
+        if (!S || !a || !p || !u || !y) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            const double *S0 = init_state ? init_state + unit * dk * dv : NULL;
+            for (int64_t e = 0; e < dk * dv; ++e)
+                S[e] = S0 ? S0[e] : 0.0;
+            for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
+                int64_t qo = (t * H + h) * dk, vo = (t * H + h) * dv, bo = t * H + h;
+                kda_token(q, k, v, g, beta, z, in_type, qo, vo, bo, dk, dv, scale,
+                          S, a, p, u, y);
+                for (int64_t j = 0; j < dv; ++j) {
+                    double d = fabs(rd(x, x_type, vo + j) - y[j]);
+                    if (!(d <= e_max))          /* NaN in x counts as infinite error */
+                        e_max = d == d ? d : INFINITY;
+                    if (fabs(y[j]) > r_max)
+                        r_max = fabs(y[j]);
+                }
+            }
+            if (final_state)
+                memcpy(final_state + unit * dk * dv, S, sizeof(double) * dk * dv);
+        }
+        err[unit] = e_max;
+        ref[unit] = r_max;
+        free(S);
+        free(a);
+        free(p);
+        free(u);
+        free(y);
+    }
+    return failed ? -2 : 0;
+}
+
 /* One decode step for N independent sequences: the body of the recurrence
  * applied once to state [N, H, dk, dv] in place.  q, k, g [N, H, dk];
  * v, z, out [N, H, dv]; beta [N, H]. */
 int kda_oracle_decode_step(const void *q, const void *k, const void *v, const void *g,
-                           const void *beta, const void *z, int in_f32, double *state,
+                           const void *beta, const void *z, int in_type, double *state,
                            double *out, int64_t N, int64_t H, int64_t dk, int64_t dv,
                            double scale, int n_threads)
 {
@@ -183,7 +259,7 @@ int kda_oracle_decode_step(const void *q, const void *k, const void *v, const vo
 #pragma omp atomic write
             failed = 1;
         } else {
-            kda_token(q, k, v, g, beta, z, in_f32, unit * dk, unit * dv, unit, dk, dv,
+            kda_token(q, k, v, g, beta, z, in_type, unit * dk, unit * dv, unit, dk, dv,
                       scale, state + unit * dk * dv, a, p, u, out + unit * dv);
         }
         free(a);
@@ -211,7 +287,7 @@ int kda_oracle_decode_step(const void *q, const void *k, const void *v, const vo
  * States are recomputed from checkpoints taken every 32 tokens. */
 #define KDA_ORACLE_SEG 32
 int kda_oracle_backward(const void *q, const void *k, const void *v, const void *g,
-                        const void *beta, const void *z, int in_f32,
+                        const void *beta, const void *z, int in_type,
                         const double *init_state, const double *dout, const double *dfinal,
                         const int64_t *cu_seqlens, int64_t n_seq, int64_t H, int64_t dk,
                         int64_t dv, double scale, int n_threads, double *dq, double *dk_out,
@@ -259,7 +335,7 @@ int kda_oracle_backward(const void *q, const void *k, const void *v, const void 
                 if (i % KDA_ORACLE_SEG == 0)
                     memcpy(ck + (i / KDA_ORACLE_SEG) * sd, S, sizeof(double) * sd);
                 const int64_t t = t0 + i;
-                kda_token(q, k, v, g, beta, z, in_f32, (t * H + h) * dk, (t * H + h) * dv,
+                kda_token(q, k, v, g, beta, z, in_type, (t * H + h) * dk, (t * H + h) * dv,
                           t * H + h, dk, dv, scale, S, a, p, u, y);
             }
             for (int64_t e = 0; e < sd; ++e)
@@ -272,46 +348,46 @@ int kda_oracle_backward(const void *q, const void *k, const void *v, const void 
                 for (int64_t i = 0; i < nl; ++i) {
                     memcpy(sb + (i + 1) * sd, sb + i * sd, sizeof(double) * sd);
                     const int64_t t = t0 + i0 + i;
-                    kda_token(q, k, v, g, beta, z, in_f32, (t * H + h) * dk, (t * H + h) * dv,
+                    kda_token(q, k, v, g, beta, z, in_type, (t * H + h) * dk, (t * H + h) * dv,
                               t * H + h, dk, dv, scale, sb + (i + 1) * sd, a, p, u, y);
                 }
                 for (int64_t i = nl - 1; i >= 0; --i) {
                     const int64_t t = t0 + i0 + i;
                     const int64_t qo = (t * H + h) * dk, vo = (t * H + h) * dv, bo = t * H + h;
                     const double *Sp = sb + i * sd, *Sn = sb + (i + 1) * sd;
-                    const double b = rd(beta, in_f32, bo);
+                    const double b = rd(beta, in_type, bo);
                     int64_t r, j;
                     /* recompute a, S~, p, u of this token */
                     for (r = 0; r < dk; ++r)
-                        a[r] = exp(rd(g, in_f32, qo + r));
+                        a[r] = exp(rd(g, in_type, qo + r));
                     for (r = 0; r < dk; ++r)
                         for (j = 0; j < dv; ++j)
                             Sd[r * dv + j] = a[r] * Sp[r * dv + j];
                     for (j = 0; j < dv; ++j)
                         p[j] = 0.0;
                     for (r = 0; r < dk; ++r) {
-                        const double kr = rd(k, in_f32, qo + r);
+                        const double kr = rd(k, in_type, qo + r);
                         for (j = 0; j < dv; ++j)
                             p[j] += Sd[r * dv + j] * kr;
                     }
                     for (j = 0; j < dv; ++j)
-                        u[j] = (rd(v, in_f32, vo + j) - p[j]) * b;
+                        u[j] = (rd(v, in_type, vo + j) - p[j]) * b;
                     /* read and gate */
                     for (j = 0; j < dv; ++j)
                         y[j] = 0.0;                        /* y = S_new^T q (unscaled) */
                     for (r = 0; r < dk; ++r) {
-                        const double qr = rd(q, in_f32, qo + r);
+                        const double qr = rd(q, in_type, qo + r);
                         for (j = 0; j < dv; ++j)
                             y[j] += Sn[r * dv + j] * qr;
                     }
                     for (j = 0; j < dv; ++j) {
-                        const double sg = sigmoid(rd(z, in_f32, vo + j));
+                        const double sg = sigmoid(rd(z, in_type, vo + j));
                         const double o = scale * y[j];
                         dz[vo + j] = dout[vo + j] * o * sg * (1.0 - sg);
                         dov[j] = dout[vo + j] * sg;
                     }
                     for (r = 0; r < dk; ++r) {
-                        const double qr = rd(q, in_f32, qo + r);
+                        const double qr = rd(q, in_type, qo + r);
                         double acc = 0.0;
                         for (j = 0; j < dv; ++j) {
                             acc += Sn[r * dv + j] * dov[j];
@@ -323,7 +399,7 @@ int kda_oracle_backward(const void *q, const void *k, const void *v, const void 
                     for (j = 0; j < dv; ++j)
                         du[j] = 0.0;
                     for (r = 0; r < dk; ++r) {
-                        const double kr = rd(k, in_f32, qo + r);
+                        const double kr = rd(k, in_type, qo + r);
                         double acc = 0.0;
                         for (j = 0; j < dv; ++j) {
                             du[j] += dS[r * dv + j] * kr;
@@ -334,7 +410,7 @@ int kda_oracle_backward(const void *q, const void *k, const void *v, const void 
                     /* correction: u = beta (v - p) */
                     double db = 0.0;
                     for (j = 0; j < dv; ++j) {
-                        const double vj = rd(v, in_f32, vo + j);
+                        const double vj = rd(v, in_type, vo + j);
                         db += du[j] * (vj - p[j]);
                         dv_out[vo + j] = b * du[j];
                         dp[j] = -b * du[j];
@@ -342,7 +418,7 @@ int kda_oracle_backward(const void *q, const void *k, const void *v, const void 
                     dbeta[bo] = db;
                     /* prediction: p = S~^T k; then the decay S~ = diag(a) S_prev */
                     for (r = 0; r < dk; ++r) {
-                        const double kr = rd(k, in_f32, qo + r);
+                        const double kr = rd(k, in_type, qo + r);
                         double acc = 0.0, da = 0.0;
                         for (j = 0; j < dv; ++j) {
                             acc += Sd[r * dv + j] * dp[j];

@@ -95,3 +95,38 @@ def test_segmented_calls_from_two_threads(dev):
         for out, fin in results[i]:
             assert torch.equal(out, alone[i][0]) and torch.equal(fin, alone[i][1]), (
                 f"thread {i}: result differs from the call made alone")
+
+
+def test_long_forward_captured_in_a_graph(dev):
+    """A forward long enough for the segmented schedule, captured in a HIP
+    graph: while the caller's stream is capturing, the library keeps every
+    kernel on that stream (no work of its shared second stream enters the
+    capture).  Each replay, with eager library work and synchronisations in
+    between, must be bitwise the eager call; the result matches the oracle."""
+    T, H = 70_000, 2
+    say(f"graph capture of B=1 H={H} T={T}, three replays")
+    x = small_inputs(torch.bfloat16, 1, T, H, 128, 128, 79, init_std=0.02)
+    xd = to(x, dev)
+    ins = [xd[k] for k in KEYS]
+    ref_out, ref_fin = kda.chunk_fwd(*ins, init_state=xd["init_state"])
+    ws = torch.empty(kda.chunk_fwd_workspace_bytes(1, T, 1, H, 128, 128, 64, torch.bfloat16,
+                                                   False), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(ref_out)
+    fin = torch.empty_like(ref_fin)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kda.chunk_fwd(*ins, init_state=xd["init_state"], workspace=ws, out=out, final_state=fin)
+    other = to(small_inputs(torch.bfloat16, 1, T, H, 128, 128, 80, init_std=0.02), dev)
+    for rep in range(3):
+        out.fill_(0)
+        fin.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin), f"replay {rep} differs"
+        # eager work of the library between replays (the segmented schedule)
+        kda.chunk_fwd(*[other[k] for k in KEYS], init_state=other["init_state"])
+        torch.cuda.synchronize()
+    ro, rf = run_oracle(x)
+    check(out, fin, ro, rf, 2e-2, 1e-2, f"graph-captured long forward T={T}")

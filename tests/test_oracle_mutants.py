@@ -17,19 +17,19 @@ SRC = os.path.join(ROOT, "oracle", "kda_oracle.c")
 
 MUTANTS = {
     "no_decay": ("S[i * dv + j] *= a[i];", "S[i * dv + j] *= 1.0;"),
-    "decay_sign": ("a[i] = exp(rd(g, in_f32, qo + i));", "a[i] = exp(-rd(g, in_f32, qo + i));"),
-    "correction_sign": ("u[j] = b * (rd(v, in_f32, vo + j) - p[j]);",
-                        "u[j] = b * (rd(v, in_f32, vo + j) + p[j]);"),
-    "no_beta": ("u[j] = b * (rd(v, in_f32, vo + j) - p[j]);",
-                "u[j] = (rd(v, in_f32, vo + j) - p[j]);"),
+    "decay_sign": ("a[i] = exp(rd(g, in_type, qo + i));", "a[i] = exp(-rd(g, in_type, qo + i));"),
+    "correction_sign": ("u[j] = b * (rd(v, in_type, vo + j) - p[j]);",
+                        "u[j] = b * (rd(v, in_type, vo + j) + p[j]);"),
+    "no_beta": ("u[j] = b * (rd(v, in_type, vo + j) - p[j]);",
+                "u[j] = (rd(v, in_type, vo + j) - p[j]);"),
     "no_write": ("S[i * dv + j] += ki * u[j];", "S[i * dv + j] += 0.0 * ki * u[j];"),
     "predict_with_query": ("p[j] += S[i * dv + j] * ki;\n    }\n    /* delta-rule",
-                           "p[j] += S[i * dv + j] * rd(q, in_f32, qo + i);\n    }\n    /* delta-rule"),
-    "no_gate": ("y[j] = sigmoid(rd(z, in_f32, vo + j)) * (scale * p[j]);",
+                           "p[j] += S[i * dv + j] * rd(q, in_type, qo + i);\n    }\n    /* delta-rule"),
+    "no_gate": ("y[j] = sigmoid(rd(z, in_type, vo + j)) * (scale * p[j]);",
                 "y[j] = (scale * p[j]);"),
-    "no_scale": ("y[j] = sigmoid(rd(z, in_f32, vo + j)) * (scale * p[j]);",
-                 "y[j] = sigmoid(rd(z, in_f32, vo + j)) * (p[j]);"),
-    "read_with_key": ("double qi = rd(q, in_f32, qo + i);", "double qi = rd(k, in_f32, qo + i);"),
+    "no_scale": ("y[j] = sigmoid(rd(z, in_type, vo + j)) * (scale * p[j]);",
+                 "y[j] = sigmoid(rd(z, in_type, vo + j)) * (p[j]);"),
+    "read_with_key": ("double qi = rd(q, in_type, qo + i);", "double qi = rd(k, in_type, qo + i);"),
 }
 
 

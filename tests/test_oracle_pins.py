@@ -386,3 +386,52 @@ def test_argument_errors():
         oracle.forward(q, k, v, g, beta, z, cu_seqlens=np.array([0, 5, 3, 8]))
     with pytest.raises(ValueError):
         oracle.forward(q, k, v, g, beta, z, init_state=np.zeros((2, 1, 2, 2)))
+
+
+# ----------------------------------------------- streaming comparison (long inputs)
+def _bf16_bits(x):
+    """Round float64 values to bfloat16 with torch (nearest even) and return
+    (the bit patterns as uint16, the same values as float32)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy(), t.float().numpy()
+
+
+def test_compare_widens_bf16_exactly_and_tracks_per_unit_maxima():
+    """bfloat16 bit patterns (rounded by torch, an independent library) widen
+    to the very values forward() sees as float32, and err / ref are the
+    per-(sequence, head) maxima numpy finds on forward()'s own output; an
+    empty sequence reports 0 and keeps its initial state."""
+    rng = np.random.default_rng(21)
+    lens = [7, 0, 19]
+    T, H, dk, dv = sum(lens), 3, 8, 6
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    bits, vals = zip(*(_bf16_bits(x) for x in random_inputs(rng, T, H, dk, dv)))
+    init = rng.standard_normal((len(lens), H, dk, dv)) * 0.1
+    ref_out, ref_fin = oracle.forward(*vals, init_state=init, cu_seqlens=cu, scale=0.8)
+    x_bits, x_vals = _bf16_bits(ref_out + rng.standard_normal(ref_out.shape) * 1e-3)
+    err, ref, fin = oracle.forward_compare(*bits, x_bits, init_state=init, cu_seqlens=cu,
+                                           scale=0.8, bf16=True)
+    np.testing.assert_array_equal(fin, ref_fin)
+    for n in range(len(lens)):
+        sl = slice(cu[n], cu[n + 1])
+        for h in range(H):
+            d = np.abs(x_vals[sl, h].astype(np.float64) - ref_out[sl, h])
+            assert err[n, h] == (d.max() if d.size else 0.0)
+            assert ref[n, h] == (np.abs(ref_out[sl, h]).max() if d.size else 0.0)
+    np.testing.assert_array_equal(fin[1], init[1])
+    # float32 inputs and output give the same maxima as their values
+    err32, ref32, _ = oracle.forward_compare(*vals, x_vals, init_state=init, cu_seqlens=cu,
+                                             scale=0.8)
+    np.testing.assert_array_equal(err32, err)
+    np.testing.assert_array_equal(ref32, ref)
+
+
+def test_compare_counts_nan_as_infinite_error():
+    rng = np.random.default_rng(22)
+    ins = [x.astype(np.float32) for x in random_inputs(rng, 12, 2, 4, 4)]
+    out, _ = oracle.forward(*ins)
+    x = out.astype(np.float32)
+    x[5, 1, 2] = np.nan
+    err, ref, _ = oracle.forward_compare(*ins, x)
+    assert err[0, 1] == np.inf and np.isfinite(err[0, 0])
