@@ -69,7 +69,9 @@ typedef enum {
                                        more than 2^31 - 1 (chunk slot, head) pairs */
     KDA_ERR_WORKSPACE_TOO_SMALL = 5,/* workspace_bytes below the required size    */
     KDA_ERR_HIP = 6,                /* a HIP launch or runtime call failed        */
-    KDA_ERR_MISALIGNED = 7          /* a pointer below its required alignment     */
+    KDA_ERR_MISALIGNED = 7,         /* a pointer below its required alignment     */
+    KDA_ERR_SCRATCH_LIMIT = 8       /* kda_chunk_fwd_noalloc: the sizes need more
+                                       than KDA_NOALLOC_SCRATCH_BYTES of scratch  */
 } kda_status;
 
 typedef enum {
@@ -138,6 +140,28 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void
                          void *out, float *final_state, const int32_t *cu_seqlens, int B, int T,
                          int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* kda_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same computation, arguments and results as kda_chunk_fwd, bit for bit,
+ * without the workspace: it is taken from a static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, which that
+ * GPU holds from the first such call until the process ends.  The call
+ * allocates nothing (no hipMalloc, no stream or event is created: every kernel
+ * runs on `stream`, also for long single sequences).  Sizes whose workspace,
+ * kda_chunk_fwd_workspace_bytes(...), exceeds KDA_NOALLOC_SCRATCH_BYTES
+ * return KDA_ERR_SCRATCH_LIMIT before anything is launched.  Every call on one
+ * GPU uses that GPU's one array: calls that overlap on a GPU (two streams or
+ * two host threads without ordering between them) race and give undefined
+ * results.  No byte of the array needs to start at zero: a call reads only
+ * what it has written earlier in the same call. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, const void *gate, const float *init_state,
+                                 void *out, float *final_state, const int32_t *cu_seqlens, int B,
+                                 int T, int N, int H, int dk, int dv, int chunk, float scale,
+                                 kda_dtype dt, hipStream_t stream);
 
 /* State snapshots for prefix caching and replay ("Kimi K3 second-pass study
  * ledger", section 1 row Q31 and section 3 Fig. 12: the serving engine keeps

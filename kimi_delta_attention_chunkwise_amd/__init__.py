@@ -11,6 +11,8 @@ Entry points (names follow the C ABI):
             cu_seqlens=None, chunk=None, scale=1.0) -> (out, final_state)
   chunk_fwd_snapshots(q, k, v, g, beta, gate, interval, ...)
             -> (out, final_state, snapshots)
+  chunk_fwd_noalloc(q, k, v, g, beta, gate, ...) -> (out, final_state)
+            (no workspace: the library's static scratch array)
   decode_step(q, k, v, g, beta, gate, state, scale=1.0) -> out   (state in place)
   decode_verify(q, k, v, g, beta, gate, state, ...) -> (out, u)  (K draft tokens, state kept)
   decode_commit(k, g, u, accepted, state, ...)                   (accepted prefix into state)
@@ -32,6 +34,7 @@ __all__ = [
     "chunk_bwd_supported", "chunk_fwd_workspace_bytes", "snapshot_slots", "snapshot_index",
     "chunk_fwd_supported", "decode_step_supported", "library_path", "load_library",
     "KDA_F32", "KDA_BF16", "G_MIN", "PRO_QK_L2NORM", "PRO_BETA_SIGMOID", "PRO_G_SOFTPLUS",
+    "chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 KDA_F32 = 0
@@ -89,7 +92,12 @@ _SIGNATURES = {
                          ctypes.c_void_p], ctypes.c_int),
     "kda_decode_step": ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
                         ctypes.c_void_p], ctypes.c_int),
+    "kda_chunk_fwd_noalloc": ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 7 + [ctypes.c_float,
+                              ctypes.c_int, ctypes.c_void_p], ctypes.c_int),
 }
+
+# size of the static scratch array of kda_chunk_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def load_library(path: str | None = None):
@@ -279,6 +287,56 @@ def chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
     out, final_state, _ = _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state,
                                       cu_seqlens, chunk, scale, workspace, out, final_state,
                                       None, None, prologue)
+    return out, final_state
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
+                      cu_seqlens=None, chunk=None, scale=1.0, out=None, final_state=None):
+    """``chunk_fwd`` through ``kda_chunk_fwd_noalloc``: the library takes its
+    workspace from a static device array of ``NOALLOC_SCRATCH_BYTES`` (one per
+    GPU) and allocates nothing.  This wrapper still allocates ``out`` and
+    ``final_state`` with torch unless they are passed in.  Calls that overlap
+    on one GPU race on that array.  Returns ``(out, final_state)``."""
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda.chunk_fwd_noalloc runs on a HIP device; tensors are on " + str(dev))
+    dt = q.dtype
+    code = _dtype_code(dt)
+    chunk = _DEFAULT_CHUNK[code] if chunk is None else int(chunk)
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)),
+                         ("g", g, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+                         ("gate", gate, (B, T, H, dv)), ("beta", beta, (B, T, H))):
+        _need(t, name, shp, dt, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+        _need(cu_seqlens, "cu_seqlens", cu_seqlens.shape, torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if init_state is not None:
+        _need(init_state, "init_state", (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", (B, T, H, dv), dt, dev)
+    if output_final_state:
+        if final_state is None:
+            final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        else:
+            _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
+    else:
+        final_state = None
+    st = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
+                                   _ptr(init_state), _ptr(out), _ptr(final_state),
+                                   _ptr(cu_seqlens), B, T, N, H, dk, dv, chunk, float(scale),
+                                   code, _stream_ptr(dev))
+    _check(st)
     return out, final_state
 
 

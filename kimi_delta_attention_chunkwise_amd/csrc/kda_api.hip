@@ -1,13 +1,51 @@
 // kda_api.hip -- the extern "C" entry points of libkda.so: host-side argument
 // validation, workspace sizing and dispatch to the gfx950 kernels.  Nothing
-// here allocates memory or keeps state between calls (the one auxiliary
+// here allocates memory.  State kept between calls: the device address of the
+// no-allocation forward's static scratch array, per device (the one auxiliary
 // stream of the long-sequence forward lives with its launcher).
 #include "kda.h"
 #include "kda_internal.h"
 
 #include <initializer_list>
+#include <mutex>
 
 namespace {
+
+// Workspace of kda_chunk_fwd_noalloc: one static array per device, in place of
+// the caller's workspace.  In host code `scratch` is only a stand-in for the
+// symbol: its device address (different on every device) comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever handed to the kernels.
+static __device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
+static_assert(KDA_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch keeps records 256-byte aligned");
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kScratchDevices];
+
+// Device address of the current device's scratch array (taken at the first
+// call on that device).
+hipError_t scratch_address(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool valid_dtype(kda_dtype dt) { return dt == KDA_F32 || dt == KDA_BF16; }
 
@@ -73,6 +111,7 @@ const char *kda_status_str(kda_status s)
     case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
     case KDA_ERR_HIP: return "KDA_ERR_HIP";
     case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED";
+    case KDA_ERR_SCRATCH_LIMIT: return "KDA_ERR_SCRATCH_LIMIT";
     }
     return "KDA_ERR_UNKNOWN";
 }
@@ -109,13 +148,20 @@ size_t kda_snapshot_slots(int B, int T, int N, int chunk, int interval, int varl
     return (size_t)B * (size_t)(T / interval);
 }
 
-kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *g,
-                            const void *beta, const void *gate, const float *init_state,
-                            void *out, float *final_state, float *snapshots,
-                            int snapshot_interval, const int32_t *cu_seqlens, int B, int T,
-                            int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
-                            unsigned prologue, void *workspace, size_t workspace_bytes,
-                            hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// The forward behind kda_chunk_fwd_ex and kda_chunk_fwd_noalloc.  noalloc:
+// the workspace is the current device's static scratch array (its size is
+// checked here, before anything else touches the device), and every kernel
+// stays on `stream`.
+kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, const void *gate, const float *init_state, void *out,
+                     float *final_state, float *snapshots, int snapshot_interval,
+                     const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                     int chunk, float scale, kda_dtype dt, unsigned prologue, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream, bool noalloc)
 {
     if (!valid_dtype(dt))
         return KDA_ERR_BAD_DTYPE;
@@ -132,10 +178,16 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const v
     if (has_tokens && (!q || !k || !v || !g || !beta || !gate || !out))
         return KDA_ERR_NULL_POINTER;
     const size_t need = kda_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
-    if (need > 0 && !workspace)
-        return KDA_ERR_NULL_POINTER;
-    if (workspace_bytes < need)
-        return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (noalloc) {
+        if (need > KDA_NOALLOC_SCRATCH_BYTES)
+            return KDA_ERR_SCRATCH_LIMIT;
+        workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    } else {
+        if (need > 0 && !workspace)
+            return KDA_ERR_NULL_POINTER;
+        if (workspace_bytes < need)
+            return KDA_ERR_WORKSPACE_TOO_SMALL;
+    }
     if (N == 0)
         return KDA_OK;
     // one workgroup per (chunk slot, head) on a 1-D grid
@@ -146,6 +198,11 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const v
         !aligned_to(workspace, kWorkspaceAlign))
         return KDA_ERR_MISALIGNED;
     const int interval = snapshots ? snapshot_interval : 0;
+    if (noalloc && dt == KDA_BF16 && need > 0) {
+        const hipError_t e = scratch_address(&workspace);
+        if (e != hipSuccess)
+            return KDA_ERR_HIP;
+    }
     if (dt == KDA_F32)
         return from_hip(kda::launch_chunk_f32(
             (const float *)q, (const float *)k, (const float *)v, (const float *)g,
@@ -155,7 +212,35 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const v
         (const kda::bf16 *)q, (const kda::bf16 *)k, (const kda::bf16 *)v, (const kda::bf16 *)g,
         (const kda::bf16 *)beta, (const kda::bf16 *)gate, init_state, (kda::bf16 *)out,
         final_state, snapshots, interval, cu_seqlens, N, T, H,
-        chunk_slots(B, T, N, chunk, varlen), scale, prologue, workspace, stream));
+        chunk_slots(B, T, N, chunk, varlen), scale, prologue, workspace, stream, !noalloc));
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const void *gate, const float *init_state,
+                            void *out, float *final_state, float *snapshots,
+                            int snapshot_interval, const int32_t *cu_seqlens, int B, int T,
+                            int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
+                            unsigned prologue, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream)
+{
+    return chunk_fwd(q, k, v, g, beta, gate, init_state, out, final_state, snapshots,
+                     snapshot_interval, cu_seqlens, B, T, N, H, dk, dv, chunk, scale, dt,
+                     prologue, workspace, workspace_bytes, stream, false);
+}
+
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, const void *gate, const float *init_state,
+                                 void *out, float *final_state, const int32_t *cu_seqlens, int B,
+                                 int T, int N, int H, int dk, int dv, int chunk, float scale,
+                                 kda_dtype dt, hipStream_t stream)
+{
+    return chunk_fwd(q, k, v, g, beta, gate, init_state, out, final_state, nullptr, 0,
+                     cu_seqlens, B, T, N, H, dk, dv, chunk, scale, dt, 0u, nullptr, 0, stream,
+                     true);
 }
 
 kda_status kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const void *g,

@@ -1168,7 +1168,8 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
                              const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
                              float *final_state, float *snaps, int snap_interval,
                              const int32_t *cu, int N, int T, int H, int64_t n_slots,
-                             float scale, unsigned pro, void *workspace, hipStream_t stream)
+                             float scale, unsigned pro, void *workspace, hipStream_t stream,
+                             bool allow_aux)
 {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     hipError_t e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, pro, ws, stream);
@@ -1178,7 +1179,7 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     // state buffer to hand the state over in; a stream that is being captured
     // into a graph keeps the single-stream schedule, so that no work of the
     // shared auxiliary stream is pulled into the capture
-    const bool segmented = !cu && N == 1 && !snaps && final_state &&
+    const bool segmented = allow_aux && !cu && N == 1 && !snaps && final_state &&
                            n_slots >= kMinSegmentedSlots && !stream_capturing(stream);
     if (!segmented) {
         e = launch_chain(init, final_state, snaps, snap_interval, cu, N, T, H, ws, stream);

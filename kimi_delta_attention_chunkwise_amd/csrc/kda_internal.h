@@ -235,11 +235,14 @@ hipError_t launch_chunk_bwd_f32(const float *q, const float *k, const float *v, 
                                 const int32_t *cu, int N, int T, int H, float scale, float *ws,
                                 hipStream_t stream);
 
+// allow_aux = false keeps every kernel on `stream` (no auxiliary stream is
+// created or used, whatever the sequence length).
 hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                              const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
                              float *final_state, float *snaps, int snap_interval,
                              const int32_t *cu, int N, int T, int H, int64_t n_slots,
-                             float scale, unsigned pro, void *workspace, hipStream_t stream);
+                             float scale, unsigned pro, void *workspace, hipStream_t stream,
+                             bool allow_aux = true);
 
 // Chunkwise backward, bf16, dk = dv = 128, 64-token chunks; the workspace
 // holds two record arrays of n_slots * H records each (forward, backward), or

@@ -15,7 +15,7 @@ import kimi_delta_attention_chunkwise_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULLP, SHAPE, DTYPE, UNSUP, WS, HIP, MISAL = range(8)
+OK, NULLP, SHAPE, DTYPE, UNSUP, WS, HIP, MISAL, SCRATCH = range(9)
 A = 1 << 20            # a fake device address with every alignment
 
 
@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
               "kda_status_str", "kda_chunk_fwd_snapshots", "kda_snapshot_slots",
               "kda_chunk_fwd_ex", "kda_decode_step_ex", "kda_decode_verify",
               "kda_decode_commit", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
-              "kda_chunk_bwd_ex",
+              "kda_chunk_bwd_ex", "kda_chunk_fwd_noalloc",
               "kda_chunk_bwd_supported"):
         assert n in names
 
@@ -52,7 +52,7 @@ def test_status_strings(lib):
     for code, name in enumerate(["KDA_OK", "KDA_ERR_NULL_POINTER", "KDA_ERR_BAD_SHAPE",
                                  "KDA_ERR_BAD_DTYPE", "KDA_ERR_UNSUPPORTED",
                                  "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_HIP",
-                                 "KDA_ERR_MISALIGNED"]):
+                                 "KDA_ERR_MISALIGNED", "KDA_ERR_SCRATCH_LIMIT"]):
         assert lib.kda_status_str(code).decode() == name
     assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
 
@@ -313,3 +313,29 @@ def test_python_binding_refuses_cpu_tensors(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(kda.KdaLibraryError):
         kda.load_library(str(tmp_path / "nope.so"))
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """kda_chunk_fwd_noalloc checks its workspace need against the static
+    scratch size before touching the device; argument errors come first."""
+    ws = lib.kda_chunk_fwd_workspace_bytes
+    rec = ws(1, 64, 1, 1, 128, 128, 64, 1, 0)
+    limit = kda.NOALLOC_SCRATCH_BYTES
+    H = 8
+    t_fit = (limit // (rec * H)) * 64          # the longest B=1, H=8 call that fits
+    assert ws(1, t_fit, 1, H, 128, 128, 64, 1, 0) <= limit
+    assert ws(1, t_fit + 64, 1, H, 128, 128, 64, 1, 0) > limit
+    fn = lib.kda_chunk_fwd_noalloc
+    p = [ctypes.c_void_p(A)] * 6
+    assert fn(*p, None, ctypes.c_void_p(A), None, None, 1, t_fit + 64, 1, H, 128, 128, 64,
+              1.0, 1, None) == SCRATCH
+    # unsupported sizes and bad shapes are reported as such, not as the limit
+    assert fn(*p, None, ctypes.c_void_p(A), None, None, 1, 64, 1, H, 64, 64, 64, 1.0, 1,
+              None) == UNSUP
+    assert fn(*p, None, ctypes.c_void_p(A), None, None, 2, 64, 1, H, 128, 128, 64, 1.0, 1,
+              None) == SHAPE
+    assert fn(None, *p[1:], None, ctypes.c_void_p(A), None, None, 1, 64, 1, H, 128, 128, 64,
+              1.0, 1, None) == NULLP
+    # without cu_seqlens N must equal B
+    assert fn(*p, None, ctypes.c_void_p(A), None, None, 1, 64, 0, H, 128, 128, 64, 1.0, 1,
+              None) == SHAPE
