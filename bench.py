@@ -408,15 +408,16 @@ def bench_backward(torch, kda, W, dev, args):
           flush=True)
     # a training step: the forward, then the backward reusing the forward's records
     ws_fwd = torch.empty(kda.chunk_fwd_workspace_bytes(B, T, B, H, DK, DV, CHUNK,
-                                                       torch.bfloat16, False),
+                                                       torch.bfloat16, False, chunk_records=True),
                          dtype=torch.uint8, device=dev)
     ws_half = torch.empty(ws.numel() - ws_fwd.numel(), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x0["v"])
 
     def train_step(i):
+        # the forward keeps per-chunk records, which the backward then reuses
         x = sets[i % n_sets]
         kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], workspace=ws_fwd,
-                      out=out, output_final_state=False)
+                      out=out, output_final_state=False, chunk_records=True)
         kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], dys[i % 2],
                       workspace=ws_half, grads=grads, fwd_workspace=ws_fwd)
 
@@ -440,7 +441,8 @@ def bench_backward(torch, kda, W, dev, args):
     return {"workload": "prefill_t4096_h8", "ms_per_call": ms, "tokens_per_s": B * T / t_s,
             "forward_ms": ms_fwd, "ratio_to_forward": ms / ms_fwd, "steps": steps,
             "train_step_ms": ms_train, "train_step_tokens_per_s": B * T / (ms_train / 1e3),
-            "train_step": "kda_chunk_fwd, then kda_chunk_bwd_ex on its records",
+            "train_step": "kda_chunk_fwd_ex with per-chunk records, then kda_chunk_bwd_ex "
+                          "on them",
             "kernels": "forward prep + chain, backward prep, chain, gradient kernel",
             "roofline": {"bound": "hbm", "achieved": bytes_call / t_s / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",

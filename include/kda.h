@@ -94,11 +94,23 @@ int kda_decode_step_supported(kda_dtype dt, int dk, int dv);
 /* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 when none
  * is needed, (size_t)-1 for an unsupported or invalid combination).
  * `N` is the number of sequences; `varlen` is 1 when cu_seqlens will be
- * passed.  The size depends only on the arguments, not on cu_seqlens'
- * contents: with cu_seqlens the bound floor(T / chunk) + N chunk slots is
- * used for every head. */
+ * passed (an argument beyond the planned interface: the slot bound differs,
+ * and cu_seqlens' contents are not known on the host).  The size depends only
+ * on the arguments: with cu_seqlens the bound floor(T / 128) + N pair slots is
+ * used for every head.
+ * For KDA_BF16 the forward composes every two consecutive chunks of a sequence
+ * into one step of the serial chunk-to-chunk pass and keeps one 164,352-byte
+ * record per (pair of chunks, head): 1,284 bytes per token-head, against 1,538
+ * bytes per token-head of inputs and outputs (B ceil(T / 128) H records, or
+ * (floor(T / 128) + N) H with cu_seqlens; 21.5 GB for 2^20 tokens x 16 heads).
+ * Calls that keep per-chunk records instead (KDA_FWD_CHUNK_RECORDS, or a
+ * snapshot interval that is an odd multiple of 64) need
+ * kda_chunk_fwd_records_bytes(...): one 131,584-byte record per
+ * (chunk, head), 2,056 bytes per token-head. */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv, int chunk,
                                      kda_dtype dt, int varlen);
+size_t kda_chunk_fwd_records_bytes(int B, int T, int N, int H, int dk, int dv, int chunk,
+                                   kda_dtype dt, int varlen);
 
 /* Chunkwise-parallel KDA forward (prefill / training forward).
  *
@@ -179,7 +191,11 @@ kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, co
  * of snapshots [slots, H, dk, dv] fp32, slots = kda_snapshot_slots(...);
  * slots that match no snapshot are not written.  Replaying a sequence from
  * snapshot m = kda_chunk_fwd on tokens m * interval .. with the snapshot as
- * init_state.  With snapshots NULL the call is exactly kda_chunk_fwd.
+ * init_state.  With snapshots NULL the call is exactly kda_chunk_fwd.  For
+ * KDA_BF16 an interval that is an odd multiple of 64 tokens falls inside a
+ * pair of chunks, so the call keeps per-chunk records and its workspace must
+ * hold kda_chunk_fwd_records_bytes(...) bytes; multiples of 128 need only
+ * kda_chunk_fwd_workspace_bytes(...).
  * kda_snapshot_slots returns (size_t)-1 for invalid sizes. */
 size_t kda_snapshot_slots(int B, int T, int N, int chunk, int interval, int varlen);
 
@@ -207,13 +223,21 @@ kda_status kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, 
 #define KDA_PRO_BETA_SIGMOID 2u
 #define KDA_PRO_G_SOFTPLUS 4u
 
-/* kda_chunk_fwd_snapshots plus the prologue bits (0 = exactly that call). */
+/* Forward flag for the *_ex entry point: keep one record per chunk (not per
+ * pair of chunks) in the workspace, as kda_chunk_bwd_ex needs them; the
+ * workspace must then hold kda_chunk_fwd_records_bytes(...) bytes.  No effect
+ * for KDA_F32 (that path keeps no records). */
+#define KDA_FWD_CHUNK_RECORDS 256u
+
+/* kda_chunk_fwd_snapshots plus `flags`: the prologue bits and
+ * KDA_FWD_CHUNK_RECORDS (0 = exactly that call).  Other bits return
+ * KDA_ERR_UNSUPPORTED. */
 kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *g,
                             const void *beta, const void *gate, const float *init_state,
                             void *out, float *final_state, float *snapshots,
                             int snapshot_interval, const int32_t *cu_seqlens, int B, int T,
                             int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
-                            unsigned prologue, void *workspace, size_t workspace_bytes,
+                            unsigned flags, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
 /* One O(1) recurrent decode step for N independent sequences, updating the
@@ -306,11 +330,12 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const void
                          hipStream_t stream);
 
 /* kda_chunk_bwd reusing the forward's work (training: forward, then backward
- * on the same inputs).  fwd_records = the workspace of a kda_chunk_fwd (or
- * _snapshots) call with KDA_BF16, prologue 0 and the same q, k, v, g, beta,
- * init_state, cu_seqlens, sizes and scale, left untouched since that call;
- * fwd_records_bytes its size.  The backward then skips recomputing every
- * chunk's entry state, and needs only kda_chunk_fwd_workspace_bytes(...) bytes
+ * on the same inputs).  fwd_records = the workspace of a kda_chunk_fwd_ex
+ * call with KDA_BF16, flags = KDA_FWD_CHUNK_RECORDS (no prologue bits) and
+ * the same q, k, v, g, beta, init_state, cu_seqlens, sizes and scale, left
+ * untouched since that call; fwd_records_bytes its size (at least
+ * kda_chunk_fwd_records_bytes(...)).  The backward then skips recomputing every
+ * chunk's entry state, and needs only kda_chunk_fwd_records_bytes(...) bytes
  * of `workspace`.  The records are consumed: their contents are undefined
  * afterwards.  fwd_records NULL = exactly kda_chunk_bwd; fwd_records with
  * KDA_F32 returns KDA_ERR_UNSUPPORTED (that path keeps no records). */

@@ -34,7 +34,7 @@ __all__ = [
     "chunk_bwd_supported", "chunk_fwd_workspace_bytes", "snapshot_slots", "snapshot_index",
     "chunk_fwd_supported", "decode_step_supported", "library_path", "load_library",
     "KDA_F32", "KDA_BF16", "G_MIN", "PRO_QK_L2NORM", "PRO_BETA_SIGMOID", "PRO_G_SOFTPLUS",
-    "chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "FWD_CHUNK_RECORDS",
 ]
 
 KDA_F32 = 0
@@ -44,6 +44,8 @@ G_MIN = -5.0
 PRO_QK_L2NORM = 1
 PRO_BETA_SIGMOID = 2
 PRO_G_SOFTPLUS = 4
+# forward flag: keep per-chunk records for the backward (KDA_FWD_CHUNK_RECORDS)
+FWD_CHUNK_RECORDS = 256
 _DEFAULT_CHUNK = {KDA_F32: 16, KDA_BF16: 64}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +70,7 @@ _SIGNATURES = {
     "kda_chunk_fwd_supported": ([ctypes.c_int] * 4, ctypes.c_int),
     "kda_decode_step_supported": ([ctypes.c_int] * 3, ctypes.c_int),
     "kda_chunk_fwd_workspace_bytes": ([ctypes.c_int] * 9, ctypes.c_size_t),
+    "kda_chunk_fwd_records_bytes": ([ctypes.c_int] * 9, ctypes.c_size_t),
     "kda_chunk_fwd": ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "kda_snapshot_slots": ([ctypes.c_int] * 6, ctypes.c_size_t),
@@ -153,9 +156,13 @@ def decode_step_supported(dtype: torch.dtype, dk: int, dv: int) -> bool:
 
 
 def chunk_fwd_workspace_bytes(B: int, T: int, N: int, H: int, dk: int, dv: int, chunk: int,
-                              dtype: torch.dtype, varlen: bool) -> int:
-    n = load_library().kda_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk,
-                                                     _dtype_code(dtype), int(varlen))
+                              dtype: torch.dtype, varlen: bool, chunk_records: bool = False) -> int:
+    """Workspace bytes of a forward; ``chunk_records``: per-chunk records (a
+    forward whose workspace a backward will reuse, or a snapshot interval that
+    is an odd multiple of 64), else the pair records of the default forward."""
+    lib = load_library()
+    fn = lib.kda_chunk_fwd_records_bytes if chunk_records else lib.kda_chunk_fwd_workspace_bytes
+    n = fn(B, T, N, H, dk, dv, chunk, _dtype_code(dtype), int(varlen))
     if n == ctypes.c_size_t(-1).value:
         raise KdaError("unsupported or invalid sizes for kda_chunk_fwd")
     return int(n)
@@ -198,7 +205,8 @@ def snapshot_index(lengths, interval: int, varlen: bool, T: int | None = None):
 
 
 def _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state, cu_seqlens, chunk,
-                scale, workspace, out, final_state, interval, snapshots, prologue):
+                scale, workspace, out, final_state, interval, snapshots, prologue,
+                chunk_records=False):
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
@@ -237,7 +245,10 @@ def _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state, cu_seqle
             _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
     else:
         final_state = None
-    nbytes = chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, cu_seqlens is not None)
+    per_chunk = bool(chunk_records) or (interval is not None and int(interval) % (2 * chunk) != 0)
+    nbytes = chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, cu_seqlens is not None,
+                                       per_chunk)
+    flags = int(prologue) | (FWD_CHUNK_RECORDS if chunk_records else 0)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < nbytes:
@@ -248,11 +259,11 @@ def _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state, cu_seqle
             snapshots = torch.empty((slots, H, dk, dv), dtype=torch.float32, device=dev)
         else:
             _need(snapshots, "snapshots", (slots, H, dk, dv), torch.float32, dev)
-    if prologue:
+    if flags:
         st = lib.kda_chunk_fwd_ex(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate), _ptr(init_state),
             _ptr(out), _ptr(final_state), _ptr(snapshots), int(interval or 0), _ptr(cu_seqlens),
-            B, T, N, H, dk, dv, chunk, float(scale), code, int(prologue), _ptr(workspace),
+            B, T, N, H, dk, dv, chunk, float(scale), code, flags, _ptr(workspace),
             workspace.numel(), _stream_ptr(dev))
     elif interval is not None:
         st = lib.kda_chunk_fwd_snapshots(
@@ -271,7 +282,7 @@ def _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state, cu_seqle
 
 def chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
               cu_seqlens=None, chunk=None, scale=1.0, workspace=None, out=None,
-              final_state=None, prologue=0):
+              final_state=None, prologue=0, chunk_records=False):
     """Chunkwise-parallel KDA forward on the GPU.
 
     q, k, g ``[B, T, H, dk]``; v, gate ``[B, T, H, dv]``; beta ``[B, T, H]``, all
@@ -281,12 +292,14 @@ def chunk_fwd(q, k, v, g, beta, gate, init_state=None, output_final_state=True,
     Optional preallocated ``workspace`` (uint8, at least
     ``chunk_fwd_workspace_bytes`` bytes), ``out`` and ``final_state``.
     ``prologue``: PRO_* bits for raw inputs (q/k L2 norm, beta logits, g
-    pre-activations); 0 for prepared inputs.
+    pre-activations); 0 for prepared inputs.  ``chunk_records``: keep per-chunk
+    records in ``workspace`` (sized by ``chunk_fwd_workspace_bytes(...,
+    chunk_records=True)``) for a following ``chunk_bwd(..., fwd_workspace=)``.
     Returns ``(out, final_state)``; final_state is None unless requested.
     """
     out, final_state, _ = _chunk_call(q, k, v, g, beta, gate, init_state, output_final_state,
                                       cu_seqlens, chunk, scale, workspace, out, final_state,
-                                      None, None, prologue)
+                                      None, None, prologue, chunk_records)
     return out, final_state
 
 
@@ -464,8 +477,9 @@ def chunk_bwd(q, k, v, g, beta, gate, grad_out, init_state=None, grad_final_stat
     (fp32 ``[N, H, dk, dv]``).  Returns a dict with ``q, k, v, g, beta, gate``
     (the input dtype) and ``init_state`` (fp32, None unless ``want_grad_init``).
     ``grads``: an optional dict of preallocated outputs with those keys.
-    ``fwd_workspace``: the workspace of a ``chunk_fwd`` call on the same inputs
-    (bf16, no prologue), untouched since; its records are reused and consumed."""
+    ``fwd_workspace``: the workspace of a ``chunk_fwd(..., chunk_records=True)``
+    call on the same inputs (bf16, no prologue), untouched since; its records
+    are reused and consumed."""
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
@@ -500,7 +514,7 @@ def chunk_bwd(q, k, v, g, beta, gate, grad_out, init_state=None, grad_final_stat
         if fwd_workspace.device != dev or fwd_workspace.dtype != torch.uint8:
             raise ValueError(f"fwd_workspace must be a uint8 tensor on {dev}")
         nbytes -= chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt,
-                                            cu_seqlens is not None)
+                                            cu_seqlens is not None, chunk_records=True)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or workspace.numel() < nbytes:

@@ -76,6 +76,17 @@ int64_t chunk_slots(int B, int T, int N, int chunk, int varlen)
     return (int64_t)B * ((T + chunk - 1) / chunk);
 }
 
+// Slots of two chunks per head (pair records).
+int64_t pair_slots(int B, int T, int N, int chunk, int varlen)
+{
+    return chunk_slots(B, T, N, 2 * chunk, varlen);
+}
+
+bool sizes_valid(int B, int T, int N, int H, int varlen)
+{
+    return !(B < 1 || T < 0 || N < 0 || H < 1 || (varlen && B != 1) || (!varlen && N != B));
+}
+
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
 // Alignment the kernels' vector accesses rely on (NULL passes): tensors 16
@@ -92,6 +103,7 @@ bool tensors_aligned(std::initializer_list<const void *> ps)
 uintptr_t elem_bytes(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
 
 constexpr unsigned kProAll = KDA_PRO_QK_L2NORM | KDA_PRO_BETA_SIGMOID | KDA_PRO_G_SOFTPLUS;
+constexpr unsigned kFwdFlags = kProAll | KDA_FWD_CHUNK_RECORDS;
 static_assert(KDA_PRO_QK_L2NORM == kda::kProQK && KDA_PRO_BETA_SIGMOID == kda::kProBeta &&
                   KDA_PRO_G_SOFTPLUS == kda::kProG,
               "prologue bits agree with the kernels");
@@ -129,9 +141,17 @@ int kda_decode_step_supported(kda_dtype dt, int dk, int dv)
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv, int chunk,
                                      kda_dtype dt, int varlen)
 {
-    if (!valid_dtype(dt) || !chunk_supported(dt, dk, dv, chunk))
+    if (!valid_dtype(dt) || !chunk_supported(dt, dk, dv, chunk) || !sizes_valid(B, T, N, H, varlen))
         return (size_t)-1;
-    if (B < 1 || T < 0 || N < 0 || H < 1 || (varlen && B != 1) || (!varlen && N != B))
+    if (dt == KDA_F32)
+        return 0;
+    return (size_t)pair_slots(B, T, N, chunk, varlen) * (size_t)H * kda::kPairRecBytes;
+}
+
+size_t kda_chunk_fwd_records_bytes(int B, int T, int N, int H, int dk, int dv, int chunk,
+                                   kda_dtype dt, int varlen)
+{
+    if (!valid_dtype(dt) || !chunk_supported(dt, dk, dv, chunk) || !sizes_valid(B, T, N, H, varlen))
         return (size_t)-1;
     if (dt == KDA_F32)
         return 0;
@@ -160,13 +180,14 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                      const void *beta, const void *gate, const float *init_state, void *out,
                      float *final_state, float *snapshots, int snapshot_interval,
                      const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
-                     int chunk, float scale, kda_dtype dt, unsigned prologue, void *workspace,
+                     int chunk, float scale, kda_dtype dt, unsigned flags, void *workspace,
                      size_t workspace_bytes, hipStream_t stream, bool noalloc)
 {
     if (!valid_dtype(dt))
         return KDA_ERR_BAD_DTYPE;
-    if (!chunk_supported(dt, dk, dv, chunk) || (prologue & ~kProAll) != 0)
+    if (!chunk_supported(dt, dk, dv, chunk) || (flags & ~kFwdFlags) != 0)
         return KDA_ERR_UNSUPPORTED;
+    const unsigned prologue = flags & kProAll;
     const int varlen = cu_seqlens != nullptr;
     if (B < 1 || T < 0 || N < 0 || H < 1)
         return KDA_ERR_BAD_SHAPE;
@@ -177,7 +198,15 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
     const bool has_tokens = (int64_t)B * T > 0;
     if (has_tokens && (!q || !k || !v || !g || !beta || !gate || !out))
         return KDA_ERR_NULL_POINTER;
-    const size_t need = kda_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
+    // bf16: pair records, unless the caller keeps per-chunk records for the
+    // backward or a snapshot falls inside a pair
+    const bool pair = dt == KDA_BF16 && !(flags & KDA_FWD_CHUNK_RECORDS) &&
+                      !(snapshots && snapshot_interval % (2 * chunk) != 0);
+    const size_t need =
+        pair ? kda_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, varlen)
+             : kda_chunk_fwd_records_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
+    const int64_t n_slots =
+        pair ? pair_slots(B, T, N, chunk, varlen) : chunk_slots(B, T, N, chunk, varlen);
     if (noalloc) {
         if (need > KDA_NOALLOC_SCRATCH_BYTES)
             return KDA_ERR_SCRATCH_LIMIT;
@@ -190,8 +219,8 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
     }
     if (N == 0)
         return KDA_OK;
-    // one workgroup per (chunk slot, head) on a 1-D grid
-    if (dt == KDA_BF16 && chunk_slots(B, T, N, chunk, varlen) * (int64_t)H > INT32_MAX)
+    // one workgroup per (slot, head) on a 1-D grid
+    if (dt == KDA_BF16 && n_slots * (int64_t)H > INT32_MAX)
         return KDA_ERR_UNSUPPORTED;
     if (!tensors_aligned({q, k, v, g, gate, out, init_state, final_state, snapshots}) ||
         !aligned_to(beta, elem_bytes(dt)) || !aligned_to(cu_seqlens, 4) ||
@@ -211,8 +240,8 @@ kda_status chunk_fwd(const void *q, const void *k, const void *v, const void *g,
     return from_hip(kda::launch_chunk_bf16(
         (const kda::bf16 *)q, (const kda::bf16 *)k, (const kda::bf16 *)v, (const kda::bf16 *)g,
         (const kda::bf16 *)beta, (const kda::bf16 *)gate, init_state, (kda::bf16 *)out,
-        final_state, snapshots, interval, cu_seqlens, N, T, H,
-        chunk_slots(B, T, N, chunk, varlen), scale, prologue, workspace, stream, !noalloc));
+        final_state, snapshots, interval, cu_seqlens, N, T, H, n_slots, scale, prologue,
+        workspace, stream, pair, !noalloc));
 }
 
 }  // namespace
@@ -224,12 +253,12 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const v
                             void *out, float *final_state, float *snapshots,
                             int snapshot_interval, const int32_t *cu_seqlens, int B, int T,
                             int N, int H, int dk, int dv, int chunk, float scale, kda_dtype dt,
-                            unsigned prologue, void *workspace, size_t workspace_bytes,
+                            unsigned flags, void *workspace, size_t workspace_bytes,
                             hipStream_t stream)
 {
     return chunk_fwd(q, k, v, g, beta, gate, init_state, out, final_state, snapshots,
-                     snapshot_interval, cu_seqlens, B, T, N, H, dk, dv, chunk, scale, dt,
-                     prologue, workspace, workspace_bytes, stream, false);
+                     snapshot_interval, cu_seqlens, B, T, N, H, dk, dv, chunk, scale, dt, flags,
+                     workspace, workspace_bytes, stream, false);
 }
 
 kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
@@ -382,8 +411,9 @@ kda_status kda_chunk_bwd_ex(const void *q, const void *k, const void *v, const v
         return KDA_ERR_NULL_POINTER;
     size_t need = kda_chunk_bwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
     if (fwd_records) {
-        // the forward records stand in for the first of the two record arrays
-        const size_t rec = kda_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
+        // the forward's per-chunk records stand in for the first of the two
+        // record arrays
+        const size_t rec = kda_chunk_fwd_records_bytes(B, T, N, H, dk, dv, chunk, dt, varlen);
         if (fwd_records_bytes < rec)
             return KDA_ERR_WORKSPACE_TOO_SMALL;
         need -= rec;

@@ -79,7 +79,9 @@ struct PrepSmem {
     float eGB[4][kDK + 4];        // e^{G_end - B_i}
     float Gref[4][kDK + 4];       // G at the end of subtiles 0, 1, 2, 3 (B_1, B_2, B_3, G_end)
     float NRM[2][8][kChunk];      // prologue: per-wave partial sums of q^2 and k^2 per row
+    float DEC0[kDK];              // pairs: e^{G_end} of chunk 0, kept for chunk 1
 };
+static_assert(sizeof(PrepSmem) <= 160 * 1024, "prep LDS fits one CU");
 
 struct TSmem {                    // overlays KR after phase 2
     float TM[kChunk][kALd];
@@ -194,341 +196,342 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const bf16 *q, const bf16 
         prep_load_token(in, q, k, v, g, beta, pt, H, wave, tg, cq, t);
 }
 
-// The prep kernel is persistent: workgroup b handles tasks b, b + G, b + 2 G,
-// ... (G = grid size, a multiple of 8 so that with H a multiple of 8 every
-// task of head h runs on XCD h % 8, where the chain walks head h).  The inputs
-// of the next task are loaded into registers while the current one is in its
-// matrix phases, so only the first task of a workgroup waits for memory.
-template <bool kPro>
-__global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ g, const bf16 *__restrict__ beta, const int32_t *__restrict__ cu,
-    int N, int T, int H, int64_t n_tasks, float scale, unsigned pro, uint8_t *__restrict__ ws)
-{
-    extern __shared__ __align__(16) uint8_t smem_raw[];
-    PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
-    TSmem &ts = *reinterpret_cast<TSmem *>(smem_raw);
+// Phases 1 to 5 of one chunk of a prep task.  `in` holds the chunk's inputs on
+// entry; while the chunk is in its matrix phases it is refilled with those of
+// `next` (when load_next).  kMode selects what is written:
+//   0  a chunk record (or a pair record of a sequence's one-chunk last pair):
+//      LN, QH, BM, O0 and DEC of the chunk;
+//   1  chunk 0 of a pair: its readout QH, O0; -L0 and Bm0 of the wave's 16
+//      columns stay in `hold` as B fragments (k = rows, perm order) and its
+//      decay in LDS, for chunk 1;
+//   2  chunk 1 of a pair: the composed map (LN = -L01, BM = Bm01, DEC = dec01)
+//      and its readout from the pair's entry state (QH1, O01).
+struct PairHold {
+    bf16x8 nl0[4];                   // -L0, column block of the wave, 4 k-steps of rows
+    bf16x8 bm0[4];                   // Bm0, the same layout
+};
 
+template <bool kPro, int kMode>
+__device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, const bf16 *q,
+                                           const bf16 *k, const bf16 *v, const bf16 *g,
+                                           const bf16 *beta, const PrepTask &pt,
+                                           const PrepTask &next, bool load_next, int H,
+                                           float scale, unsigned pro, uint8_t *rec,
+                                           PairHold &hold)
+{
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, b = lane >> 4;
     const int tg = lane & 15, cq = lane >> 4;     // phase-1 roles: token group, channel quad
 
-    int64_t t = blockIdx.x;
-    PrepTask next = t < n_tasks ? prep_task(cu, N, T, H, t) : PrepTask{};
-    PrepIn in;
-    if (t < n_tasks && next.valid)
-        prep_load(in, q, k, v, g, beta, next, H, wave, tg, cq);
-    for (; t < n_tasks; t += gridDim.x) {
-        const PrepTask pt = next;
-        const int64_t tn = t + gridDim.x;
-        if (tn < n_tasks)
-            next = prep_task(cu, N, T, H, tn);
-        const bool load_next = tn < n_tasks && next.valid;
-        if (!pt.valid) {
-            if (load_next)
-                prep_load(in, q, k, v, g, beta, next, H, wave, tg, cq);
-            continue;
+    // ---- phase 1: cumulative log-decay and elementwise operands -----------
+    // lane (tg, cq): tokens 4 tg .. + 3, channels 16 wave + 4 cq .. + 3
+    {
+        const int ch0 = 16 * wave + 4 * cq;
+        const int ib = tg >> 2;                       // subtile of the lane's tokens
+        for (int i = tid; i < kChunk * kColLd / 8; i += kPrepThreads)   // zero P
+            reinterpret_cast<bf16x8 *>(&sm.PM[0][0])[i] = bf16x8{};
+        // G: inclusive prefix over the lane's 4 tokens, then across the 16
+        // token groups of the row (rows past len carry g = 0)
+        float G[4][4];                                 // [token][channel]
+        float br[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const float bv = (float)in.beta[tt];
+            br[tt] = 4 * tg + tt < pt.len ? ((kPro && (pro & kProBeta)) ? sigmoidf_(bv) : bv) : 0.f;
         }
-        uint8_t *rec = ws + pt.rec * (int64_t)kRecBytes;
-
-        // ---- phase 1: cumulative log-decay and elementwise operands -----------
-        // lane (tg, cq): tokens 4 tg .. + 3, channels 16 wave + 4 cq .. + 3
-        {
-            const int ch0 = 16 * wave + 4 * cq;
-            const int ib = tg >> 2;                       // subtile of the lane's tokens
-            for (int i = tid; i < kChunk * kColLd / 8; i += kPrepThreads)   // zero P
-                reinterpret_cast<bf16x8 *>(&sm.PM[0][0])[i] = bf16x8{};
-            // G: inclusive prefix over the lane's 4 tokens, then across the 16
-            // token groups of the row (rows past len carry g = 0)
-            float G[4][4];                                 // [token][channel]
-            float br[4];
+        if (kPro && (pro & kProQK)) {
+            // sums of q^2 and k^2 per row: the lane's 4 channels, then the
+            // wave's 16 (lanes 16 apart), then the 8 waves through LDS
+            float sq[4], sk[4];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const float bv = (float)in.beta[tt];
-                br[tt] = 4 * tg + tt < pt.len ? ((kPro && (pro & kProBeta)) ? sigmoidf_(bv) : bv) : 0.f;
-            }
-            if (kPro && (pro & kProQK)) {
-                // sums of q^2 and k^2 per row: the lane's 4 channels, then the
-                // wave's 16 (lanes 16 apart), then the 8 waves through LDS
-                float sq[4], sk[4];
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    sq[tt] = sk[tt] = 0.f;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float qv = (float)in.q[tt][c], kv = (float)in.k[tt][c];
-                        sq[tt] += qv * qv;
-                        sk[tt] += kv * kv;
-                    }
-                    sq[tt] += __shfl_xor(sq[tt], 16);
-                    sq[tt] += __shfl_xor(sq[tt], 32);
-                    sk[tt] += __shfl_xor(sk[tt], 16);
-                    sk[tt] += __shfl_xor(sk[tt], 32);
-                }
-                if (cq == 0) {
-                    *reinterpret_cast<f32x4 *>(&sm.NRM[0][wave][4 * tg]) =
-                        f32x4{sq[0], sq[1], sq[2], sq[3]};
-                    *reinterpret_cast<f32x4 *>(&sm.NRM[1][wave][4 * tg]) =
-                        f32x4{sk[0], sk[1], sk[2], sk[3]};
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float run = 0.f;
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    const float x = (float)in.g[tt][c];
-                    const float gv = (kPro && (pro & kProG)) ? log_decay_from(x) : x;
-                    run += 4 * tg + tt < pt.len ? gv : 0.f;
-                    G[tt][c] = run;
-                }
-                const float excl = row_inclusive_sum(run) - run;
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-                    G[tt][c] += excl;
-            }
-            // G at the ends of the subtiles: B_1, B_2, B_3 and G_end
-            if ((tg & 3) == 3)
-                *reinterpret_cast<f32x4 *>(&sm.Gref[ib][ch0]) =
-                    f32x4{G[3][0], G[3][1], G[3][2], G[3][3]};
-            if (wave == 0 && cq == 0) {
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-                    sm.AM[4 * tg + tt][kChunk] = br[tt];  // beta per row, for A
-            }
-            __syncthreads();
-            if (lane < 16) {
-                // per-channel constants of channel 16 w + lane
-                const int ch = 16 * wave + lane;
-                const float b1 = sm.Gref[0][ch], b2 = sm.Gref[1][ch], b3 = sm.Gref[2][ch];
-                const float ge = sm.Gref[3][ch];
-                sm.eB[0][ch] = 1.f;
-                sm.eB[1][ch] = __expf(b1);
-                sm.eB[2][ch] = __expf(b2);
-                sm.eB[3][ch] = __expf(b3);
-                sm.eGB[0][ch] = __expf(ge);
-                sm.eGB[1][ch] = __expf(ge - b1);
-                sm.eGB[2][ch] = __expf(ge - b2);
-                sm.eGB[3][ch] = __expf(ge - b3);
-                sm.F[0][ch] = __expf(b1);                    // e^{B_1 - B_0}
-                sm.F[1][ch] = __expf(b2);                    // e^{B_2 - B_0}
-                sm.F[2][ch] = __expf(b2 - b1);
-                sm.F[3][ch] = __expf(b3);
-                sm.F[4][ch] = __expf(b3 - b1);
-                sm.F[5][ch] = __expf(b3 - b2);
-                reinterpret_cast<float *>(rec + kOffDEC)[ch] = __expf(ge);
-            }
-            __syncthreads();
-            // prologue: 1 / |q| and 1 / |k| of the lane's rows (1 without it)
-            f32x4 nq = {1.f, 1.f, 1.f, 1.f}, nk = {1.f, 1.f, 1.f, 1.f};
-            if (kPro && (pro & kProQK)) {
-                f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int w2 = 0; w2 < 8; ++w2) {
-                    aq += *reinterpret_cast<const f32x4 *>(&sm.NRM[0][w2][4 * tg]);
-                    ak += *reinterpret_cast<const f32x4 *>(&sm.NRM[1][w2][4 * tg]);
-                }
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    nq[tt] = __builtin_amdgcn_rsqf(aq[tt] + kNormEps);
-                    nk[tt] = __builtin_amdgcn_rsqf(ak[tt] + kNormEps);
-                }
-            }
-            const f32x4 Bi = ib == 0 ? f32x4{0.f, 0.f, 0.f, 0.f}
-                                     : *reinterpret_cast<const f32x4 *>(&sm.Gref[ib - 1][ch0]);
-            const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[ib][ch0]);
-            const f32x4 egb = *reinterpret_cast<const f32x4 *>(&sm.eGB[ib][ch0]);
-            bf16x4 xb[4], vb[4], kp[4];                    // [channel][token]
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const int r = 4 * tg + tt;
-                const bool ok = r < pt.len;
-                bf16x4 kr, qr, kc;
+                sq[tt] = sk[tt] = 0.f;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const float fr = __expf(G[tt][c] - Bi[c]);   // e^{G - B_i} in [e^-80, 1]
-                    const float fc = __builtin_amdgcn_rcpf(fr);  // e^{B_i - G} in [1, e^80]
-                    const float kv = ok ? (float)in.k[tt][c] * nk[tt] : 0.f;
-                    const float qv = ok ? (float)in.q[tt][c] * nq[tt] : 0.f;
-                    const float vv = ok ? (float)in.v[tt][c] : 0.f;
-                    kr[c] = (bf16)(kv * fr);
-                    qr[c] = (bf16)(qv * fr);
-                    kc[c] = (bf16)(kv * fc);
-                    xb[c][tt] = (bf16)(br[tt] * kv * (fr * eb[c]));    // beta k e^G
-                    vb[c][tt] = (bf16)(br[tt] * vv);                   // beta v
-                    kp[c][tt] = (bf16)(kv * (egb[c] * fc));            // k e^{G_end - G}
+                    const float qv = (float)in.q[tt][c], kv = (float)in.k[tt][c];
+                    sq[tt] += qv * qv;
+                    sk[tt] += kv * kv;
                 }
-                *reinterpret_cast<bf16x4 *>(&sm.KR[r][rq(r, ch0 >> 2)]) = kr;
-                *reinterpret_cast<bf16x4 *>(&sm.QR[r][rq(r, ch0 >> 2)]) = qr;
-                *reinterpret_cast<bf16x4 *>(&sm.KCD[r][rq(r, ch0 >> 2)]) = kc;
+                sq[tt] += __shfl_xor(sq[tt], 16);
+                sq[tt] += __shfl_xor(sq[tt], 32);
+                sk[tt] += __shfl_xor(sk[tt], 16);
+                sk[tt] += __shfl_xor(sk[tt], 32);
             }
+            if (cq == 0) {
+                *reinterpret_cast<f32x4 *>(&sm.NRM[0][wave][4 * tg]) =
+                    f32x4{sq[0], sq[1], sq[2], sq[3]};
+                *reinterpret_cast<f32x4 *>(&sm.NRM[1][wave][4 * tg]) =
+                    f32x4{sk[0], sk[1], sk[2], sk[3]};
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float run = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const float x = (float)in.g[tt][c];
+                const float gv = (kPro && (pro & kProG)) ? log_decay_from(x) : x;
+                run += 4 * tg + tt < pt.len ? gv : 0.f;
+                G[tt][c] = run;
+            }
+            const float excl = row_inclusive_sum(run) - run;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                G[tt][c] += excl;
+        }
+        // G at the ends of the subtiles: B_1, B_2, B_3 and G_end
+        if ((tg & 3) == 3)
+            *reinterpret_cast<f32x4 *>(&sm.Gref[ib][ch0]) =
+                f32x4{G[3][0], G[3][1], G[3][2], G[3][3]};
+        if (wave == 0 && cq == 0) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                sm.AM[4 * tg + tt][kChunk] = br[tt];  // beta per row, for A
+        }
+        __syncthreads();
+        if (lane < 16) {
+            // per-channel constants of channel 16 w + lane
+            const int ch = 16 * wave + lane;
+            const float b1 = sm.Gref[0][ch], b2 = sm.Gref[1][ch], b3 = sm.Gref[2][ch];
+            const float ge = sm.Gref[3][ch];
+            sm.eB[0][ch] = 1.f;
+            sm.eB[1][ch] = __expf(b1);
+            sm.eB[2][ch] = __expf(b2);
+            sm.eB[3][ch] = __expf(b3);
+            sm.eGB[0][ch] = __expf(ge);
+            sm.eGB[1][ch] = __expf(ge - b1);
+            sm.eGB[2][ch] = __expf(ge - b2);
+            sm.eGB[3][ch] = __expf(ge - b3);
+            sm.F[0][ch] = __expf(b1);                    // e^{B_1 - B_0}
+            sm.F[1][ch] = __expf(b2);                    // e^{B_2 - B_0}
+            sm.F[2][ch] = __expf(b2 - b1);
+            sm.F[3][ch] = __expf(b3);
+            sm.F[4][ch] = __expf(b3 - b1);
+            sm.F[5][ch] = __expf(b3 - b2);
+            if constexpr (kMode == 0)
+                reinterpret_cast<float *>(rec + kOffDEC)[ch] = __expf(ge);
+            else if constexpr (kMode == 1)
+                sm.DEC0[ch] = __expf(ge);    // read by chunk 1 of the pair (same lane) and its phase 5
+            else
+                reinterpret_cast<float *>(rec + kOffDEC)[ch] = sm.DEC0[ch] * __expf(ge);
+        }
+        __syncthreads();
+        // prologue: 1 / |q| and 1 / |k| of the lane's rows (1 without it)
+        f32x4 nq = {1.f, 1.f, 1.f, 1.f}, nk = {1.f, 1.f, 1.f, 1.f};
+        if (kPro && (pro & kProQK)) {
+            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w2 = 0; w2 < 8; ++w2) {
+                aq += *reinterpret_cast<const f32x4 *>(&sm.NRM[0][w2][4 * tg]);
+                ak += *reinterpret_cast<const f32x4 *>(&sm.NRM[1][w2][4 * tg]);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                nq[tt] = __builtin_amdgcn_rsqf(aq[tt] + kNormEps);
+                nk[tt] = __builtin_amdgcn_rsqf(ak[tt] + kNormEps);
+            }
+        }
+        const f32x4 Bi = ib == 0 ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                 : *reinterpret_cast<const f32x4 *>(&sm.Gref[ib - 1][ch0]);
+        const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[ib][ch0]);
+        const f32x4 egb = *reinterpret_cast<const f32x4 *>(&sm.eGB[ib][ch0]);
+        bf16x4 xb[4], vb[4], kp[4];                    // [channel][token]
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int r = 4 * tg + tt;
+            const bool ok = r < pt.len;
+            bf16x4 kr, qr, kc;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                *reinterpret_cast<bf16x4 *>(&sm.XB[ch0 + c][4 * tg]) = xb[c];
-                *reinterpret_cast<bf16x4 *>(&sm.VB[ch0 + c][4 * tg]) = vb[c];
-                *reinterpret_cast<bf16x4 *>(&sm.KPT[ch0 + c][4 * tg]) = kp[c];
+                const float fr = __expf(G[tt][c] - Bi[c]);   // e^{G - B_i} in [e^-80, 1]
+                const float fc = __builtin_amdgcn_rcpf(fr);  // e^{B_i - G} in [1, e^80]
+                const float kv = ok ? (float)in.k[tt][c] * nk[tt] : 0.f;
+                const float qv = ok ? (float)in.q[tt][c] * nq[tt] : 0.f;
+                const float vv = ok ? (float)in.v[tt][c] : 0.f;
+                kr[c] = (bf16)(kv * fr);
+                qr[c] = (bf16)(qv * fr);
+                kc[c] = (bf16)(kv * fc);
+                xb[c][tt] = (bf16)(br[tt] * kv * (fr * eb[c]));    // beta k e^G
+                vb[c][tt] = (bf16)(br[tt] * vv);                   // beta v
+                kp[c][tt] = (bf16)(kv * (egb[c] * fc));            // k e^{G_end - G}
             }
+            *reinterpret_cast<bf16x4 *>(&sm.KR[r][rq(r, ch0 >> 2)]) = kr;
+            *reinterpret_cast<bf16x4 *>(&sm.QR[r][rq(r, ch0 >> 2)]) = qr;
+            *reinterpret_cast<bf16x4 *>(&sm.KCD[r][rq(r, ch0 >> 2)]) = kc;
         }
-        __syncthreads();
-        // the registers of this task's inputs are free: fetch the next task's,
-        // one token of the lane's group before each of phases 2 to 5, so the
-        // loads do not all queue up in front of one phase
-        if (load_next)
-            prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            *reinterpret_cast<bf16x4 *>(&sm.XB[ch0 + c][4 * tg]) = xb[c];
+            *reinterpret_cast<bf16x4 *>(&sm.VB[ch0 + c][4 * tg]) = vb[c];
+            *reinterpret_cast<bf16x4 *>(&sm.KPT[ch0 + c][4 * tg]) = kp[c];
+        }
+    }
+    __syncthreads();
+    // the registers of this task's inputs are free: fetch the next task's,
+    // one token of the lane's group before each of phases 2 to 5, so the
+    // loads do not all queue up in front of one phase
+    if (load_next)
+        prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 0);
 
-        // ---- phase 2: 16 x 16 blocks of A and P (bf16 MFMA, fp32 accumulate) -------
-        for (int blk = wave; blk < 10; blk += kPrepThreads / 64) {
-            // blk -> (i, jb): 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) ...
-            const int i = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
-            const int jb = blk - (i * (i + 1)) / 2;
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+    // ---- phase 2: 16 x 16 blocks of A and P (bf16 MFMA, fp32 accumulate) -------
+    for (int blk = wave; blk < 10; blk += kPrepThreads / 64) {
+        // blk -> (i, jb): 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) ...
+        const int i = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
+        const int jb = blk - (i * (i + 1)) / 2;
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int ch = 32 * ks + 8 * b;
-                const bf16x8 ar = lds8_rq(sm.KR, 16 * i + m, 4 * ks + b);
-                const bf16x8 aq = lds8_rq(sm.QR, 16 * i + m, 4 * ks + b);
-                bf16x8 bc = lds8_rq(sm.KCD, 16 * jb + m, 4 * ks + b);
-                if (jb < i) {
-                    const float *f = &sm.F[pair_index(i, jb)][ch];
+        for (int ks = 0; ks < 4; ++ks) {
+            const int ch = 32 * ks + 8 * b;
+            const bf16x8 ar = lds8_rq(sm.KR, 16 * i + m, 4 * ks + b);
+            const bf16x8 aq = lds8_rq(sm.QR, 16 * i + m, 4 * ks + b);
+            bf16x8 bc = lds8_rq(sm.KCD, 16 * jb + m, 4 * ks + b);
+            if (jb < i) {
+                const float *f = &sm.F[pair_index(i, jb)][ch];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        bc[e] = (bf16)((float)bc[e] * f[e]);
-                }
-                accA = mfma16(ar, bc, accA);
-                accP = mfma16(aq, bc, accP);
+                for (int e = 0; e < 8; ++e)
+                    bc[e] = (bf16)((float)bc[e] * f[e]);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * i + 4 * b + e, col = 16 * jb + m;
-                sm.AM[row][col] = (jb < i || col < row) ? sm.AM[row][kChunk] * accA[e] : 0.f;
-                sm.PM[row][col] = (bf16)((jb < i || col <= row) ? scale * accP[e] : 0.f);
-            }
+            accA = mfma16(ar, bc, accA);
+            accP = mfma16(aq, bc, accP);
         }
-        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * i + 4 * b + e, col = 16 * jb + m;
+            sm.AM[row][col] = (jb < i || col < row) ? sm.AM[row][kChunk] * accA[e] : 0.f;
+            sm.PM[row][col] = (bf16)((jb < i || col <= row) ? scale * accP[e] : 0.f);
+        }
+    }
+    __syncthreads();
 
-        if (load_next)
-            prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 1);
-        // ---- phase 3: T = (I + A)^-1 ------------------------------------------------
-        if (wave == 0) {
-            // diagonal 16 x 16 blocks by forward substitution, one column per lane;
-            // x[s] = 0 for s < col, so the full-range sums only add zeros there
-            // (column form: once x[s] is final it updates every later row at once,
-            // so the dependency depth is 16 instead of 120)
-            const int blk = lane >> 4, col = lane & 15, o = 16 * blk;
-            float x[16];
+    if (load_next)
+        prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 1);
+    // ---- phase 3: T = (I + A)^-1 ------------------------------------------------
+    if (wave == 0) {
+        // diagonal 16 x 16 blocks by forward substitution, one column per lane;
+        // x[s] = 0 for s < col, so the full-range sums only add zeros there
+        // (column form: once x[s] is final it updates every later row at once,
+        // so the dependency depth is 16 instead of 120)
+        const int blk = lane >> 4, col = lane & 15, o = 16 * blk;
+        float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                x[r] = (r == col) ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r)
+            x[r] = (r == col) ? 1.f : 0.f;
 #pragma unroll
-            for (int s2 = 0; s2 < 15; ++s2)
+        for (int s2 = 0; s2 < 15; ++s2)
 #pragma unroll
-                for (int r = s2 + 1; r < 16; ++r)
-                    x[r] -= sm.AM[o + r][o + s2] * x[s2];
+            for (int r = s2 + 1; r < 16; ++r)
+                x[r] -= sm.AM[o + r][o + s2] * x[s2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                ts.TM[o + r][o + col] = x[r];
-        } else if (wave <= 2) {
-            // T_01 and T_23 are read by the W / U~ products: zero them
-            const int o = (wave == 1) ? 0 : 32;
+        for (int r = 0; r < 16; ++r)
+            ts.TM[o + r][o + col] = x[r];
+    } else if (wave <= 2) {
+        // T_01 and T_23 are read by the W / U~ products: zero them
+        const int o = (wave == 1) ? 0 : 32;
 #pragma unroll
-            for (int e = lane; e < 256; e += 64)
-                ts.TM[o + e / 16][o + 16 + e % 16] = 0.f;
-        }
-        __syncthreads();
-        // off-diagonal blocks by distance on fp32 MFMA (16x16x4), one block per wave:
-        // X = sum_{mm=bb}^{a-1} A_a,mm T_mm,bb ;  T_a,bb = -T_aa X
-        for (int dist = 1; dist < 4; ++dist) {
-            if (wave < 4 - dist) {
-                const int a = wave + dist, bb = wave;
-                f32x4 X = {0.f, 0.f, 0.f, 0.f};
-                for (int mm = bb; mm < a; ++mm) {
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        X = mfma4_f32(sm.AM[16 * a + m][16 * mm + 4 * kk + b],
-                                      ts.TM[16 * mm + 4 * kk + b][16 * bb + m], X);
-                }
-                // k order: MFMA kk takes k = 4 b + kk, which is X's own accumulator row
-                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+        for (int e = lane; e < 256; e += 64)
+            ts.TM[o + e / 16][o + 16 + e % 16] = 0.f;
+    }
+    __syncthreads();
+    // off-diagonal blocks by distance on fp32 MFMA (16x16x4), one block per wave:
+    // X = sum_{mm=bb}^{a-1} A_a,mm T_mm,bb ;  T_a,bb = -T_aa X
+    for (int dist = 1; dist < 4; ++dist) {
+        if (wave < 4 - dist) {
+            const int a = wave + dist, bb = wave;
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            for (int mm = bb; mm < a; ++mm) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    Y = mfma4_f32(ts.TM[16 * a + m][16 * a + 4 * b + kk], X[kk], Y);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    ts.TM[16 * a + 4 * b + i][16 * bb + m] = -Y[i];
+                    X = mfma4_f32(sm.AM[16 * a + m][16 * mm + 4 * kk + b],
+                                  ts.TM[16 * mm + 4 * kk + b][16 * bb + m], X);
             }
-            __syncthreads();
+            // k order: MFMA kk takes k = 4 b + kk, which is X's own accumulator row
+            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                Y = mfma4_f32(ts.TM[16 * a + m][16 * a + 4 * b + kk], X[kk], Y);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ts.TM[16 * a + 4 * b + i][16 * bb + m] = -Y[i];
         }
+        __syncthreads();
+    }
 
-        if (load_next)
-            prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 2);
-        // ---- phase 4: W = T X and U~ = T V for the wave's 16 channels --------------
-        const int nt = wave;                       // channels 16 nt .. 16 nt + 15
-        f32x4 accW[4], accU[4];
-        {
-            bf16x8 tf[4][2];
+    if (load_next)
+        prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 2);
+    // ---- phase 4: W = T X and U~ = T V for the wave's 16 channels --------------
+    const int nt = wave;                       // channels 16 nt .. 16 nt + 15
+    f32x4 accW[4], accU[4];
+    {
+        bf16x8 tf[4][2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    bf16x8 f = {};
-                    if (ks <= (mt >> 1)) {
-                        const float *t = &ts.TM[16 * mt + m][32 * ks + 8 * b];
-                        const f32x4 lo = *reinterpret_cast<const f32x4 *>(t);
-                        const f32x4 hi = *reinterpret_cast<const f32x4 *>(t + 4);
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 f = {};
+                if (ks <= (mt >> 1)) {
+                    const float *t = &ts.TM[16 * mt + m][32 * ks + 8 * b];
+                    const f32x4 lo = *reinterpret_cast<const f32x4 *>(t);
+                    const f32x4 hi = *reinterpret_cast<const f32x4 *>(t + 4);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            f[e] = (bf16)lo[e];
-                            f[4 + e] = (bf16)hi[e];
-                        }
+                    for (int e = 0; e < 4; ++e) {
+                        f[e] = (bf16)lo[e];
+                        f[4 + e] = (bf16)hi[e];
                     }
-                    tf[mt][ks] = f;
                 }
-            bf16x8 xf[2], vf[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                xf[ks] = lds8(&sm.XB[16 * nt + m][32 * ks + 8 * b]);
-                vf[ks] = lds8(&sm.VB[16 * nt + m][32 * ks + 8 * b]);
+                tf[mt][ks] = f;
             }
+        bf16x8 xf[2], vf[2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                accW[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                accU[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= (mt >> 1)) {
-                        accW[mt] = mfma16(tf[mt][ks], xf[ks], accW[mt]);
-                        accU[mt] = mfma16(tf[mt][ks], vf[ks], accU[mt]);
-                    }
-            }
+        for (int ks = 0; ks < 2; ++ks) {
+            xf[ks] = lds8(&sm.XB[16 * nt + m][32 * ks + 8 * b]);
+            vf[ks] = lds8(&sm.VB[16 * nt + m][32 * ks + 8 * b]);
         }
-
-        if (load_next)
-            prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 3);
-        // ---- phase 5: L, Bm, Q^, O0 for the wave's 16 channels ----------------------
-        {
-            bf16x8 wf[2], uf[2];                   // W^T as A operand, U~ as B operand (perm k)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                wf[ks] = acc_to_frag(accW[2 * ks], accW[2 * ks + 1]);
-                uf[ks] = acc_to_frag(accU[2 * ks], accU[2 * ks + 1]);
-            }
-            const int half = nt & 1, kq = nt >> 1;  // fragment half and dk k-step of these channels
+        for (int mt = 0; mt < 4; ++mt) {
+            accW[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accU[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                if (ks <= (mt >> 1)) {
+                    accW[mt] = mfma16(tf[mt][ks], xf[ks], accW[mt]);
+                    accU[mt] = mfma16(tf[mt][ks], vf[ks], accU[mt]);
+                }
+        }
+    }
+
+    if (load_next)
+        prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 3);
+    if constexpr (kMode == 2) {
+        // every wave is past phase 4: the A / T, X and V tiles are free for the
+        // composition operands below
+        __syncthreads();
+    }
+    // ---- phase 5: L, Bm, Q^, O0 for the wave's 16 channels ----------------------
+    {
+        bf16x8 wf[2], uf[2];                   // W^T as A operand, U~ as B operand (perm k)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            wf[ks] = acc_to_frag(accW[2 * ks], accW[2 * ks + 1]);
+            uf[ks] = acc_to_frag(accU[2 * ks], accU[2 * ks + 1]);
+        }
+        const int half = nt & 1, kq = nt >> 1;  // fragment half and dk k-step of these channels
+        if constexpr (kMode == 0) {
             // L^T rows 16 nt.. = W^T K'  ->  -L fragments (mt, kq), elements 4 half .. 4 half + 3
             // Bm columns 16 nt.. = K'^T U~ ->  Bm of value block nt; row tiles 2 mp and
             // 2 mp + 1 fill one 16-byte slot per lane, stored with one instruction
-#pragma unroll
+    #pragma unroll
             for (int mp = 0; mp < 4; ++mp) {
                 f32x4 bmv[2];
-#pragma unroll
+    #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const int mt = 2 * mp + s2;
                     bf16x8 kpf[2];
-#pragma unroll
+    #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
                         kpf[ks] = perm8(&sm.KPT[16 * mt + m][0], ks, b);
                     f32x4 l = {0.f, 0.f, 0.f, 0.f}, bm = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+    #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
                         l = mfma16(wf[ks], kpf[ks], l);
                         bm = mfma16(kpf[ks], uf[ks], bm);
@@ -541,16 +544,18 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                 *reinterpret_cast<bf16x8 *>(rec + kOffBM + nt * 4096 + mp * 1024 + lane * 16) =
                     bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
             }
+        }
+        if constexpr (kMode <= 1) {
             // Q^ = scale Q e^G - P W  (as Q^^T rows 16 nt..)  and  O0 = P U~ for value block nt;
             // O0 row tiles 2 tp and 2 tp + 1 share one 16-byte slot per lane
-#pragma unroll
+    #pragma unroll
             for (int tp = 0; tp < 2; ++tp) {
                 f32x4 o0v[2];
-#pragma unroll
+    #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const int mt = 2 * tp + s2;
                     bf16x8 pf[2];
-#pragma unroll
+    #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
                         pf[ks] = perm8(&sm.PM[16 * mt + m][0], ks, b);
                     // scale Q e^G at row 16 mt + m, channels 16 nt + 4 b .. + 3, from q e^{G - B_mt}
@@ -558,11 +563,11 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                         *reinterpret_cast<const bf16x4 *>(&sm.QR[16 * mt + m][rq(16 * mt + m, 4 * nt + b)]);
                     const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[mt][16 * nt + 4 * b]);
                     f32x4 qh;
-#pragma unroll
+    #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         qh[i] = -scale * (float)qr[i] * eb[i];
                     f32x4 o0 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+    #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
                         qh = mfma16(wf[ks], pf[ks], qh);   // (P W)^T - (scale Q e^G)^T
                         o0 = mfma16(uf[ks], pf[ks], o0);   // (P U~)^T
@@ -576,8 +581,243 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                     bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             }
         }
-        // the next task's phase 1 rewrites the LDS operands
-        __syncthreads();
+        if constexpr (kMode == 1) {
+            // -L0 and Bm0 with rows on the k index: L0 block (mt, nt) as K'^T W with
+            // K'^T as the A operand, so tiles 2 ks and 2 ks + 1 form k-step ks
+#pragma unroll
+            for (int ks2 = 0; ks2 < 4; ++ks2) {
+                f32x4 lc[2], bc[2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int mt = 2 * ks2 + s2;
+                    bf16x8 kpf[2];
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        kpf[ks] = perm8(&sm.KPT[16 * mt + m][0], ks, b);
+                    lc[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    bc[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        lc[s2] = mfma16(kpf[ks], wf[ks], lc[s2]);   // L0[16 mt + 4 b + i][16 nt + m]
+                        bc[s2] = mfma16(kpf[ks], uf[ks], bc[s2]);   // Bm0, same place
+                    }
+                }
+                hold.nl0[ks2] = acc_to_frag(-lc[0], -lc[1]);
+                hold.bm0[ks2] = acc_to_frag(bc[0], bc[1]);
+            }
+        }
+        if constexpr (kMode == 2) {
+            // M1 = D1 - L1 and Q^1 as A fragments (the record's LN / QH layouts) in
+            // LDS, each wave writing its 16 columns; the fp32 terms -L1 D0 and
+            // Q^1 D0 stay in registers, Bm1 and O0_1 are formed after the barrier
+            bf16x8 *m1s = reinterpret_cast<bf16x8 *>(&sm.KR[0][0]);   // [32 fragments][64 lanes]
+            bf16x8 *q1s = reinterpret_cast<bf16x8 *>(&sm.XB[0][0]);   // [16 fragments][64 lanes]
+            const f32x4 d0c = *reinterpret_cast<const f32x4 *>(&sm.DEC0[16 * nt + 4 * b]);
+            const float d1 = sm.eGB[0][16 * nt + m];                  // e^{G_end} of chunk 1
+            f32x4 nld[8], qd[4];
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                bf16x8 kpf[2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    kpf[ks] = perm8(&sm.KPT[16 * mt + m][0], ks, b);
+                f32x4 l = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    l = mfma16(wf[ks], kpf[ks], l);       // L1[16 mt + m][16 nt + 4 b + i]
+                f32x4 mm;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    mm[i] = (mt == nt && m == 4 * b + i) ? d1 - l[i] : -l[i];
+                    nld[mt][i] = -l[i] * d0c[i];
+                }
+                *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint8_t *>(&m1s[(mt * 4 + kq) * 64 + lane]) +
+                                            8 * half) = to_bf16x4(mm, 1.f);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                bf16x8 pf[2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    pf[ks] = perm8(&sm.PM[16 * tt + m][0], ks, b);
+                const bf16x4 qr =
+                    *reinterpret_cast<const bf16x4 *>(&sm.QR[16 * tt + m][rq(16 * tt + m, 4 * nt + b)]);
+                const f32x4 eb = *reinterpret_cast<const f32x4 *>(&sm.eB[tt][16 * nt + 4 * b]);
+                f32x4 qh;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    qh[i] = -scale * (float)qr[i] * eb[i];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    qh = mfma16(wf[ks], pf[ks], qh);      // -Q^1[16 tt + m][16 nt + 4 b + i]
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    qd[tt][i] = -qh[i] * d0c[i];
+                *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint8_t *>(&q1s[(tt * 4 + kq) * 64 + lane]) +
+                                            8 * half) = to_bf16x4(qh, -1.f);
+            }
+            __syncthreads();
+            // -L01 = -L1 D0 + M1 (-L0) and Bm01 = Bm1 + M1 Bm0 for the wave's columns
+#pragma unroll
+            for (int mp = 0; mp < 4; ++mp) {
+                f32x4 bmv[2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int mt = 2 * mp + s2;
+                    bf16x8 kpf[2];
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        kpf[ks] = perm8(&sm.KPT[16 * mt + m][0], ks, b);
+                    f32x4 accl = nld[mt], accb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        accb = mfma16(kpf[ks], uf[ks], accb);    // Bm1[16 mt + 4 b + i][16 nt + m]
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const bf16x8 mf = m1s[(mt * 4 + ks) * 64 + lane];
+                        accl = mfma16(hold.nl0[ks], mf, accl);   // rows 16 mt + m, cols 16 nt + 4 b + i
+                        accb = mfma16(mf, hold.bm0[ks], accb);   // rows 16 mt + 4 b + i, col 16 nt + m
+                    }
+                    *reinterpret_cast<bf16x4 *>(rec + kOffLN + (mt * 4 + kq) * kFragBytes +
+                                                lane * 16 + half * 8) = to_bf16x4(accl, 1.f);
+                    bmv[s2] = accb;
+                }
+                const bf16x4 b0 = to_bf16x4(bmv[0], 1.f), b1 = to_bf16x4(bmv[1], 1.f);
+                *reinterpret_cast<bf16x8 *>(rec + kOffBM + nt * 4096 + mp * 1024 + lane * 16) =
+                    bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            }
+            // Q^1' = Q^1 D0 + Q^1 (-L0) and O0_1' = O0_1 + Q^1 Bm0
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+                f32x4 o0v[2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int tt = 2 * tp + s2;
+                    bf16x8 pf[2];
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        pf[ks] = perm8(&sm.PM[16 * tt + m][0], ks, b);
+                    f32x4 accq = qd[tt], acco = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        acco = mfma16(uf[ks], pf[ks], acco);     // O0_1[16 tt + m][16 nt + 4 b + i]
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const bf16x8 qf = q1s[(tt * 4 + ks) * 64 + lane];
+                        accq = mfma16(hold.nl0[ks], qf, accq);   // rows 16 tt + m, cols 16 nt + 4 b + i
+                        acco = mfma16(hold.bm0[ks], qf, acco);
+                    }
+                    *reinterpret_cast<bf16x4 *>(rec + kOffQH1 + (tt * 4 + kq) * kFragBytes +
+                                                lane * 16 + half * 8) = to_bf16x4(accq, 1.f);
+                    o0v[s2] = acco;
+                }
+                const bf16x4 a0 = to_bf16x4(o0v[0], 1.f), a1 = to_bf16x4(o0v[1], 1.f);
+                *reinterpret_cast<bf16x8 *>(rec + kOffO01 + nt * 2048 + tp * 1024 + lane * 16) =
+                    bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            }
+        }
+    }
+    // the next chunk's phase 1 rewrites the LDS operands
+    __syncthreads();
+}
+
+// Chunk 0 and chunk 1 (valid = false when the sequence ends first) of pair
+// task t = pair slot * H + h; c0.valid = false for a padding slot.
+__device__ __forceinline__ void pair_tasks(const int32_t *cu, int N, int T, int H, int64_t t,
+                                           PrepTask &c0, PrepTask &c1)
+{
+    const int64_t slot = t / H;
+    c0 = PrepTask{};
+    c1 = PrepTask{};
+    c0.h = c1.h = (int)(t % H);
+    c0.rec = c1.rec = t;
+    int n;
+    int64_t j;
+    if (!slot_to_step<kPairTokens>(cu, N, T, slot, n, j))
+        return;
+    const SeqInfo si = seq_info(cu, n, T, kPairTokens);
+    const int64_t rem = si.len - j * kPairTokens;
+    const int plen = rem < kPairTokens ? (int)rem : kPairTokens;
+    c0.valid = true;
+    c0.tok0 = si.bos + j * kPairTokens;
+    c0.len = plen < kChunk ? plen : kChunk;
+    if (plen > kChunk) {
+        c1.valid = true;
+        c1.tok0 = c0.tok0 + kChunk;
+        c1.len = plen - kChunk;
+    }
+}
+
+// The prep kernel is persistent: workgroup b handles tasks b, b + G, b + 2 G,
+// ... (G = grid size, a multiple of 8 so that with H a multiple of 8 every
+// task of head h runs on XCD h % 8, where the chain walks head h).  The inputs
+// of the next chunk are loaded into registers while the current one is in its
+// matrix phases, so only the first chunk of a workgroup waits for memory.
+// kPair: a task is a pair of chunks (see kPairRecBytes), else one chunk.
+template <bool kPro, bool kPair>
+__global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ g, const bf16 *__restrict__ beta, const int32_t *__restrict__ cu,
+    int N, int T, int H, int64_t n_tasks, float scale, unsigned pro, uint8_t *__restrict__ ws)
+{
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
+    TSmem &ts = *reinterpret_cast<TSmem *>(smem_raw);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tg = lane & 15, cq = lane >> 4;
+    PairHold hold;
+    PrepIn in;
+    int64_t t = blockIdx.x;
+    if constexpr (!kPair) {
+        PrepTask next = t < n_tasks ? prep_task(cu, N, T, H, t) : PrepTask{};
+        if (t < n_tasks && next.valid)
+            prep_load(in, q, k, v, g, beta, next, H, wave, tg, cq);
+        for (; t < n_tasks; t += gridDim.x) {
+            const PrepTask pt = next;
+            const int64_t tn = t + gridDim.x;
+            if (tn < n_tasks)
+                next = prep_task(cu, N, T, H, tn);
+            const bool load_next = tn < n_tasks && next.valid;
+            if (!pt.valid) {
+                if (load_next)
+                    prep_load(in, q, k, v, g, beta, next, H, wave, tg, cq);
+                continue;
+            }
+            prep_chunk<kPro, 0>(sm, ts, in, q, k, v, g, beta, pt, next, load_next, H, scale, pro,
+                                ws + pt.rec * (int64_t)kRecBytes, hold);
+        }
+    } else {
+        PrepTask c0, c1;
+        if (t < n_tasks)
+            pair_tasks(cu, N, T, H, t, c0, c1);
+        else
+            c0 = c1 = PrepTask{};
+        if (t < n_tasks && c0.valid)
+            prep_load(in, q, k, v, g, beta, c0, H, wave, tg, cq);
+        for (; t < n_tasks; t += gridDim.x) {
+            const PrepTask p0 = c0, p1 = c1;
+            const int64_t tn = t + gridDim.x;
+            if (tn < n_tasks)
+                pair_tasks(cu, N, T, H, tn, c0, c1);
+            else
+                c0 = c1 = PrepTask{};
+            if (!p0.valid) {
+                if (c0.valid)
+                    prep_load(in, q, k, v, g, beta, c0, H, wave, tg, cq);
+                continue;
+            }
+            uint8_t *rec = ws + p0.rec * (int64_t)kPairRecBytes;
+            if (p1.valid) {
+                prep_chunk<kPro, 1>(sm, ts, in, q, k, v, g, beta, p0, p1, true, H, scale, pro, rec,
+                                    hold);
+                prep_chunk<kPro, 2>(sm, ts, in, q, k, v, g, beta, p1, c0, c0.valid, H, scale, pro,
+                                    rec, hold);
+            } else {
+                prep_chunk<kPro, 0>(sm, ts, in, q, k, v, g, beta, p0, c0, c0.valid, H, scale, pro,
+                                    rec, hold);
+            }
+        }
     }
 }
 
@@ -621,8 +861,8 @@ __device__ __forceinline__ void chain_load(ChainStage &st, const uint8_t *rec_an
 
 }  // namespace
 
-// With kSnap the chain also writes fp32 state snapshots every snap_chunks
-// chunks (see snap_slot0): the compute waves park the state in LDS at a
+// With kSnap the chain also writes fp32 state snapshots every snap_steps
+// steps (see snap_slot0): the compute waves park the state in LDS at a
 // snapshot boundary and the store wave writes it out in the next iteration, so
 // the compute waves still issue no stores inside the loop.
 //
@@ -630,12 +870,17 @@ __device__ __forceinline__ void chain_load(ChainStage &st, const uint8_t *rec_an
 // the waves apply every step to kNB adjacent 16-column blocks with the same L
 // fragments, so a (sequence, head) takes 8 / kNB workgroups, which stream L
 // once for kNB blocks.  Each side wave fetches Bm for two blocks at most.
-template <bool kSnap, int kNB = 1>
+//
+// kPair: the records are pair records (kPairRecBytes), one step per pair of
+// chunks; the step's arithmetic is the same.
+template <bool kSnap, int kNB = 1, bool kPair = false>
 __global__ __launch_bounds__(chain_threads<kNB>()) void kda_chain_bf16_kernel(
     const float *__restrict__ init, float *__restrict__ final_state, float *__restrict__ snaps,
-    int snap_chunks, const int32_t *__restrict__ cu, int T, int H, int units,
+    int snap_steps, const int32_t *__restrict__ cu, int T, int H, int units,
     uint8_t *__restrict__ ws)
 {
+    constexpr int kStep = kPair ? kPairTokens : kChunk;           // tokens per step
+    constexpr size_t kRec = kPair ? kPairRecBytes : kRecBytes;    // record stride
     static_assert(kNB == 1 || kNB == 2 || kNB == 4, "1, 2 or 4 value blocks per workgroup");
     static_assert(!kSnap || kNB == 1, "snapshots with one value block per workgroup");
     constexpr int kSideBlocks = kNB == 1 ? 1 : 2;   // value blocks per side wave
@@ -661,12 +906,12 @@ __global__ __launch_bounds__(chain_threads<kNB>()) void kda_chain_bf16_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int m = lane & 15, b = lane >> 4;
-    const SeqInfo si = seq_info(cu, n, T, kChunk);
-    const int64_t nch = (si.len + kChunk - 1) / kChunk;
-    auto rec_of = [&](int64_t jc) { return ws + ((si.slot0 + jc) * H + h) * (int64_t)kRecBytes; };
-    // a snapshot is due on entry to chunk jb (after jb full chunks)
+    const SeqInfo si = seq_info(cu, n, T, kStep);
+    const int64_t nch = (si.len + kStep - 1) / kStep;             // steps of the sequence
+    auto rec_of = [&](int64_t jc) { return ws + ((si.slot0 + jc) * H + h) * (int64_t)kRec; };
+    // a snapshot is due on entry to step jb (after jb full steps)
     auto snap_at = [&](int64_t jb) {
-        return kSnap && jb >= 1 && jb <= nch && jb % snap_chunks == 0 && jb * kChunk <= si.len;
+        return kSnap && jb >= 1 && jb <= nch && jb % snap_steps == 0 && jb * kStep <= si.len;
     };
 
     // the chunk loop runs in rounds of kPrefetch iterations; iterations past the
@@ -724,7 +969,7 @@ __global__ __launch_bounds__(chain_threads<kNB>()) void kda_chain_bf16_kernel(
         // snapshot jb: rows 16 i + lane / 4, channels 16 blk + 4 (lane % 4) .. + 3
         auto write_snap = [&](int64_t jb) {
             const int64_t slot =
-                snap_slot0(cu, n, T, snap_chunks * kChunk) + jb / snap_chunks - 1;
+                snap_slot0(cu, n, T, snap_steps * kStep) + jb / snap_steps - 1;
             float *dst = snaps + (slot * H + h) * (int64_t)(kDK * kDV) + kVBlock * blk +
                          4 * (lane & 3);
 #pragma unroll
@@ -848,15 +1093,22 @@ __global__ __launch_bounds__(chain_threads<kNB>()) void kda_chain_bf16_kernel(
 // O^T = S^T Q^^T + O0^T (each lane: one token row, 4 consecutive value
 // channels) for four value blocks at a time, parks the fp32 tile in LDS, and
 // reads it back row-major so that gate loads and output stores are 16 bytes
-// per lane and whole 128-byte lines per 8 lanes.
+// per lane and whole 128-byte lines per 8 lanes.  kPair: the workgroup takes
+// both chunks of a pair record (8 waves, waves 4..7 on chunk 1 with Q^1' and
+// O0_1'), so the pair's entry state is read once.
 constexpr int kOutLd = 68;        // fp32 row stride of a wave's 16 x 64 staging tile
 
-__global__ __launch_bounds__(256) void kda_output_bf16_kernel(
+template <bool kPair>
+__global__ __launch_bounds__(kPair ? 512 : 256) void kda_output_bf16_kernel(
     const bf16 *__restrict__ gate, bf16 *__restrict__ out, const int32_t *__restrict__ cu,
     int N, int T, int H, const uint8_t *__restrict__ ws)
 {
+    constexpr int kWaves = kPair ? 8 : 4;
+    constexpr int kThreads = 64 * kWaves;
+    constexpr int kStep = kPair ? kPairTokens : kChunk;
+    constexpr size_t kRec = kPair ? kPairRecBytes : kRecBytes;
     __shared__ bf16x8 sb_s[kNumVBlocks * 4][64];
-    __shared__ float ot_s[4][kSub][kOutLd];
+    __shared__ float ot_s[kWaves][kSub][kOutLd];
 
     // slot-major 1-D grid: workgroup id = slot * H + h.  Workgroups are dealt to
     // the 8 XCDs round-robin, so with H a multiple of 8 every chunk of head h is
@@ -866,31 +1118,36 @@ __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
     const int h = (int)((int64_t)blockIdx.x % H);
     int n;
     int64_t j;
-    if (!slot_to_chunk(cu, N, T, slot, n, j))
+    if (!slot_to_step<kStep>(cu, N, T, slot, n, j))
         return;
-    const SeqInfo si = seq_info(cu, n, T, kChunk);
-    const int64_t tok0 = si.bos + j * kChunk;
-    const int64_t lenc = si.len - j * kChunk;
-    const uint8_t *rec = ws + ((int64_t)slot * H + h) * (int64_t)kRecBytes;
+    const SeqInfo si = seq_info(cu, n, T, kStep);
+    const int64_t tok0 = si.bos + j * kStep;
+    const int64_t lenc = si.len - j * kStep;      // tokens from the slot's start (>= 1)
+    const uint8_t *rec = ws + ((int64_t)slot * H + h) * (int64_t)kRec;
     const int tid = threadIdx.x, lane = tid & 63, t = tid >> 6;
     const int m = lane & 15, b = lane >> 4;
+    // wave t: chunk c of the slot, its token rows 16 tw .. 16 tw + 15
+    const int c = t >> 2, tw = t & 3;
+    const uint8_t *qh_rec = rec + (c == 0 ? kOffQH : kOffQH1);
+    const uint8_t *o0_rec = rec + (c == 0 ? kOffO0 : kOffO01);
 
-    // state fragments: 2048 x 16 B, 8 per thread
+    // state fragments: 2048 x 16 B
+    constexpr int kStage = kNumVBlocks * 4 * 64 / kThreads;
     const bf16x8 *sbg = reinterpret_cast<const bf16x8 *>(rec + kOffSB);
-    bf16x8 stage[8];
+    bf16x8 stage[kStage];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        stage[i] = sbg[i * 256 + tid];
+    for (int i = 0; i < kStage; ++i)
+        stage[i] = sbg[i * kThreads + tid];
     bf16x8 qh[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-        qh[ks] = *reinterpret_cast<const bf16x8 *>(rec + kOffQH + (t * 4 + ks) * kFragBytes +
+        qh[ks] = *reinterpret_cast<const bf16x8 *>(qh_rec + (tw * 4 + ks) * kFragBytes +
                                                    lane * 16);
     bf16x4 o0[kNumVBlocks];
 #pragma unroll
     for (int blk = 0; blk < kNumVBlocks; ++blk)
-        o0[blk] = *reinterpret_cast<const bf16x4 *>(rec + kOffO0 + blk * 2048 + (t >> 1) * 1024 +
-                                                    lane * 16 + (t & 1) * 8);
+        o0[blk] = *reinterpret_cast<const bf16x4 *>(o0_rec + blk * 2048 + (tw >> 1) * 1024 +
+                                                    lane * 16 + (tw & 1) * 8);
     // read-back mapping: lane -> row 8 p + lane / 8 of the wave's tile, channels 8 (lane % 8) ..
     // of each 64-channel half; the gate logits of those rows are fetched now,
     // with the other loads (rows past the chunk re-read its last row)
@@ -900,15 +1157,15 @@ __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
     for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int64_t row = 16 * t + 8 * p + rq;
+            const int64_t row = 64 * c + 16 * tw + 8 * p + rq;   // from the slot's first token
             const int64_t rr = row < lenc ? row : lenc - 1;
             zr[half][p] = *reinterpret_cast<const bf16x8 *>(
                 gate + ((tok0 + rr) * H + h) * kDV + 64 * half + c8);
         }
     bf16x8 *sbl = &sb_s[0][0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        sbl[i * 256 + tid] = stage[i];
+    for (int i = 0; i < kStage; ++i)
+        sbl[i * kThreads + tid] = stage[i];
     __syncthreads();
 
 #pragma unroll
@@ -927,7 +1184,7 @@ __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int r = 8 * p + rq;
-            const int64_t row = 16 * t + r;
+            const int64_t row = 64 * c + 16 * tw + r;
             const f32x4 lo = *reinterpret_cast<const f32x4 *>(&ot_s[t][r][c8]);
             const f32x4 hi = *reinterpret_cast<const f32x4 *>(&ot_s[t][r][c8 + 4]);
             if (row < lenc) {
@@ -948,22 +1205,26 @@ __global__ __launch_bounds__(256) void kda_output_bf16_kernel(
 
 namespace {
 
-// Persistent prep over every (chunk slot, head) task: one workgroup per CU
-// (its LDS allows no more), a multiple of 8 of them.
+// Persistent prep over every (slot, head) task, a slot being a chunk or a pair
+// of chunks (pair): one workgroup per CU (its LDS allows no more), a multiple
+// of 8 of them.
+template <bool kPro, bool kPair> hipError_t prep_attr()
+{
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kda_prep_bf16_kernel<kPro, kPair>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PrepSmem));
+}
+
 hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                        const bf16 *beta, const int32_t *cu, int N, int T, int H, int64_t n_slots,
-                       float scale, unsigned pro, uint8_t *ws, hipStream_t stream)
+                       float scale, unsigned pro, uint8_t *ws, hipStream_t stream, bool pair)
 {
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(attr_once, [] {
-        attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_prep_bf16_kernel<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(PrepSmem));
-        if (attr_err == hipSuccess)
-            attr_err = hipFuncSetAttribute(
-                reinterpret_cast<const void *>(kda_prep_bf16_kernel<true>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PrepSmem));
+        for (hipError_t e : {prep_attr<false, false>(), prep_attr<true, false>(),
+                             prep_attr<false, true>(), prep_attr<true, true>()})
+            if (e != hipSuccess && attr_err == hipSuccess)
+                attr_err = e;
     });
     if (attr_err != hipSuccess)
         return attr_err;
@@ -977,15 +1238,20 @@ hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *
         return e0;
     const int64_t prep_grid = cus >= 8 ? cus / 8 * 8 : 8;
     const int64_t n_tasks = n_slots * H;
-    const int64_t grid = n_tasks < prep_grid ? n_tasks : prep_grid;
-    if (pro)
-        hipLaunchKernelGGL(kda_prep_bf16_kernel<true>, dim3((unsigned)grid), dim3(kPrepThreads),
-                           sizeof(PrepSmem), stream, q, k, v, g, beta, cu, N, T, H, n_tasks,
-                           scale, pro, ws);
+    const dim3 grid((unsigned)(n_tasks < prep_grid ? n_tasks : prep_grid));
+    const size_t lds = sizeof(PrepSmem);
+    if (pro && pair)
+        hipLaunchKernelGGL((kda_prep_bf16_kernel<true, true>), grid, dim3(kPrepThreads), lds,
+                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, pro, ws);
+    else if (pro)
+        hipLaunchKernelGGL((kda_prep_bf16_kernel<true, false>), grid, dim3(kPrepThreads), lds,
+                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, pro, ws);
+    else if (pair)
+        hipLaunchKernelGGL((kda_prep_bf16_kernel<false, true>), grid, dim3(kPrepThreads), lds,
+                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, 0u, ws);
     else
-        hipLaunchKernelGGL(kda_prep_bf16_kernel<false>, dim3((unsigned)grid), dim3(kPrepThreads),
-                           sizeof(PrepSmem), stream, q, k, v, g, beta, cu, N, T, H, n_tasks,
-                           scale, 0u, ws);
+        hipLaunchKernelGGL((kda_prep_bf16_kernel<false, false>), grid, dim3(kPrepThreads), lds,
+                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, 0u, ws);
     return hipGetLastError();
 }
 
@@ -1000,7 +1266,7 @@ constexpr int kMaxDevices = 64;              // devices with per-device library 
 // to 8 (one per XCD), times the workgroups per unit.
 int64_t chain_workgroups(int64_t units, int nb) { return (units + 7) / 8 * 8 * (kNumVBlocks / nb); }
 
-template <int kNB>
+template <int kNB, bool kPair>
 hipError_t launch_chain_nb(const float *init, float *final_state, const int32_t *cu, int N,
                            int T, int H, uint8_t *ws, hipStream_t stream, bool own_cu)
 {
@@ -1021,7 +1287,8 @@ hipError_t launch_chain_nb(const float *init, float *final_state, const int32_t 
         if (dev < 0 || dev >= kMaxDevices)
             return hipErrorInvalidDevice;
         std::call_once(attr_once[dev], [dev] {
-            const void *fn = reinterpret_cast<const void *>(kda_chain_bf16_kernel<false, kNB>);
+            const void *fn =
+                reinterpret_cast<const void *>(kda_chain_bf16_kernel<false, kNB, kPair>);
             hipFuncAttributes fa{};
             attr_err[dev] = hipFuncGetAttributes(&fa, fn);
             if (attr_err[dev] == hipSuccess && fa.sharedSizeBytes < (size_t)kChainOwnCuLds) {
@@ -1034,27 +1301,25 @@ hipError_t launch_chain_nb(const float *init, float *final_state, const int32_t 
             return attr_err[dev];
         dyn = reserve[dev];
     }
-    hipLaunchKernelGGL((kda_chain_bf16_kernel<false, kNB>),
+    hipLaunchKernelGGL((kda_chain_bf16_kernel<false, kNB, kPair>),
                        dim3((unsigned)chain_workgroups(units, kNB)), dim3(chain_threads<kNB>()),
                        dyn, stream, init, final_state, nullptr, 1, cu, T, H, (int)units, ws);
     return hipGetLastError();
 }
 
-// The chain over all units.  When its one-block workgroups outnumber the CUs
-// the chain is bound by the operand stream through the device, not by its
-// serial depth, and workgroups of 4 (or 2) value blocks stream L once for all
-// of them, as long as they still fill the device.
-hipError_t launch_chain(const float *init, float *final_state, float *snaps, int snap_interval,
-                        const int32_t *cu, int N, int T, int H, uint8_t *ws, hipStream_t stream,
-                        bool own_cu = false)
+template <bool kPair>
+hipError_t launch_chain_t(const float *init, float *final_state, float *snaps, int snap_interval,
+                          const int32_t *cu, int N, int T, int H, uint8_t *ws,
+                          hipStream_t stream, bool own_cu)
 {
     const int64_t units = (int64_t)N * H;
     if (units <= 0)
         return hipSuccess;
+    constexpr int kStep = kPair ? kPairTokens : kChunk;
     if (snaps) {
-        hipLaunchKernelGGL((kda_chain_bf16_kernel<true, 1>),
+        hipLaunchKernelGGL((kda_chain_bf16_kernel<true, 1, kPair>),
                            dim3((unsigned)chain_workgroups(units, 1)), dim3(chain_threads<1>()),
-                           0, stream, init, final_state, snaps, snap_interval / kChunk, cu, T, H,
+                           0, stream, init, final_state, snaps, snap_interval / kStep, cu, T, H,
                            (int)units, ws);
         return hipGetLastError();
     }
@@ -1065,19 +1330,38 @@ hipError_t launch_chain(const float *init, float *final_state, float *snaps, int
     if (e != hipSuccess)
         return e;
     if (!own_cu && chain_workgroups(units, 4) >= cus)
-        return launch_chain_nb<4>(init, final_state, cu, N, T, H, ws, stream, false);
+        return launch_chain_nb<4, kPair>(init, final_state, cu, N, T, H, ws, stream, false);
     if (!own_cu && chain_workgroups(units, 2) >= cus)
-        return launch_chain_nb<2>(init, final_state, cu, N, T, H, ws, stream, false);
-    return launch_chain_nb<1>(init, final_state, cu, N, T, H, ws, stream, own_cu);
+        return launch_chain_nb<2, kPair>(init, final_state, cu, N, T, H, ws, stream, false);
+    return launch_chain_nb<1, kPair>(init, final_state, cu, N, T, H, ws, stream, own_cu);
+}
+
+// The chain over all units (pair: over pair records; snapshots then at
+// multiples of kPairTokens).  When its one-block workgroups outnumber the CUs
+// the chain is bound by the operand stream through the device, not by its
+// serial depth, and workgroups of 4 (or 2) value blocks stream L once for all
+// of them, as long as they still fill the device.
+hipError_t launch_chain(const float *init, float *final_state, float *snaps, int snap_interval,
+                        const int32_t *cu, int N, int T, int H, uint8_t *ws, hipStream_t stream,
+                        bool pair, bool own_cu = false)
+{
+    return pair ? launch_chain_t<true>(init, final_state, snaps, snap_interval, cu, N, T, H, ws,
+                                       stream, own_cu)
+                : launch_chain_t<false>(init, final_state, snaps, snap_interval, cu, N, T, H, ws,
+                                        stream, own_cu);
 }
 
 hipError_t launch_output(const bf16 *gate, bf16 *out, const int32_t *cu, int N, int T, int H,
-                         int64_t n_slots, const uint8_t *ws, hipStream_t stream)
+                         int64_t n_slots, const uint8_t *ws, hipStream_t stream, bool pair)
 {
     if (n_slots <= 0 || H <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL(kda_output_bf16_kernel, dim3((unsigned)(n_slots * H)), dim3(256), 0,
-                       stream, gate, out, cu, N, T, H, ws);
+    if (pair)
+        hipLaunchKernelGGL(kda_output_bf16_kernel<true>, dim3((unsigned)(n_slots * H)),
+                           dim3(512), 0, stream, gate, out, cu, N, T, H, ws);
+    else
+        hipLaunchKernelGGL(kda_output_bf16_kernel<false>, dim3((unsigned)(n_slots * H)),
+                           dim3(256), 0, stream, gate, out, cu, N, T, H, ws);
     return hipGetLastError();
 }
 
@@ -1085,7 +1369,7 @@ hipError_t launch_output(const bf16 *gate, bf16 *out, const int32_t *cu, int N, 
 //
 // On one long sequence the chain walks thousands of chunks on H * 8
 // workgroups while the rest of the device idles.  The chain then runs on a
-// second stream in segments of kSegSlots chunks, each starting from the
+// second stream in segments of at least kSegTokens tokens, each starting from the
 // previous segment's final state (fp32, written to final_state and read back
 // unchanged, so the result is bitwise that of one chain), and the caller's
 // stream runs the output kernel of each segment as soon as that segment's
@@ -1096,8 +1380,8 @@ hipError_t launch_output(const bf16 *gate, bf16 *out, const int32_t *cu, int N, 
 // The second stream and a pool of events are created once per device, at the
 // first such call, and kept until the process ends; a mutex orders the
 // record / wait / launch sequences of concurrent host threads.
-constexpr int64_t kSegSlots = 512;
-constexpr int64_t kMinSegmentedSlots = 2 * kSegSlots;
+constexpr int64_t kSegTokens = 512 * kChunk;
+constexpr int64_t kMinSegmentedTokens = 2 * kSegTokens;
 constexpr int kMaxSegments = 32;
 
 struct AuxStream {
@@ -1169,10 +1453,13 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
                              float *final_state, float *snaps, int snap_interval,
                              const int32_t *cu, int N, int T, int H, int64_t n_slots,
                              float scale, unsigned pro, void *workspace, hipStream_t stream,
-                             bool allow_aux)
+                             bool pair, bool allow_aux)
 {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    hipError_t e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, pro, ws, stream);
+    const int64_t step = pair ? kPairTokens : kChunk;                 // tokens per slot
+    const int64_t rec_bytes = pair ? (int64_t)kPairRecBytes : (int64_t)kRecBytes;
+    hipError_t e =
+        launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, pro, ws, stream, pair);
     if (e != hipSuccess)
         return e;
     // segments need one sequence without cu_seqlens, no snapshots and a final
@@ -1180,15 +1467,15 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     // into a graph keeps the single-stream schedule, so that no work of the
     // shared auxiliary stream is pulled into the capture
     const bool segmented = allow_aux && !cu && N == 1 && !snaps && final_state &&
-                           n_slots >= kMinSegmentedSlots && !stream_capturing(stream);
+                           n_slots * step >= kMinSegmentedTokens && !stream_capturing(stream);
     if (!segmented) {
-        e = launch_chain(init, final_state, snaps, snap_interval, cu, N, T, H, ws, stream);
+        e = launch_chain(init, final_state, snaps, snap_interval, cu, N, T, H, ws, stream, pair);
         if (e == hipSuccess)
-            e = launch_output(gate, out, cu, N, T, H, n_slots, ws, stream);
+            e = launch_output(gate, out, cu, N, T, H, n_slots, ws, stream, pair);
         return e;
     }
-    int64_t seg = (n_slots + kMaxSegments - 1) / kMaxSegments;
-    seg = seg < kSegSlots ? kSegSlots : seg;
+    int64_t seg = (n_slots + kMaxSegments - 1) / kMaxSegments;       // slots per segment
+    seg = seg * step < kSegTokens ? kSegTokens / step : seg;
     const int64_t nseg = (n_slots + seg - 1) / seg;
     std::lock_guard<std::mutex> lock(g_aux_mutex);
     AuxStream *aux = nullptr;
@@ -1202,18 +1489,18 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     for (int64_t s = 0; s < nseg && e == hipSuccess; ++s) {
         const int64_t slot0 = s * seg;
         const int64_t ns = n_slots - slot0 < seg ? n_slots - slot0 : seg;
-        const int64_t tok0 = slot0 * kChunk;
-        const int Ts = (int)(T - tok0 < ns * kChunk ? T - tok0 : ns * kChunk);
-        uint8_t *wss = ws + slot0 * H * (int64_t)kRecBytes;
+        const int64_t tok0 = slot0 * step;
+        const int Ts = (int)(T - tok0 < ns * step ? T - tok0 : ns * step);
+        uint8_t *wss = ws + slot0 * H * rec_bytes;
         e = launch_chain(s == 0 ? init : final_state, final_state, nullptr, 0, nullptr, 1, Ts, H,
-                         wss, aux->stream, true);
+                         wss, aux->stream, pair, true);
         if (e == hipSuccess)
             e = hipEventRecord(aux->seg[s], aux->stream);
         if (e == hipSuccess)
             e = hipStreamWaitEvent(stream, aux->seg[s], 0);
         if (e == hipSuccess)
             e = launch_output(gate + tok0 * H * kDV, out + tok0 * H * kDV, nullptr, 1, Ts, H, ns,
-                              wss, stream);
+                              wss, stream, pair);
     }
     if (e != hipSuccess) {
         // after a failure part way, still order the caller's stream after
@@ -1244,14 +1531,14 @@ hipError_t launch_chunk_bwd_bf16(const bf16 *q, const bf16 *k, const bf16 *v, co
                                 : static_cast<uint8_t *>(workspace) + rec_bytes;
     hipError_t e = hipSuccess;
     if (!fwd_records) {
-        e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, 0u, ws_f, stream);
+        e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, 0u, ws_f, stream, false);
         if (e == hipSuccess)
-            e = launch_chain(init, nullptr, nullptr, 0, cu, N, T, H, ws_f, stream);
+            e = launch_chain(init, nullptr, nullptr, 0, cu, N, T, H, ws_f, stream, false);
     }
     if (e == hipSuccess)
         e = launch_bwd_prep_bf16(gate, dout, cu, N, T, H, n_slots, ws_f, ws_b, stream);
     if (e == hipSuccess)
-        e = launch_chain(dfinal, dinit, nullptr, 0, cu, N, T, H, ws_b, stream);
+        e = launch_chain(dfinal, dinit, nullptr, 0, cu, N, T, H, ws_b, stream, false);
     if (e == hipSuccess)
         e = launch_grad_bf16(q, k, v, g, beta, gate, dout, dq, dk, dv, dg, dbeta, dgate, cu, N,
                              T, H, n_slots, scale, ws_f, ws_b, stream);

@@ -58,6 +58,28 @@ constexpr size_t kOffSB = kOffDEC + kDK * sizeof(float);
 constexpr size_t kRecBytes = kOffSB + kNumVBlocks * 4 * kFragBytes;
 static_assert(kRecBytes % 256 == 0, "records stay 256-byte aligned");
 
+// Pair record: two consecutive chunks of a sequence whose maps are composed
+// into one step of the chain.  With M = diag(dec) - L the map of one chunk,
+// chunks 0 and 1 of a pair give S'' = M1 M0 S + M1 Bm0 + Bm1, i.e.
+//     dec01 = dec0 dec1,   L01 = L1 D0 + M1 L0,   Bm01 = Bm1 + M1 Bm0,
+// and the outputs of chunk 1 from the pair's entry state S are
+//     O1 = Q^1 (M0 S + Bm0) + O0_1 = Q^1' S + O0_1',
+//     Q^1' = Q^1 D0 - Q^1 L0,   O0_1' = O0_1 + Q^1 Bm0.
+// (D = diag(dec); the decays enter the products only as D0 scaling columns
+// in fp32 and inside M1, which multiplies L0 and Bm0, so no decay is rounded
+// to bf16 on its own.)  The first kRecBytes bytes have the layout of a chunk record (LN, BM, DEC:
+// the composed map; QH, O0: chunk 0's readout; SB: the state on entry to the
+// pair); after them:
+//   QH1 : Q^1', QH layout                                          (16 KiB)
+//   O01 : O0_1', O0 layout                                         (16 KiB)
+// A sequence's last pair may hold one chunk; it then carries that chunk's
+// own map and readout, and QH1 / O01 are not used.
+constexpr int kPairTokens = 2 * kChunk;
+constexpr size_t kOffQH1 = kRecBytes;
+constexpr size_t kOffO01 = kOffQH1 + 16 * kFragBytes;
+constexpr size_t kPairRecBytes = kOffO01 + kNumVBlocks * 2048;
+static_assert(kPairRecBytes % 256 == 0, "pair records stay 256-byte aligned");
+
 // Global-memory pointers whose address space is explicit, so the compiler
 // emits global (not flat) memory instructions for them.
 typedef __attribute__((address_space(1))) uint8_t gbyte;
@@ -171,27 +193,36 @@ __device__ __forceinline__ SeqInfo seq_info(const int32_t *cu, int n, int T, int
     return s;
 }
 
-// Chunk slot -> (sequence, chunk index).  Returns false for an unused slot.
-__device__ __forceinline__ bool slot_to_chunk(const int32_t *cu, int N, int T, int64_t slot,
-                                              int &n, int64_t &j)
+// Slot of kStep tokens (a chunk, or a pair of chunks) -> (sequence, step
+// index).  Returns false for an unused slot.
+template <int kStep>
+__device__ __forceinline__ bool slot_to_step(const int32_t *cu, int N, int T, int64_t slot, int &n,
+                                             int64_t &j)
 {
     if (cu) {
         int lo = 0, hi = N - 1;
         while (lo < hi) {                       // largest n with cu[n]/C + n <= slot
             const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)cu[mid] / kChunk + mid <= slot)
+            if ((int64_t)cu[mid] / kStep + mid <= slot)
                 lo = mid;
             else
                 hi = mid - 1;
         }
         n = lo;
-        j = slot - ((int64_t)cu[n] / kChunk + n);
-        return (int64_t)cu[n + 1] - cu[n] > j * kChunk;
+        j = slot - ((int64_t)cu[n] / kStep + n);
+        return (int64_t)cu[n + 1] - cu[n] > j * kStep;
     }
-    const int64_t nck = (T + kChunk - 1) / kChunk;
+    const int64_t nck = (T + kStep - 1) / kStep;
     n = (int)(slot / nck);
     j = slot % nck;
     return n < N;
+}
+
+// Chunk slot -> (sequence, chunk index).  Returns false for an unused slot.
+__device__ __forceinline__ bool slot_to_chunk(const int32_t *cu, int N, int T, int64_t slot,
+                                              int &n, int64_t &j)
+{
+    return slot_to_step<kChunk>(cu, N, T, slot, n, j);
 }
 
 
@@ -236,13 +267,16 @@ hipError_t launch_chunk_bwd_f32(const float *q, const float *k, const float *v, 
                                 hipStream_t stream);
 
 // allow_aux = false keeps every kernel on `stream` (no auxiliary stream is
-// created or used, whatever the sequence length).
+// created or used, whatever the sequence length).  pair = true composes
+// consecutive chunks into pair records (n_slots then counts pair slots:
+// B ceil(T / 128), or floor(T / 128) + N with cu_seqlens); snapshots then
+// need an interval that is a multiple of kPairTokens.
 hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                              const bf16 *beta, const bf16 *gate, const float *init, bf16 *out,
                              float *final_state, float *snaps, int snap_interval,
                              const int32_t *cu, int N, int T, int H, int64_t n_slots,
                              float scale, unsigned pro, void *workspace, hipStream_t stream,
-                             bool allow_aux = true);
+                             bool pair, bool allow_aux = true);
 
 // Chunkwise backward, bf16, dk = dv = 128, 64-token chunks; the workspace
 // holds two record arrays of n_slots * H records each (forward, backward), or

@@ -72,21 +72,55 @@ def test_supported_sets(lib):
 
 def test_workspace_bytes(lib):
     ws = lib.kda_chunk_fwd_workspace_bytes
-    REC = ws(1, 64, 1, 1, 128, 128, 64, 1, 0)       # one 64-token chunk of one head
-    assert REC > 0 and REC % 256 == 0
-    # fixed length: B * ceil(T / 64) slots per head
-    assert ws(1, 4096, 1, 8, 128, 128, 64, 1, 0) == 64 * 8 * REC
-    assert ws(3, 100, 3, 2, 128, 128, 64, 1, 0) == 3 * 2 * 2 * REC
+    rb = lib.kda_chunk_fwd_records_bytes
+    PREC = ws(1, 64, 1, 1, 128, 128, 64, 1, 0)      # one pair slot (here holding one chunk)
+    REC = rb(1, 64, 1, 1, 128, 128, 64, 1, 0)       # one 64-token chunk of one head
+    assert PREC % 256 == 0 and REC % 256 == 0
+    # bytes per token-head as documented: pair records 1,284, chunk records 2,056
+    assert PREC == 164352 and PREC // 128 == 1284
+    assert REC == 131584 and REC // 64 == 2056
+    # fixed length: B * ceil(T / 128) pair slots per head
+    assert ws(1, 4096, 1, 8, 128, 128, 64, 1, 0) == 32 * 8 * PREC
+    assert ws(3, 100, 3, 2, 128, 128, 64, 1, 0) == 3 * 2 * 1 * PREC
+    assert ws(3, 200, 3, 2, 128, 128, 64, 1, 0) == 3 * 2 * 2 * PREC
     assert ws(1, 0, 1, 4, 128, 128, 64, 1, 0) == 0
-    # varlen: floor(T / 64) + N slots per head
-    assert ws(1, 67000, 4, 32, 128, 128, 64, 1, 1) == (67000 // 64 + 4) * 32 * REC
-    assert ws(1, 1 << 20, 1, 16, 128, 128, 64, 1, 0) == 16384 * 16 * REC
+    # varlen: floor(T / 128) + N pair slots per head
+    assert ws(1, 67000, 4, 32, 128, 128, 64, 1, 1) == (67000 // 128 + 4) * 32 * PREC
+    # the 1M-token workload: 8,192 pairs x 16 heads, 21.5 GB (per-chunk records: 34.5 GB)
+    assert ws(1, 1 << 20, 1, 16, 128, 128, 64, 1, 0) == 8192 * 16 * PREC
+    assert ws(1, 1 << 20, 1, 16, 128, 128, 64, 1, 0) < 24e9
+    # per-chunk records: B * ceil(T / 64), or floor(T / 64) + N, chunk slots per head
+    assert rb(1, 4096, 1, 8, 128, 128, 64, 1, 0) == 64 * 8 * REC
+    assert rb(3, 100, 3, 2, 128, 128, 64, 1, 0) == 3 * 2 * 2 * REC
+    assert rb(1, 67000, 4, 32, 128, 128, 64, 1, 1) == (67000 // 64 + 4) * 32 * REC
     # fp32 path needs none
-    assert ws(1, 64, 1, 2, 16, 16, 16, 0, 0) == 0
+    assert ws(1, 64, 1, 2, 16, 16, 16, 0, 0) == 0 and rb(1, 64, 1, 2, 16, 16, 16, 0, 0) == 0
     bad = ctypes.c_size_t(-1).value
-    assert ws(1, 64, 1, 2, 64, 64, 64, 1, 0) == bad           # unsupported dims
-    assert ws(2, 64, 1, 2, 128, 128, 64, 1, 1) == bad         # varlen needs B = 1
-    assert ws(2, 64, 3, 2, 128, 128, 64, 1, 0) == bad         # N must equal B
+    for fn in (ws, rb):
+        assert fn(1, 64, 1, 2, 64, 64, 64, 1, 0) == bad           # unsupported dims
+        assert fn(2, 64, 1, 2, 128, 128, 64, 1, 1) == bad         # varlen needs B = 1
+        assert fn(2, 64, 3, 2, 128, 128, 64, 1, 0) == bad         # N must equal B
+
+
+def test_chunk_records_flag_needs_the_records_size(lib):
+    """KDA_FWD_CHUNK_RECORDS keeps one record per chunk: a workspace of the
+    pair-record size is too small for it (T = 4096: 64 chunk records of
+    131,584 B against 32 pair records of 164,352 B)."""
+    p = ctypes.c_void_p
+    PREC_ALL = lib.kda_chunk_fwd_workspace_bytes(1, 4096, 1, 1, 128, 128, 64, 1, 0)
+    REC_ALL = lib.kda_chunk_fwd_records_bytes(1, 4096, 1, 1, 128, 128, 64, 1, 0)
+    assert REC_ALL > PREC_ALL
+
+    def chunk(flags, nbytes):
+        return lib.kda_chunk_fwd_ex(p(1), p(1), p(1), p(1), p(1), p(1), None, p(1), None, None, 0,
+                                    None, 1, 4096, 1, 1, 128, 128, 64, 1.0, 1, flags, p(1), nbytes,
+                                    None)
+    assert chunk(kda.FWD_CHUNK_RECORDS, PREC_ALL) == WS
+    assert chunk(kda.FWD_CHUNK_RECORDS, REC_ALL - 1) == WS
+    assert chunk(0, PREC_ALL - 1) == WS
+    # enough bytes: the next check (the misaligned fake pointers) answers
+    assert chunk(kda.FWD_CHUNK_RECORDS, REC_ALL) == MISAL
+    assert chunk(0, PREC_ALL) == MISAL
 
 
 def _chunk(lib, **kw):
@@ -171,11 +205,12 @@ def test_snapshot_index_matches_the_documented_slots():
 
 
 def test_chunk_fwd_snapshots_rejects_bad_arguments(lib):
-    REC = lib.kda_chunk_fwd_workspace_bytes(1, 64, 1, 1, 128, 128, 64, 1, 0)
+    PREC = lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 1, 128, 128, 64, 1, 0)
+    REC = lib.kda_chunk_fwd_records_bytes(1, 256, 1, 1, 128, 128, 64, 1, 0)
     p = lambda x: None if x is None else ctypes.c_void_p(x)
 
     def call(snaps, interval, **kw):
-        a = dict(B=1, T=64, N=1, H=1, ws=1, ws_bytes=REC)
+        a = dict(B=1, T=256, N=1, H=1, ws=1, ws_bytes=REC)
         a.update(kw)
         return lib.kda_chunk_fwd_snapshots(p(1), p(1), p(1), p(1), p(1), p(1), None, p(1), None,
                                            p(snaps), interval, None, a["B"], a["T"], a["N"],
@@ -183,7 +218,13 @@ def test_chunk_fwd_snapshots_rejects_bad_arguments(lib):
                                            a["ws_bytes"], None)
     assert call(1, 100) == SHAPE
     assert call(1, 0) == SHAPE
+    # an interval of 64 or 192 tokens falls inside a pair of chunks: per-chunk
+    # records (4 x 131,584 B here); multiples of 128 need the pair records
+    assert REC > PREC
     assert call(1, 64, ws_bytes=REC - 1) == WS
+    assert call(1, 192, ws_bytes=PREC) == WS
+    assert call(1, 128, ws_bytes=PREC - 1) == WS
+    assert call(1, 128, ws_bytes=PREC) == MISAL      # enough: the fake pointers answer
     assert call(1, 64, B=2) == SHAPE
 
 
@@ -198,8 +239,8 @@ def test_prologue_rejects_unknown_bits(lib):
     def dec(pro):
         return lib.kda_decode_step_ex(p(1), p(1), p(1), p(1), p(1), p(1), p(1), p(1), 1, 1, 128,
                                       128, 1.0, 1, pro, None)
-    assert chunk(8) == UNSUP and chunk(0xFFFF) == UNSUP
-    assert dec(8) == UNSUP
+    assert chunk(8) == UNSUP and chunk(0xFFFF) == UNSUP and chunk(512) == UNSUP
+    assert dec(8) == UNSUP and dec(kda.FWD_CHUNK_RECORDS) == UNSUP
 
 
 def test_verify_and_commit_reject_bad_arguments(lib):
@@ -262,7 +303,7 @@ def test_chunk_bwd_sizes_and_argument_checks(lib):
     assert ws(1, 0, 1, 2, 16, 16, 16, 0, 0) == 0
     assert ws(2, 64, 1, 1, 16, 16, 16, 0, 0) == bad
     # bf16: a forward and a backward record per (64-token chunk slot, head)
-    REC = lib.kda_chunk_fwd_workspace_bytes(1, 64, 1, 1, 128, 128, 64, 1, 0)
+    REC = lib.kda_chunk_fwd_records_bytes(1, 64, 1, 1, 128, 128, 64, 1, 0)
     assert ws(1, 4096, 1, 8, 128, 128, 64, 1, 0) == 2 * 64 * 8 * REC
     assert ws(1, 1000, 3, 2, 128, 128, 64, 1, 1) == 2 * (1000 // 64 + 3) * 2 * REC
     assert ws(1, 64, 1, 1, 128, 128, 16, 1, 0) == bad
@@ -319,15 +360,15 @@ def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
     """kda_chunk_fwd_noalloc checks its workspace need against the static
     scratch size before touching the device; argument errors come first."""
     ws = lib.kda_chunk_fwd_workspace_bytes
-    rec = ws(1, 64, 1, 1, 128, 128, 64, 1, 0)
+    rec = ws(1, 128, 1, 1, 128, 128, 64, 1, 0)         # one pair record
     limit = kda.NOALLOC_SCRATCH_BYTES
     H = 8
-    t_fit = (limit // (rec * H)) * 64          # the longest B=1, H=8 call that fits
+    t_fit = (limit // (rec * H)) * 128          # the longest B=1, H=8 call that fits
     assert ws(1, t_fit, 1, H, 128, 128, 64, 1, 0) <= limit
-    assert ws(1, t_fit + 64, 1, H, 128, 128, 64, 1, 0) > limit
+    assert ws(1, t_fit + 1, 1, H, 128, 128, 64, 1, 0) > limit
     fn = lib.kda_chunk_fwd_noalloc
     p = [ctypes.c_void_p(A)] * 6
-    assert fn(*p, None, ctypes.c_void_p(A), None, None, 1, t_fit + 64, 1, H, 128, 128, 64,
+    assert fn(*p, None, ctypes.c_void_p(A), None, None, 1, t_fit + 1, 1, H, 128, 128, 64,
               1.0, 1, None) == SCRATCH
     # unsupported sizes and bad shapes are reported as such, not as the limit
     assert fn(*p, None, ctypes.c_void_p(A), None, None, 1, 64, 1, H, 64, 64, 64, 1.0, 1,

@@ -153,19 +153,32 @@ def test_bf16_backward_prefill_t4096_h8(dev):
 
 
 def test_bf16_backward_reusing_forward_records(dev):
-    """kda_chunk_bwd_ex on the workspace of the forward call: the same gradients
-    bit for bit as the backward alone, and within tolerance of the oracle."""
+    """kda_chunk_bwd_ex on the workspace of a forward that kept per-chunk
+    records (KDA_FWD_CHUNK_RECORDS): the same gradients bit for bit as the
+    backward alone, and within tolerance of the oracle; the forward's outputs
+    equal those of the default forward (pair records) within its tolerance."""
     say("backward bf16 reusing the forward's records (varlen, init state)")
     x = small_inputs(torch.bfloat16, 1, 0, 2, 128, 128, 36, lengths=[70, 0, 200, 64, 5],
                      init_std=0.02)
     dy, dfin = cotangents(x, 901, 0.05)
     xd = to(x, dev)
     ws_f = torch.empty(kda.chunk_fwd_workspace_bytes(1, int(x["q"].shape[1]), 5, 2, 128, 128, 64,
-                                                     torch.bfloat16, True),
+                                                     torch.bfloat16, True, chunk_records=True),
                        dtype=torch.uint8, device=dev)
-    kda.chunk_fwd(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["z"],
-                  init_state=xd["init_state"], cu_seqlens=xd["cu_seqlens"], workspace=ws_f,
-                  scale=0.5)
+    out_c, fin_c = kda.chunk_fwd(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["z"],
+                                 init_state=xd["init_state"], cu_seqlens=xd["cu_seqlens"],
+                                 workspace=ws_f, scale=0.5, chunk_records=True)
+    out_p, fin_p = kda.chunk_fwd(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["z"],
+                                 init_state=xd["init_state"], cu_seqlens=xd["cu_seqlens"],
+                                 scale=0.5)
+    torch.cuda.synchronize()
+    ro, rf = oracle.forward(*(np32(x[k]) for k in ("q", "k", "v", "g", "beta", "z")),
+                            init_state=np32(x["init_state"]),
+                            cu_seqlens=x["cu_seqlens"].numpy(), scale=0.5)
+    for label, (o, f) in (("chunk records", (out_c, fin_c)), ("pair records", (out_p, fin_p))):
+        eo, es = rel(np32(o), ro), rel(np32(f), rf)
+        say(f"forward with {label}: out rel err {eo:.3e}, state rel err {es:.3e}")
+        assert eo <= 2e-2 and es <= 1e-2
     kw = dict(init_state=xd["init_state"], grad_final_state=dfin.to(dev),
               cu_seqlens=xd["cu_seqlens"], scale=0.5)
     reused = kda.chunk_bwd(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["z"], dy.to(dev),

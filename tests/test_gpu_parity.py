@@ -185,6 +185,19 @@ def test_bf16_small_cases(dev, case):
     check(out, fin, ro, rf, TOL_BF16_OUT, TOL_BF16_STATE, f"bf16 {case}")
 
 
+@pytest.mark.parametrize("g_mode", ["slow", "zero"])
+def test_bf16_long_slow_decay(dev, g_mode):
+    """16,384 tokens with little or no decay, so every chunk's entry state
+    matters to its outputs: 128 steps of the serial pass over composed pairs
+    of chunks (and a ragged second sequence), against the oracle."""
+    say(f"bf16 long sequences with g_mode={g_mode}: B=2 T=16,333 H=2")
+    x = small_inputs(torch.bfloat16, 2, 16_333, 2, 128, 128, 24, init_std=0.02, g_mode=g_mode)
+    out, fin = run_gpu(x, dev)
+    ro, rf = run_oracle(x)
+    check(out, fin, ro, rf, TOL_BF16_OUT, TOL_BF16_STATE, f"bf16 long {g_mode} decay")
+    log_worst(f"bf16 long {g_mode} decay", out, ro, fin, rf)
+
+
 def test_bf16_scale_inplace_state_and_no_final(dev):
     say("bf16 scale 0.5, final_state aliasing init_state, then no final state")
     x = small_inputs(torch.bfloat16, 1, 130, 2, 128, 128, 15, init_std=0.02)

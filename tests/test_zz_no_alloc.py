@@ -87,8 +87,10 @@ def test_noalloc_under_graph_capture(dev):
 
 
 def test_noalloc_size_limit(dev):
-    rec = kda.chunk_fwd_workspace_bytes(1, 64, 1, 1, 128, 128, 64, torch.bfloat16, False)
-    T = (kda.NOALLOC_SCRATCH_BYTES // rec + 1) * 64          # one chunk past the limit, H = 1
+    rec = kda.chunk_fwd_workspace_bytes(1, 128, 1, 1, 128, 128, 64, torch.bfloat16, False)
+    T = (kda.NOALLOC_SCRATCH_BYTES // rec) * 128 + 1        # one token past the limit, H = 1
+    assert kda.chunk_fwd_workspace_bytes(1, T, 1, 1, 128, 128, 64, torch.bfloat16,
+                                         False) > kda.NOALLOC_SCRATCH_BYTES
     say(f"T={T}, H=1: beyond the scratch array, refused before launch")
     x = to(small_inputs(torch.bfloat16, 1, T, 1, 128, 128, 93), dev)
     out = torch.full_like(x["v"], 3.0)
