@@ -23,10 +23,11 @@
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library allocates no device memory; calls are re-entrant.  Its only
- *     state is one auxiliary HIP stream and a few events per device, created
- *     at the first kda_chunk_fwd over a long single sequence (see there) and
- *     kept until the process ends.
+ *     library allocates no device memory; calls are re-entrant.  State it
+ *     keeps until the process ends, per device: one auxiliary HIP stream and a
+ *     few events (created at the first kda_chunk_fwd over a long single
+ *     sequence, see there), its kernels' LDS attributes, and the address of
+ *     the static scratch array of kda_chunk_fwd_noalloc.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns without synchronising; work forked to the auxiliary stream is
  *     joined back into `stream` before the call's last kernel.  Arguments are validated on the host
@@ -140,12 +141,14 @@ size_t kda_chunk_fwd_records_bytes(int B, int T, int N, int H, int dk, int dv, i
  *               left undefined.  May be NULL when the size is 0.
  * Overlapping calls that share a workspace race; out must not alias any input.
  *
- * Long single sequences (KDA_BF16, cu_seqlens NULL, B = 1, at least 1,024
- * chunks, final_state not NULL, no snapshots): the serial part runs in
- * segments of at least 512 chunks on the auxiliary stream, each segment
+ * Long single sequences (KDA_BF16, cu_seqlens NULL, B = 1, at least 65,536
+ * tokens, final_state not NULL, no snapshots): the serial part runs in
+ * segments of at least 32,768 tokens on the auxiliary stream, each segment
  * starting from the fp32 state the previous one left in final_state, while
  * `stream` computes each finished segment's outputs.  The result is bitwise
  * that of one unsegmented pass; final_state is written during the call.
+ * When `stream` is capturing a graph (hipStreamIsCapturing), every kernel
+ * stays on `stream` instead, with the same result.
  */
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                          const void *beta, const void *gate, const float *init_state,
