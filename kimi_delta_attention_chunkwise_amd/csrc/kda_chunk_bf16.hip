@@ -412,7 +412,12 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
         // x[s] = 0 for s < col, so the full-range sums only add zeros there
         // (column form: once x[s] is final it updates every later row at once,
         // so the dependency depth is 16 instead of 120)
-        const int blk = lane >> 4, col = lane & 15, o = 16 * blk;
+        // the start vector depends only on the lane: made opaque here, so the
+        // compiler forms it per chunk instead of holding 16 registers (or
+        // spill slots) through the whole persistent loop
+        int col = lane & 15;
+        asm volatile("" : "+v"(col));
+        const int blk = lane >> 4, o = 16 * blk;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
