@@ -848,7 +848,21 @@ constexpr int kSideWave = kComputeWaves + 1;
 // two blocks each
 template <int kNB> constexpr int chain_side_waves() { return kNB <= 2 ? 1 : kNB / 2; }
 template <int kNB> constexpr int chain_threads() { return 64 * (kComputeWaves + 1 + chain_side_waves<kNB>()); }
-constexpr int kPrefetch = 4;         // chunks of operands in flight per compute wave
+// Chunks of operands in flight per compute wave (L) and per side wave (Bm,
+// dec).  Records in HBM (a long sequence) make a step about half again as
+// long as records still in the last-level cache, and deeper prefetch does not
+// shorten it: the step is then bound by the loads and stores one CU keeps in
+// flight, not by the latency of one load.
+constexpr int kPrefetch = 4;
+constexpr int kSideSets = kPrefetch;
+
+// the second chain of a launch that runs two (ws null: none)
+struct ChainJob2 {
+    const float *init;
+    float *final_state;
+    uint8_t *ws;
+    int wgs;        // workgroups of the first chain
+};
 
 struct ChainStage {
     bf16x8 ln[4];      // -L rows of the wave's state tile, 4 dk k-steps
@@ -878,11 +892,15 @@ __device__ __forceinline__ void chain_load(ChainStage &st, const uint8_t *rec_an
 //
 // kPair: the records are pair records (kPairRecBytes), one step per pair of
 // chunks; the step's arithmetic is the same.
+//
+// job2 (ws not null, no snapshots): a second chain over other records of the
+// same shape runs in workgroups job2.wgs .. 2 job2.wgs - 1 of the launch, with
+// its own initial and final state.
 template <bool kSnap, int kNB = 1, bool kPair = false>
 __global__ __launch_bounds__(chain_threads<kNB>()) void kda_chain_bf16_kernel(
     const float *__restrict__ init, float *__restrict__ final_state, float *__restrict__ snaps,
     int snap_steps, const int32_t *__restrict__ cu, int T, int H, int units,
-    uint8_t *__restrict__ ws)
+    uint8_t *__restrict__ ws, ChainJob2 job2)
 {
     constexpr int kStep = kPair ? kPairTokens : kChunk;           // tokens per step
     constexpr size_t kRec = kPair ? kPairRecBytes : kRecBytes;    // record stride
@@ -901,7 +919,13 @@ __global__ __launch_bounds__(chain_threads<kNB>()) void kda_chain_bf16_kernel(
     // all value blocks of one (sequence, head) land on the same XCD (blocks are
     // dealt to the 8 XCDs round-robin), so they share that XCD's L2
     constexpr int kWgPerUnit = kNumVBlocks / kNB;
-    const int id = blockIdx.x;
+    int id = blockIdx.x;
+    if (!kSnap && job2.ws && id >= job2.wgs) {
+        id -= job2.wgs;
+        init = job2.init;
+        final_state = job2.final_state;
+        ws = job2.ws;
+    }
     const int xcd = id & 7, qid = id >> 3;
     const int unit = (int)((unsigned)qid / kWgPerUnit) * 8 + xcd;
     const int blk = (int)((unsigned)qid % kWgPerUnit) * kNB;   // first value block of the workgroup
@@ -924,14 +948,16 @@ __global__ __launch_bounds__(chain_threads<kNB>()) void kda_chain_bf16_kernel(
     const int64_t niter = (nch + kPrefetch - 1) / kPrefetch * kPrefetch;
     if (chain_side_waves<kNB>() == 1 ? w == kSideWave : w >= kSideWave) {
         // side operands of chunk jc (past the end: the last chunk) into register
-        // set `set`, later into ring slot jc & 1; two sets, loaded two chunks
-        // ahead, so each wait leaves the newer set's loads in flight.  Side
-        // wave sw fetches Bm of blocks sw * kSideBlocks .. + kSideBlocks - 1
-        // (of the workgroup's), and side wave 0 the decay vector too.
+        // set jc % kSideSets, later into ring slot jc & 1: a chunk's loads are
+        // issued kSideSets steps before it is staged, so each wait leaves the
+        // newer sets' loads in flight (on a long sequence the records come
+        // from HBM, whose latency spans several steps).  Side wave sw fetches
+        // Bm of blocks sw * kSideBlocks .. + kSideBlocks - 1 (of the
+        // workgroup's), and side wave 0 the decay vector too.
         constexpr bool kOneSide = chain_side_waves<kNB>() == 1;
         const int sb0 = kOneSide ? 0 : (w - kSideWave) * kSideBlocks;
-        bf16x8 nbm[2][kSideBlocks][4];
-        f32x2 ndec[2];
+        bf16x8 nbm[kSideSets][kSideBlocks][4];
+        f32x2 ndec[kSideSets];
         auto side_load = [&](int set, int64_t jc) {
             const gbyte *rec = uniform_gptr(rec_of(jc < nch ? jc : nch - 1));
 #pragma unroll
@@ -955,18 +981,21 @@ __global__ __launch_bounds__(chain_threads<kNB>()) void kda_chain_bf16_kernel(
         if (nch > 0) {
             side_load(0, 0);
             side_store(0, 0);
-            side_load(1, 1);
-            side_load(0, 2);
+#pragma unroll
+            for (int c = 1; c <= kSideSets; ++c)
+                side_load(c % kSideSets, c);
         }
         __syncthreads();
-        // niter is a multiple of kPrefetch, so of 2
-        for (int64_t jc = 0; jc < niter; jc += 2) {
-            side_store(1, (jc + 1) & 1);   // chunk jc + 1, read in the next iteration
-            side_load(1, jc + 3);
-            __syncthreads();
-            side_store(0, jc & 1);         // chunk jc + 2
-            side_load(0, jc + 4);
-            __syncthreads();
+        // niter is a multiple of kSideSets; in step jc stage chunk jc + 1, read
+        // in the next step, and refill its set with chunk jc + 1 + kSideSets
+        for (int64_t j0 = 0; j0 < niter; j0 += kSideSets) {
+#pragma unroll
+            for (int s = 0; s < kSideSets; ++s) {
+                const int set = (s + 1) % kSideSets;
+                side_store(set, (int)((j0 + s + 1) & 1));
+                side_load(set, j0 + s + 1 + kSideSets);
+                __syncthreads();
+            }
         }
         return;
     }
@@ -1273,7 +1302,8 @@ int64_t chain_workgroups(int64_t units, int nb) { return (units + 7) / 8 * 8 * (
 
 template <int kNB, bool kPair>
 hipError_t launch_chain_nb(const float *init, float *final_state, const int32_t *cu, int N,
-                           int T, int H, uint8_t *ws, hipStream_t stream, bool own_cu)
+                           int T, int H, uint8_t *ws, hipStream_t stream, bool own_cu,
+                           ChainJob2 job2 = ChainJob2{})
 {
     const int64_t units = (int64_t)N * H;
     if (units <= 0)
@@ -1306,9 +1336,11 @@ hipError_t launch_chain_nb(const float *init, float *final_state, const int32_t 
             return attr_err[dev];
         dyn = reserve[dev];
     }
+    const int64_t wgs = chain_workgroups(units, kNB);
+    job2.wgs = (int)wgs;
     hipLaunchKernelGGL((kda_chain_bf16_kernel<false, kNB, kPair>),
-                       dim3((unsigned)chain_workgroups(units, kNB)), dim3(chain_threads<kNB>()),
-                       dyn, stream, init, final_state, nullptr, 1, cu, T, H, (int)units, ws);
+                       dim3((unsigned)(job2.ws ? 2 * wgs : wgs)), dim3(chain_threads<kNB>()), dyn,
+                       stream, init, final_state, nullptr, 1, cu, T, H, (int)units, ws, job2);
     return hipGetLastError();
 }
 
@@ -1325,7 +1357,7 @@ hipError_t launch_chain_t(const float *init, float *final_state, float *snaps, i
         hipLaunchKernelGGL((kda_chain_bf16_kernel<true, 1, kPair>),
                            dim3((unsigned)chain_workgroups(units, 1)), dim3(chain_threads<1>()),
                            0, stream, init, final_state, snaps, snap_interval / kStep, cu, T, H,
-                           (int)units, ws);
+                           (int)units, ws, ChainJob2{});
         return hipGetLastError();
     }
     int dev = 0, cus = 0;
@@ -1354,6 +1386,31 @@ hipError_t launch_chain(const float *init, float *final_state, float *snaps, int
                                        stream, own_cu)
                 : launch_chain_t<false>(init, final_state, snaps, snap_interval, cu, N, T, H, ws,
                                         stream, own_cu);
+}
+
+// Two chains over per-chunk records of the same sequences in one launch: over
+// ws_a from init_a (no final state) and over ws_b from init_b, its final state
+// to final_b.  The workgroups per unit follow the rule above for the
+// launch's two chains together.
+hipError_t launch_chain_two(const float *init_a, uint8_t *ws_a, const float *init_b,
+                            float *final_b, uint8_t *ws_b, const int32_t *cu, int N, int T, int H,
+                            hipStream_t stream)
+{
+    const int64_t units = (int64_t)N * H;
+    if (units <= 0)
+        return hipSuccess;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    const ChainJob2 job2{init_b, final_b, ws_b, 0};
+    if (2 * chain_workgroups(units, 4) >= cus)
+        return launch_chain_nb<4, false>(init_a, nullptr, cu, N, T, H, ws_a, stream, false, job2);
+    if (2 * chain_workgroups(units, 2) >= cus)
+        return launch_chain_nb<2, false>(init_a, nullptr, cu, N, T, H, ws_a, stream, false, job2);
+    return launch_chain_nb<1, false>(init_a, nullptr, cu, N, T, H, ws_a, stream, false, job2);
 }
 
 hipError_t launch_output(const bf16 *gate, bf16 *out, const int32_t *cu, int N, int T, int H,
@@ -1535,15 +1592,21 @@ hipError_t launch_chunk_bwd_bf16(const bf16 *q, const bf16 *k, const bf16 *v, co
     uint8_t *ws_b = fwd_records ? static_cast<uint8_t *>(workspace)
                                 : static_cast<uint8_t *>(workspace) + rec_bytes;
     hipError_t e = hipSuccess;
-    if (!fwd_records) {
+    if (fwd_records) {
+        e = launch_bwd_prep_bf16(gate, dout, cu, N, T, H, n_slots, ws_f, ws_b, stream);
+        if (e == hipSuccess)
+            e = launch_chain(dfinal, dinit, nullptr, 0, cu, N, T, H, ws_b, stream, false);
+    } else {
+        // The state-gradient recurrence needs the forward records but not the
+        // forward states, and the chain writes only SB, which the backward prep
+        // does not read: after both preps one launch runs the forward chain
+        // (every chunk's entry state) and the backward chain side by side.
         e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, 0u, ws_f, stream, false);
         if (e == hipSuccess)
-            e = launch_chain(init, nullptr, nullptr, 0, cu, N, T, H, ws_f, stream, false);
+            e = launch_bwd_prep_bf16(gate, dout, cu, N, T, H, n_slots, ws_f, ws_b, stream);
+        if (e == hipSuccess)
+            e = launch_chain_two(init, ws_f, dfinal, dinit, ws_b, cu, N, T, H, stream);
     }
-    if (e == hipSuccess)
-        e = launch_bwd_prep_bf16(gate, dout, cu, N, T, H, n_slots, ws_f, ws_b, stream);
-    if (e == hipSuccess)
-        e = launch_chain(dfinal, dinit, nullptr, 0, cu, N, T, H, ws_b, stream, false);
     if (e == hipSuccess)
         e = launch_grad_bf16(q, k, v, g, beta, gate, dout, dq, dk, dv, dg, dbeta, dgate, cu, N,
                              T, H, n_slots, scale, ws_f, ws_b, stream);
