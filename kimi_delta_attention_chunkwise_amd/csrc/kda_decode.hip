@@ -29,48 +29,38 @@ struct DecodeGeom {
     static_assert(DK % RG == 0, "rows split evenly");
 };
 
-// Stage exp(g), k and (when qu is given) q of one (sequence, token, head) row
-// in LDS.  With the prologue, g is mapped to the log-decay and k, q are
-// L2-normalised (wave 0 reduces the squares).  Ends with a barrier.
+// Stage exp(g), k and q of one (sequence, token, head) row in LDS (with the
+// prologue, g mapped to the log-decay; k and q as given).  Ends with a barrier.
 template <typename T, int DK, int NT, bool kPro>
 __device__ __forceinline__ void stage_token(const T *qu, const T *ku, const T *gu, float *va,
-                                            float *vk, float *vq, float *nrm, unsigned pro,
-                                            int tid)
+                                            float *vk, float *vq, unsigned pro, int tid)
 {
     for (int i = tid; i < DK; i += NT) {
         const float gx = to_f32(gu[i]);
         va[i] = __expf((kPro && (pro & kProG)) ? log_decay_from(gx) : gx);
         vk[i] = to_f32(ku[i]);
-        if (qu)
-            vq[i] = to_f32(qu[i]);
+        vq[i] = to_f32(qu[i]);
     }
     __syncthreads();
-    if (kPro && (pro & kProQK)) {
-        if (tid < 64) {
-            float sk = 0.f, sq = 0.f;
-            for (int i = tid; i < DK; i += 64) {
-                sk += vk[i] * vk[i];
-                if (qu)
-                    sq += vq[i] * vq[i];
-            }
+}
+
+// The prologue's L2 norms of k and q.  Every reduction of a step is linear
+// in k and in q, so the kernels reduce with the token's k and q as given and
+// scale afterwards: p and k . q by 1 / |k|, S~^T q and k . q by 1 / |q|, and
+// the written row k_r by 1 / |k|.  The squares are summed in a fixed order
+// (over the rows rg + RG m of row group rg, m ascending, with fused
+// multiply-adds; then over the row groups, rg ascending), which the decode,
+// verify and commit kernels share, so that the three form the same 1 / |k|.
+__device__ __forceinline__ float sq_acc(float x, float acc) { return __fmaf_rn(x, x, acc); }
+
+template <int RG>
+__device__ __forceinline__ float inv_norm(const float *part)
+{
+    float s = part[0];
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                sk += __shfl_xor(sk, o);
-                sq += __shfl_xor(sq, o);
-            }
-            if (tid == 0) {
-                nrm[0] = __builtin_amdgcn_rsqf(sk + kNormEps);
-                nrm[1] = __builtin_amdgcn_rsqf(sq + kNormEps);
-            }
-        }
-        __syncthreads();
-        for (int i = tid; i < DK; i += NT) {
-            vk[i] *= nrm[0];
-            if (qu)
-                vq[i] *= nrm[1];
-        }
-        __syncthreads();
-    }
+    for (int r = 1; r < RG; ++r)
+        s = __fadd_rn(s, part[r]);
+    return __builtin_amdgcn_rsqf(s + kNormEps);
 }
 
 // The state update of one row quad, written out so that the decode / verify
@@ -105,10 +95,11 @@ __device__ __forceinline__ void verify_tokens(
     constexpr int kG = kVerifyGroup;
     static_assert(NT % 64 == 0, "whole waves");
     __shared__ float va[kG][DK], vk[kG][DK], vq[kG][DK];
-    __shared__ float nrm[kG][2];
     __shared__ f32x4 red_p[2][RG][CG];
     __shared__ f32x4 red_s[2][RG][CG];
     __shared__ float red_kq[2][RG];
+    __shared__ float red_k2[2][RG], red_q2[2][RG];     // prologue: sums of k^2 and q^2
+    const bool qk = kPro && (pro & kProQK);
     const int cg = tid % CG, rg = tid / CG;
     for (int t0 = 0; t0 < K; t0 += kG) {
         const int nt = K - t0 < kG ? K - t0 : kG;
@@ -138,33 +129,6 @@ __device__ __forceinline__ void verify_tokens(
             }
         }
         __syncthreads();
-        if (kPro && (pro & kProQK)) {
-            // 1 / |k| and 1 / |q| of each token, summed as in a decode step
-            const int l = tid & 63;
-            for (int tt = tid >> 6; tt < nt; tt += NT / 64) {
-                float sk = 0.f, sq = 0.f;
-                for (int i = l; i < DK; i += 64) {
-                    sk += vk[tt][i] * vk[tt][i];
-                    sq += vq[tt][i] * vq[tt][i];
-                }
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) {
-                    sk += __shfl_xor(sk, o);
-                    sq += __shfl_xor(sq, o);
-                }
-                if (l == 0) {
-                    nrm[tt][0] = __builtin_amdgcn_rsqf(sk + kNormEps);
-                    nrm[tt][1] = __builtin_amdgcn_rsqf(sq + kNormEps);
-                }
-            }
-            __syncthreads();
-            for (int i = tid; i < nt * DK; i += NT) {
-                const int tt = i / DK, c = i % DK;
-                vk[tt][c] *= nrm[tt][0];
-                vq[tt][c] *= nrm[tt][1];
-            }
-            __syncthreads();
-        }
 #pragma unroll
         for (int tt = 0; tt < kG; ++tt) {
             if (tt < nt) {
@@ -172,7 +136,7 @@ __device__ __forceinline__ void verify_tokens(
                 const int par = (t0 + tt) & 1;
                 float kk[RPT];
                 f32x4 p = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
-                float kq = 0.f;
+                float kq = 0.f, k2 = 0.f, q2 = 0.f;
 #pragma unroll
                 for (int m = 0; m < RPT; ++m) {
                     const int r = rg + RG * m;
@@ -182,11 +146,20 @@ __device__ __forceinline__ void verify_tokens(
                     p += s_reg[m] * kr;
                     sq += s_reg[m] * qr;
                     kq += kr * qr;
+                    if (qk) {
+                        k2 = sq_acc(kr, k2);
+                        q2 = sq_acc(qr, q2);
+                    }
                 }
                 red_p[par][rg][cg] = p;
                 red_s[par][rg][cg] = sq;
-                if (cg == 0)
+                if (cg == 0) {
                     red_kq[par][rg] = kq;
+                    if (qk) {
+                        red_k2[par][rg] = k2;
+                        red_q2[par][rg] = q2;
+                    }
+                }
                 // buffer par is written again for token t + 2 only after every
                 // thread has passed this barrier and the next one
                 __syncthreads();
@@ -197,6 +170,15 @@ __device__ __forceinline__ void verify_tokens(
                     P += red_p[par][r][cg];
                     SQ += red_s[par][r][cg];
                     KQ += red_kq[par][r];
+                }
+                if (qk) {
+                    const float ik = inv_norm<RG>(red_k2[par]), iq = inv_norm<RG>(red_q2[par]);
+                    P = P * ik;
+                    SQ = SQ * iq;
+                    KQ = __fmul_rn(__fmul_rn(KQ, ik), iq);
+#pragma unroll
+                    for (int m = 0; m < RPT; ++m)
+                        kk[m] = __fmul_rn(kk[m], ik);
                 }
                 const float b = (kPro && (pro & kProBeta)) ? sigmoidf_(bx[tt]) : bx[tt];
                 f32x4 u;
@@ -246,7 +228,8 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     __shared__ f32x4 red_s[RG][CG];
     __shared__ float red_kq[RG];
     __shared__ float va[DK], vk[DK], vq[DK];          // exp(g), k, q of the current token
-    __shared__ float nrm[2];                           // prologue: 1 / |k|, 1 / |q|
+    __shared__ float red_k2[RG], red_q2[RG];           // prologue: sums of k^2 and q^2
+    const bool qk = kPro && (pro & kProQK);
 
     const int64_t unit = blockIdx.x;                 // n * H + h
     const int64_t n = unit / H;
@@ -266,10 +249,10 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     for (int t = 0; t < K; ++t) {
         const int64_t row = (n * K + t) * H + h;
         stage_token<T, DK, Geo::NT, kPro>(q + row * DK, k + row * DK, g + row * DK, va, vk, vq,
-                                          nrm, pro, tid);
+                                          pro, tid);
         float kk[RPT];
         f32x4 p = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
-        float kq = 0.f;
+        float kq = 0.f, k2 = 0.f, q2 = 0.f;
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int r = rg + RG * m;
@@ -279,11 +262,20 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
             p += s_reg[m] * kr;                        // prediction for the key
             sq += s_reg[m] * qr;                       // decayed state read by q
             kq += kr * qr;
+            if (qk) {
+                k2 = sq_acc(kr, k2);
+                q2 = sq_acc(qr, q2);
+            }
         }
         red_p[rg][cg] = p;
         red_s[rg][cg] = sq;
-        if (cg == 0)
+        if (cg == 0) {
             red_kq[rg] = kq;
+            if (qk) {
+                red_k2[rg] = k2;
+                red_q2[rg] = q2;
+            }
+        }
         __syncthreads();
         f32x4 P = red_p[0][cg], SQ = red_s[0][cg];
         float KQ = red_kq[0];
@@ -292,6 +284,15 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
             P += red_p[r][cg];
             SQ += red_s[r][cg];
             KQ += red_kq[r];
+        }
+        if (qk) {
+            const float ik = inv_norm<RG>(red_k2), iq = inv_norm<RG>(red_q2);
+            P = P * ik;
+            SQ = SQ * iq;
+            KQ = __fmul_rn(__fmul_rn(KQ, ik), iq);
+#pragma unroll
+            for (int m = 0; m < RPT; ++m)
+                kk[m] = __fmul_rn(kk[m], ik);
         }
         const float bx = to_f32(beta[row]);
         const float b = (kPro && (pro & kProBeta)) ? sigmoidf_(bx) : bx;
@@ -328,8 +329,8 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
 // S <- diag(exp(g_t)) S + k_t u_t^T with the corrections u_t saved by the
 // verification, which reproduces the verified states exactly.  Tokens are
 // staged kCommitGroup at a time (one load phase and one barrier per group;
-// with the prologue, wave w reduces 1 / |k| of tokens w, w + waves, ...), each
-// with the same arithmetic as a staged decode step.
+// with the prologue, one more for the partial sums of k^2), each with the same
+// arithmetic as a staged decode step.
 constexpr int kCommitGroup = 4;
 
 template <typename T, int DK, int DV, bool kPro>
@@ -341,7 +342,8 @@ __global__ __launch_bounds__(256) void kda_commit_kernel(
     constexpr int CG = Geo::CG, RG = Geo::RG, RPT = Geo::RPT, NT = Geo::NT;
     static_assert(NT % 64 == 0, "whole waves");
     __shared__ float va[kCommitGroup][DK], vk[kCommitGroup][DK];
-    __shared__ float nrm[kCommitGroup];
+    __shared__ float red_k2[kCommitGroup][RG];         // prologue: sums of k^2
+    const bool qk = kPro && (pro & kProQK);
 
     const int64_t unit = blockIdx.x;
     const int64_t n = unit / H;
@@ -374,30 +376,31 @@ __global__ __launch_bounds__(256) void kda_commit_kernel(
                 ut[tt] = *reinterpret_cast<const f32x4 *>(u + (row0 + (int64_t)tt * H) * DV +
                                                           4 * cg);
         __syncthreads();
-        if (kPro && (pro & kProQK)) {
-            const int l = tid & 63;
-            for (int tt = tid >> 6; tt < nt; tt += NT / 64) {
-                float sk = 0.f;
-                for (int i = l; i < DK; i += 64)
-                    sk += vk[tt][i] * vk[tt][i];
+        if (qk) {
+            // the decode step's partial sums of k^2, one per row group
+            if (cg == 0) {
 #pragma unroll
-                for (int o = 32; o >= 1; o >>= 1)
-                    sk += __shfl_xor(sk, o);
-                if (l == 0)
-                    nrm[tt] = __builtin_amdgcn_rsqf(sk + kNormEps);
+                for (int tt = 0; tt < kCommitGroup; ++tt) {
+                    if (tt < nt) {
+                        float k2 = 0.f;
+#pragma unroll
+                        for (int m = 0; m < RPT; ++m)
+                            k2 = sq_acc(vk[tt][rg + RG * m], k2);
+                        red_k2[tt][rg] = k2;
+                    }
+                }
             }
-            __syncthreads();
-            for (int i = tid; i < nt * DK; i += NT)
-                vk[i / DK][i % DK] *= nrm[i / DK];
             __syncthreads();
         }
 #pragma unroll
         for (int tt = 0; tt < kCommitGroup; ++tt) {
             if (tt < nt) {
+                const float ik = qk ? inv_norm<RG>(red_k2[tt]) : 1.f;
 #pragma unroll
                 for (int m = 0; m < RPT; ++m) {
                     const int r = rg + RG * m;
-                    s_reg[m] = write_row(decay_row(s_reg[m], va[tt][r]), vk[tt][r], ut[tt]);
+                    const float kr = qk ? __fmul_rn(vk[tt][r], ik) : vk[tt][r];
+                    s_reg[m] = write_row(decay_row(s_reg[m], va[tt][r]), kr, ut[tt]);
                 }
             }
         }
