@@ -142,11 +142,12 @@ size_t kda_chunk_fwd_records_bytes(int B, int T, int N, int H, int dk, int dv, i
  * Overlapping calls that share a workspace race; out must not alias any input.
  *
  * Long single sequences (KDA_BF16, cu_seqlens NULL, B = 1, at least 65,536
- * tokens, final_state not NULL, no snapshots): the serial part runs in
- * segments of at least 32,768 tokens on the auxiliary stream, each segment
- * starting from the fp32 state the previous one left in final_state, while
- * `stream` computes each finished segment's outputs.  The result is bitwise
- * that of one unsegmented pass; final_state is written during the call.
+ * tokens, final_state not NULL, no snapshots): the call runs in segments of
+ * at least 32,768 tokens.  The serial part of each segment runs on the
+ * auxiliary stream, starting from the fp32 state the previous segment left
+ * in final_state, while `stream` prepares the next segment (when H <= 32) and
+ * computes the outputs of finished ones.  The result is bitwise that of one
+ * unsegmented pass; final_state is written during the call.
  * When `stream` is capturing a graph (hipStreamIsCapturing), every kernel
  * stays on `stream` instead, with the same result.
  */

@@ -50,6 +50,7 @@
 #include "kda_internal.h"
 
 #include <mutex>
+#include <numeric>
 
 namespace kda {
 
@@ -1248,9 +1249,13 @@ template <bool kPro, bool kPair> hipError_t prep_attr()
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PrepSmem));
 }
 
+// The persistent prep over n_slots * H tasks on one workgroup per CU (at most
+// max_grid workgroups when it is positive, rounded down to a multiple of 8 so
+// that task t still runs on XCD t % 8).
 hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                        const bf16 *beta, const int32_t *cu, int N, int T, int H, int64_t n_slots,
-                       float scale, unsigned pro, uint8_t *ws, hipStream_t stream, bool pair)
+                       float scale, unsigned pro, uint8_t *ws, hipStream_t stream, bool pair,
+                       int max_grid = 0)
 {
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
@@ -1270,7 +1275,9 @@ hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *
         e0 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e0 != hipSuccess)
         return e0;
-    const int64_t prep_grid = cus >= 8 ? cus / 8 * 8 : 8;
+    int64_t prep_grid = cus >= 8 ? cus / 8 * 8 : 8;
+    if (max_grid >= 8 && max_grid < prep_grid)
+        prep_grid = max_grid / 8 * 8;
     const int64_t n_tasks = n_slots * H;
     const dim3 grid((unsigned)(n_tasks < prep_grid ? n_tasks : prep_grid));
     const size_t lds = sizeof(PrepSmem);
@@ -1388,6 +1395,15 @@ hipError_t launch_chain(const float *init, float *final_state, float *snaps, int
                                         stream, own_cu);
 }
 
+// The chain of one sequence (T tokens, H heads) on workgroups of 4 value
+// blocks that keep their CUs to themselves, for the pipelined long schedule.
+hipError_t launch_chain_own4(const float *init, float *final_state, int T, int H, uint8_t *ws,
+                             hipStream_t stream, bool pair)
+{
+    return pair ? launch_chain_nb<4, true>(init, final_state, nullptr, 1, T, H, ws, stream, true)
+                : launch_chain_nb<4, false>(init, final_state, nullptr, 1, T, H, ws, stream, true);
+}
+
 // Two chains over per-chunk records of the same sequences in one launch: over
 // ws_a from init_a (no final state) and over ws_b from init_b, its final state
 // to final_b.  The workgroups per unit follow the rule above for the
@@ -1450,7 +1466,8 @@ struct AuxStream {
     bool ready = false;
     hipStream_t stream = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
-    hipEvent_t seg[kMaxSegments] = {};
+    hipEvent_t seg[kMaxSegments] = {};    // a segment's chain is done (second stream)
+    hipEvent_t pseg[kMaxSegments] = {};   // a segment's prep is done (caller's stream)
 };
 std::mutex g_aux_mutex;
 AuxStream g_aux[kMaxDevices];
@@ -1470,15 +1487,19 @@ hipError_t aux_stream(AuxStream *&out)
             e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming);
         if (e == hipSuccess)
             e = hipEventCreateWithFlags(&a.join, hipEventDisableTiming);
-        for (int i = 0; i < kMaxSegments && e == hipSuccess; ++i)
+        for (int i = 0; i < kMaxSegments && e == hipSuccess; ++i) {
             e = hipEventCreateWithFlags(&a.seg[i], hipEventDisableTiming);
+            if (e == hipSuccess)
+                e = hipEventCreateWithFlags(&a.pseg[i], hipEventDisableTiming);
+        }
         if (e != hipSuccess) {
             // release what was created, so that a later call starts afresh
-            for (hipEvent_t &ev : a.seg)
-                if (ev) {
-                    (void)hipEventDestroy(ev);
-                    ev = nullptr;
-                }
+            for (hipEvent_t *set : {a.seg, a.pseg})
+                for (int i = 0; i < kMaxSegments; ++i)
+                    if (set[i]) {
+                        (void)hipEventDestroy(set[i]);
+                        set[i] = nullptr;
+                    }
             for (hipEvent_t *ev : {&a.fork, &a.join})
                 if (*ev) {
                     (void)hipEventDestroy(*ev);
@@ -1520,49 +1541,109 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     const int64_t step = pair ? kPairTokens : kChunk;                 // tokens per slot
     const int64_t rec_bytes = pair ? (int64_t)kPairRecBytes : (int64_t)kRecBytes;
-    hipError_t e =
-        launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, pro, ws, stream, pair);
-    if (e != hipSuccess)
-        return e;
     // segments need one sequence without cu_seqlens, no snapshots and a final
     // state buffer to hand the state over in; a stream that is being captured
     // into a graph keeps the single-stream schedule, so that no work of the
     // shared auxiliary stream is pulled into the capture
     const bool segmented = allow_aux && !cu && N == 1 && !snaps && final_state &&
                            n_slots * step >= kMinSegmentedTokens && !stream_capturing(stream);
+    hipError_t e = hipSuccess;
     if (!segmented) {
-        e = launch_chain(init, final_state, snaps, snap_interval, cu, N, T, H, ws, stream, pair);
+        e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, pro, ws, stream, pair);
+        if (e == hipSuccess)
+            e = launch_chain(init, final_state, snaps, snap_interval, cu, N, T, H, ws, stream,
+                             pair);
         if (e == hipSuccess)
             e = launch_output(gate, out, cu, N, T, H, n_slots, ws, stream, pair);
         return e;
     }
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    // Pipelined when the chain's 4-block workgroups (one CU each) need at most a
+    // quarter of the device: prep runs segment by segment on the other CUs, and
+    // each segment's chain follows its prep on the second stream while prep
+    // goes on with the next segment.  A segment then holds whole rounds of prep
+    // tasks (a multiple of prep_grid / gcd(prep_grid, H) slots).
+    const int64_t chain_cus = chain_workgroups(H, 4);
+    const bool pipelined = chain_cus * 4 <= cus;
+    const int prep_grid = pipelined ? (int)((cus - chain_cus) / 8 * 8) : 0;
     int64_t seg = (n_slots + kMaxSegments - 1) / kMaxSegments;       // slots per segment
     seg = seg * step < kSegTokens ? kSegTokens / step : seg;
-    const int64_t nseg = (n_slots + seg - 1) / seg;
+    if (pipelined) {
+        const int64_t quantum = prep_grid / std::gcd((int64_t)prep_grid, (int64_t)H);
+        seg = (seg + quantum - 1) / quantum * quantum;
+    }
+    const int64_t nseg = (n_slots + seg - 1) / seg;                   // at most kMaxSegments
+    struct Seg {
+        int64_t slot0, ns, tok0;
+        int Ts;
+        uint8_t *ws;
+    };
+    auto seg_at = [&](int64_t s) {
+        Seg r;
+        r.slot0 = s * seg;
+        r.ns = n_slots - r.slot0 < seg ? n_slots - r.slot0 : seg;
+        r.tok0 = r.slot0 * step;
+        r.Ts = (int)(T - r.tok0 < r.ns * step ? T - r.tok0 : r.ns * step);
+        r.ws = ws + r.slot0 * H * rec_bytes;
+        return r;
+    };
     std::lock_guard<std::mutex> lock(g_aux_mutex);
     AuxStream *aux = nullptr;
     e = aux_stream(aux);
     if (e != hipSuccess)
         return e;
-    e = hipEventRecord(aux->fork, stream);
-    if (e != hipSuccess)
-        return e;
-    e = hipStreamWaitEvent(aux->stream, aux->fork, 0);
-    for (int64_t s = 0; s < nseg && e == hipSuccess; ++s) {
-        const int64_t slot0 = s * seg;
-        const int64_t ns = n_slots - slot0 < seg ? n_slots - slot0 : seg;
-        const int64_t tok0 = slot0 * step;
-        const int Ts = (int)(T - tok0 < ns * step ? T - tok0 : ns * step);
-        uint8_t *wss = ws + slot0 * H * rec_bytes;
-        e = launch_chain(s == 0 ? init : final_state, final_state, nullptr, 0, nullptr, 1, Ts, H,
-                         wss, aux->stream, pair, true);
+    if (pipelined) {
+        // caller's stream: prep 0, prep 1, output 0, prep 2, output 1, ...; second
+        // stream: chain s once prep s is done.  Output s - 1 waits for chain s - 1,
+        // which ran beside prep s.
+        for (int64_t s = 0; s <= nseg && e == hipSuccess; ++s) {
+            if (s < nseg) {
+                const Seg c = seg_at(s);
+                const int64_t t0 = c.tok0 * H;
+                e = launch_prep(q + t0 * kDK, k + t0 * kDK, v + t0 * kDV, g + t0 * kDK, beta + t0,
+                                nullptr, 1, c.Ts, H, c.ns, scale, pro, c.ws, stream, pair,
+                                prep_grid);
+                if (e == hipSuccess)
+                    e = hipEventRecord(aux->pseg[s], stream);
+                if (e == hipSuccess)
+                    e = hipStreamWaitEvent(aux->stream, aux->pseg[s], 0);
+                if (e == hipSuccess)
+                    e = launch_chain_own4(s == 0 ? init : final_state, final_state, c.Ts, H, c.ws,
+                                          aux->stream, pair);
+                if (e == hipSuccess)
+                    e = hipEventRecord(aux->seg[s], aux->stream);
+            }
+            if (s >= 1 && e == hipSuccess) {
+                const Seg c = seg_at(s - 1);
+                e = hipStreamWaitEvent(stream, aux->seg[s - 1], 0);
+                if (e == hipSuccess)
+                    e = launch_output(gate + c.tok0 * H * kDV, out + c.tok0 * H * kDV, nullptr, 1,
+                                      c.Ts, H, c.ns, c.ws, stream, pair);
+            }
+        }
+    } else {
+        e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, pro, ws, stream, pair);
         if (e == hipSuccess)
-            e = hipEventRecord(aux->seg[s], aux->stream);
+            e = hipEventRecord(aux->fork, stream);
         if (e == hipSuccess)
-            e = hipStreamWaitEvent(stream, aux->seg[s], 0);
-        if (e == hipSuccess)
-            e = launch_output(gate + tok0 * H * kDV, out + tok0 * H * kDV, nullptr, 1, Ts, H, ns,
-                              wss, stream, pair);
+            e = hipStreamWaitEvent(aux->stream, aux->fork, 0);
+        for (int64_t s = 0; s < nseg && e == hipSuccess; ++s) {
+            const Seg c = seg_at(s);
+            e = launch_chain(s == 0 ? init : final_state, final_state, nullptr, 0, nullptr, 1,
+                             c.Ts, H, c.ws, aux->stream, pair, true);
+            if (e == hipSuccess)
+                e = hipEventRecord(aux->seg[s], aux->stream);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(stream, aux->seg[s], 0);
+            if (e == hipSuccess)
+                e = launch_output(gate + c.tok0 * H * kDV, out + c.tok0 * H * kDV, nullptr, 1,
+                                  c.Ts, H, c.ns, c.ws, stream, pair);
+        }
     }
     if (e != hipSuccess) {
         // after a failure part way, still order the caller's stream after
