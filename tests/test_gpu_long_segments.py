@@ -1,11 +1,17 @@
-"""GPU: a long single sequence, whose chain runs in segments on a second stream.
+"""GPU: a long single sequence, which runs in segments on two streams.
 
 From 1,024 chunks on, ``kda_chunk_fwd`` over one sequence (no cu_seqlens, no
-snapshots, a final state wanted) runs the chain in segments of at least 512
-chunks on a second stream, handing the fp32 state from segment to segment,
-while the caller's stream runs each segment's output kernel.  The state passes
-through memory unchanged, so the result must be bitwise that of calls too
-short to be segmented, chained by hand; and it must match the oracle.
+snapshots, a final state wanted) runs in segments of at least 512 chunks,
+handing the fp32 state from segment to segment.  Up to 32 heads it is
+pipelined: the caller's stream prepares segment by segment and runs finished
+segments' outputs, and a second stream runs each segment's chain (on
+workgroups of four value blocks) beside the next preparation.  With more
+heads the whole preparation runs first and each segment's chain (one value
+block per workgroup) on the second stream, the outputs beside it.  The state
+passes through memory unchanged, so either way the result must be bitwise
+that of calls too short to be segmented, chained by hand, or of the same
+sequence given through cu_seqlens (which keeps one stream); and it must match
+the oracle.
 """
 from __future__ import annotations
 
@@ -130,3 +136,31 @@ def test_long_forward_captured_in_a_graph(dev):
         torch.cuda.synchronize()
     ro, rf = run_oracle(x)
     check(out, fin, ro, rf, 2e-2, 1e-2, f"graph-captured long forward T={T}")
+
+
+LONG_CASES = {
+    # name: (H, prologue bits, per-chunk records)
+    "pipelined_with_prologue": (2, kda.PRO_QK_L2NORM | kda.PRO_BETA_SIGMOID | kda.PRO_G_SOFTPLUS,
+                                False),
+    "pipelined_per_chunk_records": (2, 0, True),
+    "prep_first_40_heads": (40, 0, False),     # the chain would need more than a quarter of the CUs
+}
+
+
+@pytest.mark.parametrize("case", list(LONG_CASES))
+def test_segmented_schedules_equal_one_stream(dev, case):
+    """Each segmented schedule against the same sequence given through
+    cu_seqlens = [0, T], which keeps every kernel on one stream: bitwise."""
+    H, pro, per_chunk = LONG_CASES[case]
+    T = 66_000
+    say(f"{case}: B=1 H={H} T={T} prologue={pro} chunk_records={per_chunk}")
+    xd = to(small_inputs(torch.bfloat16, 1, T, H, 128, 128, 79, init_std=0.02), dev)
+    args = [xd[k] for k in KEYS]
+    out, fin = kda.chunk_fwd(*args, init_state=xd["init_state"], prologue=pro,
+                             chunk_records=per_chunk)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    ro, rf = kda.chunk_fwd(*args, init_state=xd["init_state"], cu_seqlens=cu, prologue=pro,
+                           chunk_records=per_chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ro), f"{case}: outputs differ from the one-stream call"
+    assert torch.equal(fin, rf), f"{case}: final state differs from the one-stream call"
