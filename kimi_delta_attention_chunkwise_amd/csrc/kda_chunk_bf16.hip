@@ -376,8 +376,16 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
         prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 0);
 
     // ---- phase 2: 16 x 16 blocks of A and P (bf16 MFMA, fp32 accumulate) -------
-    for (int blk = wave; blk < 10; blk += kPrepThreads / 64) {
+    // ten blocks on eight waves: the two waves that take two blocks take
+    // diagonal ones (no cross-subtile factor to apply), and each of the six
+    // off-diagonal blocks has a wave of its own
+    static_assert(kPrepThreads == 512, "the block assignment is for eight waves");
+    for (int nb = 0; nb < (wave < 2 ? 2 : 1); ++nb) {
         // blk -> (i, jb): 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) ...
+        // wave 0: blocks 0, 9; wave 1: 2, 5; waves 2..7: 1, 3, 4, 6, 7, 8
+        const int blk = wave == 0 ? 9 * nb
+                      : wave == 1 ? 2 + 3 * nb
+                      : wave == 2 ? 1 : wave < 5 ? wave : wave + 1;
         const int i = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
         const int jb = blk - (i * (i + 1)) / 2;
         f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
