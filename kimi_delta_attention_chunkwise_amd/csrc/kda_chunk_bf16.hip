@@ -1469,6 +1469,12 @@ hipError_t launch_output(const bf16 *gate, bf16 *out, const int32_t *cu, int N, 
 constexpr int64_t kSegTokens = 512 * kChunk;
 constexpr int64_t kMinSegmentedTokens = 2 * kSegTokens;
 constexpr int kMaxSegments = 32;
+// segments of the pipelined schedule: fewer and longer than the chain's alone,
+// since each also ends a prep launch, but not so few that the last segment's
+// chain and output, which run after all prep, take long (measured on 1M tokens
+// x 16 heads, ms per call: 6 segments 19.0, 9 18.5-18.8, 11 18.4-18.6, 16
+// 18.2-18.5, 31 18.5-18.9, 59 19.2-19.7)
+constexpr int kPipeSegments = 16;
 
 struct AuxStream {
     bool ready = false;
@@ -1583,6 +1589,8 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
     seg = seg * step < kSegTokens ? kSegTokens / step : seg;
     if (pipelined) {
         const int64_t quantum = prep_grid / std::gcd((int64_t)prep_grid, (int64_t)H);
+        seg = (n_slots + kPipeSegments - 1) / kPipeSegments;
+        seg = seg * step < kSegTokens ? kSegTokens / step : seg;
         seg = (seg + quantum - 1) / quantum * quantum;
     }
     const int64_t nseg = (n_slots + seg - 1) / seg;                   // at most kMaxSegments
