@@ -155,7 +155,7 @@ size_t kda_chunk_fwd_records_bytes(int B, int T, int N, int H, int dk, int dv, i
         return (size_t)-1;
     if (dt == KDA_F32)
         return 0;
-    return (size_t)chunk_slots(B, T, N, chunk, varlen) * (size_t)H * kda::kRecBytes;
+    return (size_t)chunk_slots(B, T, N, chunk, varlen) * (size_t)H * kda::kChunkRecBytes;
 }
 
 size_t kda_snapshot_slots(int B, int T, int N, int chunk, int interval, int varlen)
@@ -382,7 +382,7 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
     const size_t units = (size_t)chunk_slots(B, T, N, chunk, varlen) * (size_t)H;
     if (dt == KDA_F32)   // one fp32 dk x dv entry state per (chunk slot, head)
         return units * (size_t)dk * (size_t)dv * sizeof(float);
-    return 2 * units * kda::kRecBytes;   // forward and backward records
+    return 2 * units * kda::kChunkRecBytes;   // forward and backward records
 }
 
 kda_status kda_chunk_bwd_ex(const void *q, const void *k, const void *v, const void *g,

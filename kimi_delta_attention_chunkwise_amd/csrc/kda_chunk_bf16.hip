@@ -110,26 +110,6 @@ __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4 &a, float s)
 }
 
 
-// DPP lane move (as int bits) with every lane active; lanes whose source is
-// out of range (bound_ctrl) or whose row is masked off read 0
-template <int kCtrl, int kRowMask, bool kBound>
-__device__ __forceinline__ float dpp_add_src(float x)
-{
-    return __int_as_float(
-        __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xf, kBound));
-}
-
-// inclusive prefix sum over each 16-lane row of a wave (row_shr 1, 2, 4, 8;
-// lanes whose source falls outside the row add 0)
-__device__ __forceinline__ float row_inclusive_sum(float x)
-{
-    x += dpp_add_src<0x111, 0xf, true>(x);
-    x += dpp_add_src<0x112, 0xf, true>(x);
-    x += dpp_add_src<0x114, 0xf, true>(x);
-    x += dpp_add_src<0x118, 0xf, true>(x);
-    return x;
-}
-
 }  // namespace
 
 // Inputs of one prep task held in registers: lane (tg, cq) of wave w has
@@ -207,12 +187,14 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const bf16 *q, const bf16 
 //      decay in LDS, for chunk 1;
 //   2  chunk 1 of a pair: the composed map (LN = -L01, BM = Bm01, DEC = dec01)
 //      and its readout from the pair's entry state (QH1, O01).
+// kExt (mode 0 in a per-chunk record, never in a pair record): also the
+// record's extension XW, XU, XT, XP for the gradient kernel.
 struct PairHold {
     bf16x8 nl0[4];                   // -L0, column block of the wave, 4 k-steps of rows
     bf16x8 bm0[4];                   // Bm0, the same layout
 };
 
-template <bool kPro, int kMode>
+template <bool kPro, int kMode, bool kExt = false>
 __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, const bf16 *q,
                                            const bf16 *k, const bf16 *v, const bf16 *g,
                                            const bf16 *beta, const PrepTask &pt,
@@ -220,6 +202,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
                                            float scale, unsigned pro, uint8_t *rec,
                                            PairHold &hold)
 {
+    static_assert(!kExt || kMode == 0, "the extension belongs to per-chunk records");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, b = lane >> 4;
@@ -512,6 +495,25 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
                     accU[mt] = mfma16(tf[mt][ks], vf[ks], accU[mt]);
                 }
         }
+        if constexpr (kExt) {
+            // per-chunk records also keep W and U~ as row fragments for the
+            // gradient kernel: the transposed products X^T T^T = W^T and
+            // V^T T^T = U~^T leave the wave's 16 channels of one token row as
+            // four consecutive k of the row's fragment (half of a 16-byte slot)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 wt = {0.f, 0.f, 0.f, 0.f}, ut = wt;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    if (ks <= (mt >> 1)) {
+                        wt = mfma16(xf[ks], tf[mt][ks], wt);
+                        ut = mfma16(vf[ks], tf[mt][ks], ut);
+                    }
+                const size_t off = (mt * 4 + (nt >> 1)) * kFragBytes + lane * 16 + (nt & 1) * 8;
+                *reinterpret_cast<bf16x4 *>(rec + kOffXW + off) = to_bf16x4(wt, 1.f);
+                *reinterpret_cast<bf16x4 *>(rec + kOffXU + off) = to_bf16x4(ut, 1.f);
+            }
+        }
     }
 
     if (load_next)
@@ -594,6 +596,20 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
                 *reinterpret_cast<bf16x8 *>(rec + kOffO0 + nt * 2048 + tp * 1024 + lane * 16) =
                     bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             }
+        }
+        if constexpr (kExt) {
+            // T^T and P^T, eight elements of one row per thread (T below its
+            // diagonal blocks only: the tiles above them are not all written)
+            const int r = tid >> 3, s0 = 8 * (tid & 7);
+            bf16x8 tt, pt8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int s = s0 + e;
+                tt[e] = (bf16)(s >= r ? ts.TM[s][r] : 0.f);
+                pt8[e] = sm.PM[s][r];
+            }
+            *reinterpret_cast<bf16x8 *>(rec + kOffXT + (size_t)(r * kChunk + s0) * 2) = tt;
+            *reinterpret_cast<bf16x8 *>(rec + kOffXP + (size_t)(r * kChunk + s0) * 2) = pt8;
         }
         if constexpr (kMode == 1) {
             // -L0 and Bm0 with rows on the k index: L0 block (mt, nt) as K'^T W with
@@ -798,8 +814,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                     prep_load(in, q, k, v, g, beta, next, H, wave, tg, cq);
                 continue;
             }
-            prep_chunk<kPro, 0>(sm, ts, in, q, k, v, g, beta, pt, next, load_next, H, scale, pro,
-                                ws + pt.rec * (int64_t)kRecBytes, hold);
+            prep_chunk<kPro, 0, true>(sm, ts, in, q, k, v, g, beta, pt, next, load_next, H, scale,
+                                      pro, ws + pt.rec * (int64_t)kChunkRecBytes, hold);
         }
     } else {
         PrepTask c0, c1;
@@ -912,7 +928,7 @@ __global__ __launch_bounds__(chain_threads<kNB>()) void kda_chain_bf16_kernel(
     uint8_t *__restrict__ ws, ChainJob2 job2)
 {
     constexpr int kStep = kPair ? kPairTokens : kChunk;           // tokens per step
-    constexpr size_t kRec = kPair ? kPairRecBytes : kRecBytes;    // record stride
+    constexpr size_t kRec = kPair ? kPairRecBytes : kChunkRecBytes;    // record stride
     static_assert(kNB == 1 || kNB == 2 || kNB == 4, "1, 2 or 4 value blocks per workgroup");
     static_assert(!kSnap || kNB == 1, "snapshots with one value block per workgroup");
     constexpr int kSideBlocks = kNB == 1 ? 1 : 2;   // value blocks per side wave
@@ -1149,7 +1165,7 @@ __global__ __launch_bounds__(kPair ? 512 : 256) void kda_output_bf16_kernel(
     constexpr int kWaves = kPair ? 8 : 4;
     constexpr int kThreads = 64 * kWaves;
     constexpr int kStep = kPair ? kPairTokens : kChunk;
-    constexpr size_t kRec = kPair ? kPairRecBytes : kRecBytes;
+    constexpr size_t kRec = kPair ? kPairRecBytes : kChunkRecBytes;
     __shared__ bf16x8 sb_s[kNumVBlocks * 4][64];
     __shared__ float ot_s[kWaves][kSub][kOutLd];
 
@@ -1554,7 +1570,7 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
 {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     const int64_t step = pair ? kPairTokens : kChunk;                 // tokens per slot
-    const int64_t rec_bytes = pair ? (int64_t)kPairRecBytes : (int64_t)kRecBytes;
+    const int64_t rec_bytes = pair ? (int64_t)kPairRecBytes : (int64_t)kChunkRecBytes;
     // segments need one sequence without cu_seqlens, no snapshots and a final
     // state buffer to hand the state over in; a stream that is being captured
     // into a graph keeps the single-stream schedule, so that no work of the
@@ -1683,7 +1699,7 @@ hipError_t launch_chunk_bwd_bf16(const bf16 *q, const bf16 *k, const bf16 *v, co
                                  float scale, void *fwd_records, void *workspace,
                                  hipStream_t stream)
 {
-    const size_t rec_bytes = (size_t)n_slots * (size_t)H * kRecBytes;
+    const size_t rec_bytes = (size_t)n_slots * (size_t)H * kChunkRecBytes;
     uint8_t *ws_f = fwd_records ? static_cast<uint8_t *>(fwd_records)
                                 : static_cast<uint8_t *>(workspace);
     uint8_t *ws_b = fwd_records ? static_cast<uint8_t *>(workspace)

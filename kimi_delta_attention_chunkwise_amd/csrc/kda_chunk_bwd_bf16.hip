@@ -15,30 +15,38 @@
 //      reverse chunk order, so that
 //   3. the unchanged chain kernel, started from dS_final, yields dS_{j+1} for
 //      every chunk (record SB) and dS_0;
-//   4. gradient kernel (here): one workgroup per (chunk, head) recomputes the
-//      chunk subtile by subtile (16 tokens, so every decay factor stays within
-//      exp(+-40) around the subtile midpoint and fp32 / bf16 never overflow):
-//      a forward sweep gives the states on entry to subtiles 1..3, a backward
-//      sweep from dS_{j+1} gives the gradients of the chunk's tokens.
+//   4. gradient kernel (here): one workgroup per (chunk, head) computes the
+//      chunk's gradients at chunk level from the forward record (Q^, O0, the
+//      entry state S and the per-chunk extension W, U~, T^T, P^T written by
+//      the prep) and dS' = dS_{j+1}; no pass over the chunk is serial.
 //
-// Algebra of one 16-token subtile with entry state S (r, s its rows; G the
-// cumulative log-decay from the subtile start including the row; Ge = G of
-// row 15; B = G of row 7):
-//   Qs = scale Q e^G, Ks = K e^G, Kp = K e^{Ge-G}, Qr = scale Q e^{G-B},
-//   Kr = K e^{G-B}, Kc = K e^{B-G};  M = Kr Kc^T, A = strict_lower(diag(beta) M),
-//   P = lower_incl(Qr Kc^T), T = (I + A)^-1, W = T diag(beta) Ks,
-//   U~ = T diag(beta) V, U = U~ - W S, O = Qs S + P U, S' = diag(e^Ge) S + Kp^T U.
-// Backward, given dS' and dO:
-//   dU = Kp dS' + P^T dO,  dS = diag(e^Ge) dS' + Qs^T dO - W^T dU,
-//   dKp = U dS'^T, dQs = dO S^T, dW = -dU S^T, dP = lower_incl(dO U^T),
-//   dT = dW (diag(beta) Ks)^T + dU (diag(beta) V)^T, dA = strict_lower(-T^T dT T^T),
-//   dKs = diag(beta) T^T dW, dV = diag(beta) T^T dU, dKr = diag(beta) dA Kc,
-//   dKc = dA^T diag(beta) Kr + dP^T Qr, dQr = dP Kc,
-//   dbeta = rowsum((T^T dW) Ks + (T^T dU) V + dA M),
+// Algebra of one 64-token chunk with entry state S (r, s its rows; G the
+// cumulative log-decay from the chunk start including the row; Ge = G of the
+// last row; B_I = G before 16-token subtile I, B_0 = 0):
+//   Qs = scale Q e^G, Ks = K e^G, Kp = K e^{Ge-G};  M = strict_lower([k_r e^{G_r-G_s} k_s]),
+//   A = diag(beta) M, P = scale lower_incl([q_r e^{G_r-G_s} k_s]), T = (I + A)^-1,
+//   W = T diag(beta) Ks, U~ = T diag(beta) V, U = U~ - W S, O = Q^ S + O0 = Qs S + P U,
+//   S' = diag(e^Ge) S + Kp^T U.
+// Backward, given dS' and dO = dY sigmoid(Z):
+//   dU = Kp dS' + P^T dO,  dKp = U dS'^T, dQs = dO S^T, dW = -dU S^T,
+//   dP = lower_incl(dO U^T),  dX = T^T dW, dY~ = T^T dU,
+//   dA = -T^T dT T^T = strict_lower(-dX W^T - dY~ U~^T)
+//        (dT = dW (diag(beta) Ks)^T + dU (diag(beta) V)^T and T X = W, T Y = U~),
+//   dKs = diag(beta) dX, dV = diag(beta) dY~, dbeta = rowsum(dX Ks + dY~ V + dA M).
+// The products with the 16 x 16 blocks of A and P carry the decay with
+// references at subtile starts: with Kr_I = K_I e^{G - B_I}, Qr_I = scale Q_I e^{G - B_I}
+// and Kc_J^(I) = K_J e^{B_I - G} for block (I, J), J <= I,
+//   Z_I = sum_J dA_IJ Kc_J^(I),  dKr_I = diag(beta) Z_I,  dQr_I = sum_J dP_IJ Kc_J^(I),
+//   dKc_J = sum_{I >= J} (diag(beta) dA_IJ)^T Kr_I^(J) + dP_IJ^T Qr_I^(J)
+//   (row factors K_I e^{G - B_J}, scale Q_I e^{G - B_J}: references B_J), and
+//   dM's rowsum term of dbeta is rowsum(Kr Z);
 //   dQ = scale (e^G dQs + e^{G-B} dQr), dK = e^G dKs + e^{G-B} dKr + e^{B-G} dKc + e^{Ge-G} dKp,
 //   dG = dQs Qs + dQr Qr + dKs Ks + dKr Kr - dKc Kc - dKp Kp,
 //   dGe = colsum(dKp Kp) + e^Ge rowsum(dS' S),  dg_u = sum_{r >= u} dG_r + dGe.
-// B cancels inside M and P, so it carries no gradient.
+// The references cancel inside M and P, so they carry no gradient.  Every
+// factor stays in range because g >= -5 and a subtile is 16 tokens: e^{G - B}
+// lies in [e^-80, 1] on its own subtile, e^{B - G} in [1, e^80], and every
+// factor between different subtiles is at most 1.
 #include "kda_internal.h"
 
 #include <mutex>
@@ -76,8 +84,8 @@ __global__ __launch_bounds__(kBpThreads) void kda_bwd_prep_bf16_kernel(
     const int64_t nch = (si.len + kChunk - 1) / kChunk;
     const int64_t tok0 = si.bos + j * kChunk;
     const int len = (int)((si.len - j * kChunk) < kChunk ? (si.len - j * kChunk) : kChunk);
-    const uint8_t *rf = ws_f + (slot * H + h) * (int64_t)kRecBytes;
-    uint8_t *rb = ws_b + ((si.slot0 + nch - 1 - j) * H + h) * (int64_t)kRecBytes;
+    const uint8_t *rf = ws_f + (slot * H + h) * (int64_t)kChunkRecBytes;
+    uint8_t *rb = ws_b + ((si.slot0 + nch - 1 - j) * H + h) * (int64_t)kChunkRecBytes;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int m = lane & 15, b = lane >> 4;
 
@@ -162,12 +170,9 @@ __global__ __launch_bounds__(kBpThreads) void kda_bwd_prep_bf16_kernel(
 // ------------------------------------------------------------ gradient kernel
 constexpr int kGThreads = 512;
 constexpr int kGWaves = kGThreads / 64;
-constexpr int kRL = kDK + 8;     // bf16 row stride of [16][128] and [128][128] tiles
-constexpr int kFL = kDK + 4;     // fp32 row stride of [16][128] tiles
-constexpr int kTL = kSub + 8;    // bf16 row stride of transposed [128][16] tiles
-constexpr int kSL = kSub + 1;    // fp32 row stride of 16 x 16 matrices
-
-typedef float Sq[kSub][kSL];
+constexpr int kXL = kDK + 8;     // bf16 row stride of [64][128] and [128][128] tiles
+constexpr int kTL = kChunk + 8;  // bf16 row stride of [64][64] tiles
+constexpr int kAL = kChunk + 4;  // fp32 row stride of [64][64] tiles
 
 // Lane kS of the caller's 16-lane row, to every lane of that row (DPP
 // row_newbcast: a VALU move, no LDS traffic).
@@ -177,92 +182,6 @@ __device__ __forceinline__ float row_bcast(float x)
     return __int_as_float(
         __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + kS, 0xf, 0xf, false));
 }
-
-// Step kS of the in-wave forward substitution for T = (I + A)^-1 in column
-// form: lane (b, m) owns T[4 b + i2][m] and A[4 b + i2][m]; once row kS of T is
-// final it updates every later row.  Row kS of T comes from row group kS / 4
-// by a lane shuffle, A[4 b + i2][kS] from lane kS of the lane's own row.
-template <int kS>
-__device__ __forceinline__ void tsolve_step(f32x4 &t, const f32x4 &a, int b, int m)
-{
-    const float ts = __shfl(t[kS & 3], m + 16 * (kS >> 2));
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-        const float ars = row_bcast<kS>(a[i2]);
-        if (4 * b + i2 > kS)
-            t[i2] -= ars * ts;
-    }
-}
-
-template <int... kS>
-__device__ __forceinline__ void tsolve(f32x4 &t, const f32x4 &a, int b, int m,
-                                       std::integer_sequence<int, kS...>)
-{
-    (tsolve_step<kS>(t, a, b, m), ...);
-}
-
-// Column of element [x][r] of a transposed [128][16] tile: the four groups of
-// four tokens of a row are XOR-permuted by bits 3..4 of the channel x.  A
-// group stays contiguous for the 8-byte MFMA operand reads, while the
-// transposed 2-byte writes of 32 consecutive-by-4 channels spread over eight
-// banks instead of two.
-__device__ __forceinline__ int tcol(int x, int r)
-{
-    return 4 * ((r >> 2) ^ ((x >> 3) & 3)) + (r & 3);
-}
-
-struct GradSmem {
-    // small and often-read arrays first, so that their addresses fit the
-    // 16-bit offsets of LDS instructions
-    Sq M, Tm, P, dP, dTu, dA;
-    alignas(16) float Bref[kDK];
-    alignas(16) float Ge[kDK];
-    alignas(16) float dec[kDK];
-    alignas(16) float dGeD[kDK];        // e^Ge rowsum(dS' S)
-    alignas(16) float beta[kSub];
-    alignas(16) float dbp[kGWaves][kSub];   // per-wave partial sums of dbeta
-    alignas(16) bf16 dbst[kSub];        // dbeta of the subtile, staged for its store
-    alignas(16) float G[kSub][kFL];     // cumulative log-decay within the subtile
-    alignas(16) bf16 Kin[kSub][kRL];    // k and q as given (bf16, exact); the pair factors
-    alignas(16) bf16 Qin[kSub][kRL];    // of the 16-token contractions are formed from them
-    alignas(16) bf16 Ks[kSub][kRL];
-    alignas(16) bf16 V[kSub][kRL];
-    alignas(16) bf16 U[kSub][kRL];
-    alignas(16) bf16 dO[kSub][kRL];
-    alignas(16) bf16 dU[kSub][kRL];
-    union {
-        struct {                         // operands of the state products
-            alignas(16) bf16 Qs[kSub][kRL];
-            alignas(16) bf16 Kp[kSub][kRL];
-            alignas(16) bf16 QsT[kDK][kTL];
-            alignas(16) bf16 KpT[kDK][kTL];
-            union {
-                struct {                 // bf16 operands of M and P
-                    alignas(16) bf16 Kr[kSub][kRL];
-                    alignas(16) bf16 Kc[kSub][kRL];
-                    alignas(16) bf16 Qr[kSub][kRL];
-                } mp;
-                struct {                 // written once T exists
-                    alignas(16) bf16 W[kSub][kRL];
-                    alignas(16) bf16 WT[kDK][kTL];
-                } w;
-            } x;
-        } a;
-        struct {
-            alignas(16) float dW[kSub][kFL];
-        } b;
-    } u;
-    union {
-        struct {
-            alignas(16) bf16 Sb[kDK][kRL];      // S on entry to the subtile, [dk][dv]
-            alignas(16) bf16 dSb[kDK][kRL];     // dS' on exit of the subtile, [dk][dv]
-        } s;
-        // once the sums over the value channels are done: the subtile's token
-        // gradients dq, dk, dv, dg, dz, staged for row-contiguous stores
-        alignas(16) bf16 out[5][kSub][kRL];
-    } v;
-};
-static_assert(sizeof(GradSmem) <= 160 * 1024, "gradient kernel LDS fits one CU");
 
 // D += A B with a 16-wide k: lane (b, m) gives A[m][4 b + e] and B[4 b + e][m]
 // (e = 0..3).  Issued as the 16x16x32 product with elements 4..7 of both
@@ -282,12 +201,11 @@ __device__ __forceinline__ bf16x4 bf4(const f32x4 &x)
     return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
 }
 
-// Zero, hidden from the optimizer (an empty asm statement that only claims to
-// modify the value; no instruction is emitted).  Adding it to the LDS base at
-// the top of every pass keeps the compiler from hoisting the several dozen
-// loop-invariant LDS addresses of a pass out of the pass loops, where they
-// would hold registers for the whole kernel and force spills; recomputing
-// them costs a few integer adds per pass.
+// Zero the optimizer cannot see through (an empty asm statement that claims
+// to modify it; no instruction).  The LDS base is re-derived from it at the
+// top of every phase: the kernel's LDS spans more than the 16-bit offset of
+// LDS instructions, and without it the compiler keeps dozens of per-lane LDS
+// addresses of later phases live from the first one, which forces spills.
 __device__ __forceinline__ uint32_t opaque_zero()
 {
     uint32_t z = 0;
@@ -295,39 +213,107 @@ __device__ __forceinline__ uint32_t opaque_zero()
     return z;
 }
 
-// Inputs of one subtile pass, loaded a pass ahead: row er, channels ec..ec+3
-// of k, g, v, q and beta of row er (elementwise mapping), and the gate logits
-// and dY of rows 4 b + i, channel col (the wave's mapping).
-// The 16-bit values are kept as raw bits, one per register, and converted
-// where used: packing or converting them right after the load would make the
-// compiler wait for every load in flight.
-struct GradIn {
-    bf16x4 k, g, v, q;
-    uint16_t beta;
-    uint16_t z[4], dy[4];
-};
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t x)
+// A 16 x 16 tile from the row layout to accumulator order (see the kernel),
+// exactly, as its product with the identity: lane (b, m) gives elements
+// (token m, channel 4 b + e) and receives (token 4 b + i, channel m).
+// The identity's position comes from an opaque copy of the lane index, so
+// that transposes in different phases are formed again where they are used
+// instead of being merged and held in registers in between.
+__device__ __forceinline__ bf16x4 acc_order(const bf16x4 &x, int b, int m)
 {
-    return __uint_as_float((uint32_t)x << 16);
+    int mm = m;
+    asm volatile("" : "+v"(mm));
+    bf16x4 id;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        id[e] = (bf16)(4 * b + e == mm ? 1.f : 0.f);
+    return bf4(mfma16k16(x, id, f32x4{0.f, 0.f, 0.f, 0.f}));
+}
+__device__ __forceinline__ f32x4 acc_order(const f32x4 &x, int b, int m)
+{
+    int mm = m;
+    asm volatile("" : "+v"(mm));
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        d = mfma4_f32(x[kk], 4 * b + kk == mm ? 1.f : 0.f, d);
+    return d;
 }
 
-// Layout of the per-wave tiles below: wave w owns key (or value) channels
-// 16 w .. 16 w + 15; lane (b, m) = (lane / 16, lane % 16) holds rows 4 b + i
-// (i = 0..3) of channel 16 w + m, the accumulator layout of the 16x16 MFMAs.
-// A chunk is worked in passes over its 16-token subtiles: forward passes
-// 0 .. nsub - 2 (states on entry to subtiles 1 .. nsub - 1), then backward
-// passes nsub - 1 .. 0.
+__device__ __forceinline__ f32x4 f4(const bf16x4 &x)
+{
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+// LDS of the gradient kernel, by phase (see the kernel): 151,296 bytes, one
+// workgroup per CU.
+struct GradSmem {
+    union {
+        struct {                          // phase 1: the record's Q^ and W fragments
+            bf16x8 QH[16][64];
+            bf16x8 W[16][64];
+        } f;
+        struct {                          // phase 2: S and dS' as [dk][dv] tiles
+            bf16 Sb[kDK][kXL];
+            bf16 dSb[kDK][kXL];
+        } s;
+        struct {                          // phases 3 to 5
+            bf16 DX[kChunk][kXL];         // T^T dW   [token][dk]
+            bf16 DY[kChunk][kXL];         // T^T dU   [token][dv]
+            float dA[kChunk][kAL];
+        } x;
+    } a;
+    bf16 DO[kChunk][kXL];                 // dO = dY sigmoid(Z)   [token][dv]
+    bf16 U[kChunk][kXL];                  // U = U~ - W S
+    bf16 DU[kChunk][kXL];                 // dU
+    union {
+        bf16 KP[kChunk][kXL];             // K' = K e^{Ge - G} (phase 1)
+        float dP[kChunk][kAL];            // phases 2 to 5
+    } p;
+    union {
+        bf16 PT[kChunk][kTL];             // P^T (phase 1)
+        bf16 TT[kChunk][kTL];             // T^T (phase 3)
+    } t;
+    alignas(16) float beta[kChunk];
+    alignas(16) float ref[4][kDK];        // G before subtiles 1, 2, 3 (B_1..B_3) and G_end
+    alignas(16) float dgeD[kDK];          // e^Ge rowsum(dS' S) per key channel
+    alignas(16) float dbp[kGWaves][kChunk];   // per-wave partial sums of dbeta
+};
+static_assert(sizeof(GradSmem) <= 160 * 1024, "gradient kernel LDS fits one CU");
+
+// G before tile t (B_t; B_0 = 0) of channels c .. c + 3
+__device__ __forceinline__ f32x4 ref4(const GradSmem &sm, int t, int c)
+{
+    return t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4 *>(&sm.ref[t - 1][c]);
+}
+
+// Block (I, J) of a 4 x 4 lower block triangle for wave w; waves 0 and 1 take
+// a second one (nb = 1): 0:(0,0) 9:(3,3) / 2:(1,1) 5:(2,2) / 1, 3, 4, 6, 7, 8.
+__device__ __forceinline__ void lower_block(int w, int nb, int &I, int &J)
+{
+    const int blk = w == 0 ? 9 * nb : w == 1 ? 2 + 3 * nb : w == 2 ? 1 : w < 5 ? w : w + 1;
+    I = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
+    J = blk - (I * (I + 1)) / 2;
+}
+
+// One workgroup of 8 waves per (chunk, head).  Two register layouts:
+//   row layout: element [t][i] of lane (b, m) is token 16 t + m, channel
+//     16 w + 4 b + i -- the accumulator of a product whose MFMA rows are the
+//     wave's 16 channels and whose columns are tokens; four consecutive
+//     channels of one token, so loads and stores of a row are 8 bytes;
+//   accumulator order: element [t][i] is token 16 t + 4 b + i, channel
+//     16 w + m -- the operand of a product over tokens (16-wide k).
+// Wave w owns value block w (phase 1, dY~) and key block w (phases 2, 3, 5).
 __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ g, const bf16 *__restrict__ beta, const bf16 *__restrict__ gate,
     const bf16 *__restrict__ dout, bf16 *__restrict__ dq, bf16 *__restrict__ dk,
     bf16 *__restrict__ dv, bf16 *__restrict__ dg, bf16 *__restrict__ dbeta,
     bf16 *__restrict__ dgate, const int32_t *__restrict__ cu, int N, int T, int H, float scale,
-    uint8_t *__restrict__ ws_f, const uint8_t *__restrict__ ws_b)
+    const uint8_t *__restrict__ ws_f, const uint8_t *__restrict__ ws_b)
 {
     extern __shared__ __align__(16) uint8_t smem_raw[];
-    // re-derived from an opaque zero at the top of every pass (see opaque_zero)
+    // re-derived from an opaque zero at the top of every phase (see opaque_zero)
     GradSmem *smp = reinterpret_cast<GradSmem *>(smem_raw);
     const int64_t slot = (int64_t)blockIdx.x / H;
     const int h = (int)((int64_t)blockIdx.x % H);
@@ -339,535 +325,464 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
     const int64_t nch = (si.len + kChunk - 1) / kChunk;
     const int64_t tok0 = si.bos + j * kChunk;
     const int len = (int)((si.len - j * kChunk) < kChunk ? (si.len - j * kChunk) : kChunk);
-    const int nsub = (len + kSub - 1) / kSub;
-    const int npass = 2 * nsub - 1;
-    uint8_t *rf = ws_f + (slot * H + h) * (int64_t)kRecBytes;
-    const uint8_t *rb = ws_b + ((si.slot0 + nch - 1 - j) * H + h) * (int64_t)kRecBytes;
+    // wave-uniform bases, per-lane 32-bit byte offsets
+    const gbyte *rf = uniform_gptr(ws_f + (slot * H + h) * (int64_t)kChunkRecBytes);
+    const gbyte *rb = uniform_gptr(ws_b + ((si.slot0 + nch - 1 - j) * H + h) * (int64_t)kChunkRecBytes);
+    const int64_t e0 = (tok0 * H + h) * (int64_t)kDK;   // (first token, head h, channel 0)
+    const gbyte *gq = uniform_gptr(q + e0), *gk = uniform_gptr(k + e0), *gv_ = uniform_gptr(v + e0);
+    const gbyte *gg = uniform_gptr(g + e0), *gz = uniform_gptr(gate + e0);
+    const gbyte *gy = uniform_gptr(dout + e0);
+    gbyte *oq = uniform_gptr(dq + e0), *ok_ = uniform_gptr(dk + e0), *ov = uniform_gptr(dv + e0);
+    gbyte *og_ = uniform_gptr(dg + e0), *oz = uniform_gptr(dgate + e0);
+    const uint32_t tstride = (uint32_t)H * kDK * 2;       // bytes from one token to the next
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, b = lane >> 4;
-    const int col = kVBlock * w + m;                          // the lane's channel
-    const int er = tid >> 5, ec = 4 * (tid & 31);            // elementwise: row, 4 channels
-
-    // The state on entry to subtile i as this wave's B fragments (perm order):
-    // subtile 0 from the forward record's SB; subtiles 1..nsub-2 are parked in
-    // the same record's first 96 KiB (LN, QH, BM, O0, no longer read once the
-    // backward records exist), 32 KiB per subtile, each lane reading back only
-    // the 16-byte slots it wrote.
-    static_assert(kOffDEC >= 3 * 32768, "three parked states fit before DEC");
-    auto sfrag_ptr = [&](int i, int ks) -> uint8_t * {
-        return i == 0 ? rf + kOffSB + w * 4096 + ks * 1024 + lane * 16
-                      : rf + (i - 1) * 32768 + w * 4096 + ks * 1024 + lane * 16;
-    };
-    auto pass_sub = [&](int p) { return p < nsub - 1 ? p : 2 * nsub - 2 - p; };
-
-    // token inputs of subtile i (q only for a backward pass)
-    auto load_tok = [&](GradIn &in, int i, bool bwd) {
-        const int r0 = kSub * i;
-        const int64_t etok = tok0 + r0 + er;
-        const int64_t eoff = (etok * H + h) * (int64_t)kDK + ec;
-        in.k = in.g = in.v = in.q = bf16x4{};
-        in.beta = 0;
-        if (r0 + er < len) {
-            in.k = *reinterpret_cast<const bf16x4 *>(k + eoff);
-            in.g = *reinterpret_cast<const bf16x4 *>(g + eoff);
-            in.v = *reinterpret_cast<const bf16x4 *>(v + eoff);
-            if (bwd)
-                in.q = *reinterpret_cast<const bf16x4 *>(q + eoff);
-            if ((tid & 31) == 0)
-                in.beta = reinterpret_cast<const uint16_t *>(beta)[etok * H + h];
-        }
-    };
-    // gate and output gradient of subtile i on the lane's value channel.  A row
-    // past the end reads the last row of the chunk (always in range) and is
-    // masked where it is used: branch-free loads, so that nothing that depends
-    // on a loaded value is scheduled next to its load.
-    auto load_gate = [&](GradIn &in, int i) {
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-            const int row = min(kSub * i + 4 * b + i2, len - 1);
-            const int64_t off = ((tok0 + row) * H + h) * (int64_t)kDV + col;
-            in.z[i2] = reinterpret_cast<const uint16_t *>(gate)[off];
-            in.dy[i2] = reinterpret_cast<const uint16_t *>(dout)[off];
-        }
+    const int c0 = 16 * w + 4 * b;            // the lane's channels in the row layout
+    // byte offset of (token 16 t + m, channel c0) in a [.., H, 128] tensor from
+    // the chunk's base; a row past the chunk's end reads its last row (in
+    // range), zeroed where used
+    auto roff = [&](int t) -> uint32_t {
+        const int r = 16 * t + m < len ? 16 * t + m : len - 1;
+        return (uint32_t)r * tstride + 2 * c0;
     };
 
-    // A pass's token inputs are loaded one pass ahead, as soon as the pass
-    // before it has copied its own into LDS; a backward pass's gate, output
-    // gradient and state fragments (first needed after the operand set-up) right
-    // after that, at the top of the pass itself.  All global stores come after
-    // these loads and none at the end of a pass: loads and stores share one
-    // in-order counter, so a wait for a load also waits for every store issued
-    // before it.
-    GradIn cur;
-    bf16x8 sf[4];                    // state fragments of the current subtile
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(0, ks));
-    load_tok(cur, pass_sub(0), npass == 1);
-
-    // Row-contiguous stores of the token gradients of subtile i staged in LDS
-    // (16 bytes per lane: array a, row r, channels 8 c8 ..) and of its dbeta, by
-    // the nthr threads rt = 0 .. nthr - 1.  In a backward pass they are issued by
-    // waves 2..7 while waves 0 and 1 form M, A, T and P, after the pass's loads,
-    // so that no load waits behind them.
-    auto store_staged = [&](int i, int rt, int nthr) {
-        bf16 *const dst[5] = {dq, dk, dv, dg, dgate};
-        const int r0 = kSub * i;
-        for (int idx = rt; idx < 5 * kSub * 16; idx += nthr) {
-            const int a = idx / (kSub * 16), r = (idx / 16) % kSub, c8 = idx % 16;
-            if (r0 + r < len)
-                *reinterpret_cast<bf16x8 *>(dst[a] + ((tok0 + r0 + r) * H + h) * (int64_t)kDK +
-                                            8 * c8) = lds8(&smp->v.out[a][r][8 * c8]);
-        }
-        if (rt < kSub && r0 + rt < len)
-            dbeta[(tok0 + r0 + rt) * H + h] = smp->dbst[rt];
-    };
-
-    // Operands of the subtile of pass p: G, factored K / Q tiles, M, A (P), T,
-    // W and U~ (returned).  Issues the next pass's token loads once this pass's
-    // tokens are in LDS, then a backward pass's own gate and state loads; in a
-    // backward pass after the first, waves 2..7 store the previous pass's staged
-    // gradients (subtile i + 1) during the M / A / T / P step.
-    auto prep_pass = [&](int p, bool bwd, int i) -> f32x4 {
-        if ((tid & 31) == 0)
-            smp->beta[er] = bf16_bits_to_f32(cur.beta);
-        *reinterpret_cast<f32x4 *>(&smp->G[er][ec]) =
-            f32x4{(float)cur.g[0], (float)cur.g[1], (float)cur.g[2], (float)cur.g[3]};
-        *reinterpret_cast<bf16x4 *>(&smp->V[er][ec]) = cur.v;
-        *reinterpret_cast<bf16x4 *>(&smp->Kin[er][ec]) = cur.k;
-        *reinterpret_cast<bf16x4 *>(&smp->Qin[er][ec]) = cur.q;
-        if (p + 1 < npass)
-            load_tok(cur, pass_sub(p + 1), p + 1 >= nsub - 1);
-        if (bwd) {
-            load_gate(cur, i);
-            if (p > nsub - 1) {      // the first backward pass has S_{nsub-1} in registers
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    sf[ks] = *reinterpret_cast<const bf16x8 *>(sfrag_ptr(i, ks));
-            }
-        }
-        __syncthreads();
-        if (tid < kDK) {
-            float acc = 0.f;
-#pragma unroll
-            for (int r = 0; r < kSub; ++r) {
-                acc += smp->G[r][tid];
-                smp->G[r][tid] = acc;
-                if (r == kSub / 2 - 1)
-                    smp->Bref[tid] = acc;
-            }
-            smp->Ge[tid] = acc;
-            smp->dec[tid] = __expf(acc);
-        }
-        __syncthreads();
-        {
-            bf16x4 ks, kp, qs, kr, kc, qr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int x = ec + e;
-                const float G = smp->G[er][x], d = G - smp->Bref[x], Ge = smp->Ge[x];
-                const float eG = __expf(G), eP = __expf(Ge - G), eGB = __expf(d), eBG = __expf(-d);
-                const float kv = (float)smp->Kin[er][x], qv = scale * (float)smp->Qin[er][x];
-                ks[e] = (bf16)(kv * eG);
-                kp[e] = (bf16)(kv * eP);
-                qs[e] = (bf16)(qv * eG);
-                kr[e] = (bf16)(kv * eGB);
-                kc[e] = (bf16)(kv * eBG);
-                qr[e] = (bf16)(qv * eGB);
-                smp->u.a.KpT[x][tcol(x, er)] = kp[e];
-                if (bwd)
-                    smp->u.a.QsT[x][tcol(x, er)] = qs[e];
-            }
-            *reinterpret_cast<bf16x4 *>(&smp->Ks[er][ec]) = ks;
-            *reinterpret_cast<bf16x4 *>(&smp->u.a.Kp[er][ec]) = kp;
-            *reinterpret_cast<bf16x4 *>(&smp->u.a.x.mp.Kr[er][ec]) = kr;
-            *reinterpret_cast<bf16x4 *>(&smp->u.a.x.mp.Kc[er][ec]) = kc;
-            if (bwd) {
-                *reinterpret_cast<bf16x4 *>(&smp->u.a.Qs[er][ec]) = qs;
-                *reinterpret_cast<bf16x4 *>(&smp->u.a.x.mp.Qr[er][ec]) = qr;
-            }
-        }
-        __syncthreads();
-        // M = Kr Kc^T, A and T = (I + A)^-1 (wave 0); P = lower_incl(Qr Kc^T) (wave 1)
-        if (w == 0 || (bwd && w == 1)) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const bf16 *xr = w == 0 ? &smp->u.a.x.mp.Kr[m][0] : &smp->u.a.x.mp.Qr[m][0];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                acc = mfma16(lds8(xr + 32 * ks + 8 * b), lds8(&smp->u.a.x.mp.Kc[m][32 * ks + 8 * b]),
-                             acc);
-            if (w == 0) {
-                // lane (b, m) holds A[4 b + i2][m]
-                f32x4 a;
-#pragma unroll
-                for (int i2 = 0; i2 < 4; ++i2) {
-                    const int r = 4 * b + i2;
-                    a[i2] = m < r ? smp->beta[r] * acc[i2] : 0.f;
-                    smp->M[r][m] = acc[i2];
-                }
-                // T = (I + A)^-1 by forward substitution inside the wave
-                f32x4 t;
-#pragma unroll
-                for (int i2 = 0; i2 < 4; ++i2)
-                    t[i2] = (4 * b + i2 == m) ? 1.f : 0.f;
-                tsolve(t, a, b, m, std::make_integer_sequence<int, kSub - 1>{});
-#pragma unroll
-                for (int i2 = 0; i2 < 4; ++i2)
-                    smp->Tm[4 * b + i2][m] = t[i2];
-            } else {
-#pragma unroll
-                for (int i2 = 0; i2 < 4; ++i2) {
-                    const int r = 4 * b + i2;
-                    smp->P[r][m] = m <= r ? acc[i2] : 0.f;
-                }
-            }
-        } else if (bwd && p > nsub - 1) {
-            // waves 2..7; the staging area is next written in this pass's U / O step
-            store_staged(i + 1, tid - 2 * 64, kGThreads - 2 * 64);
-        }
-        __syncthreads();
-        // W = T diag(beta) Ks and U~ = T diag(beta) V on the wave's channels (fp32 MFMA)
-        f32x4 ut;
-        {
-            f32x4 wt = {0.f, 0.f, 0.f, 0.f}, u = wt;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int s = 4 * kk + b;
-                const float t = smp->Tm[m][s], bs = smp->beta[s];
-                wt = mfma4_f32(t, bs * (float)smp->Ks[s][col], wt);
-                u = mfma4_f32(t, bs * (float)smp->V[s][col], u);
-            }
-            ut = u;
-#pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-                smp->u.a.x.w.W[4 * b + i2][col] = (bf16)wt[i2];
-                smp->u.a.x.w.WT[col][tcol(col, 4 * b + i2)] = (bf16)wt[i2];
-            }
-        }
-        __syncthreads();
-        return ut;
-    };
-
-    // ---------------- forward passes: states on entry to subtiles 1 .. nsub - 1
-    if (nsub > 1) {
-        f32x4 S[8];                  // the fp32 state of the wave's value channels
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                S[2 * ks][i] = (float)sf[ks][i];
-                S[2 * ks + 1][i] = (float)sf[ks][4 + i];
-            }
-#pragma unroll 1
-        for (int p = 0; p < nsub - 1; ++p) {
-            const int i = p;
-            smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
-            const f32x4 ut = prep_pass(p, false, i);
-            // S' = diag(e^Ge) S + Kp^T U, U = U~ - W S
-            f32x4 ws = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                ws = mfma16(perm8(&smp->u.a.x.w.W[m][0], ks, b), sf[ks], ws);
-            const bf16x4 ub = bf4(ut - ws);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const f32x4 dc = *reinterpret_cast<const f32x4 *>(&smp->dec[16 * t + 4 * b]);
-                S[t] = S[t] * dc;
-                S[t] = mfma16k16(*reinterpret_cast<const bf16x4 *>(
-                                     &smp->u.a.KpT[16 * t + m][tcol(16 * t + m, 4 * b)]),
-                                 ub, S[t]);
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                sf[ks] = acc_to_frag(S[2 * ks], S[2 * ks + 1]);
-            __syncthreads();
-            if (i + 1 < nsub - 1) {       // S_{nsub-1} stays in registers for the first backward pass
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    *reinterpret_cast<bf16x8 *>(sfrag_ptr(i + 1, ks)) = sf[ks];
-            }
-        }
-    }
-
-    // ---------------- backward passes over the subtiles, last to first
-    f32x4 dS[8];                     // dS' of the wave's value channels, from the backward record
+    // ---- phase 0: record operands into LDS, G, K' ----------------------------
+    bf16x8 sf[4], df[4];        // S and dS' of value block w as B fragments (perm order)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 d = *reinterpret_cast<const bf16x8 *>(rb + kOffSB + w * 4096 + ks * 1024 +
-                                                           lane * 16);
+        sf[ks] = gload<bf16x8>(rf, kOffSB + w * 4096 + ks * 1024 + lane * 16);
+        df[ks] = gload<bf16x8>(rb, kOffSB + w * 4096 + ks * 1024 + lane * 16);
+    }
+    {
+        const int r = tid >> 3, c8 = 8 * (tid & 7);
+        const bf16x8 q0 = gload<bf16x8>(rf, kOffQH + 16 * tid);
+        const bf16x8 q1 = gload<bf16x8>(rf, kOffQH + 16 * (tid + kGThreads));
+        const bf16x8 w0 = gload<bf16x8>(rf, kOffXW + 16 * tid);
+        const bf16x8 w1 = gload<bf16x8>(rf, kOffXW + 16 * (tid + kGThreads));
+        const bf16x8 p8 =
+            gload<bf16x8>(rf, kOffXP + (size_t)(r * kChunk + c8) * 2);
+        bf16x8 *sq = &smp->a.f.QH[0][0], *sw = &smp->a.f.W[0][0];
+        sq[tid] = q0;
+        sq[tid + kGThreads] = q1;
+        sw[tid] = w0;
+        sw[tid + kGThreads] = w1;
+        *reinterpret_cast<bf16x8 *>(&smp->t.PT[r][c8]) = p8;
+        if (tid < kChunk)
+            smp->beta[tid] = tid < len ? (float)beta[(tok0 + tid) * H + h] : 0.f;
+    }
+    // G (row layout): prefix over the 16 tokens of a tile (DPP), carried over the
+    // tiles; G before tiles 1..3 (the references of those subtiles) and G_end
+    // go to LDS
+    float G[4][4];
+    bf16x4 kv[4], qv[4];                      // k and q of the lane's elements (zero past the end)
+    {
+        bf16x4 gv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dS[2 * ks][i] = (float)d[i];
-            dS[2 * ks + 1][i] = (float)d[4 + i];
+        for (int t = 0; t < 4; ++t) {
+            gv[t] = gload<bf16x4>(gg, roff(t));
+            kv[t] = gload<bf16x4>(gk, roff(t));
+            qv[t] = gload<bf16x4>(gq, roff(t));
+        }
+        float carry[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bool ok = 16 * t + m < len;
+            if (!ok) {
+                kv[t] = bf16x4{};
+                qv[t] = bf16x4{};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float incl = row_inclusive_sum(ok ? (float)gv[t][i] : 0.f);
+                G[t][i] = carry[i] + incl;
+                carry[i] += row_bcast<15>(incl);
+            }
+            if (m == 0)
+                *reinterpret_cast<f32x4 *>(&smp->ref[t][c0]) = f32x4{carry[0], carry[1], carry[2], carry[3]};
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            bf16x4 kp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                kp[i] = (bf16)((float)kv[t][i] * __expf(carry[i] - G[t][i]));
+            *reinterpret_cast<bf16x4 *>(&smp->p.KP[16 * t + m][c0]) = kp;
         }
     }
-#pragma unroll 1
-    for (int p = nsub - 1; p < npass; ++p) {
-        const int i = pass_sub(p);
-        const int r0 = kSub * i;
-        smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
-        const f32x4 ut = prep_pass(p, true, i);
-        // U and O on the wave's value channels
-        f32x4 ws = {0.f, 0.f, 0.f, 0.f}, o = ws;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            ws = mfma16(perm8(&smp->u.a.x.w.W[m][0], ks, b), sf[ks], ws);
-            o = mfma16(perm8(&smp->u.a.Qs[m][0], ks, b), sf[ks], o);
-        }
-        const bf16x4 ub = bf4(ut - ws);
-        {
-            bf16x4 pa;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                pa[e] = (bf16)smp->P[m][4 * b + e];
-            o = mfma16k16(pa, ub, o);
-        }
-        // gate: dZ (kept until the outputs are staged), and dO = dY sigmoid(Z)
-        f32x4 dOv;
-        bf16x4 dz4;
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-            const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-bf16_bits_to_f32(cur.z[i2])));
-            const float dyv = r0 + 4 * b + i2 < len ? bf16_bits_to_f32(cur.dy[i2]) : 0.f;
-            dz4[i2] = (bf16)(dyv * o[i2] * sg * (1.f - sg));
-            dOv[i2] = dyv * sg;
-        }
-        const bf16x4 dob = bf4(dOv);
-        // dU = Kp dS' + P^T dO
-        f32x4 du = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            du = mfma16(perm8(&smp->u.a.Kp[m][0], ks, b), acc_to_frag(dS[2 * ks], dS[2 * ks + 1]),
-                        du);
-        {
-            bf16x4 pt;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                pt[e] = (bf16)smp->P[4 * b + e][m];
-            du = mfma16k16(pt, dob, du);
-        }
-        const bf16x4 dub = bf4(du);
-        // U, dO, dU, S and dS' of the wave's value channels into LDS
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-            const int r = 4 * b + i2;
-            smp->U[r][col] = ub[i2];
-            smp->dO[r][col] = dob[i2];
-            smp->dU[r][col] = dub[i2];
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                smp->v.s.Sb[perm_row(ks, b, e)][col] = sf[ks][e];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2)
-                smp->v.s.dSb[16 * t + 4 * b + i2][col] = (bf16)dS[t][i2];
-        // dS on entry to the subtile: diag(e^Ge) dS' + Qs^T dO - W^T dU
-        __builtin_amdgcn_sched_barrier(0);
-        {
-            const bf16x4 ndub = bf16x4{(bf16)(-du[0]), (bf16)(-du[1]), (bf16)(-du[2]),
-                                       (bf16)(-du[3])};
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const f32x4 dc = *reinterpret_cast<const f32x4 *>(&smp->dec[16 * t + 4 * b]);
-                f32x4 x = dS[t] * dc;
-                x = mfma16k16(*reinterpret_cast<const bf16x4 *>(
-                                  &smp->u.a.QsT[16 * t + m][tcol(16 * t + m, 4 * b)]),
-                              dob, x);
-                dS[t] = mfma16k16(
-                    *reinterpret_cast<const bf16x4 *>(
-                        &smp->u.a.x.w.WT[16 * t + m][tcol(16 * t + m, 4 * b)]), ndub, x);
-            }
-        }
-        __syncthreads();
+    __syncthreads();
 
-        // sums over the value channels on the wave's key channels col:
-        // dKp = U dS'^T, dQs = dO S^T, dW = -dU S^T
-        f32x4 dkp = {0.f, 0.f, 0.f, 0.f}, dqs = dkp, dw = dkp;
+    smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
+    // ---- phase 1: value block w.  O^T = S^T Q^^T + O0^T and U^T = U~^T - S^T W^T
+    // (row layout), then the gate: dZ = dY O s (1 - s), dO = dY s, s = sigmoid(Z)
+    {
+        f32x4 o[4], u[4];
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            const bf16x8 x = gload<bf16x8>(rf, kOffO0 + w * 2048 +
+                                                               tp * 1024 + lane * 16);
+            o[2 * tp] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+            o[2 * tp + 1] = f32x4{(float)x[4], (float)x[5], (float)x[6], (float)x[7]};
+        }
+        bf16x4 zb[4], yb[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            u[t] = f4(gload<bf16x4>(rf, kOffXU + (t * 4 + (w >> 1)) * kFragBytes +
+                                                       lane * 16 + (w & 1) * 8));
+            zb[t] = gload<bf16x4>(gz, roff(t));
+            yb[t] = gload<bf16x4>(gy, roff(t));
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 ws = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                o[t] = mfma16(sf[ks], smp->a.f.QH[t * 4 + ks][lane], o[t]);
+                ws = mfma16(sf[ks], smp->a.f.W[t * 4 + ks][lane], ws);
+            }
+            u[t] -= ws;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bool ok = 16 * t + m < len;
+            bf16x4 dz4, do4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-(float)zb[t][i]));
+                const float dy = ok ? (float)yb[t][i] : 0.f;
+                dz4[i] = (bf16)(dy * o[t][i] * sg * (1.f - sg));
+                do4[i] = (bf16)(dy * sg);
+            }
+            if (ok)
+                gstore(oz, roff(t), dz4);
+            *reinterpret_cast<bf16x4 *>(&smp->DO[16 * t + m][c0]) = do4;
+            *reinterpret_cast<bf16x4 *>(&smp->U[16 * t + m][c0]) = bf4(u[t]);
+        }
+    }
+    __syncthreads();
+
+    smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
+    // S and dS' as [dk][dv] tiles for the sums over dv (the fragments' space is free)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            smp->a.s.Sb[perm_row(ks, b, e)][16 * w + m] = sf[ks][e];
+            smp->a.s.dSb[perm_row(ks, b, e)][16 * w + m] = df[ks][e];
+        }
+    // dU^T = dS'^T K'^T + dO^T P (row layout, value block w); dO enters in
+    // accumulator order as the operand of the product over tokens
+    {
+        bf16x4 doa[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                doa[s][i] = smp->DO[16 * s + 4 * b + i][16 * w + m];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                a = mfma16(df[ks], perm8(&smp->p.KP[16 * t + m][0], ks, b), a);
+#pragma unroll
+            for (int s = t; s < 4; ++s)
+                a = mfma16k16(doa[s],
+                              *reinterpret_cast<const bf16x4 *>(&smp->t.PT[16 * t + m][16 * s + 4 * b]),
+                              a);
+            *reinterpret_cast<bf16x4 *>(&smp->DU[16 * t + m][c0]) = bf4(a);
+        }
+    }
+    __syncthreads();
+
+    smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
+    // ---- phase 2: key block w, sums over the value channels:
+    // dQs^T = S dO^T, dK'^T = dS' U^T (row layout), dW = -dU S^T (accumulator order)
+    f32x4 aq[4], ak[4], aG[4];              // dq, dk and dG of the lane's elements
+    float kpk[4] = {0.f, 0.f, 0.f, 0.f};    // sum over the lane's tokens of K' dK'
+    bf16x4 dwa[4];
+    const f32x4 Ge = *reinterpret_cast<const f32x4 *>(&smp->ref[3][c0]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kc = 32 * ks + 8 * b;
-            const bf16x8 srow = lds8(&smp->v.s.Sb[col][kc]);
-            dkp = mfma16(lds8(&smp->U[m][kc]), lds8(&smp->v.s.dSb[col][kc]), dkp);
-            dqs = mfma16(lds8(&smp->dO[m][kc]), srow, dqs);
-            dw = mfma16(lds8(&smp->dU[m][kc]), srow, dw);
+            const bf16x8 srow = lds8(&smp->a.s.Sb[16 * w + m][kc]);
+            a1 = mfma16(srow, lds8(&smp->DO[16 * t + m][kc]), a1);
+            a2 = mfma16(lds8(&smp->a.s.dSb[16 * w + m][kc]), lds8(&smp->U[16 * t + m][kc]), a2);
+            a3 = mfma16(lds8(&smp->DU[16 * t + m][kc]), srow, a3);
         }
-        dw = -dw;
+        dwa[t] = bf4(-a3);
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2)
-            smp->u.b.dW[4 * b + i2][col] = dw[i2];
-        {
-            // e^Ge rowsum(dS' S) of key channel col, 32 value channels per lane group
-            float pr = 0.f;
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const bf16x8 sv = lds8(&smp->v.s.Sb[col][32 * b + 8 * pp]);
-                const bf16x8 dv8 = lds8(&smp->v.s.dSb[col][32 * b + 8 * pp]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pr += (float)sv[e] * (float)dv8[e];
-            }
-            pr += __shfl_xor(pr, 16);
-            pr += __shfl_xor(pr, 32);
-            if (b == 0)
-                smp->dGeD[col] = smp->dec[col] * pr;
-        }
-        if (w == 0 || w == 1) {
-            // wave 0: dP = lower_incl(dO U^T); wave 1: dU (diag(beta) V)^T
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const bf16 *ar = w == 0 ? &smp->dO[m][0] : &smp->dU[m][0];
-            const bf16 *br = w == 0 ? &smp->U[m][0] : &smp->V[m][0];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                acc = mfma16(lds8(ar + 32 * ks + 8 * b), lds8(br + 32 * ks + 8 * b), acc);
-#pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-                const int r = 4 * b + i2;
-                if (w == 0)
-                    smp->dP[r][m] = m <= r ? acc[i2] : 0.f;
-                else
-                    smp->dTu[r][m] = smp->beta[m] * acc[i2];
-            }
-        }
-        __syncthreads();
-        // dT = dW (diag(beta) Ks)^T + dU (diag(beta) V)^T, then
-        // dA = strict_lower(-T^T (dT T^T)), all in wave 0 and in registers: an
-        // accumulator tile (lane (b, n) holds D[4 b + i][n]) is used directly as
-        // the next 16x16x4 product's operand, with the contraction index of step
-        // kk taken as k = 4 b + kk on both sides
-        if (w == 0) {
-            // dT^T: lane (b, m) holds dT[m][4 b + i]
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int kc = 32 * ks + 8 * b;
-                const f32x4 lo = *reinterpret_cast<const f32x4 *>(&smp->u.b.dW[m][kc]);
-                const f32x4 hi = *reinterpret_cast<const f32x4 *>(&smp->u.b.dW[m][kc + 4]);
-                acc = mfma16(lds8(&smp->Ks[m][kc]), acc_to_frag(lo, hi), acc);
-            }
-            f32x4 dtt;
-#pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2)
-                dtt[i2] = smp->beta[4 * b + i2] * acc[i2] + smp->dTu[m][4 * b + i2];
-            // Y = dT T^T: A[m][k] = dT[m][k] is dtt[kk], B[k][n] = T[n][k]
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                y = mfma4_f32(dtt[kk], smp->Tm[m][4 * b + kk], y);
-            // T^T Y: A[m][k] = T[k][m], B[k][n] = Y[k][n] is y[kk]
-            f32x4 x2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                x2 = mfma4_f32(smp->Tm[4 * b + kk][m], y[kk], x2);
-#pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-                const int r = 4 * b + i2;
-                smp->dA[r][m] = m < r ? -x2[i2] : 0.f;
-            }
-        }
-        __syncthreads();
-
-        // the contractions over the subtile's 16 tokens, on the wave's channels:
-        // T^T dW, T^T dU, dP^T Qr + dA^T diag(beta) Kr, dA Kc, dP Kc.  Kr, Kc and
-        // Qr enter in fp32: every pair (r, s) of A and P adds a term to dG_r and
-        // its negative to dG_s, and the two cancel in the reverse cumulative sum
-        // that gives dg, so both must be formed from the same fp32 factors.
-        f32x4 tdw = {0.f, 0.f, 0.f, 0.f}, tdu = tdw, dkc = tdw, dkr = tdw, dqr = tdw;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int s = 4 * kk + b;
-            const float t_ms = smp->Tm[s][m];
-            const float d = smp->G[s][col] - smp->Bref[col];
-            const float egb = __expf(d), ebg = __expf(-d);
-            const float ks_ = (float)smp->Kin[s][col];
-            const float kc_s = ks_ * ebg, kr_s = ks_ * egb;
-            const float qr_s = scale * (float)smp->Qin[s][col] * egb;
-            tdw = mfma4_f32(t_ms, smp->u.b.dW[s][col], tdw);
-            tdu = mfma4_f32(t_ms, (float)smp->dU[s][col], tdu);
-            dkc = mfma4_f32(smp->dP[s][m], qr_s, dkc);
-            dkc = mfma4_f32(smp->dA[s][m] * smp->beta[s], kr_s, dkc);
-            dkr = mfma4_f32(smp->dA[m][s], kc_s, dkr);
-            dqr = mfma4_f32(smp->dP[m][s], kc_s, dqr);
-        }
-        // per element: row r = 4 b + i2, channel col (all reads first, stores last)
-        float dGv[4], pb[4], kpk = 0.f;
-        bf16x4 oq, ok, ov;
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-            const int r = 4 * b + i2;
-            const float kv = (float)smp->Kin[r][col];
-            const float qv = scale * (float)smp->Qin[r][col];
-            const float G = smp->G[r][col], d = G - smp->Bref[col], Ge = smp->Ge[col];
-            const float eG = __expf(G), eGB = __expf(d), eBG = __expf(-d), eP = __expf(Ge - G);
-            const float br = smp->beta[r];
-            const float dks = br * tdw[i2], dkr_ = br * dkr[i2];
-            oq[i2] = (bf16)(scale * (eG * dqs[i2] + eGB * dqr[i2]));
-            ok[i2] = (bf16)(eG * dks + eGB * dkr_ + eBG * dkc[i2] + eP * dkp[i2]);
-            ov[i2] = (bf16)(br * tdu[i2]);
-            dGv[i2] = dqs[i2] * qv * eG + dqr[i2] * qv * eGB + dks * kv * eG + dkr_ * kv * eGB -
-                      dkc[i2] * kv * eBG - dkp[i2] * kv * eP;
-            kpk += dkp[i2] * kv * eP;
-            // dbeta terms of this element; wave 0 adds the dA M term of row r (its lane
-            // m is the column of A)
-            pb[i2] = tdw[i2] * kv * eG + tdu[i2] * (float)smp->V[r][col];
-            if (w == 0)
-                pb[i2] += smp->dA[r][m] * smp->M[r][m];
-        }
-        // sums of pb over the wave's 16 channels for the lane group's four rows, as
-        // a butterfly that also spreads the rows: afterwards lanes with m % 4 == 0
-        // hold the sum of row 4 b + 2 ((m >> 3) & 1) + ((m >> 2) & 1)
-        {
-            const bool hi = (m & 8) != 0, mid = (m & 4) != 0;
-            const float a0 = (hi ? pb[2] : pb[0]) + __shfl_xor(hi ? pb[0] : pb[2], 8);
-            const float a1 = (hi ? pb[3] : pb[1]) + __shfl_xor(hi ? pb[1] : pb[3], 8);
-            float c = (mid ? a1 : a0) + __shfl_xor(mid ? a0 : a1, 4);
-            c += __shfl_xor(c, 2);
-            c += __shfl_xor(c, 1);
-            if ((m & 3) == 0)
-                smp->dbp[w][4 * b + 2 * (hi ? 1 : 0) + (mid ? 1 : 0)] = c;
-        }
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-            const int r = 4 * b + i2;
-            smp->v.out[0][r][col] = oq[i2];
-            smp->v.out[1][r][col] = ok[i2];
-            smp->v.out[2][r][col] = ov[i2];
-            smp->v.out[4][r][col] = dz4[i2];
-        }
-        // dg_u = sum_{r >= u} dG_r + dGe with dGe = dGeD + colsum(dKp Kp): the rows of
-        // channel col are spread over the four lane groups b
-        {
-            kpk += __shfl_xor(kpk, 16);
-            kpk += __shfl_xor(kpk, 32);
-            float suf[4];
-            suf[3] = dGv[3];
-#pragma unroll
-            for (int i2 = 2; i2 >= 0; --i2)
-                suf[i2] = suf[i2 + 1] + dGv[i2];
-            const float t1 = __shfl(suf[0], m + 16 * ((b + 1) & 3));
-            const float t2 = __shfl(suf[0], m + 16 * ((b + 2) & 3));
-            const float t3 = __shfl(suf[0], m + 16 * ((b + 3) & 3));
-            const float later = (b < 3 ? t1 : 0.f) + (b < 2 ? t2 : 0.f) + (b < 1 ? t3 : 0.f);
-            const float dge = smp->dGeD[col] + kpk + later;
-#pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2)
-                smp->v.out[3][4 * b + i2][col] = (bf16)(dge + suf[i2]);
-        }
-        __syncthreads();
-        if (tid < kSub) {
-            float acc = 0.f;
-#pragma unroll
-            for (int x = 0; x < kGWaves; ++x)
-                acc += smp->dbp[x][tid];
-            smp->dbst[tid] = (bf16)acc;
+        for (int i = 0; i < 4; ++i) {
+            const float eG = __expf(G[t][i]), eP = __expf(Ge[i] - G[t][i]);
+            const float qs = scale * (float)qv[t][i] * eG, kp = (float)kv[t][i] * eP;
+            aq[t][i] = scale * eG * a1[i];
+            ak[t][i] = eP * a2[i];
+            aG[t][i] = qs * a1[i] - kp * a2[i];
+            kpk[i] += kp * a2[i];
         }
     }
-    store_staged(0, tid, kGThreads);
+    {
+        // e^Ge rowsum(dS' S) of key channel 16 w + m, 32 value channels per lane group
+        float pr = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+            const bf16x8 sv = lds8(&smp->a.s.Sb[16 * w + m][32 * b + 8 * pp]);
+            const bf16x8 dv8 = lds8(&smp->a.s.dSb[16 * w + m][32 * b + 8 * pp]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pr += (float)sv[e] * (float)dv8[e];
+        }
+        pr += __shfl_xor(pr, 16);
+        pr += __shfl_xor(pr, 32);
+        if (b == 0)
+            smp->dgeD[16 * w + m] = gload<float>(rf, kOffDEC + 4 * (16 * w + m)) * pr;
+    }
+    // dP = lower_incl(dO U^T), 16 x 16 blocks
+    for (int nb = 0; nb < (w < 2 ? 2 : 1); ++nb) {
+        int I, J;
+        lower_block(w, nb, I, J);
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kc = 32 * ks + 8 * b;
+            a = mfma16(lds8(&smp->DO[16 * I + m][kc]), lds8(&smp->U[16 * J + m][kc]), a);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * I + 4 * b + i, col = 16 * J + m;
+            smp->p.dP[row][col] = (J < I || col <= row) ? a[i] : 0.f;
+        }
+    }
+    {
+        // T^T into P^T's space (P^T was last read before the previous barrier)
+        const int r = tid >> 3, c8 = 8 * (tid & 7);
+        *reinterpret_cast<bf16x8 *>(&smp->t.TT[r][c8]) =
+            gload<bf16x8>(rf, kOffXT + (size_t)(r * kChunk + c8) * 2);
+    }
+    __syncthreads();
+
+    smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
+    // ---- phase 3: dQr (dq complete); dX^T = dW^T T (key block w) and
+    // dY~^T = dU^T T (value block w), row layout; dv = beta dY~, dKs = beta dX
+    float pb[4] = {0.f, 0.f, 0.f, 0.f};     // dbeta terms of the lane's tokens, its 4 channels
+    {
+        bf16x4 dua[4], vv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dua[s][i] = smp->DU[16 * s + 4 * b + i][16 * w + m];
+            vv[s] = gload<bf16x4>(gv_, roff(s));
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 dx = {0.f, 0.f, 0.f, 0.f}, dy = dx;
+#pragma unroll
+            for (int s = t; s < 4; ++s) {
+                const bf16x4 tt =
+                    *reinterpret_cast<const bf16x4 *>(&smp->t.TT[16 * t + m][16 * s + 4 * b]);
+                dx = mfma16k16(dwa[s], tt, dx);
+                dy = mfma16k16(dua[s], tt, dy);
+            }
+            const bool ok = 16 * t + m < len;
+            const float br = smp->beta[16 * t + m];
+            bf16x4 dv4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float eG = __expf(G[t][i]);
+                const float ks = (float)kv[t][i] * eG;
+                dv4[i] = (bf16)(br * dy[i]);
+                ak[t][i] += eG * br * dx[i];
+                aG[t][i] += ks * br * dx[i];
+                pb[t] += dx[i] * ks + dy[i] * (ok ? (float)vv[t][i] : 0.f);
+            }
+            if (ok)
+                gstore(ov, roff(t), dv4);
+            *reinterpret_cast<bf16x4 *>(&smp->a.x.DX[16 * t + m][c0]) = bf4(dx);
+            *reinterpret_cast<bf16x4 *>(&smp->a.x.DY[16 * t + m][c0]) = bf4(dy);
+        }
+    }
+    // The products over tokens with the blocks of dP (here) and dA (phase 5)
+    // run on fp32 factors: every pair of rows (r, s) of A and P adds a term to
+    // dG_r and its negative to dG_s, which cancel in the suffix sums of dg, so
+    // both must come from the same fp32 values.  Block (I, J) takes the column
+    // factors K_J e^{B_I - G_J} for the row gradients (at most 1 off the
+    // diagonal blocks, e^80 on them).
+    {
+        // k and G in accumulator order (channel 16 w + m), transposed from the
+        // row layout; Ba[t] = G before tile t of that channel
+        bf16x4 ka[4];
+        f32x4 Ga[4];
+        float Ba[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            ka[t] = acc_order(kv[t], b, m);
+            Ga[t] = acc_order(f32x4{G[t][0], G[t][1], G[t][2], G[t][3]}, b, m);
+            Ba[t] = t == 0 ? 0.f : smp->ref[t - 1][16 * w + m];
+        }
+        // dQr^T = (dP Kc)^T for row tile I, then dq = scale (e^G dQs + e^{G-B} dQr)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            f32x4 ap = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int J = 0; J <= I; ++J) {
+                const f32x4 pr =
+                    *reinterpret_cast<const f32x4 *>(&smp->p.dP[16 * I + m][16 * J + 4 * b]);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    ap = mfma4_f32((float)ka[J][kk] * __expf(Ba[I] - Ga[J][kk]), pr[kk], ap);
+            }
+            const f32x4 Bi = ref4(*smp, I, c0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float eGB = __expf(G[I][i] - Bi[i]);
+                aq[I][i] += scale * eGB * ap[i];
+                aG[I][i] += scale * (float)qv[I][i] * eGB * ap[i];
+            }
+            if (16 * I + m < len)
+                gstore(oq, roff(I), bf4(aq[I]));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+
+    smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
+    // ---- phase 4: dA = strict_lower(-dX W^T - dY~ U~^T), 16 x 16 blocks ------
+    for (int nb = 0; nb < (w < 2 ? 2 : 1); ++nb) {
+        int I, J;
+        lower_block(w, nb, I, J);
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const size_t off = (J * 4 + ks) * kFragBytes + lane * 16;
+            const bf16x8 wfr = gload<bf16x8>(rf, kOffXW + off);
+            const bf16x8 ufr = gload<bf16x8>(rf, kOffXU + off);
+            a = mfma16(perm8(&smp->a.x.DX[16 * I + m][0], ks, b), wfr, a);
+            a = mfma16(perm8(&smp->a.x.DY[16 * I + m][0], ks, b), ufr, a);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * I + 4 * b + i, col = 16 * J + m;
+            smp->a.x.dA[row][col] = (J < I || col < row) ? -a[i] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
+    // ---- phase 5: the products over tokens with the blocks of dA (and dP for
+    // the column gradients), fp32, as in phase 3.  Block (I, J) takes the row
+    // factors K_I e^{G_I - B_J}, q_I e^{G_I - B_J} for the column gradients.
+    {
+        bf16x4 ka[4], qa[4];
+        f32x4 Ga[4];
+        float Ba[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            ka[t] = acc_order(kv[t], b, m);
+            qa[t] = acc_order(qv[t], b, m);
+            Ga[t] = acc_order(f32x4{G[t][0], G[t][1], G[t][2], G[t][3]}, b, m);
+            Ba[t] = t == 0 ? 0.f : smp->ref[t - 1][16 * w + m];
+        }
+        // row gradients: Z^T = (dA Kc)^T for row tile I, dKr = diag(beta) Z
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            f32x4 az = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int J = 0; J <= I; ++J) {
+                const f32x4 ar = *reinterpret_cast<const f32x4 *>(&smp->a.x.dA[16 * I + m][16 * J + 4 * b]);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    az = mfma4_f32((float)ka[J][kk] * __expf(Ba[I] - Ga[J][kk]), ar[kk], az);
+            }
+            const float br = smp->beta[16 * I + m];
+            const f32x4 Bi = ref4(*smp, I, c0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float eGB = __expf(G[I][i] - Bi[i]);
+                const float kr = (float)kv[I][i] * eGB;
+                ak[I][i] += eGB * br * az[i];
+                aG[I][i] += kr * br * az[i];
+                pb[I] += kr * az[i];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // column gradients: dKc^T = ((beta dA)^T Kr + dP^T Qr)^T for column tile J
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int I = J; I < 4; ++I) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int r = 16 * I + 4 * b + kk;
+                    const float e = __expf(Ga[I][kk] - Ba[J]);
+                    a = mfma4_f32((float)ka[I][kk] * e, smp->beta[r] * smp->a.x.dA[r][16 * J + m], a);
+                    a = mfma4_f32(scale * (float)qa[I][kk] * e, smp->p.dP[r][16 * J + m], a);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const f32x4 Bj = ref4(*smp, J, c0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float eBG = __expf(Bj[i] - G[J][i]);
+                ak[J][i] += eBG * a[i];
+                aG[J][i] -= (float)kv[J][i] * eBG * a[i];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
+    // ---- phase 6: dbeta, dGe, dg = suffix sums of dG + dGe; stores ------------
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float x = pb[t];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        if (b == 0)
+            smp->dbp[w][16 * t + m] = x;
+    }
+    {
+        float carry[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x = kpk[i];                  // over the 16 tokens m of the lane's row
+            x += __shfl_xor(x, 1);
+            x += __shfl_xor(x, 2);
+            x += __shfl_xor(x, 4);
+            x += __shfl_xor(x, 8);
+            carry[i] = smp->dgeD[c0 + i] + x;    // dGe of channel c0 + i
+        }
+        bf16x4 og[4];
+#pragma unroll
+        for (int t = 3; t >= 0; --t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = aG[t][i];
+                const float incl = row_inclusive_sum(x);
+                const float tot = row_bcast<15>(incl);
+                og[t][i] = (bf16)(carry[i] + tot - incl + x);
+                carry[i] += tot;
+            }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (16 * t + m < len) {
+                gstore(ok_, roff(t), bf4(ak[t]));
+                gstore(og_, roff(t), og[t]);
+            }
+    }
+    __syncthreads();
+    if (tid < len) {
+        float s = 0.f;
+#pragma unroll
+        for (int x = 0; x < kGWaves; ++x)
+            s += smp->dbp[x][tid];
+        dbeta[(tok0 + tid) * H + h] = (bf16)s;
+    }
 }
 
 }  // namespace

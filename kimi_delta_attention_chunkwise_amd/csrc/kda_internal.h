@@ -80,6 +80,23 @@ constexpr size_t kOffO01 = kOffQH1 + 16 * kFragBytes;
 constexpr size_t kPairRecBytes = kOffO01 + kNumVBlocks * 2048;
 static_assert(kPairRecBytes % 256 == 0, "pair records stay 256-byte aligned");
 
+// Per-chunk records (kept for the backward, or for snapshots inside a pair)
+// add the chunk's intra-chunk factors after the first kRecBytes bytes, for
+// the chunk-level gradient kernel:
+//   XW : W = T diag(beta) K e^G as row fragments: fragment (token row tile t,
+//        dk k-step ks) at (4 t + ks) KiB, lane (b, m) holding row 16 t + m,
+//        dk 32 ks + 16 (e / 4) + 4 b + e % 4 (perm order)              (16 KiB)
+//   XU : U~ = T diag(beta) V, the same layout over dv                  (16 KiB)
+//   XT : T^T, bf16 [64][64] row-major (XT[r][s] = T[s][r])             (8 KiB)
+//   XP : P^T, bf16 [64][64] row-major, P = scale * lower_incl(Q e^G (K e^-G)^T)
+//                                                                       (8 KiB)
+constexpr size_t kOffXW = kRecBytes;
+constexpr size_t kOffXU = kOffXW + 16 * kFragBytes;
+constexpr size_t kOffXT = kOffXU + 16 * kFragBytes;
+constexpr size_t kOffXP = kOffXT + (size_t)kChunk * kChunk * 2;
+constexpr size_t kChunkRecBytes = kOffXP + (size_t)kChunk * kChunk * 2;
+static_assert(kChunkRecBytes % 256 == 0, "chunk records stay 256-byte aligned");
+
 // Global-memory pointers whose address space is explicit, so the compiler
 // emits global (not flat) memory instructions for them.
 typedef __attribute__((address_space(1))) uint8_t gbyte;
@@ -143,6 +160,26 @@ __device__ __forceinline__ bf16x8 acc_to_frag(const f32x4 &lo, const f32x4 &hi)
 __device__ __forceinline__ f32x4 mfma4_f32(float a, float b, const f32x4 &c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// DPP lane move (as int bits) with every lane active; lanes whose source is
+// out of range (bound_ctrl) or whose row is masked off read 0
+template <int kCtrl, int kRowMask, bool kBound>
+__device__ __forceinline__ float dpp_add_src(float x)
+{
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xf, kBound));
+}
+
+// inclusive prefix sum over each 16-lane row of a wave (row_shr 1, 2, 4, 8;
+// lanes whose source falls outside the row add 0)
+__device__ __forceinline__ float row_inclusive_sum(float x)
+{
+    x += dpp_add_src<0x111, 0xf, true>(x);
+    x += dpp_add_src<0x112, 0xf, true>(x);
+    x += dpp_add_src<0x114, 0xf, true>(x);
+    x += dpp_add_src<0x118, 0xf, true>(x);
+    return x;
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -297,9 +334,9 @@ hipError_t launch_bwd_prep_bf16(const bf16 *gate, const bf16 *dout, const int32_
                                 int T, int H, int64_t n_slots, const uint8_t *ws_f,
                                 uint8_t *ws_b, hipStream_t stream);
 
-// Per-chunk gradients from the entry states (SB of ws_f) and the exit state
-// gradients (SB of the reversed records of ws_b); overwrites the LN, QH, BM
-// and O0 parts of the forward records.
+// Per-chunk gradients from the forward records (Q^, O0, the entry state SB and
+// the extension XW, XU, XT, XP) and the exit state gradients (SB of the
+// reversed records of ws_b); writes no record.
 hipError_t launch_grad_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                             const bf16 *beta, const bf16 *gate, const bf16 *dout, bf16 *dq,
                             bf16 *dk, bf16 *dv, bf16 *dg, bf16 *dbeta, bf16 *dgate,

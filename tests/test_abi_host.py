@@ -76,9 +76,9 @@ def test_workspace_bytes(lib):
     PREC = ws(1, 64, 1, 1, 128, 128, 64, 1, 0)      # one pair slot (here holding one chunk)
     REC = rb(1, 64, 1, 1, 128, 128, 64, 1, 0)       # one 64-token chunk of one head
     assert PREC % 256 == 0 and REC % 256 == 0
-    # bytes per token-head as documented: pair records 1,284, chunk records 2,056
+    # bytes per token-head as documented: pair records 1,284, chunk records 2,824
     assert PREC == 164352 and PREC // 128 == 1284
-    assert REC == 131584 and REC // 64 == 2056
+    assert REC == 180736 and REC // 64 == 2824
     # fixed length: B * ceil(T / 128) pair slots per head
     assert ws(1, 4096, 1, 8, 128, 128, 64, 1, 0) == 32 * 8 * PREC
     assert ws(3, 100, 3, 2, 128, 128, 64, 1, 0) == 3 * 2 * 1 * PREC
@@ -86,7 +86,7 @@ def test_workspace_bytes(lib):
     assert ws(1, 0, 1, 4, 128, 128, 64, 1, 0) == 0
     # varlen: floor(T / 128) + N pair slots per head
     assert ws(1, 67000, 4, 32, 128, 128, 64, 1, 1) == (67000 // 128 + 4) * 32 * PREC
-    # the 1M-token workload: 8,192 pairs x 16 heads, 21.5 GB (per-chunk records: 34.5 GB)
+    # the 1M-token workload: 8,192 pairs x 16 heads, 21.5 GB (per-chunk records: 47.4 GB)
     assert ws(1, 1 << 20, 1, 16, 128, 128, 64, 1, 0) == 8192 * 16 * PREC
     assert ws(1, 1 << 20, 1, 16, 128, 128, 64, 1, 0) < 24e9
     # per-chunk records: B * ceil(T / 64), or floor(T / 64) + N, chunk slots per head
@@ -105,7 +105,7 @@ def test_workspace_bytes(lib):
 def test_chunk_records_flag_needs_the_records_size(lib):
     """KDA_FWD_CHUNK_RECORDS keeps one record per chunk: a workspace of the
     pair-record size is too small for it (T = 4096: 64 chunk records of
-    131,584 B against 32 pair records of 164,352 B)."""
+    180,736 B against 32 pair records of 164,352 B)."""
     p = ctypes.c_void_p
     PREC_ALL = lib.kda_chunk_fwd_workspace_bytes(1, 4096, 1, 1, 128, 128, 64, 1, 0)
     REC_ALL = lib.kda_chunk_fwd_records_bytes(1, 4096, 1, 1, 128, 128, 64, 1, 0)
