@@ -245,7 +245,7 @@ __device__ __forceinline__ f32x4 f4(const bf16x4 &x)
     return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
 }
 
-// LDS of the gradient kernel, by phase (see the kernel): 151,296 bytes, one
+// LDS of the gradient kernel, by phase (see the kernel): 153,344 bytes, one
 // workgroup per CU.
 struct GradSmem {
     union {
@@ -261,11 +261,17 @@ struct GradSmem {
             bf16 DX[kChunk][kXL];         // T^T dW   [token][dk]
             bf16 DY[kChunk][kXL];         // T^T dU   [token][dv]
             float dA[kChunk][kAL];
+            float dPT[kChunk][kAL];       // dP^T
         } x;
     } a;
-    bf16 DO[kChunk][kXL];                 // dO = dY sigmoid(Z)   [token][dv]
-    bf16 U[kChunk][kXL];                  // U = U~ - W S
-    bf16 DU[kChunk][kXL];                 // dU
+    union {
+        struct {                          // phases 1 to 3
+            bf16 DO[kChunk][kXL];         // dO = dY sigmoid(Z)   [token][dv]
+            bf16 U[kChunk][kXL];          // U = U~ - W S
+            bf16 DU[kChunk][kXL];         // dU
+        } d;
+        float dAbT[kChunk][kAL];          // phases 4, 5: (diag(beta) dA)^T
+    } d;
     union {
         bf16 KP[kChunk][kXL];             // K' = K e^{Ge - G} (phase 1)
         float dP[kChunk][kAL];            // phases 2 to 5
@@ -456,8 +462,8 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             }
             if (ok)
                 gstore(oz, roff(t), dz4);
-            *reinterpret_cast<bf16x4 *>(&smp->DO[16 * t + m][c0]) = do4;
-            *reinterpret_cast<bf16x4 *>(&smp->U[16 * t + m][c0]) = bf4(u[t]);
+            *reinterpret_cast<bf16x4 *>(&smp->d.d.DO[16 * t + m][c0]) = do4;
+            *reinterpret_cast<bf16x4 *>(&smp->d.d.U[16 * t + m][c0]) = bf4(u[t]);
         }
     }
     __syncthreads();
@@ -479,7 +485,7 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                doa[s][i] = smp->DO[16 * s + 4 * b + i][16 * w + m];
+                doa[s][i] = smp->d.d.DO[16 * s + 4 * b + i][16 * w + m];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
@@ -491,7 +497,7 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                 a = mfma16k16(doa[s],
                               *reinterpret_cast<const bf16x4 *>(&smp->t.PT[16 * t + m][16 * s + 4 * b]),
                               a);
-            *reinterpret_cast<bf16x4 *>(&smp->DU[16 * t + m][c0]) = bf4(a);
+            *reinterpret_cast<bf16x4 *>(&smp->d.d.DU[16 * t + m][c0]) = bf4(a);
         }
     }
     __syncthreads();
@@ -510,9 +516,9 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
         for (int ks = 0; ks < 4; ++ks) {
             const int kc = 32 * ks + 8 * b;
             const bf16x8 srow = lds8(&smp->a.s.Sb[16 * w + m][kc]);
-            a1 = mfma16(srow, lds8(&smp->DO[16 * t + m][kc]), a1);
-            a2 = mfma16(lds8(&smp->a.s.dSb[16 * w + m][kc]), lds8(&smp->U[16 * t + m][kc]), a2);
-            a3 = mfma16(lds8(&smp->DU[16 * t + m][kc]), srow, a3);
+            a1 = mfma16(srow, lds8(&smp->d.d.DO[16 * t + m][kc]), a1);
+            a2 = mfma16(lds8(&smp->a.s.dSb[16 * w + m][kc]), lds8(&smp->d.d.U[16 * t + m][kc]), a2);
+            a3 = mfma16(lds8(&smp->d.d.DU[16 * t + m][kc]), srow, a3);
         }
         dwa[t] = bf4(-a3);
 #pragma unroll
@@ -541,21 +547,29 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
         if (b == 0)
             smp->dgeD[16 * w + m] = gload<float>(rf, kOffDEC + 4 * (16 * w + m)) * pr;
     }
-    // dP = lower_incl(dO U^T), 16 x 16 blocks
-    for (int nb = 0; nb < (w < 2 ? 2 : 1); ++nb) {
+    // dP = lower_incl(dO U^T), 16 x 16 blocks; the blocks stay in registers
+    // for their transposed copy (phase 3: its space is still in use)
+    f32x4 dpb[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        dpb[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (nb == 1 && w >= 2)
+            break;
         int I, J;
         lower_block(w, nb, I, J);
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kc = 32 * ks + 8 * b;
-            a = mfma16(lds8(&smp->DO[16 * I + m][kc]), lds8(&smp->U[16 * J + m][kc]), a);
+            a = mfma16(lds8(&smp->d.d.DO[16 * I + m][kc]), lds8(&smp->d.d.U[16 * J + m][kc]), a);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * I + 4 * b + i, col = 16 * J + m;
-            smp->p.dP[row][col] = (J < I || col <= row) ? a[i] : 0.f;
+            a[i] = (J < I || col <= row) ? a[i] : 0.f;
+            smp->p.dP[row][col] = a[i];
         }
+        dpb[nb] = a;
     }
     {
         // T^T into P^T's space (P^T was last read before the previous barrier)
@@ -569,13 +583,23 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
     // ---- phase 3: dQr (dq complete); dX^T = dW^T T (key block w) and
     // dY~^T = dU^T T (value block w), row layout; dv = beta dY~, dKs = beta dX
     float pb[4] = {0.f, 0.f, 0.f, 0.f};     // dbeta terms of the lane's tokens, its 4 channels
+    // dP^T: block element (row 16 I + 4 b + i, column 16 J + m) of the lane is
+    // element i of the transposed row 16 J + m (one 16-byte store)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        if (nb == 1 && w >= 2)
+            break;
+        int I, J;
+        lower_block(w, nb, I, J);
+        *reinterpret_cast<f32x4 *>(&smp->a.x.dPT[16 * J + m][16 * I + 4 * b]) = dpb[nb];
+    }
     {
         bf16x4 dua[4], vv[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                dua[s][i] = smp->DU[16 * s + 4 * b + i][16 * w + m];
+                dua[s][i] = smp->d.d.DU[16 * s + 4 * b + i][16 * w + m];
             vv[s] = gload<bf16x4>(gv_, roff(s));
         }
 #pragma unroll
@@ -645,7 +669,6 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             }
             if (16 * I + m < len)
                 gstore(oq, roff(I), bf4(aq[I]));
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();
@@ -664,18 +687,24 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             a = mfma16(perm8(&smp->a.x.DX[16 * I + m][0], ks, b), wfr, a);
             a = mfma16(perm8(&smp->a.x.DY[16 * I + m][0], ks, b), ufr, a);
         }
+        f32x4 bt;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * I + 4 * b + i, col = 16 * J + m;
-            smp->a.x.dA[row][col] = (J < I || col < row) ? -a[i] : 0.f;
+            const float x = (J < I || col < row) ? -a[i] : 0.f;
+            smp->a.x.dA[row][col] = x;
+            bt[i] = smp->beta[row] * x;
         }
+        *reinterpret_cast<f32x4 *>(&smp->d.dAbT[16 * J + m][16 * I + 4 * b]) = bt;
     }
     __syncthreads();
 
     smp = reinterpret_cast<GradSmem *>(smem_raw + opaque_zero());
     // ---- phase 5: the products over tokens with the blocks of dA (and dP for
     // the column gradients), fp32, as in phase 3.  Block (I, J) takes the row
-    // factors K_I e^{G_I - B_J}, q_I e^{G_I - B_J} for the column gradients.
+    // factors K_I e^{G_I - B_J}, q_I e^{G_I - B_J} for the column gradients;
+    // their operands (diag(beta) dA)^T and dP^T are read as rows of the
+    // transposed copies.
     {
         bf16x4 ka[4], qa[4];
         f32x4 Ga[4];
@@ -708,7 +737,6 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                 aG[I][i] += kr * br * az[i];
                 pb[I] += kr * az[i];
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         // column gradients: dKc^T = ((beta dA)^T Kr + dP^T Qr)^T for column tile J
 #pragma unroll
@@ -716,14 +744,14 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int I = J; I < 4; ++I) {
+                const f32x4 ab = *reinterpret_cast<const f32x4 *>(&smp->d.dAbT[16 * J + m][16 * I + 4 * b]);
+                const f32x4 pt = *reinterpret_cast<const f32x4 *>(&smp->a.x.dPT[16 * J + m][16 * I + 4 * b]);
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const int r = 16 * I + 4 * b + kk;
                     const float e = __expf(Ga[I][kk] - Ba[J]);
-                    a = mfma4_f32((float)ka[I][kk] * e, smp->beta[r] * smp->a.x.dA[r][16 * J + m], a);
-                    a = mfma4_f32(scale * (float)qa[I][kk] * e, smp->p.dP[r][16 * J + m], a);
+                    a = mfma4_f32((float)ka[I][kk] * e, ab[kk], a);
+                    a = mfma4_f32(scale * (float)qa[I][kk] * e, pt[kk], a);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
             const f32x4 Bj = ref4(*smp, J, c0);
 #pragma unroll
@@ -732,7 +760,6 @@ __global__ __launch_bounds__(kGThreads) void kda_grad_bf16_kernel(
                 ak[J][i] += eBG * a[i];
                 aG[J][i] -= (float)kv[J][i] * eBG * a[i];
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
