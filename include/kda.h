@@ -106,8 +106,9 @@ int kda_decode_step_supported(kda_dtype dt, int dk, int dv);
  * (floor(T / 128) + N) H with cu_seqlens; 21.5 GB for 2^20 tokens x 16 heads).
  * Calls that keep per-chunk records instead (KDA_FWD_CHUNK_RECORDS, or a
  * snapshot interval that is an odd multiple of 64) need
- * kda_chunk_fwd_records_bytes(...): one 131,584-byte record per
- * (chunk, head), 2,056 bytes per token-head. */
+ * kda_chunk_fwd_records_bytes(...): one 180,736-byte record per
+ * (chunk, head), 2,824 bytes per token-head (the chunk's map and readout,
+ * and the intra-chunk factors the backward's gradient kernel reads). */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv, int chunk,
                                      kda_dtype dt, int varlen);
 size_t kda_chunk_fwd_records_bytes(int B, int T, int N, int H, int dk, int dv, int chunk,

@@ -219,7 +219,7 @@ def test_chunk_fwd_snapshots_rejects_bad_arguments(lib):
     assert call(1, 100) == SHAPE
     assert call(1, 0) == SHAPE
     # an interval of 64 or 192 tokens falls inside a pair of chunks: per-chunk
-    # records (4 x 131,584 B here); multiples of 128 need the pair records
+    # records (4 x 180,736 B here); multiples of 128 need the pair records
     assert REC > PREC
     assert call(1, 64, ws_bytes=REC - 1) == WS
     assert call(1, 192, ws_bytes=PREC) == WS
