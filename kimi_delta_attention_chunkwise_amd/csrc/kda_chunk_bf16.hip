@@ -84,6 +84,11 @@ struct PrepSmem {
 };
 static_assert(sizeof(PrepSmem) <= 160 * 1024, "prep LDS fits one CU");
 
+// the backward's dO^T tile ([dv][token], kColLd stride) overlays KCD and F
+static_assert(offsetof(PrepSmem, F) + sizeof(PrepSmem::F) - offsetof(PrepSmem, KCD) >=
+                  sizeof(bf16) * kDV * kColLd,
+              "dO^T fits in KCD and F");
+
 struct TSmem {                    // overlays KR after phase 2
     float TM[kChunk][kALd];
 };
@@ -127,6 +132,8 @@ struct PrepTask {
     int len;                         // tokens in the chunk, 1 .. 64
     int64_t tok0;                    // first token
     int64_t rec;                     // record index: slot * H + h
+    int64_t brec;                    // backward record index: the chunk's slot mirrored
+                                     // within its sequence (see the backward), * H + h
 };
 
 __device__ __forceinline__ PrepTask prep_task(const int32_t *cu, int N, int T, int H, int64_t t)
@@ -141,10 +148,12 @@ __device__ __forceinline__ PrepTask prep_task(const int32_t *cu, int N, int T, i
     pt.valid = slot_to_chunk(cu, N, T, slot, n, j);
     pt.len = 0;
     pt.tok0 = 0;
+    pt.brec = 0;
     if (pt.valid) {
         const SeqInfo si = seq_info(cu, n, T, kChunk);
         pt.tok0 = si.bos + j * kChunk;
         pt.len = (int)((si.len - j * kChunk) < kChunk ? (si.len - j * kChunk) : kChunk);
+        pt.brec = (si.slot0 + (si.len + kChunk - 1) / kChunk - 1 - j) * H + pt.h;
     }
     return pt;
 }
@@ -189,20 +198,30 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const bf16 *q, const bf16 
 //      and its readout from the pair's entry state (QH1, O01).
 // kExt (mode 0 in a per-chunk record, never in a pair record): also the
 // record's extension XW, XU, XT, XP for the gradient kernel.
+// kBwd (with kExt): also the chunk's backward record at brec (LN = -L^T,
+// BM = Q^^T dO with dO = dY sigmoid(Z), DEC), what the backward prep kernel
+// would form from the forward record.
 struct PairHold {
     bf16x8 nl0[4];                   // -L0, column block of the wave, 4 k-steps of rows
     bf16x8 bm0[4];                   // Bm0, the same layout
 };
 
-template <bool kPro, int kMode, bool kExt = false>
+// Operands of the fused backward record (kBwd).
+struct BwdOut {
+    const bf16 *gate, *dout;         // Z and dY  [.., H, dv]
+    uint8_t *rec;                    // the chunk's backward record
+};
+
+template <bool kPro, int kMode, bool kExt = false, bool kBwd = false>
 __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, const bf16 *q,
                                            const bf16 *k, const bf16 *v, const bf16 *g,
                                            const bf16 *beta, const PrepTask &pt,
                                            const PrepTask &next, bool load_next, int H,
                                            float scale, unsigned pro, uint8_t *rec,
-                                           PairHold &hold)
+                                           PairHold &hold, BwdOut bo = BwdOut{})
 {
     static_assert(!kExt || kMode == 0, "the extension belongs to per-chunk records");
+    static_assert(!kBwd || kExt, "the backward record comes with a per-chunk record");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, b = lane >> 4;
@@ -294,7 +313,11 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
             sm.F[4][ch] = __expf(b3 - b1);
             sm.F[5][ch] = __expf(b3 - b2);
             if constexpr (kMode == 0)
+            {
                 reinterpret_cast<float *>(rec + kOffDEC)[ch] = __expf(ge);
+                if constexpr (kBwd)
+                    reinterpret_cast<float *>(bo.rec + kOffDEC)[ch] = __expf(ge);
+            }
             else if constexpr (kMode == 1)
                 sm.DEC0[ch] = __expf(ge);    // read by chunk 1 of the pair (same lane) and its phase 5
             else
@@ -457,6 +480,17 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
     if (load_next)
         prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 2);
     // ---- phase 4: W = T X and U~ = T V for the wave's 16 channels --------------
+    // (kBwd) dY and Z of token tid / 8, channels 16 (tid % 8) .. + 15, for dO
+    bf16x8 dyb[2], zb[2];
+    if constexpr (kBwd) {
+        const int r = tid >> 3, cb = 16 * (tid & 7);
+        const int64_t off = ((pt.tok0 + (r < pt.len ? r : pt.len - 1)) * H + pt.h) * (int64_t)kDV + cb;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            dyb[p] = *reinterpret_cast<const bf16x8 *>(bo.dout + off + 8 * p);
+            zb[p] = *reinterpret_cast<const bf16x8 *>(bo.gate + off + 8 * p);
+        }
+    }
     const int nt = wave;                       // channels 16 nt .. 16 nt + 15
     f32x4 accW[4], accU[4];
     {
@@ -518,6 +552,22 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
 
     if (load_next)
         prep_load_token(in, q, k, v, g, beta, next, H, wave, tg, cq, 3);
+    // (kBwd) dO^T = (dY sigmoid(Z))^T [dv][token] in KCD's space (free since phase
+    // 2); the 8-token group of row c sits at group ^ ((c >> 4) & 7), so that the
+    // rows 16 apart that one wave writes at once fall in different LDS banks
+    bf16 (*const dot)[kColLd] = reinterpret_cast<bf16 (*)[kColLd]>(&sm.KCD[0][0]);
+    if constexpr (kBwd) {
+        const int r = tid >> 3, cb = 16 * (tid & 7);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = cb + 8 * p + e;
+                const float x = r < pt.len ? (float)dyb[p][e] * sigmoidf_((float)zb[p][e]) : 0.f;
+                dot[c][8 * ((r >> 3) ^ ((c >> 4) & 7)) + (r & 7)] = (bf16)x;
+            }
+        __syncthreads();
+    }
     if constexpr (kMode == 2) {
         // every wave is past phase 4: the A / T, X and V tiles are free for the
         // composition operands below
@@ -551,6 +601,18 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
                     for (int ks = 0; ks < 2; ++ks) {
                         l = mfma16(wf[ks], kpf[ks], l);
                         bm = mfma16(kpf[ks], uf[ks], bm);
+                    }
+                    if constexpr (kBwd) {
+                        // -L^T fragment (row tile nt, k-step mt / 2), elements
+                        // 4 (mt % 2) .. + 3: the same bf16 values as the -L stored
+                        // above, transposed exactly (a product with the identity)
+                        bf16x4 id;
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            id[e] = (bf16)(4 * b + e == m ? 1.f : 0.f);
+                        const f32x4 tr = mfma16k16(to_bf16x4(l, -1.f), id, f32x4{0.f, 0.f, 0.f, 0.f});
+                        *reinterpret_cast<bf16x4 *>(bo.rec + kOffLN + (nt * 4 + (mt >> 1)) * kFragBytes +
+                                                    lane * 16 + (mt & 1) * 8) = to_bf16x4(tr, 1.f);
                     }
                     *reinterpret_cast<bf16x4 *>(rec + kOffLN + (mt * 4 + kq) * kFragBytes +
                                                 lane * 16 + half * 8) = to_bf16x4(l, -1.f);
@@ -590,11 +652,39 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
                     }
                     *reinterpret_cast<bf16x4 *>(rec + kOffQH + (mt * 4 + kq) * kFragBytes +
                                                 lane * 16 + half * 8) = to_bf16x4(qh, -1.f);
+                    if constexpr (kBwd) {
+                        // Q^^T [dk][token] in XB's space (free since phase 4)
+                        const bf16x4 qv = to_bf16x4(qh, -1.f);
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            sm.XB[16 * nt + 4 * b + i][16 * mt + m] = qv[i];
+                    }
                     o0v[s2] = o0;
                 }
                 const bf16x4 a0 = to_bf16x4(o0v[0], 1.f), a1 = to_bf16x4(o0v[1], 1.f);
                 *reinterpret_cast<bf16x8 *>(rec + kOffO0 + nt * 2048 + tp * 1024 + lane * 16) =
                     bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            }
+        }
+        if constexpr (kBwd) {
+            // Q^^T dO for value block nt, in the record's Bm layout (fragment i2
+            // holds dk row tiles 2 i2 and 2 i2 + 1), from the Q^^T and dO^T tiles
+            __syncthreads();
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+                f32x4 acc[2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int t = 2 * i2 + s2;
+                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        a = mfma16(lds8(&sm.XB[16 * t + m][32 * ks + 8 * b]),
+                                   lds8(&dot[16 * nt + m][8 * ((4 * ks + b) ^ nt)]), a);
+                    acc[s2] = a;
+                }
+                *reinterpret_cast<bf16x8 *>(bo.rec + kOffBM + nt * 4096 + i2 * 1024 + lane * 16) =
+                    acc_to_frag(acc[0], acc[1]);
             }
         }
         if constexpr (kExt) {
@@ -784,12 +874,16 @@ __device__ __forceinline__ void pair_tasks(const int32_t *cu, int N, int T, int 
 // of the next chunk are loaded into registers while the current one is in its
 // matrix phases, so only the first chunk of a workgroup waits for memory.
 // kPair: a task is a pair of chunks (see kPairRecBytes), else one chunk.
-template <bool kPro, bool kPair>
+// kBwd (per-chunk records only): also every chunk's backward record in ws_b,
+// from the gate logits and dY.
+template <bool kPro, bool kPair, bool kBwd = false>
 __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ g, const bf16 *__restrict__ beta, const int32_t *__restrict__ cu,
-    int N, int T, int H, int64_t n_tasks, float scale, unsigned pro, uint8_t *__restrict__ ws)
+    int N, int T, int H, int64_t n_tasks, float scale, unsigned pro, uint8_t *__restrict__ ws,
+    const bf16 *__restrict__ gate, const bf16 *__restrict__ dout, uint8_t *__restrict__ ws_b)
 {
+    static_assert(!kBwd || (!kPair && !kPro), "the fused backward record needs per-chunk records");
     extern __shared__ __align__(16) uint8_t smem_raw[];
     PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
     TSmem &ts = *reinterpret_cast<TSmem *>(smem_raw);
@@ -814,8 +908,10 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_bf16_kernel(
                     prep_load(in, q, k, v, g, beta, next, H, wave, tg, cq);
                 continue;
             }
-            prep_chunk<kPro, 0, true>(sm, ts, in, q, k, v, g, beta, pt, next, load_next, H, scale,
-                                      pro, ws + pt.rec * (int64_t)kChunkRecBytes, hold);
+            prep_chunk<kPro, 0, true, kBwd>(
+                sm, ts, in, q, k, v, g, beta, pt, next, load_next, H, scale, pro,
+                ws + pt.rec * (int64_t)kChunkRecBytes, hold,
+                BwdOut{gate, dout, kBwd ? ws_b + pt.brec * (int64_t)kChunkRecBytes : nullptr});
         }
     } else {
         PrepTask c0, c1;
@@ -1267,25 +1363,30 @@ namespace {
 // Persistent prep over every (slot, head) task, a slot being a chunk or a pair
 // of chunks (pair): one workgroup per CU (its LDS allows no more), a multiple
 // of 8 of them.
-template <bool kPro, bool kPair> hipError_t prep_attr()
+template <bool kPro, bool kPair, bool kBwd = false> hipError_t prep_attr()
 {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(kda_prep_bf16_kernel<kPro, kPair>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PrepSmem));
+    return hipFuncSetAttribute(
+        reinterpret_cast<const void *>(kda_prep_bf16_kernel<kPro, kPair, kBwd>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PrepSmem));
 }
 
 // The persistent prep over n_slots * H tasks on one workgroup per CU (at most
 // max_grid workgroups when it is positive, rounded down to a multiple of 8 so
 // that task t still runs on XCD t % 8).
+// gate, dout, ws_b: per-chunk records (pair = false, pro = 0) that also write
+// every chunk's backward record to ws_b (see kda_prep_bf16_kernel); NULL for none.
 hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *g,
                        const bf16 *beta, const int32_t *cu, int N, int T, int H, int64_t n_slots,
                        float scale, unsigned pro, uint8_t *ws, hipStream_t stream, bool pair,
-                       int max_grid = 0)
+                       int max_grid = 0, const bf16 *gate = nullptr, const bf16 *dout = nullptr,
+                       uint8_t *ws_b = nullptr)
 {
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(attr_once, [] {
         for (hipError_t e : {prep_attr<false, false>(), prep_attr<true, false>(),
-                             prep_attr<false, true>(), prep_attr<true, true>()})
+                             prep_attr<false, true>(), prep_attr<true, true>(),
+                             prep_attr<false, false, true>()})
             if (e != hipSuccess && attr_err == hipSuccess)
                 attr_err = e;
     });
@@ -1305,18 +1406,28 @@ hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *
     const int64_t n_tasks = n_slots * H;
     const dim3 grid((unsigned)(n_tasks < prep_grid ? n_tasks : prep_grid));
     const size_t lds = sizeof(PrepSmem);
-    if (pro && pair)
+    if (ws_b) {
+        if (pro || pair || !gate || !dout)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL((kda_prep_bf16_kernel<false, false, true>), grid, dim3(kPrepThreads),
+                           lds, stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, 0u, ws, gate,
+                           dout, ws_b);
+    } else if (pro && pair)
         hipLaunchKernelGGL((kda_prep_bf16_kernel<true, true>), grid, dim3(kPrepThreads), lds,
-                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, pro, ws);
+                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, pro, ws, nullptr,
+                           nullptr, nullptr);
     else if (pro)
         hipLaunchKernelGGL((kda_prep_bf16_kernel<true, false>), grid, dim3(kPrepThreads), lds,
-                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, pro, ws);
+                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, pro, ws, nullptr,
+                           nullptr, nullptr);
     else if (pair)
         hipLaunchKernelGGL((kda_prep_bf16_kernel<false, true>), grid, dim3(kPrepThreads), lds,
-                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, 0u, ws);
+                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, 0u, ws, nullptr,
+                           nullptr, nullptr);
     else
         hipLaunchKernelGGL((kda_prep_bf16_kernel<false, false>), grid, dim3(kPrepThreads), lds,
-                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, 0u, ws);
+                           stream, q, k, v, g, beta, cu, N, T, H, n_tasks, scale, 0u, ws, nullptr,
+                           nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -1711,12 +1822,11 @@ hipError_t launch_chunk_bwd_bf16(const bf16 *q, const bf16 *k, const bf16 *v, co
             e = launch_chain(dfinal, dinit, nullptr, 0, cu, N, T, H, ws_b, stream, false);
     } else {
         // The state-gradient recurrence needs the forward records but not the
-        // forward states, and the chain writes only SB, which the backward prep
-        // does not read: after both preps one launch runs the forward chain
+        // forward states, and the chain writes only SB: the prep writes the
+        // backward records too, and then one launch runs the forward chain
         // (every chunk's entry state) and the backward chain side by side.
-        e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, 0u, ws_f, stream, false);
-        if (e == hipSuccess)
-            e = launch_bwd_prep_bf16(gate, dout, cu, N, T, H, n_slots, ws_f, ws_b, stream);
+        e = launch_prep(q, k, v, g, beta, cu, N, T, H, n_slots, scale, 0u, ws_f, stream, false, 0,
+                        gate, dout, ws_b);
         if (e == hipSuccess)
             e = launch_chain_two(init, ws_f, dfinal, dinit, ws_b, cu, N, T, H, stream);
     }

@@ -183,19 +183,6 @@ __device__ __forceinline__ float row_bcast(float x)
         __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + kS, 0xf, 0xf, false));
 }
 
-// D += A B with a 16-wide k: lane (b, m) gives A[m][4 b + e] and B[4 b + e][m]
-// (e = 0..3).  Issued as the 16x16x32 product with elements 4..7 of both
-// operands zero (k = 8 b + e then stands for 4 b + e on both sides), so that
-// every bf16 matrix instruction of the kernel has one shape: a 16x16x16
-// accumulating directly onto a chain of 16x16x32 products has been seen to
-// read part of its accumulator input stale on gfx950.
-__device__ __forceinline__ f32x4 mfma16k16(const bf16x4 &a, const bf16x4 &b, const f32x4 &c)
-{
-    const bf16 z = (bf16)0.f;
-    return mfma16(bf16x8{a[0], a[1], a[2], a[3], z, z, z, z},
-                  bf16x8{b[0], b[1], b[2], b[3], z, z, z, z}, c);
-}
-
 __device__ __forceinline__ bf16x4 bf4(const f32x4 &x)
 {
     return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};

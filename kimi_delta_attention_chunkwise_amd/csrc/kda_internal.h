@@ -156,6 +156,19 @@ __device__ __forceinline__ bf16x8 acc_to_frag(const f32x4 &lo, const f32x4 &hi)
                   (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
 }
 
+// D += A B with a 16-wide k: lane (b, m) gives A[m][4 b + e] and B[4 b + e][m]
+// (e = 0..3).  Issued as the 16x16x32 product with elements 4..7 of both
+// operands zero (k = 8 b + e then stands for 4 b + e on both sides), so that
+// every bf16 matrix instruction of the kernel has one shape: a 16x16x16
+// accumulating directly onto a chain of 16x16x32 products has been seen to
+// read part of its accumulator input stale on gfx950.
+__device__ __forceinline__ f32x4 mfma16k16(const bf16x4 &a, const bf16x4 &b, const f32x4 &c)
+{
+    const bf16 z = (bf16)0.f;
+    return mfma16(bf16x8{a[0], a[1], a[2], a[3], z, z, z, z},
+                  bf16x8{b[0], b[1], b[2], b[3], z, z, z, z}, c);
+}
+
 // fp32 16x16x4: lane l gives A[l % 16][l / 16] and B[l / 16][l % 16]
 __device__ __forceinline__ f32x4 mfma4_f32(float a, float b, const f32x4 &c)
 {
