@@ -50,7 +50,6 @@
 #include "kda_internal.h"
 
 #include <mutex>
-#include <utility>
 
 namespace kda {
 

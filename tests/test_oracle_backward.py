@@ -5,7 +5,12 @@
   recompute segments, with varlen packing, an initial state and scale != 1;
 * Euler's identity: out and the final state are jointly linear in (v, S0), so
   <dL/dv, v> + <dL/dS0, S0> = L exactly;
-* the gate's closed form: dz = dout * out * (1 - sigmoid(z)).
+* the gate's closed form: dz = dout * out * (1 - sigmoid(z));
+* the chunk-level form (``oracle.chunkwise.backward``: entry states and exit
+  gradients per chunk, blockwise token products with block-start references)
+  equals the token-by-token backward, on ragged varlen packing with empty,
+  one-token and exactly-one-chunk sequences, a channel pinned at the gate
+  floor and a no-decay stretch.
 """
 from __future__ import annotations
 
@@ -13,6 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import chunkwise
 
 
 def case(seed, lengths, H, dk, dv, init=True):
@@ -89,3 +95,20 @@ def test_no_final_gradient_and_zero_init_are_defaults():
                          init_state=np.zeros((1, 1, 2, 2)), dfinal=np.zeros((1, 1, 2, 2)))
     for key in r:
         np.testing.assert_array_equal(r[key], r0[key])
+
+
+@pytest.mark.parametrize("chunk,sub", [(64, 16), (32, 8), (16, 16)])
+def test_chunk_level_form_equals_token_backward(chunk, sub):
+    lengths = [150, 0, 64, 1, 17, 65]
+    x, cu, s0, dy, df = case(20 + chunk, lengths, 2, 8, 6)
+    rng = np.random.default_rng(chunk)
+    x["g"] = rng.uniform(-5.0, 0.0, x["g"].shape)
+    x["g"][20:110, 1, 3] = -5.0                   # a channel pinned at the floor
+    x["g"][160:190, 0, :] = 0.0                   # no decay
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], dy)
+    ref = oracle.backward(*args, init_state=s0, dfinal=df, cu_seqlens=cu, scale=0.8)
+    got = chunkwise.backward(*args, init_state=s0, dfinal=df, cu_seqlens=cu, chunk=chunk,
+                             sub=sub, scale=0.8)
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "dz", "dinit"):
+        err = np.max(np.abs(got[key] - ref[key])) / max(np.max(np.abs(ref[key])), 1e-30)
+        assert err < 1e-10, f"{key}: {err}"
