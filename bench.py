@@ -35,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -62,11 +63,22 @@ def flops_per_token_head(C=CHUNK, dk=DK, dv=DV):
     return 6 * dk * dv + (3 * C - 1) * dk + 2 * C * dv + C * C / 3.0
 
 
+# comments, string and character literals of C/C++ source
+_C_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def _code_only(text: str) -> str:
+    """The source with comments removed and whitespace runs collapsed, so that
+    an edit of a comment does not count as a change of the kernels."""
+    text = _C_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), text)
+    return " ".join(text.split())
+
+
 def source_digest(paths=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     for p in paths:
-        with open(p, "rb") as fh:
-            h.update(fh.read())
+        with open(p, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -11,10 +11,13 @@
 //     dS_j = (diag(dec) - L^T) dS_{j+1} + Q^^T dO_j,    dO = dY sigmoid(Z),
 // which is the same recurrence with L^T for L and Q^^T dO for Bm.  So:
 //   1. forward prep + chain: every chunk's entry state S_j (record SB);
-//   2. backward prep (here): records with -L^T, Q^^T dO and dec, stored in
-//      reverse chunk order, so that
-//   3. the unchanged chain kernel, started from dS_final, yields dS_{j+1} for
-//      every chunk (record SB) and dS_0;
+//   2. backward records with -L^T, Q^^T dO and dec, stored in reverse chunk
+//      order: written by the forward prep itself when the backward runs its
+//      own forward, or by the backward prep kernel (here) from the records of
+//      an earlier forward call, so that
+//   3. the same chain kernel, started from dS_final, yields dS_{j+1} for
+//      every chunk (record SB) and dS_0 (in one launch with step 1's chain
+//      when the backward runs its own forward);
 //   4. gradient kernel (here): one workgroup per (chunk, head) computes the
 //      chunk's gradients at chunk level from the forward record (Q^, O0, the
 //      entry state S and the per-chunk extension W, U~, T^T, P^T written by
