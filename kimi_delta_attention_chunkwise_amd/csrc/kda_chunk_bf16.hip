@@ -212,6 +212,21 @@ struct BwdOut {
     uint8_t *rec;                    // the chunk's backward record
 };
 
+// The two steps inside phase 1 exchange data only between lanes of one wave
+// (G at the subtile ends -> the wave's per-channel constants -> the wave's
+// operands), so a wave-level fence is enough; the q / k norms of the prologue
+// are summed over all waves and need the workgroup barrier.
+__device__ __forceinline__ void phase1_sync(bool across_waves)
+{
+    if (across_waves) {
+        __syncthreads();
+    } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
 template <bool kPro, int kMode, bool kExt = false, bool kBwd = false>
 __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, const bf16 *q,
                                            const bf16 *k, const bf16 *v, const bf16 *g,
@@ -292,7 +307,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
             for (int tt = 0; tt < 4; ++tt)
                 sm.AM[4 * tg + tt][kChunk] = br[tt];  // beta per row, for A
         }
-        __syncthreads();
+        phase1_sync(kPro && (pro & kProQK));
         if (lane < 16) {
             // per-channel constants of channel 16 w + lane
             const int ch = 16 * wave + lane;
@@ -323,7 +338,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
             else
                 reinterpret_cast<float *>(rec + kOffDEC)[ch] = sm.DEC0[ch] * __expf(ge);
         }
-        __syncthreads();
+        phase1_sync(kPro && (pro & kProQK));
         // prologue: 1 / |q| and 1 / |k| of the lane's rows (1 without it)
         f32x4 nq = {1.f, 1.f, 1.f, 1.f}, nk = {1.f, 1.f, 1.f, 1.f};
         if (kPro && (pro & kProQK)) {
