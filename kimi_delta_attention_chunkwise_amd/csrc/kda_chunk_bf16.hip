@@ -212,11 +212,12 @@ struct BwdOut {
     uint8_t *rec;                    // the chunk's backward record
 };
 
-// The two steps inside phase 1 exchange data only between lanes of one wave
-// (G at the subtile ends -> the wave's per-channel constants -> the wave's
-// operands), so a wave-level fence is enough; the q / k norms of the prologue
-// are summed over all waves and need the workgroup barrier.
-__device__ __forceinline__ void phase1_sync(bool across_waves)
+// A workgroup barrier when data passes between waves, else a wave-level fence
+// (LDS operations of one wave take effect in order).  Inside phase 1, G at the
+// subtile ends, the per-channel constants and the operands built from them
+// pass between lanes of one wave; only the q / k norms of the prologue are
+// summed over all waves.
+__device__ __forceinline__ void wave_or_group_sync(bool across_waves)
 {
     if (across_waves) {
         __syncthreads();
@@ -307,7 +308,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
             for (int tt = 0; tt < 4; ++tt)
                 sm.AM[4 * tg + tt][kChunk] = br[tt];  // beta per row, for A
         }
-        phase1_sync(kPro && (pro & kProQK));
+        wave_or_group_sync(kPro && (pro & kProQK));
         if (lane < 16) {
             // per-channel constants of channel 16 w + lane
             const int ch = 16 * wave + lane;
@@ -338,7 +339,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
             else
                 reinterpret_cast<float *>(rec + kOffDEC)[ch] = sm.DEC0[ch] * __expf(ge);
         }
-        phase1_sync(kPro && (pro & kProQK));
+        wave_or_group_sync(kPro && (pro & kProQK));
         // prologue: 1 / |q| and 1 / |k| of the lane's rows (1 without it)
         f32x4 nq = {1.f, 1.f, 1.f, 1.f}, nk = {1.f, 1.f, 1.f, 1.f};
         if (kPro && (pro & kProQK)) {
@@ -489,7 +490,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
             for (int i = 0; i < 4; ++i)
                 ts.TM[16 * a + 4 * b + i][16 * bb + m] = -Y[i];
         }
-        __syncthreads();
+        // wave bb reads and writes only column bb of T (besides the diagonal
+        // blocks, final since the barrier above), so only the last distance
+        // needs the workgroup barrier, before phase 4 reads all of T
+        wave_or_group_sync(dist == 3);
     }
 
     if (load_next)
