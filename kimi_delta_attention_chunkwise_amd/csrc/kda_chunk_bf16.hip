@@ -1354,7 +1354,8 @@ __global__ __launch_bounds__(kPair ? 512 : 256) void kda_output_bf16_kernel(
                 o = mfma16(sb_s[blk * 4 + ks][lane], qh[ks], o);
             *reinterpret_cast<f32x4 *>(&ot_s[t][m][16 * bb + 4 * b]) = o;
         }
-        __syncthreads();
+        // wave t alone writes and reads back ot_s[t]
+        wave_or_group_sync(false);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int r = 8 * p + rq;
@@ -1373,7 +1374,7 @@ __global__ __launch_bounds__(kPair ? 512 : 256) void kda_output_bf16_kernel(
                 __builtin_nontemporal_store(y, reinterpret_cast<bf16x8 *>(out + off));
             }
         }
-        __syncthreads();
+        wave_or_group_sync(false);
     }
 }
 
