@@ -19,7 +19,7 @@ namespace {
 static __device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
 static_assert(KDA_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch keeps records 256-byte aligned");
 
-constexpr int kScratchDevices = 64;
+constexpr int kScratchDevices = kda::kMaxDevices;
 std::mutex g_scratch_mutex;
 void *g_scratch_ptr[kScratchDevices];
 

@@ -1401,14 +1401,13 @@ hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *
                        int max_grid = 0, const bf16 *gate = nullptr, const bf16 *dout = nullptr,
                        uint8_t *ws_b = nullptr)
 {
-    static std::once_flag attr_once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(attr_once, [] {
+    const hipError_t attr_err = once_per_device<0>([]() -> hipError_t {
         for (hipError_t e : {prep_attr<false, false>(), prep_attr<true, false>(),
                              prep_attr<false, true>(), prep_attr<true, true>(),
                              prep_attr<false, false, true>()})
-            if (e != hipSuccess && attr_err == hipSuccess)
-                attr_err = e;
+            if (e != hipSuccess)
+                return e;
+        return hipSuccess;
     });
     if (attr_err != hipSuccess)
         return attr_err;
@@ -1456,7 +1455,6 @@ hipError_t launch_prep(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *
 // use, so that no workgroup of a kernel running beside it shares its CU (and
 // the CU's memory pipeline, which bounds the chain's step).
 constexpr int kChainOwnCuLds = 152 * 1024;   // static + reserved LDS per chain workgroup
-constexpr int kMaxDevices = 64;              // devices with per-device library state
 
 // Workgroups of the chain for `units` (sequence, head) units: units rounded up
 // to 8 (one per XCD), times the workgroups per unit.

@@ -807,12 +807,10 @@ hipError_t launch_bwd_prep_bf16(const bf16 *gate, const bf16 *dout, const int32_
                                 int T, int H, int64_t n_slots, const uint8_t *ws_f,
                                 uint8_t *ws_b, hipStream_t stream)
 {
-    static std::once_flag once;
-    static hipError_t err = hipSuccess;
-    std::call_once(once, [] {
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_bwd_prep_bf16_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)sizeof(BwdPrepSmem));
+    const hipError_t err = once_per_device<1>([]() -> hipError_t {
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(kda_bwd_prep_bf16_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)sizeof(BwdPrepSmem));
     });
     if (err != hipSuccess)
         return err;
@@ -829,12 +827,10 @@ hipError_t launch_grad_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const b
                             const int32_t *cu, int N, int T, int H, int64_t n_slots, float scale,
                             uint8_t *ws_f, const uint8_t *ws_b, hipStream_t stream)
 {
-    static std::once_flag once;
-    static hipError_t err = hipSuccess;
-    std::call_once(once, [] {
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_grad_bf16_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)sizeof(GradSmem));
+    const hipError_t err = once_per_device<2>([]() -> hipError_t {
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(kda_grad_bf16_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)sizeof(GradSmem));
     });
     if (err != hipSuccess)
         return err;

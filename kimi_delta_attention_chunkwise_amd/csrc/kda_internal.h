@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace kda {
 
 typedef __bf16 bf16;
@@ -338,6 +340,27 @@ hipError_t launch_chunk_bwd_bf16(const bf16 *q, const bf16 *k, const bf16 *v, co
                                  const int32_t *cu, int N, int T, int H, int64_t n_slots,
                                  float scale, void *fwd_records, void *workspace,
                                  hipStream_t stream);
+
+// Devices with per-device library state (kernel attributes, the second
+// stream of the long-sequence schedule, the static workspace).
+constexpr int kMaxDevices = 64;
+
+// Runs set() once per device, with that device current, and returns its
+// result to every call on that device (kSite tells the callers apart).  For
+// kernel attributes such as the dynamic LDS limit, which are set per device.
+template <int kSite> inline hipError_t once_per_device(hipError_t (*set)())
+{
+    static std::once_flag flag[kMaxDevices];
+    static hipError_t err[kMaxDevices];
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::call_once(flag[dev], [&] { err[dev] = set(); });
+    return err[dev];
+}
 
 // Backward records: for chunk j of a sequence with nch chunks, record
 // slot0 + nch - 1 - j of ws_b gets LN = -L^T, BM = Q^^T dO (dO = dY sigmoid(Z))
