@@ -372,12 +372,13 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
                 const float kv = ok ? (float)in.k[tt][c] * nk[tt] : 0.f;
                 const float qv = ok ? (float)in.q[tt][c] * nq[tt] : 0.f;
                 const float vv = ok ? (float)in.v[tt][c] : 0.f;
-                kr[c] = (bf16)(kv * fr);
+                const float kfr = kv * fr, kfc = kv * fc;
+                kr[c] = (bf16)kfr;
                 qr[c] = (bf16)(qv * fr);
-                kc[c] = (bf16)(kv * fc);
-                xb[c][tt] = (bf16)(br[tt] * kv * (fr * eb[c]));    // beta k e^G
+                kc[c] = (bf16)kfc;
+                xb[c][tt] = (bf16)(kfr * eb[c] * br[tt]);          // beta k e^G
                 vb[c][tt] = (bf16)(br[tt] * vv);                   // beta v
-                kp[c][tt] = (bf16)(kv * (egb[c] * fc));            // k e^{G_end - G}
+                kp[c][tt] = (bf16)(kfc * egb[c]);                  // k e^{G_end - G}
             }
             *reinterpret_cast<bf16x4 *>(&sm.KR[r][rq(r, ch0 >> 2)]) = kr;
             *reinterpret_cast<bf16x4 *>(&sm.QR[r][rq(r, ch0 >> 2)]) = qr;
@@ -651,9 +652,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
     #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const int mt = 2 * tp + s2;
+                    // P is lower triangular: token tiles 0 and 1 have no columns in k-step 1
                     bf16x8 pf[2];
     #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
+                    for (int ks = 0; ks <= (mt >> 1); ++ks)
                         pf[ks] = perm8(&sm.PM[16 * mt + m][0], ks, b);
                     // scale Q e^G at row 16 mt + m, channels 16 nt + 4 b .. + 3, from q e^{G - B_mt}
                     const bf16x4 qr =
@@ -665,7 +667,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
                         qh[i] = -scale * (float)qr[i] * eb[i];
                     f32x4 o0 = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
+                    for (int ks = 0; ks <= (mt >> 1); ++ks) {
                         qh = mfma16(wf[ks], pf[ks], qh);   // (P W)^T - (scale Q e^G)^T
                         o0 = mfma16(uf[ks], pf[ks], o0);   // (P U~)^T
                     }
@@ -777,7 +779,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
             for (int tt = 0; tt < 4; ++tt) {
                 bf16x8 pf[2];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
+                for (int ks = 0; ks <= (tt >> 1); ++ks)
                     pf[ks] = perm8(&sm.PM[16 * tt + m][0], ks, b);
                 const bf16x4 qr =
                     *reinterpret_cast<const bf16x4 *>(&sm.QR[16 * tt + m][rq(16 * tt + m, 4 * nt + b)]);
@@ -787,7 +789,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
                 for (int i = 0; i < 4; ++i)
                     qh[i] = -scale * (float)qr[i] * eb[i];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
+                for (int ks = 0; ks <= (tt >> 1); ++ks)
                     qh = mfma16(wf[ks], pf[ks], qh);      // -Q^1[16 tt + m][16 nt + 4 b + i]
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -834,11 +836,11 @@ __device__ __forceinline__ void prep_chunk(PrepSmem &sm, TSmem &ts, PrepIn &in, 
                     const int tt = 2 * tp + s2;
                     bf16x8 pf[2];
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
+                    for (int ks = 0; ks <= (tt >> 1); ++ks)
                         pf[ks] = perm8(&sm.PM[16 * tt + m][0], ks, b);
                     f32x4 accq = qd[tt], acco = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
+                    for (int ks = 0; ks <= (tt >> 1); ++ks)
                         acco = mfma16(uf[ks], pf[ks], acco);     // O0_1[16 tt + m][16 nt + 4 b + i]
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
