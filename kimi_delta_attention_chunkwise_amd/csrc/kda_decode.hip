@@ -77,10 +77,11 @@ __device__ __forceinline__ f32x4 write_row(const f32x4 &s, float kr, const f32x4
 }
 
 // The K draft tokens of a verification, on the state in registers: the
-// tokens are staged kVerifyGroup at a time (q, k and exp(g) in LDS, v, beta and
-// the gate logits in registers: one load phase per group), the reductions of
-// token t go to LDS buffer t & 1 (one barrier per token), and each token takes
-// exactly the arithmetic of a decode step.
+// tokens are staged kVerifyGroup at a time (q, k, exp(g), v, the gate logits
+// and beta in LDS: one load phase per group, and no token values held in
+// registers beside the state), the reductions of token t go to LDS buffer
+// t & 1 (one barrier per token), and each token takes exactly the arithmetic
+// of a decode step.
 constexpr int kVerifyGroup = 4;
 
 template <typename T, int DK, int DV, bool kPro>
@@ -95,6 +96,7 @@ __device__ __forceinline__ void verify_tokens(
     constexpr int kG = kVerifyGroup;
     static_assert(NT % 64 == 0, "whole waves");
     __shared__ float va[kG][DK], vk[kG][DK], vq[kG][DK];
+    __shared__ float vv[kG][DV], vz[kG][DV], vbeta[kG];
     __shared__ f32x4 red_p[2][RG][CG];
     __shared__ f32x4 red_s[2][RG][CG];
     __shared__ float red_kq[2][RG];
@@ -112,36 +114,26 @@ __device__ __forceinline__ void verify_tokens(
             vk[tt][c] = to_f32(k[row * DK + c]);
             vq[tt][c] = to_f32(q[row * DK + c]);
         }
-        float vb[kG][4], bx[kG], zb[kG][4];
-#pragma unroll
-        for (int tt = 0; tt < kG; ++tt) {
-            if (tt < nt) {
-                const int64_t row = row0 + (int64_t)tt * H;
-                bx[tt] = to_f32(beta[row]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    vb[tt][i] = to_f32(v[row * DV + 4 * cg + i]);
-                if (rg == 0) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        zb[tt][i] = to_f32(gate[row * DV + 4 * cg + i]);
-                }
-            }
+        for (int i = tid; i < nt * DV; i += NT) {
+            const int tt = i / DV, c = i % DV;
+            const int64_t row = row0 + (int64_t)tt * H;
+            vv[tt][c] = to_f32(v[row * DV + c]);
+            vz[tt][c] = to_f32(gate[row * DV + c]);
         }
+        if (tid < nt)
+            vbeta[tid] = to_f32(beta[row0 + (int64_t)tid * H]);
         __syncthreads();
 #pragma unroll
         for (int tt = 0; tt < kG; ++tt) {
             if (tt < nt) {
                 const int64_t row = row0 + (int64_t)tt * H;
                 const int par = (t0 + tt) & 1;
-                float kk[RPT];
                 f32x4 p = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
                 float kq = 0.f, k2 = 0.f, q2 = 0.f;
 #pragma unroll
                 for (int m = 0; m < RPT; ++m) {
                     const int r = rg + RG * m;
                     const float kr = vk[tt][r], qr = vq[tt][r];
-                    kk[m] = kr;
                     s_reg[m] = decay_row(s_reg[m], va[tt][r]);
                     p += s_reg[m] * kr;
                     sq += s_reg[m] * qr;
@@ -171,29 +163,32 @@ __device__ __forceinline__ void verify_tokens(
                     SQ += red_s[par][r][cg];
                     KQ += red_kq[par][r];
                 }
+                float ik = 1.f;
                 if (qk) {
-                    const float ik = inv_norm<RG>(red_k2[par]), iq = inv_norm<RG>(red_q2[par]);
+                    const float iq = inv_norm<RG>(red_q2[par]);
+                    ik = inv_norm<RG>(red_k2[par]);
                     P = P * ik;
                     SQ = SQ * iq;
                     KQ = __fmul_rn(__fmul_rn(KQ, ik), iq);
-#pragma unroll
-                    for (int m = 0; m < RPT; ++m)
-                        kk[m] = __fmul_rn(kk[m], ik);
                 }
-                const float b = (kPro && (pro & kProBeta)) ? sigmoidf_(bx[tt]) : bx[tt];
+                const float b = (kPro && (pro & kProBeta)) ? sigmoidf_(vbeta[tt]) : vbeta[tt];
+                const f32x4 vb = *reinterpret_cast<const f32x4 *>(&vv[tt][4 * cg]);
                 f32x4 u;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    u[i] = b * (vb[tt][i] - P[i]);
+                    u[i] = b * (vb[i] - P[i]);
 #pragma unroll
-                for (int m = 0; m < RPT; ++m)
-                    s_reg[m] = write_row(s_reg[m], kk[m], u);
+                for (int m = 0; m < RPT; ++m) {
+                    const float kr = vk[tt][rg + RG * m];
+                    s_reg[m] = write_row(s_reg[m], qk ? __fmul_rn(kr, ik) : kr, u);
+                }
                 if (rg == 0) {
+                    const f32x4 zb = *reinterpret_cast<const f32x4 *>(&vz[tt][4 * cg]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int c = 4 * cg + i;
                         const float o = scale * (SQ[i] + KQ * u[i]);
-                        out[row * DV + c] = from_f32<T>(sigmoidf_(zb[tt][i]) * o);
+                        out[row * DV + c] = from_f32<T>(sigmoidf_(zb[i]) * o);
                     }
                     if (u_out)
                         *reinterpret_cast<f32x4 *>(u_out + row * DV + 4 * cg) = u;
