@@ -1775,9 +1775,20 @@ hipError_t launch_chunk_bf16(const bf16 *q, const bf16 *k, const bf16 *v, const 
                     e = hipEventRecord(aux->pseg[s], stream);
                 if (e == hipSuccess)
                     e = hipStreamWaitEvent(aux->stream, aux->pseg[s], 0);
-                if (e == hipSuccess)
-                    e = launch_chain_own4(s == 0 ? init : final_state, final_state, c.Ts, H, c.ws,
-                                          aux->stream, pair);
+                if (e == hipSuccess) {
+                    // the last segment's chain has no prep beside it, only the
+                    // outputs of the segment before, and bounds the end of the
+                    // call: workgroups of 2 value blocks (twice the CUs, each
+                    // still to itself) walk it faster than those of 4
+                    if (s + 1 == nseg)
+                        e = (pair ? launch_chain_nb<2, true>
+                                  : launch_chain_nb<2, false>)(
+                            s == 0 ? init : final_state, final_state, nullptr, 1, c.Ts, H, c.ws,
+                            aux->stream, true, ChainJob2{});
+                    else
+                        e = launch_chain_own4(s == 0 ? init : final_state, final_state, c.Ts, H,
+                                              c.ws, aux->stream, pair);
+                }
                 if (e == hipSuccess)
                     e = hipEventRecord(aux->seg[s], aux->stream);
             }
