@@ -97,7 +97,7 @@ def test_no_final_gradient_and_zero_init_are_defaults():
         np.testing.assert_array_equal(r[key], r0[key])
 
 
-@pytest.mark.parametrize("chunk,sub", [(64, 16), (32, 8), (16, 16)])
+@pytest.mark.parametrize("chunk,sub", [(64, 16), (32, 8), (16, 16), (16, 4)])
 def test_chunk_level_form_equals_token_backward(chunk, sub):
     lengths = [150, 0, 64, 1, 17, 65]
     x, cu, s0, dy, df = case(20 + chunk, lengths, 2, 8, 6)
