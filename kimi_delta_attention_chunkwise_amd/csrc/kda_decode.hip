@@ -233,10 +233,18 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     const int cg = tid % CG, rg = tid / CG;
     float *S = state + unit * (int64_t)(DK * DV);
 
+    // A verification only reads the slice, and nontemporal loads stream it past
+    // the caches (4% faster there); the step, which writes the slice back in
+    // place, loads it plainly (nontemporal loads made it about 15% slower).
     f32x4 s_reg[RPT];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m)
-        s_reg[m] = *reinterpret_cast<const f32x4 *>(S + (rg + RG * m) * DV + 4 * cg);
+    for (int m = 0; m < RPT; ++m) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(S + (rg + RG * m) * DV + 4 * cg);
+        if constexpr (kVerify)
+            s_reg[m] = __builtin_nontemporal_load(src);
+        else
+            s_reg[m] = *src;
+    }
     if constexpr (kVerify) {
         verify_tokens<T, DK, DV, kPro>(q, k, v, g, beta, gate, out, u_out, s_reg, n, h, K, H,
                                        scale, pro, tid);
