@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     float *S = state + unit * (int64_t)(DK * DV);
 
     // A verification only reads the slice, and nontemporal loads stream it past
-    // the caches (4% faster there); the step, which writes the slice back in
+    // the caches (about 5% faster there); the step, which writes the slice back in
     // place, loads it plainly (nontemporal loads made it about 15% slower).
     f32x4 s_reg[RPT];
 #pragma unroll
